@@ -1,0 +1,148 @@
+#!/usr/bin/env python3
+"""Decode-throughput benchmark of the gated-DeltaNet stack on one MI355X.
+
+A step is one decode token through the whole stack (every layer: in_proj GEMV, conv + SiLU,
+L2 norms, decay, delta rule, readout, gated RMSNorm, out_proj GEMV). The default workload is 30
+independent layers at the hybrid-35B DeltaNet shape (d_model 2048, 16 key heads x 128, 32 value
+heads x 128, int8 weights with per-row fp32 scales, fp32 32x128x128 state per layer), single
+sequence, 200 tokens, synthetic seeded inputs already resident in HBM.
+
+Prints ONE JSON line. Bytes per step = quantised weights + fp32 scales + conv taps + norm weight
++ 2 x fp32 state, over all layers.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="stack", choices=["stack", "stack_int4", "layer", "batched"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the decode step of one stack "
+                                   "is measured on a single MI355X (--gpus 1)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dn_inputs as gi
+    import gated_deltanet_layer_dn_amd as dn
+
+    cfg = gi.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    t0 = time.time()
+    layers, stream = gi.generate(cfg)
+    log(f"[bench] generated {cfg.name}: L={cfg.n_layers} B={cfg.batch} T={cfg.n_tokens} in {time.time() - t0:.1f}s")
+
+    st = dn.DeltaNetStack.from_config(cfg, layers)
+    S0 = np.ascontiguousarray(np.stack([l.S0 for l in layers]))
+    R0 = np.ascontiguousarray(np.stack([l.ring0 for l in layers]))
+    S0d = torch.from_numpy(S0).to(dev)
+    R0d = torch.from_numpy(R0).to(dev)
+    st.set_state(S0d, R0d)
+    x = torch.from_numpy(np.ascontiguousarray(stream.x)).to(dev)
+    al = torch.from_numpy(np.ascontiguousarray(stream.alpha)).to(dev)
+    be = torch.from_numpy(np.ascontiguousarray(stream.beta)).to(dev)
+    T = cfg.n_tokens
+    outs = torch.empty((max(args.steps, 1), cfg.n_layers, cfg.batch, cfg.d_model), dtype=torch.float32, device=dev)
+    scratch_out = st.new_out()
+
+    # warmup, then restart from the initial state so the timed run is the workload itself
+    for i in range(args.warmup):
+        t = i % T
+        st.step(x[t], al[t], be[t], scratch_out)
+    torch.cuda.synchronize()
+    st.set_state(S0d, R0d)
+    torch.cuda.synchronize()
+
+    stream_t = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream_t)
+    for i in range(args.steps):
+        t = i % T
+        st.step(x[t], al[t], be[t], outs[i])
+    ev1.record(stream_t)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    sec = ms / 1e3
+    steps_per_s = args.steps / sec
+    tokens_per_s = steps_per_s * cfg.batch
+    bytes_step = cfg.metric_bytes_per_step()
+    gbs = bytes_step * args.steps / sec / 1e9
+    assert torch.isfinite(outs).all().item(), "non-finite output"
+    log(f"[bench] {args.steps} steps in {ms:.3f} ms: {ms * 1e3 / args.steps:.2f} us/step, "
+        f"{tokens_per_s:.1f} tok/s, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+
+    # the dominant kernel is the whole-stack decode kernel: one launch per step on this stream
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        orc.lib()
+        # calibrate on one token, then run a bounded sample of the same workload
+        c0 = time.time()
+        orc.run(cfg, layers, stream, n_tokens=1)
+        per_tok = max(time.time() - c0, 1e-3)
+        n = int(max(1, min(T, args.cpu_seconds / per_tok)))
+        c0 = time.time()
+        orc.run(cfg, layers, stream, n_tokens=n)
+        csec = time.time() - c0
+        cpu = {"value": round(n * cfg.batch / csec, 3), "unit": "tokens/s", "cores": orc.threads(),
+               "kind": "oracle",
+               "sample": f"first {n} of {T} tokens of the same workload (fp64 oracle, {csec:.1f} s)"}
+        log(f"[bench] oracle: {n} tokens in {csec:.1f}s on {orc.threads()} threads")
+
+    rec = {
+        "metric": "DeltaNet decode tokens/s (30-layer stack) + achieved HBM GB/s % of peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if cfg.weight_bits == 8 else "int4",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_layers} layers x d_model {cfg.d_model}, "
+                               f"{cfg.n_k_heads}x{cfg.d_k} key / {cfg.n_v_heads}x{cfg.d_v} value heads, "
+                               f"batch {cfg.batch}, {T} tokens, {cfg.weight_bits}-bit weights",
+                   "layers": cfg.n_layers, "batch": cfg.batch, "tokens": T,
+                   "bytes_per_step": bytes_step},
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": f"{props.name} {getattr(props, 'gcnArchName', '')}".strip(),
+    }
+    st.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

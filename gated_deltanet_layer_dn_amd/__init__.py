@@ -1,0 +1,184 @@
+"""Thin Python binding of libdn (the gated-DeltaNet decode step on MI355X).
+
+Argument marshalling only: every step of the decode token runs in the HIP kernels of
+``libdn.so``. PyTorch provides device memory and streams. The functions carry the C ABI's
+names (``dn_create``, ``dn_set_state``, ``dn_get_state``, ``dn_step``, ``dn_destroy``);
+``DeltaNetStack`` wraps them. Loading fails loudly when the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdn.so")
+
+DN_OK, DN_E_INVAL, DN_E_NOMEM, DN_E_DEVICE, DN_E_DISABLED, DN_E_FAULT = 0, -1, -2, -3, -4, -5
+DN_X_RMSNORM = 1
+EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy")
+
+_ERR = {DN_OK: "ok", DN_E_INVAL: "invalid argument", DN_E_NOMEM: "out of device memory",
+        DN_E_DEVICE: "device error", DN_E_DISABLED: "layer disabled after a failed step",
+        DN_E_FAULT: "injected fault"}
+
+
+class DNError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        super().__init__(f"{what}: {_ERR.get(rc, 'unknown error')} ({rc})")
+        self.rc = rc
+
+
+class dn_config(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int), ("n_k_heads", ctypes.c_int), ("d_k", ctypes.c_int),
+                ("n_v_heads", ctypes.c_int), ("d_v", ctypes.c_int), ("conv_k", ctypes.c_int),
+                ("batch", ctypes.c_int), ("n_layers", ctypes.c_int), ("weight_bits", ctypes.c_int),
+                ("flags", ctypes.c_uint), ("eps_l2", ctypes.c_float), ("eps_rms", ctypes.c_float),
+                ("q_scale", ctypes.c_float)]
+
+
+class dn_weights(ctypes.Structure):
+    _fields_ = [("w_in", ctypes.c_void_p), ("s_in", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
+                ("norm_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("s_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdn.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libdn.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.dn_create.argtypes = [ctypes.POINTER(dn_config), ctypes.POINTER(dn_weights), ctypes.POINTER(P)]
+        L.dn_create.restype = ctypes.c_int
+        L.dn_set_state.argtypes = [P, P, P]; L.dn_set_state.restype = ctypes.c_int
+        L.dn_get_state.argtypes = [P, P, P]; L.dn_get_state.restype = ctypes.c_int
+        L.dn_step.argtypes = [P, P, P, P, P, P]; L.dn_step.restype = ctypes.c_int
+        L.dn_destroy.argtypes = [P]; L.dn_destroy.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        assert t.is_contiguous(), "tensors passed to libdn must be contiguous"
+        return t.data_ptr()
+    return int(t)
+
+
+def _check(rc: int, what: str):
+    if rc != DN_OK:
+        raise DNError(rc, what)
+
+
+# --- the five calls ------------------------------------------------------------------------
+
+def dn_create(cfg: dn_config, weights: list[dn_weights]) -> int:
+    arr = (dn_weights * len(weights))(*weights)
+    h = ctypes.c_void_p()
+    _check(lib().dn_create(ctypes.byref(cfg), arr, ctypes.byref(h)), "dn_create")
+    return h.value
+
+
+def dn_set_state(h: int, S, ring=None) -> None:
+    _check(lib().dn_set_state(h, _ptr(S), _ptr(ring)), "dn_set_state")
+
+
+def dn_get_state(h: int, S, ring=None) -> None:
+    _check(lib().dn_get_state(h, _ptr(S), _ptr(ring)), "dn_get_state")
+
+
+def dn_step(h: int, x, alpha, beta, out, stream=None) -> int:
+    """Enqueue one token; returns the C return code (no exception, so callers can test errors)."""
+    s = torch.cuda.current_stream().cuda_stream if stream is None else (
+        stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return lib().dn_step(h, _ptr(x), _ptr(alpha), _ptr(beta), _ptr(out), s)
+
+
+def dn_destroy(h: int) -> None:
+    if h:
+        lib().dn_destroy(h)
+
+
+# --- convenience wrapper -------------------------------------------------------------------
+
+def _dev(a, dtype, device):
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=dtype).contiguous()
+    return torch.from_numpy(a).to(device=device, dtype=dtype).contiguous()
+
+
+class DeltaNetStack:
+    """A handle over n_layers layers. ``layers`` are objects with attributes w_in, s_in, conv_w,
+    norm_w, w_out, s_out (numpy arrays or tensors, in the layouts of include/dn.h)."""
+
+    def __init__(self, *, d_model, n_k_heads, d_k, n_v_heads, d_v, layers, conv_k=4, batch=1,
+                 weight_bits=8, flags=0, eps_l2=1e-6, eps_rms=1e-6, q_scale=1.0, device="cuda:0"):
+        self.device = torch.device(device)
+        self.cfg = dn_config(d_model, n_k_heads, d_k, n_v_heads, d_v, conv_k, batch, len(layers),
+                             weight_bits, flags, eps_l2, eps_rms, q_scale)
+        wdt = torch.int8 if weight_bits == 8 else torch.uint8
+        self._keep = []
+        ws = []
+        for lay in layers:
+            t = [_dev(lay.w_in, wdt, self.device), _dev(lay.s_in, torch.float32, self.device),
+                 _dev(lay.conv_w, torch.float32, self.device), _dev(lay.norm_w, torch.float32, self.device),
+                 _dev(lay.w_out, wdt, self.device), _dev(lay.s_out, torch.float32, self.device)]
+            self._keep.append(t)
+            ws.append(dn_weights(*[x.data_ptr() for x in t]))
+        with torch.cuda.device(self.device):
+            self.h = dn_create(self.cfg, ws)
+        self.L, self.B, self.D = len(layers), batch, d_model
+        self.Hv, self.dk, self.dv, self.K = n_v_heads, d_k, d_v, conv_k
+        self.C = 2 * n_k_heads * d_k + n_v_heads * d_v
+
+    @classmethod
+    def from_config(cls, cfg, layers, device="cuda:0"):
+        return cls(d_model=cfg.d_model, n_k_heads=cfg.n_k_heads, d_k=cfg.d_k, n_v_heads=cfg.n_v_heads,
+                   d_v=cfg.d_v, layers=layers, conv_k=cfg.conv_k, batch=cfg.batch,
+                   weight_bits=cfg.weight_bits, flags=cfg.flags, eps_l2=cfg.eps_l2, eps_rms=cfg.eps_rms,
+                   q_scale=cfg.q_scale, device=device)
+
+    def state_shapes(self):
+        return (self.L, self.B, self.Hv, self.dk, self.dv), (self.L, self.B, self.K - 1, self.C)
+
+    def set_state(self, S, ring=None):
+        S = _dev(S, torch.float32, self.device)
+        ring = None if ring is None else _dev(ring, torch.float32, self.device)
+        dn_set_state(self.h, S, ring)
+
+    def get_state(self):
+        ss, rs = self.state_shapes()
+        S = torch.empty(ss, dtype=torch.float32, device=self.device)
+        ring = torch.empty(rs, dtype=torch.float32, device=self.device)
+        dn_get_state(self.h, S, ring)
+        return S, ring
+
+    def new_out(self):
+        return torch.empty((self.L, self.B, self.D), dtype=torch.float32, device=self.device)
+
+    def step(self, x, alpha, beta, out=None, stream=None, check=True):
+        if out is None:
+            out = self.new_out()
+        rc = dn_step(self.h, x, alpha, beta, out, stream)
+        if check:
+            _check(rc, "dn_step")
+        return out if check else rc
+
+    def close(self):
+        if getattr(self, "h", None):
+            dn_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

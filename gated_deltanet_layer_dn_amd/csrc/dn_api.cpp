@@ -1,0 +1,201 @@
+// C-ABI host side of libdn: handle lifecycle, validation, state movement, launch sequence.
+//
+// The handle is the per-layer device object of page "qwen36: run the DeltaNet layer end to end
+// on the card" (section "What the PR does", Backend and Tier paragraphs): it owns the conv
+// history, the recurrent state and one token's scratch; the state moves only through
+// dn_set_state / dn_get_state, and dn_get_state still works after a failed step.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "dn.h"
+#include "dn_internal.h"
+
+#define DN_API extern "C" __attribute__((visibility("default")))
+
+struct dn_layer {
+  dn_config cfg;
+  std::vector<dn_weights> w;
+  int device = 0;
+  int R = 0, C = 0, V = 0;
+  size_t s_elems = 0;     // per layer: B*Hv*dk*dv
+  size_t ring_elems = 0;  // per layer: B*(K-1)*C
+  float* S = nullptr;     // [L][B][Hv][dk][dv]
+  float* ring = nullptr;  // [L][B][K-1][C], oldest first
+  float* u = nullptr;     // [B][R] scratch: post-conv q|k|v, raw z
+  float* y = nullptr;     // [B][V] scratch: gated RMSNorm output
+  bool disabled = false;
+  long steps = 0;
+  long fault_step = 0;    // 1-based step to fail (0 = never)
+  bool sync_debug = false;
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate(const dn_config* c) {
+  if (!c) return DN_E_INVAL;
+  if (c->weight_bits != 8 && c->weight_bits != 4) return DN_E_INVAL;
+  const int col_mult = c->weight_bits == 8 ? 16 : 32;
+  if (c->d_model <= 0 || c->d_model > 16384 || c->d_model % col_mult) return DN_E_INVAL;
+  if (c->n_k_heads <= 0 || c->n_v_heads <= 0 || c->n_v_heads > 64) return DN_E_INVAL;
+  if (c->n_v_heads % c->n_k_heads) return DN_E_INVAL;
+  if (c->d_k <= 0 || c->d_k > 256 || c->d_v <= 0 || c->d_v > 256) return DN_E_INVAL;
+  const long V = (long)c->n_v_heads * c->d_v;
+  if (V % col_mult || V > 16384) return DN_E_INVAL;
+  if (c->conv_k < 1 || c->conv_k > 4) return DN_E_INVAL;
+  if (c->batch < 1 || c->batch > 1024) return DN_E_INVAL;
+  if (c->n_layers < 1 || c->n_layers > 256) return DN_E_INVAL;
+  if (c->flags & ~DN_X_RMSNORM) return DN_E_INVAL;
+  if (!(c->eps_l2 >= 0.f) || !(c->eps_rms >= 0.f)) return DN_E_INVAL;
+  return DN_OK;
+}
+
+void free_all(dn_layer* h) {
+  if (h->S) (void)hipFree(h->S);
+  if (h->ring) (void)hipFree(h->ring);
+  if (h->u) (void)hipFree(h->u);
+  if (h->y) (void)hipFree(h->y);
+  h->S = h->ring = h->u = h->y = nullptr;
+}
+
+int fail(dn_layer* h, int rc) {
+  h->disabled = true;
+  return rc;
+}
+
+}  // namespace
+
+DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) {
+  if (!out) return DN_E_INVAL;
+  *out = nullptr;
+  if (validate(cfg) != DN_OK || !w) return DN_E_INVAL;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dn_weights& x = w[l];
+    if (!x.w_in || !x.s_in || !x.conv_w || !x.norm_w || !x.w_out || !x.s_out) return DN_E_INVAL;
+    if (!aligned16(x.w_in) || !aligned16(x.w_out)) return DN_E_INVAL;
+    if (!aligned16(x.s_in) || !aligned16(x.s_out)) return DN_E_INVAL;
+  }
+  dn_layer* h = new (std::nothrow) dn_layer();
+  if (!h) return DN_E_NOMEM;
+  h->cfg = *cfg;
+  h->w.assign(w, w + cfg->n_layers);
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return DN_E_DEVICE;
+  }
+  const int QK = cfg->n_k_heads * cfg->d_k;
+  h->V = cfg->n_v_heads * cfg->d_v;
+  h->C = 2 * QK + h->V;
+  h->R = h->C + h->V;
+  const size_t L = cfg->n_layers, B = cfg->batch;
+  h->s_elems = B * cfg->n_v_heads * (size_t)cfg->d_k * cfg->d_v;
+  h->ring_elems = B * (size_t)(cfg->conv_k - 1) * h->C;
+  bool ok = hipMalloc(&h->S, sizeof(float) * L * h->s_elems) == hipSuccess;
+  ok = ok && hipMalloc(&h->ring, sizeof(float) * (L * h->ring_elems + 1)) == hipSuccess;
+  ok = ok && hipMalloc(&h->u, sizeof(float) * B * h->R) == hipSuccess;
+  ok = ok && hipMalloc(&h->y, sizeof(float) * B * h->V) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    free_all(h);
+    delete h;
+    return DN_E_NOMEM;
+  }
+  ok = hipMemset(h->S, 0, sizeof(float) * L * h->s_elems) == hipSuccess;
+  ok = ok && hipMemset(h->ring, 0, sizeof(float) * (L * h->ring_elems + 1)) == hipSuccess;
+  ok = ok && hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    free_all(h);
+    delete h;
+    return DN_E_DEVICE;
+  }
+  if (const char* e = std::getenv("DN_FAULT_STEP")) h->fault_step = std::atol(e);
+  if (const char* e = std::getenv("DN_SYNC_DEBUG")) h->sync_debug = std::atoi(e) != 0;
+  *out = h;
+  return DN_OK;
+}
+
+DN_API int dn_set_state(dn_layer* h, const float* S, const float* ring) {
+  if (!h || !S) return DN_E_INVAL;
+  if (hipSetDevice(h->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return DN_E_DEVICE;
+  const size_t L = h->cfg.n_layers;
+  if (hipMemcpy(h->S, S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) return DN_E_DEVICE;
+  if (ring && h->ring_elems &&
+      hipMemcpy(h->ring, ring, sizeof(float) * L * h->ring_elems, hipMemcpyDefault) != hipSuccess)
+    return DN_E_DEVICE;
+  if (hipDeviceSynchronize() != hipSuccess) return DN_E_DEVICE;
+  h->disabled = false;
+  return DN_OK;
+}
+
+DN_API int dn_get_state(dn_layer* h, float* S, float* ring) {
+  if (!h || !S) return DN_E_INVAL;
+  if (hipSetDevice(h->device) != hipSuccess) return DN_E_DEVICE;
+  (void)hipDeviceSynchronize();  // a failed step may have left an error; copy what the device holds
+  (void)hipGetLastError();
+  const size_t L = h->cfg.n_layers;
+  if (hipMemcpy(S, h->S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) return DN_E_DEVICE;
+  if (ring && h->ring_elems &&
+      hipMemcpy(ring, h->ring, sizeof(float) * L * h->ring_elems, hipMemcpyDefault) != hipSuccess)
+    return DN_E_DEVICE;
+  return hipDeviceSynchronize() == hipSuccess ? DN_OK : DN_E_DEVICE;
+}
+
+DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float* beta, float* out, void* hip_stream) {
+  if (!h || !x || !alpha || !beta || !out) return DN_E_INVAL;
+  if (h->disabled) return DN_E_DISABLED;
+  const dn_config& c = h->cfg;
+  const size_t L = c.n_layers, B = c.batch, D = c.d_model;
+  // out must not overlap x
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* ob = reinterpret_cast<const char*>(out);
+  if (ob < xb + sizeof(float) * B * D && xb < ob + sizeof(float) * L * B * D) return DN_E_INVAL;
+  ++h->steps;
+  if (h->fault_step > 0 && h->steps == h->fault_step) return fail(h, DN_E_FAULT);
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  for (size_t l = 0; l < L; ++l) {
+    const dn_weights& w = h->w[l];
+    const float* xl = l == 0 ? x : out + (l - 1) * B * D;
+    dn::GemvArgs gi{};
+    gi.W = w.w_in; gi.s = w.s_in; gi.x = xl; gi.out = h->u;
+    gi.rows = h->R; gi.cols = (int)D; gi.batch = (int)B;
+    gi.x_stride = (int)D; gi.out_stride = h->R;
+    gi.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; gi.eps = c.eps_rms;
+    gi.conv_w = w.conv_w; gi.ring = h->ring + l * h->ring_elems; gi.C = h->C; gi.K = c.conv_k;
+    if (dn::launch_gemv(gi, c.weight_bits, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
+
+    dn::HeadArgs ha{};
+    ha.u = h->u; ha.S = h->S + l * h->s_elems;
+    ha.alpha = alpha + l * B * c.n_v_heads; ha.beta = beta + l * B * c.n_v_heads;
+    ha.norm_w = w.norm_w; ha.y = h->y;
+    ha.Hk = c.n_k_heads; ha.Hv = c.n_v_heads; ha.dk = c.d_k; ha.dv = c.d_v;
+    ha.R = h->R; ha.C = h->C; ha.batch = (int)B;
+    ha.eps_l2 = c.eps_l2; ha.eps_rms = c.eps_rms; ha.q_scale = c.q_scale;
+    if (dn::launch_head(ha, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
+
+    dn::GemvArgs go{};
+    go.W = w.w_out; go.s = w.s_out; go.x = h->y; go.out = out + l * B * D;
+    go.rows = (int)D; go.cols = h->V; go.batch = (int)B;
+    go.x_stride = h->V; go.out_stride = (int)D;
+    go.prenorm = 0; go.eps = 0.f;
+    go.conv_w = nullptr; go.ring = nullptr; go.C = 0; go.K = 0;
+    if (dn::launch_gemv(go, c.weight_bits, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
+  }
+  return DN_OK;
+}
+
+DN_API void dn_destroy(dn_layer* h) {
+  if (!h) return;
+  (void)hipSetDevice(h->device);
+  (void)hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+}

@@ -1,0 +1,355 @@
+// HIP kernels of the gated-DeltaNet decode step for CDNA4 (gfx950).
+//
+// Steps (page "qwen36: run the DeltaNet layer end to end on the card", section "What the PR
+// does", Backend paragraph): in_proj GEMV -> causal conv + SiLU with the history advancing ->
+// per value head L2 norms (double, eps inside the sqrt) -> decay -> delta against the decayed
+// state -> write-back -> out = q^T S over the updated state -> gated RMSNorm with silu(z) ->
+// out_proj GEMV.
+//
+// GEMV arithmetic. The weights are exact small integers. The activation vector is split into
+// three int8 terms, x ~= s1*(x0 + (x1 + x2/254)/254) with s1 = max|x|/127, so that each row's
+// dot product is three exact int32 dot products (v_dot4_i32_i8 / sdot4) combined in double.
+// The split leaves |x - xhat| <= s1/(2*254^2) per element, below 1e-7 of the dot product's
+// magnitude for Gaussian activations (the level of fp32 rounding), and cuts the VALU work per
+// weight byte from two instructions (convert + FMA) to three quarters.
+#include <hip/hip_runtime.h>
+#include <cmath>
+
+#include "dn_internal.h"
+
+namespace dn {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Reductions over a 256-thread workgroup (4 waves). `buf` holds 4 elements; every thread
+// gets the result. Fixed order, so results are run-to-run identical.
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* buf) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) buf[wave] = v;
+  __syncthreads();
+  return (buf[0] + buf[1]) + (buf[2] + buf[3]);
+}
+__device__ __forceinline__ float block_max(float v, float* buf) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) buf[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(buf[0], buf[1]), fmaxf(buf[2], buf[3]));
+}
+
+// Position of column c in the staged int8 activations. For 4-bit weights each packed dword
+// holds columns 8m..8m+7 as nibbles (low nibble first); masking gives the even columns in one
+// dword and the odd columns in another, so the activations are staged even-first per group of 8.
+template <int BITS>
+__device__ __forceinline__ int x_pos(int c) {
+  if (BITS == 8) return c;
+  return (c & ~7) | ((c & 1) << 2) | ((c >> 1) & 3);
+}
+
+// ---------------------------------------------------------------------------------------------
+// GEMV: one wave streams RB rows at a time; each lane loads NCH 16-byte chunks per row (chunk
+// index lane + 64k), so one load instruction covers 1 KiB of one row. Grid-stride over rows.
+// ---------------------------------------------------------------------------------------------
+template <int BITS, int NCH, int RB>
+__global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
+  extern __shared__ int smem[];  // staged x: three int8 terms, [cols] bytes each
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y;
+  const float* xb = a.x + (size_t)b * a.x_stride;
+
+  // 1. statistics of x: sum of squares (pre-norm) and max |x| (split scale)
+  float ss = 0.f, mx = 0.f;
+  for (int c = tid; c < a.cols; c += 256) {
+    const float v = xb[c];
+    ss = fmaf(v, v, ss);
+    mx = fmaxf(mx, fabsf(v));
+  }
+  ss = block_sum(ss, redf);
+  mx = block_max(mx, redf);
+  const float scale = a.prenorm ? rsqrtf(ss / (float)a.cols + a.eps) : 1.0f;
+  float s1 = mx * scale * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2;
+  const float s3 = s2 * (1.0f / 254.0f), inv3 = 1.0f / s3;
+
+  // 2. split x into three int8 terms, staged in LDS
+  int8_t* xh8 = reinterpret_cast<int8_t*>(smem);
+  int8_t* xm8 = xh8 + a.cols;
+  int8_t* xl8 = xm8 + a.cols;
+  int sum_h = 0, sum_m = 0, sum_l = 0;
+  for (int c = tid; c < a.cols; c += 256) {
+    const float v = xb[c] * scale;
+    const float h = fminf(fmaxf(rintf(v * inv1), -127.f), 127.f);
+    const float r1 = fmaf(-s1, h, v);
+    const float m = fminf(fmaxf(rintf(r1 * inv2), -127.f), 127.f);
+    const float r2 = fmaf(-s2, m, r1);
+    const float l = fminf(fmaxf(rintf(r2 * inv3), -127.f), 127.f);
+    const int p = x_pos<BITS>(c);
+    xh8[p] = (int8_t)h;
+    xm8[p] = (int8_t)m;
+    xl8[p] = (int8_t)l;
+    sum_h += (int)h;
+    sum_m += (int)m;
+    sum_l += (int)l;
+  }
+  if (BITS == 4) {
+    sum_h = block_sum(sum_h, redi);
+    sum_m = block_sum(sum_m, redi);
+    sum_l = block_sum(sum_l, redi);
+  }
+  __syncthreads();
+
+  // 3. stream rows
+  const int nchunk = (BITS == 8 ? a.cols : a.cols / 2) >> 4;
+  const v4i* W = reinterpret_cast<const v4i*>(a.W);
+  const v4i* XH = reinterpret_cast<const v4i*>(xh8);
+  const v4i* XM = reinterpret_cast<const v4i*>(xm8);
+  const v4i* XL = reinterpret_cast<const v4i*>(xl8);
+  const int wave_stride = gridDim.x * 4 * RB;
+  for (int r0 = (blockIdx.x * 4 + wave) * RB; r0 < a.rows; r0 += wave_stride) {
+    v4i w[RB][NCH];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int c = lane + 64 * k, r = r0 + i;
+        if (r < a.rows && c < nchunk) w[i][k] = __builtin_nontemporal_load(&W[(size_t)r * nchunk + c]);
+        else w[i][k] = v4i{0, 0, 0, 0};
+      }
+    int ah[RB], am[RB], al[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) ah[i] = am[i] = al[i] = 0;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = lane + 64 * k;
+      if (c < nchunk) {
+        if (BITS == 8) {
+          const v4i xh = XH[c], xm = XM[c], xl = XL[c];
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ah[i] = sdot4(w[i][k][e], xh[e], ah[i]);
+              am[i] = sdot4(w[i][k][e], xm[e], am[i]);
+              al[i] = sdot4(w[i][k][e], xl[e], al[i]);
+            }
+          }
+        } else {
+          const v4i xh0 = XH[2 * c], xh1 = XH[2 * c + 1], xm0 = XM[2 * c], xm1 = XM[2 * c + 1];
+          const v4i xl0 = XL[2 * c], xl1 = XL[2 * c + 1];
+          const int xhE[4] = {xh0[0], xh0[2], xh1[0], xh1[2]}, xhO[4] = {xh0[1], xh0[3], xh1[1], xh1[3]};
+          const int xmE[4] = {xm0[0], xm0[2], xm1[0], xm1[2]}, xmO[4] = {xm0[1], xm0[3], xm1[1], xm1[3]};
+          const int xlE[4] = {xl0[0], xl0[2], xl1[0], xl1[2]}, xlO[4] = {xl0[1], xl0[3], xl1[1], xl1[3]};
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // nibble n (two's complement w) xor 8 gives w + 8 in 0..15
+              const unsigned p = (unsigned)w[i][k][e] ^ 0x88888888u;
+              const int lo = (int)(p & 0x0F0F0F0Fu), hi = (int)((p >> 4) & 0x0F0F0F0Fu);
+              ah[i] = sdot4(lo, xhE[e], ah[i]);
+              ah[i] = sdot4(hi, xhO[e], ah[i]);
+              am[i] = sdot4(lo, xmE[e], am[i]);
+              am[i] = sdot4(hi, xmO[e], am[i]);
+              al[i] = sdot4(lo, xlE[e], al[i]);
+              al[i] = sdot4(hi, xlO[e], al[i]);
+            }
+          }
+        }
+      }
+    }
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      int th = wave_sum(ah[i]), tm = wave_sum(am[i]), tl = wave_sum(al[i]);
+      if (BITS == 4) {
+        th -= 8 * sum_h;
+        tm -= 8 * sum_m;
+        tl -= 8 * sum_l;
+      }
+      const float dot = (float)((double)s1 * ((double)th + ((double)tm + (double)tl * (1.0 / 254.0)) * (1.0 / 254.0)));
+      if (lane == i) mine = dot;
+    }
+    const int r = r0 + lane;
+    if (lane < RB && r < a.rows) {
+      const float u = a.s[r] * mine;
+      float* ob = a.out + (size_t)b * a.out_stride;
+      if (a.conv_w != nullptr && r < a.C) {
+        const int K = a.K;
+        const float* cw = a.conv_w + (size_t)r * K;
+        float* rg = a.ring + (size_t)b * (K - 1) * a.C + r;
+        float hist[3] = {0.f, 0.f, 0.f};
+        float acc = cw[K - 1] * u;
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          if (j < K - 1) {
+            hist[j] = rg[(size_t)j * a.C];
+            acc = fmaf(cw[j], hist[j], acc);
+          }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (j + 1 < K - 1) rg[(size_t)j * a.C] = hist[j + 1];
+        if (K > 1) rg[(size_t)(K - 2) * a.C] = u;
+        ob[r] = silu(acc);
+      } else {
+        ob[r] = u;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Value head: one workgroup per (head, sequence). Column chunks of 64 (one column per lane);
+// the four waves split the key rows i = wave + 4t.
+// ---------------------------------------------------------------------------------------------
+template <int DKMAX>
+__global__ __launch_bounds__(256) void k_head(const HeadArgs a) {
+  constexpr int TPR = DKMAX / 4;  // key rows per thread
+  __shared__ float qs[256], ks[256], os[256];
+  __shared__ float red[4][64];
+  __shared__ double redd[4];
+  __shared__ float redf[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = h / (a.Hv / a.Hk);
+  const int dk = a.dk, dv = a.dv, QK = a.Hk * dk;
+  const float* ub = a.u + (size_t)b * a.R;
+  const float* q = ub + (size_t)g * dk;
+  const float* k = ub + QK + (size_t)g * dk;
+  const float* v = ub + 2 * QK + (size_t)h * dv;
+  const float* z = ub + a.C + (size_t)h * dv;
+
+  // L2 norms in double, eps inside the sqrt
+  double sq = 0.0, sk = 0.0;
+  for (int i = tid; i < dk; i += 256) {
+    const float qv = q[i], kv = k[i];
+    qs[i] = qv;
+    ks[i] = kv;
+    sq += (double)qv * qv;
+    sk += (double)kv * kv;
+  }
+  sq = block_sum(sq, redd);
+  sk = block_sum(sk, redd);
+  const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
+  const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
+  __syncthreads();
+  for (int i = tid; i < dk; i += 256) {
+    qs[i] *= qn;
+    ks[i] *= kn;
+  }
+  __syncthreads();
+
+  const float alpha = a.alpha[(size_t)b * a.Hv + h], beta = a.beta[(size_t)b * a.Hv + h];
+  float* S = a.S + ((size_t)b * a.Hv + h) * dk * dv;
+  for (int j0 = 0; j0 < dv; j0 += 64) {
+    const int j = j0 + lane;
+    const bool jv = j < dv;
+    float s[TPR];
+    float kvp = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPR; ++t) {
+      const int i = wave + 4 * t;
+      s[t] = 0.f;
+      if (i < dk && jv) {
+        s[t] = alpha * S[(size_t)i * dv + j];
+        kvp = fmaf(s[t], ks[i], kvp);
+      }
+    }
+    red[wave][lane] = kvp;
+    __syncthreads();
+    const float kv = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    __syncthreads();
+    const float delta = jv ? beta * (v[j] - kv) : 0.f;
+    float op = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPR; ++t) {
+      const int i = wave + 4 * t;
+      if (i < dk && jv) {
+        s[t] = fmaf(ks[i], delta, s[t]);
+        S[(size_t)i * dv + j] = s[t];
+        op = fmaf(s[t], qs[i], op);
+      }
+    }
+    red[wave][lane] = op;
+    __syncthreads();
+    const float o = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    if (wave == 0 && jv) os[j] = o;
+    __syncthreads();
+  }
+
+  // gated RMSNorm over dv with silu(z)
+  float ssq = 0.f;
+  for (int j = tid; j < dv; j += 256) ssq = fmaf(os[j], os[j], ssq);
+  ssq = block_sum(ssq, redf);
+  const float inv = rsqrtf(ssq / (float)dv + a.eps_rms);
+  float* yb = a.y + (size_t)b * a.Hv * dv + (size_t)h * dv;
+  for (int j = tid; j < dv; j += 256) yb[j] = a.norm_w[j] * os[j] * inv * silu(z[j]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------------
+template <int BITS, int NCH, int RB>
+static hipError_t go_gemv(const GemvArgs& a, hipStream_t st) {
+  const int rows_per_block = 4 * RB;
+  int grid = (a.rows + rows_per_block - 1) / rows_per_block;
+  if (grid > 2048) grid = 2048;
+  const size_t lds = 3 * (size_t)a.cols;
+  hipLaunchKernelGGL((k_gemv<BITS, NCH, RB>), dim3(grid, a.batch), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t gemv_bits(const GemvArgs& a, hipStream_t st) {
+  const int nchunk = (BITS == 8 ? a.cols : a.cols / 2) >> 4;
+  const int nch = (nchunk + 63) / 64;
+  if (nch <= 1) return go_gemv<BITS, 1, 8>(a, st);
+  if (nch <= 2) return go_gemv<BITS, 2, 8>(a, st);
+  if (nch <= 4) return go_gemv<BITS, 4, 4>(a, st);
+  if (nch <= 8) return go_gemv<BITS, 8, 2>(a, st);
+  if (nch <= 16) return go_gemv<BITS, 16, 1>(a, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(const GemvArgs& a, int bits, hipStream_t st) {
+  return bits == 8 ? gemv_bits<8>(a, st) : gemv_bits<4>(a, st);
+}
+
+template <int DKMAX>
+static hipError_t go_head(const HeadArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_head<DKMAX>), dim3(a.Hv, a.batch), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head(const HeadArgs& a, hipStream_t st) {
+  if (a.dk <= 16) return go_head<16>(a, st);
+  if (a.dk <= 32) return go_head<32>(a, st);
+  if (a.dk <= 64) return go_head<64>(a, st);
+  if (a.dk <= 128) return go_head<128>(a, st);
+  if (a.dk <= 256) return go_head<256>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dn

@@ -64,7 +64,18 @@ void dno_gemv(int rows, int cols, const void *W, int bits, const float *s, const
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < rows; ++r) {
     double acc = 0.0;
-    for (int c = 0; c < cols; ++c) acc += (double)dno_weight(W, bits, cols, r, c) * x[c];
+    if (bits == 8) {
+      const int8_t *row = (const int8_t *)W + (long)r * cols;
+      for (int c = 0; c < cols; ++c) acc += (double)row[c] * x[c];
+    } else {
+      const uint8_t *row = (const uint8_t *)W + (long)r * (cols / 2);
+      for (int m = 0; m < cols / 2; ++m) {
+        /* a nibble n is the 4-bit two's complement value (n ^ 8) - 8 */
+        const int lo = row[m] & 15, hi = row[m] >> 4;
+        acc += (double)((lo ^ 8) - 8) * x[2 * m];
+        acc += (double)((hi ^ 8) - 8) * x[2 * m + 1];
+      }
+    }
     y[r] = (double)s[r] * acc;
   }
 }

@@ -1,0 +1,56 @@
+"""Helpers shared by the GPU tests: run the HIP path through the C ABI and measure errors
+against the oracle."""
+import numpy as np
+import torch
+
+import gated_deltanet_layer_dn_amd as dn
+
+# tolerances of the decode step: out max-abs error relative to each token's output RMS, and
+# relative Frobenius error of the final state
+OUT_TOL = 2e-3
+STATE_TOL = 1e-3
+
+
+def make_stack(cfg, layers, S0=None, ring0=None):
+    st = dn.DeltaNetStack.from_config(cfg, layers)
+    S = np.stack([l.S0 for l in layers]) if S0 is None else S0
+    R = np.stack([l.ring0 for l in layers]) if ring0 is None else ring0
+    st.set_state(np.ascontiguousarray(S, np.float32), np.ascontiguousarray(R, np.float32))
+    return st
+
+
+def upload_stream(stream, T=None, dev="cuda:0"):
+    T = stream.x.shape[0] if T is None else T
+    x = torch.from_numpy(np.ascontiguousarray(stream.x[:T])).to(dev)
+    a = torch.from_numpy(np.ascontiguousarray(stream.alpha[:T])).to(dev)
+    b = torch.from_numpy(np.ascontiguousarray(stream.beta[:T])).to(dev)
+    return x, a, b
+
+
+def run_gpu(st, stream, T=None, t0=0):
+    """Run tokens t0..t0+T-1; returns out [T][L][B][D] (numpy fp32)."""
+    T = stream.x.shape[0] - t0 if T is None else T
+    x, a, b = upload_stream(stream, t0 + T)
+    outs = torch.empty((T, st.L, st.B, st.D), dtype=torch.float32, device=st.device)
+    for t in range(T):
+        st.step(x[t0 + t], a[t0 + t], b[t0 + t], outs[t])
+    torch.cuda.synchronize()
+    return outs.cpu().numpy()
+
+
+def out_err(gpu, ref):
+    """max over tokens of max|gpu - ref| / rms(ref) (per token, over the last axis groups)."""
+    g = gpu.reshape(gpu.shape[0], -1).astype(np.float64)
+    r = ref.reshape(ref.shape[0], -1)
+    rms = np.sqrt(np.mean(r * r, axis=1))
+    return float(np.max(np.max(np.abs(g - r), axis=1) / rms))
+
+
+def state_err(gS, rS):
+    """max over (layer, sequence) of ||gS - rS||_F / ||rS||_F."""
+    L, B = rS.shape[:2]
+    g = np.asarray(gS, np.float64).reshape(L, B, -1)
+    r = np.asarray(rS, np.float64).reshape(L, B, -1)
+    num = np.linalg.norm(g - r, axis=2)
+    den = np.linalg.norm(r, axis=2)
+    return float(np.max(num / np.maximum(den, 1e-30)))

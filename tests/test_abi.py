@@ -1,0 +1,50 @@
+"""The C-ABI library loads and exports exactly the entry points include/dn.h declares
+(no compute calls: runs without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "gated_deltanet_layer_dn_amd", "libdn.so")
+HDR = os.path.join(ROOT, "include", "dn.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set(re.findall(r"^\s*(?:int|void)\s+\*?\s*(dn_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def built():
+    if not os.path.exists(LIB):
+        from gated_deltanet_layer_dn_amd import build
+        build.build()
+    return LIB
+
+
+def test_header_declares_the_five_calls():
+    assert _declared() == {"dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy"}
+
+
+def test_library_exports_exactly_the_declared_symbols(built):
+    out = subprocess.run(["nm", "-D", "--defined-only", built], capture_output=True, text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.split() and l.split()[-1].startswith("dn_")}
+    assert syms == _declared()
+
+
+def test_library_loads_and_resolves(built):
+    L = ctypes.CDLL(built)
+    for n in _declared():
+        assert getattr(L, n) is not None
+
+
+def test_binding_names_match():
+    import gated_deltanet_layer_dn_amd as dn
+    assert set(dn.EXPORTED) == _declared()
+    for n in dn.EXPORTED:
+        assert callable(getattr(dn, n))

@@ -25,6 +25,8 @@ MUTATIONS = [
     ("norm_weight_dropped", "y[j] = (double)w[j] * o[j] * inv * dno_silu(z[j]);", "y[j] = o[j] * inv * dno_silu(z[j]);", 0),
     ("nibble_order", "int nib = (c & 1) ? (byte >> 4) : (byte & 15);", "int nib = (c & 1) ? (byte & 15) : (byte >> 4);", 0),
     ("nibble_unsigned", "return nib >= 8 ? nib - 16 : nib;", "return nib;", 0),
+    ("gemv_int4_nibble_order", "const int lo = row[m] & 15, hi = row[m] >> 4;", "const int lo = row[m] >> 4, hi = row[m] & 15;", 0),
+    ("gemv_int4_unsigned", "acc += (double)((lo ^ 8) - 8) * x[2 * m];", "acc += (double)lo * x[2 * m];", 0),
     ("row_scale_index", "y[r] = (double)s[r] * acc;", "y[r] = (double)s[0] * acc;", 0),
     ("history_order", "if (K > 1) memcpy(hist + (long)(K - 2) * C, u, sizeof(double) * C);", "if (K > 1) memcpy(hist, u, sizeof(double) * C);", 0),
     ("q_reads_k", "dno_l2norm(dk, c + (long)g * dk, d->eps_l2, qh);", "dno_l2norm(dk, c + QK + (long)g * dk, d->eps_l2, qh);", 0),
