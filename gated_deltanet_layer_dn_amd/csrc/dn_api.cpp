@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -28,6 +29,17 @@ struct dn_layer {
   float* ring = nullptr;  // [L][B][K-1][C], oldest first
   float* u = nullptr;     // [B][R] scratch: post-conv q|k|v, raw z
   float* y = nullptr;     // [B][V] scratch: gated RMSNorm output
+  // whole-stack kernel (single sequence, 128 x 128 state tiles)
+  bool persist = false;
+  int nwg = 0;
+  dn::PersistShape ps{};
+  dn::LayerW* d_layers = nullptr;
+  uint64_t* X = nullptr;    // tagged hand-off buffers
+  uint64_t* U = nullptr;
+  uint64_t* G = nullptr;
+  dn::Ctl* ctl = nullptr;
+  float* stage = nullptr;   // canonical-layout staging of the state for set/get
+  unsigned* err_host = nullptr;  // pinned copy of the device error flag, refreshed after each step
   bool disabled = false;
   long steps = 0;
   long fault_step = 0;    // 1-based step to fail (0 = never)
@@ -56,12 +68,63 @@ int validate(const dn_config* c) {
   return DN_OK;
 }
 
+template <typename T>
+void dfree(T*& p) {
+  if (p) (void)hipFree(p);
+  p = nullptr;
+}
+
 void free_all(dn_layer* h) {
-  if (h->S) (void)hipFree(h->S);
-  if (h->ring) (void)hipFree(h->ring);
-  if (h->u) (void)hipFree(h->u);
-  if (h->y) (void)hipFree(h->y);
-  h->S = h->ring = h->u = h->y = nullptr;
+  dfree(h->S);
+  dfree(h->ring);
+  dfree(h->u);
+  dfree(h->y);
+  dfree(h->d_layers);
+  dfree(h->X);
+  dfree(h->U);
+  dfree(h->G);
+  dfree(h->ctl);
+  dfree(h->stage);
+  if (h->err_host) (void)hipHostFree(h->err_host);
+  h->err_host = nullptr;
+}
+
+// Set up the whole-stack kernel when the shape allows it: hand-off buffers, control words,
+// the device copy of the weight table, and the staging buffer of the tiled state.
+int setup_persist(dn_layer* h) {
+  const dn_config& c = h->cfg;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) return DN_E_DEVICE;
+  h->nwg = prop.multiProcessorCount;
+  dn::PersistShape& ps = h->ps;
+  ps.batch = c.batch; ps.D = c.d_model; ps.V = h->V; ps.R = h->R; ps.dk = c.d_k; ps.dv = c.d_v;
+  ps.Hv = c.n_v_heads; ps.K = c.conv_k; ps.bits = c.weight_bits;
+  const char* force = std::getenv("DN_LAYER_KERNELS");
+  if ((force && std::atoi(force) != 0) || !dn::persist_supported(ps, h->nwg)) return DN_OK;
+  int per_cu = 0;
+  if (dn::persist_occupancy(ps, &per_cu) != hipSuccess || per_cu < 1) return DN_OK;
+  const size_t L = c.n_layers;
+  bool ok = hipMalloc(&h->d_layers, sizeof(dn::LayerW) * L) == hipSuccess;
+  ok = ok && hipMalloc(&h->X, sizeof(uint64_t) * c.d_model) == hipSuccess;
+  ok = ok && hipMalloc(&h->U, sizeof(uint64_t) * h->R) == hipSuccess;
+  ok = ok && hipMalloc(&h->G, sizeof(uint64_t) * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMalloc(&h->ctl, sizeof(dn::Ctl)) == hipSuccess;
+  ok = ok && hipMalloc(&h->stage, sizeof(float) * L * h->s_elems) == hipSuccess;
+  ok = ok && hipHostMalloc(&h->err_host, sizeof(unsigned)) == hipSuccess;
+  if (!ok) return DN_E_NOMEM;
+  std::vector<dn::LayerW> lw(L);
+  for (size_t l = 0; l < L; ++l)
+    lw[l] = dn::LayerW{h->w[l].w_in, h->w[l].s_in, h->w[l].conv_w, h->w[l].norm_w, h->w[l].w_out, h->w[l].s_out};
+  const dn::Ctl ctl0{1u, 0u, 0u, 0u};
+  ok = hipMemcpy(h->d_layers, lw.data(), sizeof(dn::LayerW) * L, hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemset(h->X, 0, sizeof(uint64_t) * c.d_model) == hipSuccess;
+  ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * h->R) == hipSuccess;
+  ok = ok && hipMemset(h->G, 0, sizeof(uint64_t) * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMemcpy(h->ctl, &ctl0, sizeof(ctl0), hipMemcpyHostToDevice) == hipSuccess;
+  if (!ok) return DN_E_DEVICE;
+  *h->err_host = 0;
+  h->persist = true;
+  return DN_OK;
 }
 
 int fail(dn_layer* h, int rc) {
@@ -114,8 +177,21 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
     delete h;
     return DN_E_DEVICE;
   }
+  if (int rc = setup_persist(h); rc != DN_OK) {
+    free_all(h);
+    delete h;
+    return rc;
+  }
+  if (hipDeviceSynchronize() != hipSuccess) {
+    free_all(h);
+    delete h;
+    return DN_E_DEVICE;
+  }
   if (const char* e = std::getenv("DN_FAULT_STEP")) h->fault_step = std::atol(e);
   if (const char* e = std::getenv("DN_SYNC_DEBUG")) h->sync_debug = std::atoi(e) != 0;
+  if (const char* e = std::getenv("DN_VERBOSE"); e && std::atoi(e) != 0)
+    std::fprintf(stderr, "[dn] handle: %d layer(s), batch %d: %s\n", cfg->n_layers, cfg->batch,
+                 h->persist ? "whole-stack kernel" : "per-layer kernels");
   *out = h;
   return DN_OK;
 }
@@ -124,7 +200,17 @@ DN_API int dn_set_state(dn_layer* h, const float* S, const float* ring) {
   if (!h || !S) return DN_E_INVAL;
   if (hipSetDevice(h->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return DN_E_DEVICE;
   const size_t L = h->cfg.n_layers;
-  if (hipMemcpy(h->S, S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) return DN_E_DEVICE;
+  if (h->persist) {
+    if (hipMemcpy(h->stage, S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) return DN_E_DEVICE;
+    if (dn::launch_state_tile(h->stage, h->S, (int)L, h->cfg.n_v_heads, h->cfg.d_k, h->cfg.d_v, true, nullptr) !=
+        hipSuccess)
+      return DN_E_DEVICE;
+    const unsigned zero = 0;
+    if (hipMemcpy(&h->ctl->error, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return DN_E_DEVICE;
+    *h->err_host = 0;
+  } else if (hipMemcpy(h->S, S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) {
+    return DN_E_DEVICE;
+  }
   if (ring && h->ring_elems &&
       hipMemcpy(h->ring, ring, sizeof(float) * L * h->ring_elems, hipMemcpyDefault) != hipSuccess)
     return DN_E_DEVICE;
@@ -139,7 +225,15 @@ DN_API int dn_get_state(dn_layer* h, float* S, float* ring) {
   (void)hipDeviceSynchronize();  // a failed step may have left an error; copy what the device holds
   (void)hipGetLastError();
   const size_t L = h->cfg.n_layers;
-  if (hipMemcpy(S, h->S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) return DN_E_DEVICE;
+  if (h->persist) {
+    if (dn::launch_state_tile(h->S, h->stage, (int)L, h->cfg.n_v_heads, h->cfg.d_k, h->cfg.d_v, false, nullptr) !=
+            hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
+      return DN_E_DEVICE;
+    if (hipMemcpy(S, h->stage, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) return DN_E_DEVICE;
+  } else if (hipMemcpy(S, h->S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) {
+    return DN_E_DEVICE;
+  }
   if (ring && h->ring_elems &&
       hipMemcpy(ring, h->ring, sizeof(float) * L * h->ring_elems, hipMemcpyDefault) != hipSuccess)
     return DN_E_DEVICE;
@@ -158,6 +252,20 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
   ++h->steps;
   if (h->fault_step > 0 && h->steps == h->fault_step) return fail(h, DN_E_FAULT);
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  if (h->persist) {
+    if (*h->err_host) return fail(h, DN_E_DEVICE);  // a previous launch reported a stalled hand-off
+    dn::PersistArgs a{};
+    a.layers = h->d_layers; a.S = h->S; a.ring = h->ring; a.x = x; a.alpha = alpha; a.beta = beta; a.out = out;
+    a.X = h->X; a.U = h->U; a.G = h->G; a.ctl = h->ctl;
+    a.L = (int)L; a.R = h->R; a.C = h->C; a.QK = c.n_k_heads * c.d_k; a.K = c.conv_k;
+    a.Hk = c.n_k_heads; a.Hv = c.n_v_heads; a.flags = c.flags;
+    a.eps_l2 = c.eps_l2; a.eps_rms = c.eps_rms; a.q_scale = c.q_scale;
+    if (dn::launch_persist(a, h->ps, h->nwg, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (hipMemcpyAsync(h->err_host, &h->ctl->error, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
+      return fail(h, DN_E_DEVICE);
+    if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || *h->err_host)) return fail(h, DN_E_DEVICE);
+    return DN_OK;
+  }
   for (size_t l = 0; l < L; ++l) {
     const dn_weights& w = h->w[l];
     const float* xl = l == 0 ? x : out + (l - 1) * B * D;

@@ -40,4 +40,51 @@ struct HeadArgs {
 hipError_t launch_gemv(const GemvArgs& a, int bits, hipStream_t st);
 hipError_t launch_head(const HeadArgs& a, hipStream_t st);
 
+// ---- whole-stack kernel (single sequence, 128 x 128 state tiles) ----
+struct LayerW {
+  const void* w_in;
+  const float* s_in;
+  const float* conv_w;
+  const float* norm_w;
+  const void* w_out;
+  const float* s_out;
+};
+
+// Control words of one handle in device memory: the tag base of the next launch, the count of
+// workgroups that finished the current launch, and a sticky error flag.
+struct Ctl {
+  unsigned epoch;
+  unsigned done;
+  unsigned error;
+  unsigned pad;
+};
+
+struct PersistArgs {
+  const LayerW* layers;  // [L], device memory
+  float* S;              // [L][Hv][dv/16][dk][16] (tiled)
+  float* ring;           // [L][K-1][C], oldest first
+  const float* x;        // [D]
+  const float* alpha;    // [L][Hv]
+  const float* beta;     // [L][Hv]
+  float* out;            // [L][D]
+  uint64_t* X;           // [D]  tagged layer output
+  uint64_t* U;           // [R]  tagged in_proj output (post-conv q|k|v, raw z)
+  uint64_t* G;           // [V + 256] tagged gated readout and partial sums of squares of the
+                         // readout, in four segments [V/4 columns | partials of those heads | pad]
+  Ctl* ctl;
+  int L, R, C, QK, K, Hk, Hv;
+  unsigned flags;
+  float eps_l2, eps_rms, q_scale;
+};
+
+struct PersistShape {
+  int batch, D, V, R, dk, dv, Hv, K, bits;
+};
+
+bool persist_supported(const PersistShape& s, int nwg);
+hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu);
+hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, hipStream_t st);
+hipError_t launch_state_tile(const float* src, float* dst, int L, int Hv, int dk, int dv, bool to_tiled,
+                             hipStream_t st);
+
 }  // namespace dn

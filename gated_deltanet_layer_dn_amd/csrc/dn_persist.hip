@@ -1,0 +1,691 @@
+// Whole-stack decode kernel for single-sequence stacks with 128x128 value-head state tiles.
+//
+// One launch runs one decode token through every layer of the stack (page "qwen36: run the
+// DeltaNet layer end to end on the card", section "What the PR does", Backend paragraph: in_proj
+// GEMV, conv + SiLU with the history advancing, per value head L2 norms with eps inside the sqrt,
+// decay, delta rule against the decayed state, write-back, readout over the updated state, gated
+// RMSNorm with silu(z), out_proj GEMV).
+//
+// Layout of the work. One workgroup per compute unit, each with eight compute waves and four
+// communication waves.
+//  * Phase A (in_proj + conv + SiLU): each workgroup owns a contiguous band of in_proj rows; each
+//    compute wave streams RA of them. The rows' weights are loaded into registers one layer ahead,
+//    as soon as the previous layer's phase A has used them, so the HBM stream never waits for the
+//    activations.
+//  * Phase B (recurrence): workgroup b owns value head b / (dv/16) and 16 of its value columns; its
+//    first communication wave keeps that 128x16 slice of the state in registers, prefetched one
+//    layer ahead, and performs decay, delta rule, readout and the gate for those columns.
+//  * Phase C (gated RMSNorm finish + out_proj): each workgroup owns D/NWG out_proj rows.
+// Hand-offs between workgroups carry no fences: every cross-workgroup value travels as a 64-bit
+// word (fp32 value, 32-bit tag) stored and loaded with device-coherent (sc1) accesses; a reader
+// spins until each word carries the tag of the current layer and token. Tags grow by one per
+// layer and never repeat within 2^32 layer steps, so buffers need no reset.
+// Compute waves never poll, so their outstanding weight prefetches never delay a hand-off (a
+// wave's loads complete in order); the communication waves poll, stage activations into LDS, and
+// run phase B.
+//
+// GEMV arithmetic as in the layer kernels: activations split into three int8 terms, exact int32
+// dot products with v_dot4_i32_i8, combined in double.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dn_internal.h"
+
+namespace dn {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int NCW = 8;                 // compute waves per workgroup
+constexpr int NCM = 4;                 // communication waves per workgroup
+constexpr int NTHR = (NCW + NCM) * 64;
+constexpr int DK = 128;                // key rows of a state tile
+constexpr int CB = 16;                 // value columns per phase-B workgroup
+constexpr unsigned SPIN_CAP = 1u << 22;
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+__device__ __forceinline__ void ll_store(uint64_t* p, float v, unsigned tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned coherent_load_u32(const unsigned* p) {
+  return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store_u32(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T wsum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Sum 16 per-lane values over the 64 lanes of a wave. On return lane l holds the total of value
+// (l >> 2). Butterfly reduce-scatter: each step keeps half of the values and adds the partner's.
+__device__ __forceinline__ float rs16(float (&a)[16], int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool up = lane & 32;
+    const float send = up ? a[i] : a[i + 8];
+    const float keep = up ? a[i + 8] : a[i];
+    a[i] = keep + __shfl_xor(send, 32);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool up = lane & 16;
+    const float send = up ? a[i] : a[i + 4];
+    const float keep = up ? a[i + 4] : a[i];
+    a[i] = keep + __shfl_xor(send, 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bool up = lane & 8;
+    const float send = up ? a[i] : a[i + 2];
+    const float keep = up ? a[i + 2] : a[i];
+    a[i] = keep + __shfl_xor(send, 8);
+  }
+  {
+    const bool up = lane & 4;
+    const float send = up ? a[0] : a[1];
+    const float keep = up ? a[1] : a[0];
+    a[0] = keep + __shfl_xor(send, 4);
+  }
+  float s = a[0];
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 1);
+  return s;
+}
+
+// Staged activation position of column c (4-bit weights hold 8 columns per dword as nibbles;
+// the masked low and high nibbles are the even and odd columns).
+template <int BITS>
+__device__ __forceinline__ int xpos(int c) {
+  if (BITS == 8) return c;
+  return (c & ~7) | ((c & 1) << 2) | ((c >> 1) & 3);
+}
+
+// Three-term int8 split of v with scale s1 (|v| <= 127 s1): v ~= s1 (h + (m + l/254)/254).
+__device__ __forceinline__ void split3(float v, float s1, float inv1, float s2, float inv2, float inv3,
+                                       int8_t& h8, int8_t& m8, int8_t& l8) {
+  const float h = fminf(fmaxf(rintf(v * inv1), -127.f), 127.f);
+  const float r1 = fmaf(-s1, h, v);
+  const float m = fminf(fmaxf(rintf(r1 * inv2), -127.f), 127.f);
+  const float r2 = fmaf(-s2, m, r1);
+  const float l = fminf(fmaxf(rintf(r2 * inv3), -127.f), 127.f);
+  h8 = (int8_t)h;
+  m8 = (int8_t)m;
+  l8 = (int8_t)l;
+}
+
+__device__ __forceinline__ float combine3(int th, int tm, int tl, float s1) {
+  return (float)((double)s1 * ((double)th + ((double)tm + (double)tl * (1.0 / 254.0)) * (1.0 / 254.0)));
+}
+
+// Dot products of RB rows (NCH 16-byte chunks per lane each) with the staged three-term
+// activations in LDS. acc[i][t] gets lane partial sums of term t for row i.
+template <int BITS, int RB, int NCH>
+__device__ __forceinline__ void dot_rows(const v4i (&w)[RB][NCH], const int8_t* xs, int cols, int lane,
+                                         int (&acc)[RB][3]) {
+#pragma unroll
+  for (int i = 0; i < RB; ++i) acc[i][0] = acc[i][1] = acc[i][2] = 0;
+  const v4i* X0 = reinterpret_cast<const v4i*>(xs);
+  const v4i* X1 = reinterpret_cast<const v4i*>(xs + cols);
+  const v4i* X2 = reinterpret_cast<const v4i*>(xs + 2 * cols);
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c = lane + 64 * k;
+    if (BITS == 8) {
+      const v4i x0 = X0[c], x1 = X1[c], x2 = X2[c];
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[i][0] = sdot4(w[i][k][e], x0[e], acc[i][0]);
+          acc[i][1] = sdot4(w[i][k][e], x1[e], acc[i][1]);
+          acc[i][2] = sdot4(w[i][k][e], x2[e], acc[i][2]);
+        }
+    } else {
+      const v4i a0 = X0[2 * c], b0 = X0[2 * c + 1], a1 = X1[2 * c], b1 = X1[2 * c + 1];
+      const v4i a2 = X2[2 * c], b2 = X2[2 * c + 1];
+      const int e0[4] = {a0[0], a0[2], b0[0], b0[2]}, o0[4] = {a0[1], a0[3], b0[1], b0[3]};
+      const int e1[4] = {a1[0], a1[2], b1[0], b1[2]}, o1[4] = {a1[1], a1[3], b1[1], b1[3]};
+      const int e2[4] = {a2[0], a2[2], b2[0], b2[2]}, o2[4] = {a2[1], a2[3], b2[1], b2[3]};
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // signed nibbles moved to the high half of each byte: bytes hold 16 * w
+          const unsigned p = (unsigned)w[i][k][e];
+          const int lo = (int)((p << 4) & 0xF0F0F0F0u), hi = (int)(p & 0xF0F0F0F0u);
+          acc[i][0] = sdot4(hi, o0[e], sdot4(lo, e0[e], acc[i][0]));
+          acc[i][1] = sdot4(hi, o1[e], sdot4(lo, e1[e], acc[i][1]));
+          acc[i][2] = sdot4(hi, o2[e], sdot4(lo, e2[e], acc[i][2]));
+        }
+    }
+  }
+}
+
+// Reduce the lane partials of RB rows; lane i (< RB) receives row i's dot product.
+template <int BITS, int RB>
+__device__ __forceinline__ float reduce_rows(int (&acc)[RB][3], float s1, int lane) {
+  float mine = 0.f;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    int th = wsum(acc[i][0]), tm = wsum(acc[i][1]), tl = wsum(acc[i][2]);
+    if (BITS == 4) {  // products carried a factor 16
+      th >>= 4;
+      tm >>= 4;
+      tl >>= 4;
+    }
+    const float d = combine3(th, tm, tl, s1);
+    if (lane == i) mine = d;
+  }
+  return mine;
+}
+
+struct Smem {
+  float raw[4096];         // staged activations (x or gated readout), fp32
+  int8_t xs[3 * 4096];     // three-term split of x for phase A
+  int8_t ys[3 * 4096];     // three-term split of y for phase C
+  float inv[64];           // per value head 1/rms of the readout
+  float stat[16];          // partial statistics from the communication waves, split scales
+  int abort_flag;
+};
+
+// Poll N tagged words per lane, word i at base + i * STRIDE, until every one carries `want`;
+// values go to v[]. Returns false if the spin cap is hit or another workgroup reported an error.
+// The base pointer is laundered through an empty asm statement each round so that the compiler
+// rebuilds the addresses from one register pair with immediate offsets instead of keeping N
+// 64-bit addresses alive across the loop.
+template <int N, int STRIDE>
+__device__ __forceinline__ bool poll_words(const uint64_t* base, unsigned want, float (&v)[N], unsigned nvalid,
+                                           const unsigned* err) {
+  static_assert(N <= 32, "at most 32 words per lane per poll");
+  unsigned pend = N == 32 ? 0xFFFFFFFFu : ((1u << N) - 1u);
+  pend &= nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
+  unsigned it = 0;
+  while (__any(pend != 0)) {
+    const uint64_t* b = base;
+    asm volatile("" : "+v"(b));
+    uint64_t w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((pend >> i) & 1) w[i] = ll_load(b + i * STRIDE);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (((pend >> i) & 1) && (unsigned)(w[i] >> 32) == want) {
+        v[i] = __uint_as_float((unsigned)w[i]);
+        pend &= ~(1u << i);
+      }
+    if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
+  }
+  return true;
+}
+
+// As poll_words, with word i at base + off[i] (element offsets).
+template <int N>
+__device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&off)[N], unsigned want, float (&v)[N],
+                                              unsigned nvalid, const unsigned* err) {
+  unsigned pend = (1u << N) - 1u;
+  pend &= (1u << nvalid) - 1u;
+  unsigned it = 0;
+  while (__any(pend != 0)) {
+    const uint64_t* b = base;
+    asm volatile("" : "+v"(b));
+    uint64_t w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((pend >> i) & 1) w[i] = ll_load(b + off[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (((pend >> i) & 1) && (unsigned)(w[i] >> 32) == want) {
+        v[i] = __uint_as_float((unsigned)w[i]);
+        pend &= ~(1u << i);
+      }
+    if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
+  }
+  return true;
+}
+
+// Work split shared by both wave roles.
+struct Geo {
+  int a_row0, a_row_end, c_row0, c_row_end;
+  bool has_b;
+  int bh, bcb, bg;
+};
+
+template <int BITS, int D>
+__device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid) {
+  const float ss = (sm.stat[0] + sm.stat[1]) + (sm.stat[2] + sm.stat[3]);
+  const float mx = fmaxf(fmaxf(sm.stat[4], sm.stat[5]), fmaxf(sm.stat[6], sm.stat[7]));
+  const float scale = (a.flags & DN_X_RMSNORM) ? rsqrtf(ss / (float)D + a.eps_rms) : 1.0f;
+  float s1 = mx * scale * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+  for (int c = tid; c < D; c += NTHR) {
+    int8_t h, m, lo;
+    split3(sm.raw[c] * scale, s1, inv1, s2, inv2, inv3, h, m, lo);
+    const int p = xpos<BITS>(c);
+    sm.xs[p] = h;
+    sm.xs[D + p] = m;
+    sm.xs[2 * D + p] = lo;
+  }
+  if (tid == 0) sm.stat[8] = s1;
+}
+
+template <int BITS, int V, int DV>
+__device__ __forceinline__ void split_y(Smem& sm, int tid) {
+  float s1 = fmaxf(fmaxf(sm.stat[9], sm.stat[10]), fmaxf(sm.stat[11], sm.stat[12])) * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+  for (int c = tid; c < V; c += NTHR) {
+    int8_t h, m, lo;
+    split3(sm.raw[c] * sm.inv[c / DV], s1, inv1, s2, inv2, inv3, h, m, lo);
+    const int p = xpos<BITS>(c);
+    sm.ys[p] = h;
+    sm.ys[V + p] = m;
+    sm.ys[2 * V + p] = lo;
+  }
+  if (tid == 0) sm.stat[13] = s1;
+}
+
+// Compute waves: phase A and phase C, weights prefetched one layer ahead in registers.
+template <int BITS, int NCHA, int NCHC, int RA, int RC>
+__device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
+                                             int tid, int lane) {
+  constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
+  constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC, DV = 128;
+  constexpr int rowbytes_in = BITS == 8 ? D : D / 2;
+  constexpr int rowbytes_out = BITS == 8 ? V : V / 2;
+  const int C = a.C, K = a.K;
+  v4i wa[RA][NCHA];
+  v4i wc[RC][NCHC];
+  float ra_s = 0.f, ra_cw[4] = {0.f, 0.f, 0.f, 0.f}, ra_ring[3] = {0.f, 0.f, 0.f};
+  float rc_s = 0.f;
+
+  auto load_a = [&](int l) {
+    const LayerW& W = a.layers[l];
+    const int8_t* wbase = reinterpret_cast<const int8_t*>(W.w_in);
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      const int r = g.a_row0 + i;
+#pragma unroll
+      for (int k = 0; k < NCHA; ++k) {
+        if (r < g.a_row_end)
+          wa[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_in) + lane + 64 * k);
+        else
+          wa[i][k] = v4i{0, 0, 0, 0};
+      }
+    }
+    const int r = g.a_row0 + lane;
+    if (lane < RA && r < g.a_row_end) {
+      ra_s = W.s_in[r];
+      if (r < C) {
+        const float* cwp = W.conv_w + (size_t)r * K;
+        const float* rg = a.ring + (size_t)l * (K - 1) * C + r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ra_cw[j] = j < K ? cwp[j] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) ra_ring[j] = j < K - 1 ? rg[(size_t)j * C] : 0.f;
+      }
+    }
+  };
+  auto load_c = [&](int l) {
+    const LayerW& W = a.layers[l];
+    const int8_t* wbase = reinterpret_cast<const int8_t*>(W.w_out);
+#pragma unroll
+    for (int i = 0; i < RC; ++i) {
+      const int r = g.c_row0 + i;
+#pragma unroll
+      for (int k = 0; k < NCHC; ++k) {
+        if (r < g.c_row_end)
+          wc[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_out) + lane + 64 * k);
+        else
+          wc[i][k] = v4i{0, 0, 0, 0};
+      }
+    }
+    const int r = g.c_row0 + lane;
+    if (lane < RC && r < g.c_row_end) rc_s = W.s_out[r];
+  };
+
+  load_a(0);
+  load_c(0);
+  for (int l = 0; l < a.L; ++l) {
+    const unsigned tag = base_tag + (unsigned)l;
+    __syncthreads();  // (1) raw x staged
+    if (sm.abort_flag) break;
+    split_x<BITS, D>(sm, a, tid);
+    __syncthreads();  // (2) x split staged
+    {
+      // phase A: in_proj + conv + SiLU
+      const float s1 = sm.stat[8];
+      int acc[RA][3];
+      dot_rows<BITS, RA, NCHA>(wa, sm.xs, D, lane, acc);
+      const float dot = reduce_rows<BITS, RA>(acc, s1, lane);
+      const int r = g.a_row0 + lane;
+      if (lane < RA && r < g.a_row_end) {
+        const float u = ra_s * dot;
+        float outv = u;
+        if (r < C) {
+          float accv = ra_cw[K - 1] * u;
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            if (j < K - 1) accv = fmaf(ra_cw[j], ra_ring[j], accv);
+          float* rg = a.ring + (size_t)l * (K - 1) * C + r;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (j + 1 < K - 1) rg[(size_t)j * C] = ra_ring[j + 1];
+          if (K > 1) rg[(size_t)(K - 2) * C] = u;
+          outv = silu(accv);
+        }
+        ll_store(a.U + r, outv, tag);
+      }
+      if (l + 1 < a.L) load_a(l + 1);
+    }
+    __syncthreads();  // (3) gated readout staged
+    if (sm.abort_flag) break;
+    split_y<BITS, V, DV>(sm, tid);
+    __syncthreads();  // (4) y split staged
+    {
+      // phase C: out_proj
+      const float s1 = sm.stat[13];
+      int acc[RC][3];
+      dot_rows<BITS, RC, NCHC>(wc, sm.ys, V, lane, acc);
+      const float dot = reduce_rows<BITS, RC>(acc, s1, lane);
+      const int r = g.c_row0 + lane;
+      if (lane < RC && r < g.c_row_end) {
+        const float o = rc_s * dot;
+        a.out[(size_t)l * D + r] = o;
+        if (l + 1 < a.L) ll_store(a.X + r, o, tag);
+      }
+      if (l + 1 < a.L) load_c(l + 1);
+    }
+  }
+}
+
+// Communication waves: poll and stage x and the gated readout; the first one also runs phase B.
+template <int BITS, int NCHA, int NCHC>
+__device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
+                                          int tid, int lane, int cw, int wg) {
+  constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
+  constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC, DV = 128;
+  constexpr int XW = D / (64 * NCM);  // x words per lane
+  constexpr int GW = V / (64 * NCM);  // gated readout words per lane
+  constexpr int nblk = DV / CB;
+  constexpr int GSEG = V / NCM + 64;  // words per communication wave segment of the G buffer
+  static_assert(XW <= 32 && GW < 32, "");
+  const int C = a.C, QK = a.QK, Hv = a.Hv;
+  const int npart = Hv * nblk;
+  const unsigned* err = &a.ctl->error;
+  v4f st[2][CB / 4];  // rows lane and lane+64 of the state slice
+  auto s_slice = [&](int l) { return a.S + (((size_t)l * Hv + g.bh) * nblk + g.bcb) * (DK * CB); };
+  auto load_s = [&](int l) {
+    const float* S = s_slice(l);
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+      for (int q = 0; q < CB / 4; ++q)
+        st[hlf][q] = *reinterpret_cast<const v4f*>(S + (size_t)(lane + 64 * hlf) * CB + 4 * q);
+  };
+  auto fail = [&]() {
+    if (lane == 0) {
+      sm.abort_flag = 1;
+      coherent_store_u32(&a.ctl->error, 1u);
+    }
+  };
+  const bool runs_b = cw == 0 && g.has_b;
+  if (runs_b) load_s(0);
+
+  for (int l = 0; l < a.L; ++l) {
+    const unsigned tag = base_tag + (unsigned)l;
+    // stage x: this wave polls a quarter of the columns
+    {
+      float xv[XW];
+      const int col0 = cw * (D / NCM) + lane;
+      bool ok = true;
+      if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < XW; ++i) xv[i] = a.x[col0 + 64 * i];
+      } else {
+        ok = poll_words<XW, 64>(a.X + col0, tag - 1, xv, XW, err);
+      }
+      float ss = 0.f, mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < XW; ++i) {
+        sm.raw[col0 + 64 * i] = xv[i];
+        ss = fmaf(xv[i], xv[i], ss);
+        mx = fmaxf(mx, fabsf(xv[i]));
+      }
+      ss = wsum(ss);
+      mx = wmax(mx);
+      if (lane == 0) {
+        sm.stat[cw] = ss;
+        sm.stat[4 + cw] = mx;
+      }
+      if (!__all(ok)) fail();
+    }
+    __syncthreads();  // (1)
+    if (sm.abort_flag) break;
+    split_x<BITS, D>(sm, a, tid);
+    __syncthreads();  // (2)
+
+    bool ok = true;
+    if (runs_b) {
+      // phase B: recurrence on the 128 x 16 state slice (rows lane and lane+64)
+      const int vcol = g.bh * DV + g.bcb * CB;
+      // q and k rows lane and lane+64 of key head bg; lanes < 16 also v and z of column lane
+      const int qo = g.bg * DK + lane;
+      const int off[6] = {qo, qo + 64, QK + qo, QK + qo + 64, 2 * QK + vcol + lane, C + vcol + lane};
+      float val[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      ok = poll_words_at<6>(a.U, off, tag, val, lane < CB ? 6u : 4u, err);
+      if (__all(ok)) {
+        double sq = (double)val[0] * val[0] + (double)val[1] * val[1];
+        double sk = (double)val[2] * val[2] + (double)val[3] * val[3];
+        sq = wsum(sq);
+        sk = wsum(sk);
+        const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
+        const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
+        const float q0 = val[0] * qn, q1 = val[1] * qn, k0 = val[2] * kn, k1 = val[3] * kn;
+        const float alpha = a.alpha[(size_t)l * Hv + g.bh], beta = a.beta[(size_t)l * Hv + g.bh];
+        float s0[CB], s1v[CB], p[CB];
+#pragma unroll
+        for (int q = 0; q < CB / 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s0[4 * q + e] = alpha * st[0][q][e];
+            s1v[4 * q + e] = alpha * st[1][q][e];
+          }
+#pragma unroll
+        for (int j = 0; j < CB; ++j) p[j] = fmaf(s0[j], k0, s1v[j] * k1);
+        const float kv = rs16(p, lane);  // column lane >> 2
+        const int jc = lane >> 2;
+        const float vj = __shfl(val[4], jc);
+        const float dl = beta * (vj - kv);
+        float d[CB];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) d[j] = __shfl(dl, 4 * j);
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+          s0[j] = fmaf(k0, d[j], s0[j]);
+          s1v[j] = fmaf(k1, d[j], s1v[j]);
+          p[j] = fmaf(s0[j], q0, s1v[j] * q1);
+        }
+        float* S = s_slice(l);
+#pragma unroll
+        for (int q = 0; q < CB / 4; ++q) {
+          *reinterpret_cast<v4f*>(S + (size_t)lane * CB + 4 * q) =
+              v4f{s0[4 * q], s0[4 * q + 1], s0[4 * q + 2], s0[4 * q + 3]};
+          *reinterpret_cast<v4f*>(S + (size_t)(lane + 64) * CB + 4 * q) =
+              v4f{s1v[4 * q], s1v[4 * q + 1], s1v[4 * q + 2], s1v[4 * q + 3]};
+        }
+        const float o = rs16(p, lane);  // readout of column lane >> 2
+        const float zj = __shfl(val[5], jc);
+        const float gt = a.layers[l].norm_w[g.bcb * CB + jc] * o * silu(zj);
+        const float osq = wsum((lane & 3) == 0 ? o * o : 0.f);
+        // G buffer: NCM segments of [V/NCM gated columns | partials of the same heads]
+        const int gc = vcol + jc, gw = gc / (V / NCM);
+        if ((lane & 3) == 0) ll_store(a.G + gw * GSEG + (gc - gw * (V / NCM)), gt, tag);
+        const int pw = g.bh / (Hv / NCM);
+        if (lane == 0) ll_store(a.G + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
+        if (l + 1 < a.L) load_s(l + 1);
+      }
+    }
+    if (__all(ok)) {
+      // stage the gated readout: value columns [cw*V/NCM, (cw+1)*V/NCM) and the partials of those
+      // heads, which follow them in this wave's segment of the buffer
+      float gv[GW + 1];
+#pragma unroll
+      for (int i = 0; i <= GW; ++i) gv[i] = 0.f;
+      const int pn = npart / NCM, pbase = cw * pn;
+      ok = poll_words<GW + 1, 64>(a.G + cw * GSEG + lane, tag, gv, lane < pn ? GW + 1 : GW, err);
+      constexpr int PW = 1;
+      const float pv[PW] = {gv[GW]};
+      const int gcol0 = cw * (V / NCM) + lane;
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        float s = pv[i];
+#pragma unroll
+        for (int o = 1; o < nblk; o <<= 1) s += __shfl_xor(s, o);
+        const int q = lane + 64 * i;
+        if ((lane % nblk) == 0 && q < pn) sm.inv[(pbase + q) / nblk] = rsqrtf(s / (float)DV + a.eps_rms);
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const int c = gcol0 + 64 * i;
+        sm.raw[c] = gv[i];
+        mx = fmaxf(mx, fabsf(gv[i] * sm.inv[c / DV]));
+      }
+      mx = wmax(mx);
+      if (lane == 0) sm.stat[9 + cw] = mx;
+    }
+    if (!__all(ok)) fail();
+    __syncthreads();  // (3)
+    if (sm.abort_flag) break;
+    split_y<BITS, V, DV>(sm, tid);
+    __syncthreads();  // (4)
+  }
+}
+
+template <int BITS, int NCHA, int NCHC, int RA, int RC>
+__global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
+  constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
+  constexpr int D = COLS_PER_CHUNK * NCHA;
+  constexpr int nblk = 128 / CB;
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NWG = gridDim.x, wg = blockIdx.x;
+  const unsigned base_tag = coherent_load_u32(&a.ctl->epoch);
+
+  Geo g;
+  const int a_per_wg = (a.R + NWG - 1) / NWG;
+  const int a_per_wave = (a_per_wg + NCW - 1) / NCW;
+  g.a_row0 = wg * a_per_wg + wave * a_per_wave;
+  g.a_row_end = min(min(wg * a_per_wg + a_per_wg, a.R), g.a_row0 + a_per_wave);
+  const int c_per_wg = (D + NWG - 1) / NWG;
+  const int c_per_wave = (c_per_wg + NCW - 1) / NCW;
+  g.c_row0 = wg * c_per_wg + wave * c_per_wave;
+  g.c_row_end = min(min(wg * c_per_wg + c_per_wg, D), g.c_row0 + c_per_wave);
+  g.has_b = wg < a.Hv * nblk;
+  g.bh = g.has_b ? wg / nblk : 0;
+  g.bcb = g.has_b ? wg % nblk : 0;
+  g.bg = g.bh / (a.Hv / a.Hk);
+
+  if (tid == 0) sm.abort_flag = 0;
+  // The two roles run separate loops with the same sequence of four workgroup barriers per
+  // layer, so each role's registers are its own.
+  if (wave < NCW) compute_role<BITS, NCHA, NCHC, RA, RC>(sm, a, g, base_tag, tid, lane);
+  else comm_role<BITS, NCHA, NCHC>(sm, a, g, base_tag, tid, lane, wave - NCW, wg);
+
+  // the last workgroup to finish advances the tag base for the next launch
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == (unsigned)NWG - 1) {
+      coherent_store_u32(&a.ctl->done, 0u);
+      coherent_store_u32(&a.ctl->epoch, base_tag + (unsigned)a.L);
+    }
+  }
+}
+
+template <int BITS, int NCHA, int NCHC>
+hipError_t go(const PersistArgs& a, int nwg, hipStream_t st) {
+  hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1>), dim3(nwg), dim3(NTHR), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int NCHA, int NCHC>
+hipError_t occ(int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1>, NTHR, 0);
+}
+
+}  // namespace
+
+// Chunk counts (16-byte chunks per lane) of an in_proj and out_proj row, or 0 if unsupported.
+static int chunks(int cols, int bits) {
+  const int bytes = bits == 8 ? cols : cols / 2;
+  if (bytes % 1024) return 0;
+  return bytes / 1024;
+}
+
+bool persist_supported(const PersistShape& s, int nwg) {
+  if (s.batch != 1 || s.dk != DK || s.dv != 128 || s.K < 1 || s.K > 4) return false;
+  const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
+  const bool inst = s.bits == 8 ? ((na == 2 && nc == 4) || (na == 1 && nc == 1))
+                                : ((na == 1 && nc == 2) || (na == 1 && nc == 1));
+  if (!inst) return false;
+  if (s.D > 4096 || s.V > 4096 || s.Hv > 32 || (s.Hv % NCM)) return false;
+  if (s.Hv * (s.dv / CB) > nwg) return false;
+  const int a_per_wg = (s.R + nwg - 1) / nwg, c_per_wg = (s.D + nwg - 1) / nwg;
+  if ((a_per_wg + NCW - 1) / NCW > 6 || (c_per_wg + NCW - 1) / NCW > 1) return false;
+  return true;
+}
+
+hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu) {
+  const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
+  if (s.bits == 8) return na == 2 ? occ<8, 2, 4>(blocks_per_cu) : occ<8, 1, 1>(blocks_per_cu);
+  return nc == 2 ? occ<4, 1, 2>(blocks_per_cu) : occ<4, 1, 1>(blocks_per_cu);
+}
+
+hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, hipStream_t st) {
+  const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
+  if (s.bits == 8) return na == 2 ? go<8, 2, 4>(a, nwg, st) : go<8, 1, 1>(a, nwg, st);
+  return nc == 2 ? go<4, 1, 2>(a, nwg, st) : go<4, 1, 1>(a, nwg, st);
+}
+
+// Canonical state [L][Hv][dk][dv] <-> tiled [L][Hv][dv/16][dk][16].
+__global__ void k_state_tile(const float* __restrict__ src, float* __restrict__ dst, int L, int Hv, int dk, int dv,
+                             int to_tiled) {
+  const size_t n = (size_t)L * Hv * dk * dv;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+    const int j = (int)(e % dv);
+    size_t t = e / dv;
+    const int i = (int)(t % dk);
+    t /= dk;  // l * Hv + h
+    const size_t tiled = ((t * (dv / CB) + j / CB) * dk + i) * CB + (j % CB);
+    if (to_tiled) dst[tiled] = src[e];
+    else dst[e] = src[tiled];
+  }
+}
+
+hipError_t launch_state_tile(const float* src, float* dst, int L, int Hv, int dk, int dv, bool to_tiled,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(k_state_tile, dim3(1024), dim3(256), 0, st, src, dst, L, Hv, dk, dv, to_tiled ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace dn

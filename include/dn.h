@@ -32,6 +32,17 @@ extern "C" {
 #define DN_E_DISABLED -4  /* dn_step after a failed step; dn_set_state re-arms */
 #define DN_E_FAULT    -5  /* injected failure (environment DN_FAULT_STEP=n fails the n-th dn_step, 1-based) */
 
+/* Environment read by dn_create:
+ *   DN_FAULT_STEP=n     fail the n-th dn_step of the handle before it launches anything
+ *   DN_SYNC_DEBUG=1     synchronise after every launch and check for errors
+ *   DN_LAYER_KERNELS=1  use the per-layer kernels even where the whole-stack kernel applies
+ *   DN_VERBOSE=1        print which path the handle uses to stderr
+ *
+ * Execution paths. A single-sequence handle (batch 1) with d_k = d_v = 128 and supported widths
+ * runs each dn_step as one whole-stack kernel launch that occupies every compute unit of the
+ * device; two such steps must not run concurrently on one device (issue them on one stream).
+ * Other shapes run three kernels per layer. */
+
 /* dn_config.flags */
 #define DN_X_RMSNORM 1u   /* RMS-normalise each layer's input, x / sqrt(mean(x^2) + eps_rms) (stack pre-norm) */
 
