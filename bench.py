@@ -34,6 +34,8 @@ def main():
     ap.add_argument("--config", default="stack", choices=["stack", "stack_int4", "layer", "batched"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 10 times (reference for the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -44,6 +46,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": src.numel() * 4,
+                          "copy_calibration_bytes_written_per_launch": dst.numel() * 4}))
+        return
 
     import dn_inputs as gi
     import gated_deltanet_layer_dn_amd as dn

@@ -13,7 +13,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdn.so")
+# DN_LIB selects another build of the library (an instrumented one, for instance)
+LIB_PATH = os.environ.get("DN_LIB") or os.path.join(_PKG, "libdn.so")
 
 DN_OK, DN_E_INVAL, DN_E_NOMEM, DN_E_DEVICE, DN_E_DISABLED, DN_E_FAULT = 0, -1, -2, -3, -4, -5
 DN_X_RMSNORM = 1

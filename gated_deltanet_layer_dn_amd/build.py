@@ -25,9 +25,12 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + sources()
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile libdn.so; `defines` adds preprocessor macros (DN_PHASE_TIMERS for an
+    instrumented build written to `out`)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                                                          "-o", tmp] + sources()
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,8 +39,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + errs)
     if verbose and errs.strip():
         print(errs, flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -40,6 +40,7 @@ struct dn_layer {
   dn::Ctl* ctl = nullptr;
   float* stage = nullptr;   // canonical-layout staging of the state for set/get
   unsigned* err_host = nullptr;  // pinned copy of the device error flag, refreshed after each step
+  unsigned long long* timers = nullptr;  // instrumented builds: phase timestamps of the last step
   bool disabled = false;
   long steps = 0;
   long fault_step = 0;    // 1-based step to fail (0 = never)
@@ -87,6 +88,7 @@ void free_all(dn_layer* h) {
   dfree(h->stage);
   if (h->err_host) (void)hipHostFree(h->err_host);
   h->err_host = nullptr;
+  dfree(h->timers);
 }
 
 // Set up the whole-stack kernel when the shape allows it: hand-off buffers, control words,
@@ -105,21 +107,25 @@ int setup_persist(dn_layer* h) {
   if (dn::persist_occupancy(ps, &per_cu) != hipSuccess || per_cu < 1) return DN_OK;
   const size_t L = c.n_layers;
   bool ok = hipMalloc(&h->d_layers, sizeof(dn::LayerW) * L) == hipSuccess;
-  ok = ok && hipMalloc(&h->X, sizeof(uint64_t) * c.d_model) == hipSuccess;
+  ok = ok && hipMalloc(&h->X, sizeof(uint64_t) * 8 * c.d_model) == hipSuccess;
   ok = ok && hipMalloc(&h->U, sizeof(uint64_t) * h->R) == hipSuccess;
-  ok = ok && hipMalloc(&h->G, sizeof(uint64_t) * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMalloc(&h->G, sizeof(uint64_t) * 8 * (h->V + 256)) == hipSuccess;
   ok = ok && hipMalloc(&h->ctl, sizeof(dn::Ctl)) == hipSuccess;
   ok = ok && hipMalloc(&h->stage, sizeof(float) * L * h->s_elems) == hipSuccess;
   ok = ok && hipHostMalloc(&h->err_host, sizeof(unsigned)) == hipSuccess;
+#ifdef DN_PHASE_TIMERS
+  ok = ok && hipMalloc(&h->timers, sizeof(unsigned long long) * h->nwg * L * 32) == hipSuccess;
+  ok = ok && hipMemset(h->timers, 0, sizeof(unsigned long long) * h->nwg * L * 32) == hipSuccess;
+#endif
   if (!ok) return DN_E_NOMEM;
   std::vector<dn::LayerW> lw(L);
   for (size_t l = 0; l < L; ++l)
     lw[l] = dn::LayerW{h->w[l].w_in, h->w[l].s_in, h->w[l].conv_w, h->w[l].norm_w, h->w[l].w_out, h->w[l].s_out};
   const dn::Ctl ctl0{1u, 0u, 0u, 0u};
   ok = hipMemcpy(h->d_layers, lw.data(), sizeof(dn::LayerW) * L, hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemset(h->X, 0, sizeof(uint64_t) * c.d_model) == hipSuccess;
+  ok = ok && hipMemset(h->X, 0, sizeof(uint64_t) * 8 * c.d_model) == hipSuccess;
   ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * h->R) == hipSuccess;
-  ok = ok && hipMemset(h->G, 0, sizeof(uint64_t) * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMemset(h->G, 0, sizeof(uint64_t) * 8 * (h->V + 256)) == hipSuccess;
   ok = ok && hipMemcpy(h->ctl, &ctl0, sizeof(ctl0), hipMemcpyHostToDevice) == hipSuccess;
   if (!ok) return DN_E_DEVICE;
   *h->err_host = 0;
@@ -256,7 +262,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     if (*h->err_host) return fail(h, DN_E_DEVICE);  // a previous launch reported a stalled hand-off
     dn::PersistArgs a{};
     a.layers = h->d_layers; a.S = h->S; a.ring = h->ring; a.x = x; a.alpha = alpha; a.beta = beta; a.out = out;
-    a.X = h->X; a.U = h->U; a.G = h->G; a.ctl = h->ctl;
+    a.X = h->X; a.U = h->U; a.G = h->G; a.ctl = h->ctl; a.timers = h->timers;
     a.L = (int)L; a.R = h->R; a.C = h->C; a.QK = c.n_k_heads * c.d_k; a.K = c.conv_k;
     a.Hk = c.n_k_heads; a.Hv = c.n_v_heads; a.flags = c.flags;
     a.eps_l2 = c.eps_l2; a.eps_rms = c.eps_rms; a.q_scale = c.q_scale;
@@ -304,6 +310,17 @@ DN_API void dn_destroy(dn_layer* h) {
   if (!h) return;
   (void)hipSetDevice(h->device);
   (void)hipDeviceSynchronize();
+#ifdef DN_PHASE_TIMERS
+  if (const char* path = std::getenv("DN_PHASE_TIMERS"); path && h->timers) {
+    std::vector<unsigned long long> t((size_t)h->nwg * h->cfg.n_layers * 32);
+    if (hipMemcpy(t.data(), h->timers, t.size() * sizeof(t[0]), hipMemcpyDeviceToHost) == hipSuccess) {
+      if (FILE* f = std::fopen(path, "wb")) {
+        std::fwrite(t.data(), sizeof(t[0]), t.size(), f);
+        std::fclose(f);
+      }
+    }
+  }
+#endif
   free_all(h);
   delete h;
 }

@@ -67,11 +67,13 @@ struct PersistArgs {
   const float* alpha;    // [L][Hv]
   const float* beta;     // [L][Hv]
   float* out;            // [L][D]
-  uint64_t* X;           // [D]  tagged layer output
+  uint64_t* X;           // [8][D]  tagged layer output, one copy per XCD
   uint64_t* U;           // [R]  tagged in_proj output (post-conv q|k|v, raw z)
-  uint64_t* G;           // [V + 256] tagged gated readout and partial sums of squares of the
-                         // readout, in four segments [V/4 columns | partials of those heads | pad]
+  uint64_t* G;           // [8][V + 256] tagged gated readout and partial sums of squares of the
+                         // readout, in four segments [V/4 columns | partials of those heads | pad],
+                         // one copy per XCD
   Ctl* ctl;
+  unsigned long long* timers;  // instrumented builds only: [NWG][L][16] phase timestamps
   int L, R, C, QK, K, Hk, Hv;
   unsigned flags;
   float eps_l2, eps_rms, q_scale;

@@ -44,6 +44,39 @@ constexpr int NTHR = (NCW + NCM) * 64;
 constexpr int DK = 128;                // key rows of a state tile
 constexpr int CB = 16;                 // value columns per phase-B workgroup
 constexpr unsigned SPIN_CAP = 1u << 22;
+constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
+// Weight prefetch throttle: a compute wave keeps at most this many 1 KiB row-chunk loads in
+// flight, so that the compute unit's memory pipeline is never full and the communication
+// waves' hand-off loads and stores are not queued behind a whole layer of weights.
+#ifndef DN_PREFETCH_INFLIGHT
+#define DN_PREFETCH_INFLIGHT 4
+#endif
+static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
+// s_waitcnt with vmcnt <= n and the other counters unconstrained
+#define DN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
+// Instrumented builds (-DDN_PHASE_TIMERS) record the 100 MHz wall clock at phase boundaries.
+#ifdef DN_PHASE_TIMERS
+#define DN_MARK(a, l, k)                                                                       \
+  do {                                                                                         \
+    if ((threadIdx.x & 63) == 0)                                                               \
+      (a).timers[((size_t)blockIdx.x * (a).L + (l)) * 32 + (k)] = wall_clock64();              \
+  } while (0)
+#define DN_TS(a, l, k) ((a).timers + ((size_t)blockIdx.x * (a).L + (l)) * 32 + (k))
+#define DN_COUNT(a, l, k, v)                                                                   \
+  do {                                                                                         \
+    if ((threadIdx.x & 63) == 0) (a).timers[((size_t)blockIdx.x * (a).L + (l)) * 32 + (k)] = (v); \
+  } while (0)
+#else
+#define DN_MARK(a, l, k) \
+  do {                   \
+  } while (0)
+#define DN_TS(a, l, k) ((a).timers + ((size_t)blockIdx.x * (a).L + (l)) * 32 + (k))
+#define DN_COUNT(a, l, k, v) \
+  do {                       \
+  } while (0)
+#define DN_TS(a, l, k) nullptr
+#endif
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
@@ -179,13 +212,68 @@ __device__ __forceinline__ void dot_rows(const v4i (&w)[RB][NCH], const int8_t* 
   }
 }
 
+struct Smem {
+  float raw[4096];         // staged layer input x, fp32
+  float yf[4096];          // gated, normalised readout y (input of out_proj), fp32
+  int8_t xs[3 * 4096];     // three-term split of x for phase A
+  float inv[64];           // per value head 1/rms of the readout
+  float stat[16];          // partial statistics from the communication waves, split scale
+  float gate[MAXL][2];     // alpha, beta of this workgroup's value head, per layer
+  float nw[MAXL][CB];      // gated RMSNorm weights of this workgroup's value columns, per layer
+  int a_done, b_done, c_done;  // progress counters of this workgroup's waves
+  int abort_flag;
+};
+
+// Wait (within the workgroup) until an LDS progress counter reaches `target` or the workgroup
+// aborts. The waves that advance the counter never wait on the waiting wave, so this ends.
+__device__ __forceinline__ void wait_counter(const int* ctr, int target, const int* abort_flag) {
+  while (__hip_atomic_load(const_cast<int*>(ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target &&
+         !__hip_atomic_load(const_cast<int*>(abort_flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+    __builtin_amdgcn_s_sleep(1);
+}
+__device__ __forceinline__ int bump_counter(int* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Replicas of the broadcast hand-off buffers: producers write one copy per XCD and each consumer
+// reads the copy of its own XCD, so a polled line is shared by the 32 workgroups of one XCD
+// rather than by all 256.
+constexpr int NREP = 8;
+__device__ __forceinline__ int xcd_id() { return (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7); }
+
+// Sum over the 64 lanes of a wave with DPP lane permutations (pairs, quads, half rows, rows,
+// then across rows); the total is returned uniformly. Fixed order: run-to-run identical.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ int wave_total_i(int v) {
+  v += dpp_i<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_i<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_i<0x141>(v);       // row_half_mirror
+  v += dpp_i<0x140>(v);       // row_mirror
+  v += dpp_i<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float wave_total_f(float x) {
+  int v = __float_as_int(x);
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0xB1>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0x4E>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0x141>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0x140>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0x142, 0xA>(v)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0x143, 0xC>(v)));
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
 // Reduce the lane partials of RB rows; lane i (< RB) receives row i's dot product.
 template <int BITS, int RB>
 __device__ __forceinline__ float reduce_rows(int (&acc)[RB][3], float s1, int lane) {
   float mine = 0.f;
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    int th = wsum(acc[i][0]), tm = wsum(acc[i][1]), tl = wsum(acc[i][2]);
+    int th = wave_total_i(acc[i][0]), tm = wave_total_i(acc[i][1]), tl = wave_total_i(acc[i][2]);
     if (BITS == 4) {  // products carried a factor 16
       th >>= 4;
       tm >>= 4;
@@ -197,15 +285,6 @@ __device__ __forceinline__ float reduce_rows(int (&acc)[RB][3], float s1, int la
   return mine;
 }
 
-struct Smem {
-  float raw[4096];         // staged activations (x or gated readout), fp32
-  int8_t xs[3 * 4096];     // three-term split of x for phase A
-  int8_t ys[3 * 4096];     // three-term split of y for phase C
-  float inv[64];           // per value head 1/rms of the readout
-  float stat[16];          // partial statistics from the communication waves, split scales
-  int abort_flag;
-};
-
 // Poll N tagged words per lane, word i at base + i * STRIDE, until every one carries `want`;
 // values go to v[]. Returns false if the spin cap is hit or another workgroup reported an error.
 // The base pointer is laundered through an empty asm statement each round so that the compiler
@@ -213,7 +292,8 @@ struct Smem {
 // 64-bit addresses alive across the loop.
 template <int N, int STRIDE>
 __device__ __forceinline__ bool poll_words(const uint64_t* base, unsigned want, float (&v)[N], unsigned nvalid,
-                                           const unsigned* err) {
+                                           const unsigned* err, unsigned* rounds = nullptr,
+                                           unsigned long long* round_ts = nullptr) {
   static_assert(N <= 32, "at most 32 words per lane per poll");
   unsigned pend = N == 32 ? 0xFFFFFFFFu : ((1u << N) - 1u);
   pend &= nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
@@ -231,15 +311,20 @@ __device__ __forceinline__ bool poll_words(const uint64_t* base, unsigned want, 
         v[i] = __uint_as_float((unsigned)w[i]);
         pend &= ~(1u << i);
       }
+#ifdef DN_PHASE_TIMERS
+    if (round_ts && it < 4 && (threadIdx.x & 63) == 0) round_ts[it] = wall_clock64();
+#endif
     if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
   }
+  if (rounds) *rounds = it;
   return true;
 }
 
 // As poll_words, with word i at base + off[i] (element offsets).
 template <int N>
 __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&off)[N], unsigned want, float (&v)[N],
-                                              unsigned nvalid, const unsigned* err) {
+                                              unsigned nvalid, const unsigned* err, unsigned* rounds = nullptr,
+                                              unsigned long long* round_ts = nullptr) {
   unsigned pend = (1u << N) - 1u;
   pend &= (1u << nvalid) - 1u;
   unsigned it = 0;
@@ -256,13 +341,18 @@ __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&
         v[i] = __uint_as_float((unsigned)w[i]);
         pend &= ~(1u << i);
       }
+#ifdef DN_PHASE_TIMERS
+    if (round_ts && it < 4 && (threadIdx.x & 63) == 0) round_ts[it] = wall_clock64();
+#endif
     if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
   }
+  if (rounds) *rounds = it;
   return true;
 }
 
 // Work split shared by both wave roles.
 struct Geo {
+  int a_per_wg;
   int a_row0, a_row_end, c_row0, c_row_end;
   bool has_b;
   int bh, bcb, bg;
@@ -287,28 +377,12 @@ __device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid)
   if (tid == 0) sm.stat[8] = s1;
 }
 
-template <int BITS, int V, int DV>
-__device__ __forceinline__ void split_y(Smem& sm, int tid) {
-  float s1 = fmaxf(fmaxf(sm.stat[9], sm.stat[10]), fmaxf(sm.stat[11], sm.stat[12])) * (1.0f / 127.0f);
-  if (!(s1 > 0.f)) s1 = 1.0f;
-  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
-  for (int c = tid; c < V; c += NTHR) {
-    int8_t h, m, lo;
-    split3(sm.raw[c] * sm.inv[c / DV], s1, inv1, s2, inv2, inv3, h, m, lo);
-    const int p = xpos<BITS>(c);
-    sm.ys[p] = h;
-    sm.ys[V + p] = m;
-    sm.ys[2 * V + p] = lo;
-  }
-  if (tid == 0) sm.stat[13] = s1;
-}
-
 // Compute waves: phase A and phase C, weights prefetched one layer ahead in registers.
 template <int BITS, int NCHA, int NCHC, int RA, int RC>
 __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
                                              int tid, int lane) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
-  constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC, DV = 128;
+  constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC;
   constexpr int rowbytes_in = BITS == 8 ? D : D / 2;
   constexpr int rowbytes_out = BITS == 8 ? V : V / 2;
   const int C = a.C, K = a.K;
@@ -325,6 +399,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       const int r = g.a_row0 + i;
 #pragma unroll
       for (int k = 0; k < NCHA; ++k) {
+        if ((i * NCHA + k) >= DN_PREFETCH_INFLIGHT) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
         if (r < g.a_row_end)
           wa[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_in) + lane + 64 * k);
         else
@@ -352,6 +427,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       const int r = g.c_row0 + i;
 #pragma unroll
       for (int k = 0; k < NCHC; ++k) {
+        if ((i * NCHC + k) >= DN_PREFETCH_INFLIGHT) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
         if (r < g.c_row_end)
           wc[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_out) + lane + 64 * k);
         else
@@ -370,6 +446,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
     if (sm.abort_flag) break;
     split_x<BITS, D>(sm, a, tid);
     __syncthreads();  // (2) x split staged
+    if (tid == 0) DN_MARK(a, l, 2);
     {
       // phase A: in_proj + conv + SiLU
       const float s1 = sm.stat[8];
@@ -394,30 +471,87 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
         }
         ll_store(a.U + r, outv, tag);
       }
+      if (lane == 0) bump_counter(&sm.a_done);
+      if (tid == 0) DN_MARK(a, l, 3);
       if (l + 1 < a.L) load_a(l + 1);
     }
     __syncthreads();  // (3) gated readout staged
     if (sm.abort_flag) break;
-    split_y<BITS, V, DV>(sm, tid);
-    __syncthreads();  // (4) y split staged
+    if (tid == 0) DN_MARK(a, l, 7);
     {
-      // phase C: out_proj
-      const float s1 = sm.stat[13];
-      int acc[RC][3];
-      dot_rows<BITS, RC, NCHC>(wc, sm.ys, V, lane, acc);
-      const float dot = reduce_rows<BITS, RC>(acc, s1, lane);
-      const int r = g.c_row0 + lane;
-      if (lane < RC && r < g.c_row_end) {
-        const float o = rc_s * dot;
-        a.out[(size_t)l * D + r] = o;
-        if (l + 1 < a.L) ll_store(a.X + r, o, tag);
+      // phase C: out_proj in fp32 on the staged readout. Weight bytes are biased to unsigned
+      // (w + 128, or w + 8 for nibbles) for the byte conversions; the bias times sum(y) is
+      // removed after the row sum.
+      const float sumy = (sm.stat[9] + sm.stat[10]) + (sm.stat[11] + sm.stat[12]);
+      float acc[RC];
+#pragma unroll
+      for (int i = 0; i < RC; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NCHC; ++k) {
+        const int c = lane + 64 * k;
+        if (BITS == 8) {
+          const v4f* Y = reinterpret_cast<const v4f*>(sm.yf + 16 * c);
+          const v4f y0 = Y[0], y1 = Y[1], y2 = Y[2], y3 = Y[3];
+          const v4f yq[4] = {y0, y1, y2, y3};
+#pragma unroll
+          for (int i = 0; i < RC; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const unsigned u = (unsigned)wc[i][k][e] ^ 0x80808080u;
+              acc[i] = fmaf((float)(u & 0xFFu), yq[e][0], acc[i]);
+              acc[i] = fmaf((float)((u >> 8) & 0xFFu), yq[e][1], acc[i]);
+              acc[i] = fmaf((float)((u >> 16) & 0xFFu), yq[e][2], acc[i]);
+              acc[i] = fmaf((float)(u >> 24), yq[e][3], acc[i]);
+            }
+        } else {
+          const v4f* Y = reinterpret_cast<const v4f*>(sm.yf + 32 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const v4f ya = Y[2 * e], yb = Y[2 * e + 1];  // columns 32c + 8e .. +7
+#pragma unroll
+            for (int i = 0; i < RC; ++i) {
+              const unsigned p = (unsigned)wc[i][k][e] ^ 0x88888888u;
+              const unsigned lo = p & 0x0F0F0F0Fu, hi = (p >> 4) & 0x0F0F0F0Fu;
+              acc[i] = fmaf((float)(lo & 0xFFu), ya[0], acc[i]);
+              acc[i] = fmaf((float)(hi & 0xFFu), ya[1], acc[i]);
+              acc[i] = fmaf((float)((lo >> 8) & 0xFFu), ya[2], acc[i]);
+              acc[i] = fmaf((float)((hi >> 8) & 0xFFu), ya[3], acc[i]);
+              acc[i] = fmaf((float)((lo >> 16) & 0xFFu), yb[0], acc[i]);
+              acc[i] = fmaf((float)((hi >> 16) & 0xFFu), yb[1], acc[i]);
+              acc[i] = fmaf((float)(lo >> 24), yb[2], acc[i]);
+              acc[i] = fmaf((float)(hi >> 24), yb[3], acc[i]);
+            }
+          }
+        }
       }
+      float mine = 0.f;
+#pragma unroll
+      for (int i = 0; i < RC; ++i) {
+        const float tot = wave_total_f(acc[i]) - (BITS == 8 ? 128.0f : 8.0f) * sumy;
+        if (lane == i) mine = tot;
+      }
+      const int r = g.c_row0 + lane;
+      const float o = rc_s * mine;
+      if (lane < RC && r < g.c_row_end) a.out[(size_t)l * D + r] = o;
+      if (l + 1 < a.L) {
+        // lanes 0..NREP-1 write the replicas of each row, row i's value taken from lane i
+#pragma unroll
+        for (int i = 0; i < RC; ++i) {
+          const float oi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o), i));
+          const int ri = g.c_row0 + i;
+          if (lane < NREP && ri < g.c_row_end) ll_store(a.X + (size_t)lane * D + ri, oi, tag);
+        }
+      }
+      if (lane == 0) bump_counter(&sm.c_done);
+      if (tid == 0) DN_MARK(a, l, 8);
       if (l + 1 < a.L) load_c(l + 1);
     }
   }
 }
 
 // Communication waves: poll and stage x and the gated readout; the first one also runs phase B.
+// Each poll starts only once this workgroup's own share of the data it waits for is done, so
+// that the rounds that are bound to miss are not issued.
 template <int BITS, int NCHA, int NCHC>
 __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
                                           int tid, int lane, int cw, int wg) {
@@ -447,12 +581,23 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
       coherent_store_u32(&a.ctl->error, 1u);
     }
   };
+  const int rep = xcd_id();
   const bool runs_b = cw == 0 && g.has_b;
-  if (runs_b) load_s(0);
+  if (runs_b) {
+    // the per-layer gates and norm weights this workgroup needs, fetched once per launch
+    for (int l = lane; l < a.L; l += 64) {
+      sm.gate[l][0] = a.alpha[(size_t)l * Hv + g.bh];
+      sm.gate[l][1] = a.beta[(size_t)l * Hv + g.bh];
+    }
+    for (int e = lane; e < a.L * CB; e += 64) sm.nw[e / CB][e % CB] = a.layers[e / CB].norm_w[g.bcb * CB + e % CB];
+    load_s(0);
+  }
 
   for (int l = 0; l < a.L; ++l) {
     const unsigned tag = base_tag + (unsigned)l;
-    // stage x: this wave polls a quarter of the columns
+    // stage x: this wave polls a quarter of the columns, once this workgroup's phase C of the
+    // previous layer is done
+    if (cw == 0) DN_MARK(a, l, 0);
     {
       float xv[XW];
       const int col0 = cw * (D / NCM) + lane;
@@ -461,7 +606,10 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
 #pragma unroll
         for (int i = 0; i < XW; ++i) xv[i] = a.x[col0 + 64 * i];
       } else {
-        ok = poll_words<XW, 64>(a.X + col0, tag - 1, xv, XW, err);
+        wait_counter(&sm.c_done, NCW * l, &sm.abort_flag);
+        unsigned rounds = 0;
+        ok = poll_words<XW, 64>(a.X + rep * D + col0, tag - 1, xv, XW, err, &rounds, cw == 0 ? DN_TS(a, l, 16) : nullptr);
+
       }
       float ss = 0.f, mx = 0.f;
 #pragma unroll
@@ -477,8 +625,10 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
         sm.stat[4 + cw] = mx;
       }
       if (!__all(ok)) fail();
+      if (cw == 0) DN_MARK(a, l, 1);
     }
     __syncthreads();  // (1)
+    if (cw == 0) DN_MARK(a, l, 9);
     if (sm.abort_flag) break;
     split_x<BITS, D>(sm, a, tid);
     __syncthreads();  // (2)
@@ -491,7 +641,11 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
       const int qo = g.bg * DK + lane;
       const int off[6] = {qo, qo + 64, QK + qo, QK + qo + 64, 2 * QK + vcol + lane, C + vcol + lane};
       float val[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      ok = poll_words_at<6>(a.U, off, tag, val, lane < CB ? 6u : 4u, err);
+      wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
+      DN_MARK(a, l, 10);
+      unsigned rounds = 0;
+      ok = poll_words_at<6>(a.U, off, tag, val, lane < CB ? 6u : 4u, err, &rounds, DN_TS(a, l, 20));
+      DN_MARK(a, l, 4);
       if (__all(ok)) {
         double sq = (double)val[0] * val[0] + (double)val[1] * val[1];
         double sk = (double)val[2] * val[2] + (double)val[3] * val[3];
@@ -500,7 +654,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
         const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
         const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
         const float q0 = val[0] * qn, q1 = val[1] * qn, k0 = val[2] * kn, k1 = val[3] * kn;
-        const float alpha = a.alpha[(size_t)l * Hv + g.bh], beta = a.beta[(size_t)l * Hv + g.bh];
+        DN_MARK(a, l, 11);
+        const float alpha = sm.gate[l][0], beta = sm.gate[l][1];
         float s0[CB], s1v[CB], p[CB];
 #pragma unroll
         for (int q = 0; q < CB / 4; ++q)
@@ -518,6 +673,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
         float d[CB];
 #pragma unroll
         for (int j = 0; j < CB; ++j) d[j] = __shfl(dl, 4 * j);
+        DN_MARK(a, l, 13);
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
           s0[j] = fmaf(k0, d[j], s0[j]);
@@ -532,52 +688,69 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
           *reinterpret_cast<v4f*>(S + (size_t)(lane + 64) * CB + 4 * q) =
               v4f{s1v[4 * q], s1v[4 * q + 1], s1v[4 * q + 2], s1v[4 * q + 3]};
         }
+        DN_MARK(a, l, 14);
         const float o = rs16(p, lane);  // readout of column lane >> 2
+        DN_MARK(a, l, 15);
         const float zj = __shfl(val[5], jc);
-        const float gt = a.layers[l].norm_w[g.bcb * CB + jc] * o * silu(zj);
+        const float gt = sm.nw[l][jc] * o * silu(zj);
         const float osq = wsum((lane & 3) == 0 ? o * o : 0.f);
         // G buffer: NCM segments of [V/NCM gated columns | partials of the same heads]
         const int gc = vcol + jc, gw = gc / (V / NCM);
-        if ((lane & 3) == 0) ll_store(a.G + gw * GSEG + (gc - gw * (V / NCM)), gt, tag);
         const int pw = g.bh / (Hv / NCM);
-        if (lane == 0) ll_store(a.G + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
+        // every lane of a column's group of four holds its value: lane l writes replicas
+        // 2(l&3) and 2(l&3)+1; lanes 0..7 write one replica each of the partial sum
+        {
+          const size_t off = (size_t)gw * GSEG + (gc - gw * (V / NCM));
+          const int r0 = 2 * (lane & 3);
+          ll_store(a.G + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
+          ll_store(a.G + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
+          if (lane < NREP)
+            ll_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
+        }
+        DN_MARK(a, l, 5);
         if (l + 1 < a.L) load_s(l + 1);
       }
+      if (lane == 0) bump_counter(&sm.b_done);
+    } else if (cw == 0) {
+      wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
+      if (lane == 0) bump_counter(&sm.b_done);
     }
     if (__all(ok)) {
       // stage the gated readout: value columns [cw*V/NCM, (cw+1)*V/NCM) and the partials of those
       // heads, which follow them in this wave's segment of the buffer
+      wait_counter(&sm.b_done, l + 1, &sm.abort_flag);
       float gv[GW + 1];
 #pragma unroll
       for (int i = 0; i <= GW; ++i) gv[i] = 0.f;
       const int pn = npart / NCM, pbase = cw * pn;
-      ok = poll_words<GW + 1, 64>(a.G + cw * GSEG + lane, tag, gv, lane < pn ? GW + 1 : GW, err);
-      constexpr int PW = 1;
-      const float pv[PW] = {gv[GW]};
-      const int gcol0 = cw * (V / NCM) + lane;
+      if (cw == 0) DN_MARK(a, l, 12);
+      unsigned rounds = 0;
+      ok = poll_words<GW + 1, 64>(a.G + rep * (NCM * GSEG) + cw * GSEG + lane, tag, gv, lane < pn ? GW + 1 : GW, err,
+                                  &rounds, cw == 0 ? DN_TS(a, l, 24) : nullptr);
+      if (cw == 0) DN_MARK(a, l, 6);
+      // per-head sums of the partials: head h's nblk partials sit in nblk consecutive lanes
+      {
+        float sp = gv[GW];
 #pragma unroll
-      for (int i = 0; i < PW; ++i) {
-        float s = pv[i];
-#pragma unroll
-        for (int o = 1; o < nblk; o <<= 1) s += __shfl_xor(s, o);
-        const int q = lane + 64 * i;
-        if ((lane % nblk) == 0 && q < pn) sm.inv[(pbase + q) / nblk] = rsqrtf(s / (float)DV + a.eps_rms);
+        for (int o = 1; o < nblk; o <<= 1) sp += __shfl_xor(sp, o);
+        if ((lane % nblk) == 0 && lane < pn) sm.inv[(pbase + lane) / nblk] = rsqrtf(sp / (float)DV + a.eps_rms);
       }
-      float mx = 0.f;
+      // y = g / rms(head), staged for phase C, and the sum of this quarter of y
+      float sy = 0.f;
+      const int gcol0 = cw * (V / NCM) + lane;
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
         const int c = gcol0 + 64 * i;
-        sm.raw[c] = gv[i];
-        mx = fmaxf(mx, fabsf(gv[i] * sm.inv[c / DV]));
+        const float y = gv[i] * sm.inv[c / DV];
+        sm.yf[c] = y;
+        sy += y;
       }
-      mx = wmax(mx);
-      if (lane == 0) sm.stat[9 + cw] = mx;
+      sy = wave_total_f(sy);
+      if (lane == 0) sm.stat[9 + cw] = sy;
     }
     if (!__all(ok)) fail();
     __syncthreads();  // (3)
     if (sm.abort_flag) break;
-    split_y<BITS, V, DV>(sm, tid);
-    __syncthreads();  // (4)
   }
 }
 
@@ -593,6 +766,7 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
 
   Geo g;
   const int a_per_wg = (a.R + NWG - 1) / NWG;
+  g.a_per_wg = a_per_wg;
   const int a_per_wave = (a_per_wg + NCW - 1) / NCW;
   g.a_row0 = wg * a_per_wg + wave * a_per_wave;
   g.a_row_end = min(min(wg * a_per_wg + a_per_wg, a.R), g.a_row0 + a_per_wave);
@@ -605,8 +779,12 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   g.bcb = g.has_b ? wg % nblk : 0;
   g.bg = g.bh / (a.Hv / a.Hk);
 
-  if (tid == 0) sm.abort_flag = 0;
-  // The two roles run separate loops with the same sequence of four workgroup barriers per
+  if (tid == 0) {
+    sm.abort_flag = 0;
+    sm.a_done = sm.b_done = sm.c_done = 0;
+  }
+  __syncthreads();
+  // The two roles run separate loops with the same sequence of three workgroup barriers per
   // layer, so each role's registers are its own.
   if (wave < NCW) compute_role<BITS, NCHA, NCHC, RA, RC>(sm, a, g, base_tag, tid, lane);
   else comm_role<BITS, NCHA, NCHC>(sm, a, g, base_tag, tid, lane, wave - NCW, wg);
