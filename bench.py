@@ -26,6 +26,62 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ("gated_deltanet_layer_dn_amd/csrc/dn_persist.hip", "gated_deltanet_layer_dn_amd/csrc/dn_internal.h")
+
+
+def create_reporting_path(dn, cfg, layers):
+    """Create the handle with DN_VERBOSE set and read which execution path the library chose
+    from the line it prints on stderr (file descriptor 2)."""
+    import tempfile
+    os.environ["DN_VERBOSE"] = "1"
+    sys.stderr.flush()
+    saved = os.dup(2)
+    with tempfile.TemporaryFile() as tf:
+        os.dup2(tf.fileno(), 2)
+        try:
+            st = dn.DeltaNetStack.from_config(cfg, layers)
+        finally:
+            os.dup2(saved, 2)
+            os.close(saved)
+            del os.environ["DN_VERBOSE"]
+        tf.seek(0)
+        text = tf.read().decode(errors="replace")
+    path = "whole-stack kernel" if "whole-stack kernel" in text else "per-layer kernels"
+    return st, path
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM-side bytes per launch of the whole-stack kernel, from the committed counter summary.
+
+    The summary holds FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by what the same counter
+    read for a plain copy of known size, and the hash of the kernel source it was taken on; once
+    the source differs the figure no longer describes this kernel and None is returned."""
+    path = os.path.join(ROOT, "profiles", f"k_persist_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -67,7 +123,8 @@ def main():
     layers, stream = gi.generate(cfg)
     log(f"[bench] generated {cfg.name}: L={cfg.n_layers} B={cfg.batch} T={cfg.n_tokens} in {time.time() - t0:.1f}s")
 
-    st = dn.DeltaNetStack.from_config(cfg, layers)
+    st, path = create_reporting_path(dn, cfg, layers)
+    log(f"[bench] execution path: {path}")
     S0 = np.ascontiguousarray(np.stack([l.S0 for l in layers]))
     R0 = np.ascontiguousarray(np.stack([l.ring0 for l in layers]))
     S0d = torch.from_numpy(S0).to(dev)
@@ -88,16 +145,18 @@ def main():
     st.set_state(S0d, R0d)
     torch.cuda.synchronize()
 
+    # every launch goes to this stream; an event after each one brackets each launch
     stream_t = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream_t)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream_t)
     for i in range(args.steps):
         t = i % T
-        st.step(x[t], al[t], be[t], outs[i])
-    ev1.record(stream_t)
+        st.step(x[t], al[t], be[t], outs[i], stream=stream_t)
+        evs[i + 1].record(stream_t)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
+    ms = evs[0].elapsed_time(evs[-1])
+    launch_us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
     sec = ms / 1e3
     steps_per_s = args.steps / sec
     tokens_per_s = steps_per_s * cfg.batch
@@ -107,9 +166,20 @@ def main():
     log(f"[bench] {args.steps} steps in {ms:.3f} ms: {ms * 1e3 / args.steps:.2f} us/step, "
         f"{tokens_per_s:.1f} tok/s, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
 
-    # the dominant kernel is the whole-stack decode kernel: one launch per step on this stream
-    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    # Dominant kernel: for single-sequence stacks one whole-stack launch per step moves all the
+    # metric bytes, so its algorithmic bytes per launch are the step's; elsewhere (per-layer
+    # kernels) the step's rate is reported.
+    whole_stack = path == "whole-stack kernel"
+    kern_us = float(launch_us.mean())
+    achieved = bytes_step / (kern_us * 1e-6) / 1e9 if whole_stack else gbs
+    traffic = measured_traffic(cfg.name) if whole_stack else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_persist (whole-stack decode, one launch per token)" if whole_stack
+                          else "per-layer kernels (whole step)",
+                "launch_us_mean": round(kern_us, 2), "launch_us_min": round(float(launch_us.min()), 2),
+                "launch_us_max": round(float(launch_us.max()), 2), "bytes_per_launch": bytes_step}
+    log(f"[bench] launch time mean {kern_us:.2f} us (min {launch_us.min():.2f}, max {launch_us.max():.2f})")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -39,7 +39,8 @@ struct dn_layer {
   uint64_t* G = nullptr;
   dn::Ctl* ctl = nullptr;
   float* stage = nullptr;   // canonical-layout staging of the state for set/get
-  unsigned* err_host = nullptr;  // pinned copy of the device error flag, refreshed after each step
+  unsigned* err_host = nullptr;  // pinned host word the whole-stack kernel writes its error flag to
+  unsigned* err_dev = nullptr;   // the same word as the device addresses it
   unsigned long long* timers = nullptr;  // instrumented builds: phase timestamps of the last step
   bool disabled = false;
   long steps = 0;
@@ -112,7 +113,8 @@ int setup_persist(dn_layer* h) {
   ok = ok && hipMalloc(&h->G, sizeof(uint64_t) * 8 * (h->V + 256)) == hipSuccess;
   ok = ok && hipMalloc(&h->ctl, sizeof(dn::Ctl)) == hipSuccess;
   ok = ok && hipMalloc(&h->stage, sizeof(float) * L * h->s_elems) == hipSuccess;
-  ok = ok && hipHostMalloc(&h->err_host, sizeof(unsigned)) == hipSuccess;
+  ok = ok && hipHostMalloc(&h->err_host, sizeof(unsigned), hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
+  ok = ok && hipHostGetDevicePointer(reinterpret_cast<void**>(&h->err_dev), h->err_host, 0) == hipSuccess;
 #ifdef DN_PHASE_TIMERS
   ok = ok && hipMalloc(&h->timers, sizeof(unsigned long long) * h->nwg * L * 32) == hipSuccess;
   ok = ok && hipMemset(h->timers, 0, sizeof(unsigned long long) * h->nwg * L * 32) == hipSuccess;
@@ -132,6 +134,10 @@ int setup_persist(dn_layer* h) {
   h->persist = true;
   return DN_OK;
 }
+
+// The whole-stack kernel stores its error flag into host memory at the end of each launch; the
+// host reads it without synchronising, so a failure is seen at the first call after that launch.
+unsigned host_err(const dn_layer* h) { return *reinterpret_cast<volatile const unsigned*>(h->err_host); }
 
 int fail(dn_layer* h, int rc) {
   h->disabled = true;
@@ -259,17 +265,15 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
   if (h->fault_step > 0 && h->steps == h->fault_step) return fail(h, DN_E_FAULT);
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   if (h->persist) {
-    if (*h->err_host) return fail(h, DN_E_DEVICE);  // a previous launch reported a stalled hand-off
+    if (host_err(h)) return fail(h, DN_E_DEVICE);  // a completed launch reported a stalled hand-off
     dn::PersistArgs a{};
     a.layers = h->d_layers; a.S = h->S; a.ring = h->ring; a.x = x; a.alpha = alpha; a.beta = beta; a.out = out;
-    a.X = h->X; a.U = h->U; a.G = h->G; a.ctl = h->ctl; a.timers = h->timers;
+    a.X = h->X; a.U = h->U; a.G = h->G; a.ctl = h->ctl; a.err_host = h->err_dev; a.timers = h->timers;
     a.L = (int)L; a.R = h->R; a.C = h->C; a.QK = c.n_k_heads * c.d_k; a.K = c.conv_k;
     a.Hk = c.n_k_heads; a.Hv = c.n_v_heads; a.flags = c.flags;
     a.eps_l2 = c.eps_l2; a.eps_rms = c.eps_rms; a.q_scale = c.q_scale;
     if (dn::launch_persist(a, h->ps, h->nwg, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    if (hipMemcpyAsync(h->err_host, &h->ctl->error, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
-      return fail(h, DN_E_DEVICE);
-    if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || *h->err_host)) return fail(h, DN_E_DEVICE);
+    if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
     return DN_OK;
   }
   for (size_t l = 0; l < L; ++l) {

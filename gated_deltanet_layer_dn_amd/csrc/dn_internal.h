@@ -73,7 +73,8 @@ struct PersistArgs {
                          // readout, in four segments [V/4 columns | partials of those heads | pad],
                          // one copy per XCD
   Ctl* ctl;
-  unsigned long long* timers;  // instrumented builds only: [NWG][L][16] phase timestamps
+  unsigned* err_host;          // host-mapped pinned word: the launch's error flag, written by the last workgroup
+  unsigned long long* timers;  // instrumented builds only: [NWG][L][32] phase timestamps
   int L, R, C, QK, K, Hk, Hv;
   unsigned flags;
   float eps_l2, eps_rms, q_scale;

@@ -796,6 +796,8 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
     if (prev == (unsigned)NWG - 1) {
       coherent_store_u32(&a.ctl->done, 0u);
       coherent_store_u32(&a.ctl->epoch, base_tag + (unsigned)a.L);
+      // publish this launch's error flag to the host without a copy on the stream
+      __hip_atomic_store(a.err_host, coherent_load_u32(&a.ctl->error), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }

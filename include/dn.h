@@ -110,7 +110,10 @@ int dn_get_state(dn_layer *h, float *S, float *ring);
  *                              out[L-1] is the stack's output. Must not overlap x.
  * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only: returns
  * before the work completes. Returns DN_OK, DN_E_INVAL, DN_E_DISABLED, DN_E_FAULT
- * or DN_E_DEVICE (the last two latch the handle off). */
+ * or DN_E_DEVICE (the last two latch the handle off). A whole-stack launch whose
+ * workgroups stop waiting for one another (a bounded wait ran out) abandons the
+ * token and records an error in host memory at its end; the first dn_step after that
+ * launch has completed returns DN_E_DEVICE. */
 int dn_step(dn_layer *h, const float *x, const float *alpha, const float *beta, float *out, void *hip_stream);
 
 /* Free everything the handle owns (waits for the device first). NULL-safe. */
