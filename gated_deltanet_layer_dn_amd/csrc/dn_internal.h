@@ -61,7 +61,7 @@ struct Ctl {
 
 struct PersistArgs {
   const LayerW* layers;  // [L], device memory
-  float* S;              // [L][Hv][dv/16][dk][16] (tiled)
+  float* S;              // [L][Hv][dv][dk]: each head's state stored transposed
   float* ring;           // [L][K-1][C], oldest first
   const float* x;        // [D]
   const float* alpha;    // [L][Hv]

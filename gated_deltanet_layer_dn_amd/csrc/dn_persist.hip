@@ -13,8 +13,9 @@
 //    as soon as the previous layer's phase A has used them, so the HBM stream never waits for the
 //    activations.
 //  * Phase B (recurrence): workgroup b owns value head b / (dv/16) and 16 of its value columns; its
-//    first communication wave keeps that 128x16 slice of the state in registers, prefetched one
-//    layer ahead, and performs decay, delta rule, readout and the gate for those columns.
+//    first communication wave keeps that 128x16 slice of the state in registers (lane 4j+p: column
+//    j, key rows 32p..32p+31), prefetched one layer ahead, and performs decay, delta rule, readout
+//    and the gate for those columns; sums over the key rows are in-lane plus two DPP steps.
 //  * Phase C (gated RMSNorm finish + out_proj): each workgroup owns D/NWG out_proj rows.
 // Hand-offs between workgroups carry no fences: every cross-workgroup value travels as a 64-bit
 // word (fp32 value, 32-bit tag) stored and loaded with device-coherent (sc1) accesses; a reader
@@ -22,7 +23,7 @@
 // layer and never repeat within 2^32 layer steps, so buffers need no reset.
 // Compute waves never poll, so their outstanding weight prefetches never delay a hand-off (a
 // wave's loads complete in order); the communication waves poll, stage activations into LDS, and
-// run phase B.
+// run phase B. The next layer's in_proj rows are requested only after phase B's inputs arrived.
 //
 // GEMV arithmetic as in the layer kernels: activations split into three int8 terms, exact int32
 // dot products with v_dot4_i32_i8, combined in double.
@@ -49,7 +50,7 @@ constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
 // flight, so that the compute unit's memory pipeline is never full and the communication
 // waves' hand-off loads and stores are not queued behind a whole layer of weights.
 #ifndef DN_PREFETCH_INFLIGHT
-#define DN_PREFETCH_INFLIGHT 4
+#define DN_PREFETCH_INFLIGHT 2
 #endif
 static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
 // s_waitcnt with vmcnt <= n and the other counters unconstrained
@@ -71,7 +72,6 @@ static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
 #define DN_MARK(a, l, k) \
   do {                   \
   } while (0)
-#define DN_TS(a, l, k) ((a).timers + ((size_t)blockIdx.x * (a).L + (l)) * 32 + (k))
 #define DN_COUNT(a, l, k, v) \
   do {                       \
   } while (0)
@@ -105,42 +105,6 @@ __device__ __forceinline__ float wmax(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
-}
-
-// Sum 16 per-lane values over the 64 lanes of a wave. On return lane l holds the total of value
-// (l >> 2). Butterfly reduce-scatter: each step keeps half of the values and adds the partner's.
-__device__ __forceinline__ float rs16(float (&a)[16], int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const bool up = lane & 32;
-    const float send = up ? a[i] : a[i + 8];
-    const float keep = up ? a[i + 8] : a[i];
-    a[i] = keep + __shfl_xor(send, 32);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool up = lane & 16;
-    const float send = up ? a[i] : a[i + 4];
-    const float keep = up ? a[i + 4] : a[i];
-    a[i] = keep + __shfl_xor(send, 16);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const bool up = lane & 8;
-    const float send = up ? a[i] : a[i + 2];
-    const float keep = up ? a[i + 2] : a[i];
-    a[i] = keep + __shfl_xor(send, 8);
-  }
-  {
-    const bool up = lane & 4;
-    const float send = up ? a[0] : a[1];
-    const float keep = up ? a[1] : a[0];
-    a[0] = keep + __shfl_xor(send, 4);
-  }
-  float s = a[0];
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 1);
-  return s;
 }
 
 // Staged activation position of column c (4-bit weights hold 8 columns per dword as nibbles;
@@ -217,10 +181,14 @@ struct Smem {
   float yf[4096];          // gated, normalised readout y (input of out_proj), fp32
   int8_t xs[3 * 4096];     // three-term split of x for phase A
   float inv[64];           // per value head 1/rms of the readout
+  float qk[2 * DK];        // raw q and k of phase B's key head
+  v4f sbuf[8 * 64];        // phase B's updated state slice until its write-back
   float stat[16];          // partial statistics from the communication waves, split scale
   float gate[MAXL][2];     // alpha, beta of this workgroup's value head, per layer
   float nw[MAXL][CB];      // gated RMSNorm weights of this workgroup's value columns, per layer
   int a_done, b_done, c_done;  // progress counters of this workgroup's waves
+  int u_done;                  // phase-B inputs received (the next layer's in_proj prefetch may start)
+  int s_ready;                 // compute waves whose chunk of the layer's state slice is in LDS
   int abort_flag;
 };
 
@@ -265,6 +233,26 @@ __device__ __forceinline__ float wave_total_f(float x) {
   v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0x142, 0xA>(v)));
   v = __float_as_int(__int_as_float(v) + __int_as_float(dpp_i<0x143, 0xC>(v)));
   return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
+__device__ __forceinline__ double wave_total_d(double x) {
+#define DN_DPP_D(CTRL, RM)                                                                          \
+  x += __hiloint2double(dpp_i<CTRL, RM>(__double2hiint(x)), dpp_i<CTRL, RM>(__double2loint(x)))
+  DN_DPP_D(0xB1, 0xF);
+  DN_DPP_D(0x4E, 0xF);
+  DN_DPP_D(0x141, 0xF);
+  DN_DPP_D(0x140, 0xF);
+  DN_DPP_D(0x142, 0xA);
+  DN_DPP_D(0x143, 0xC);
+#undef DN_DPP_D
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), 63),
+                          __builtin_amdgcn_readlane(__double2loint(x), 63));
+}
+// Sum over each group of four consecutive lanes; all four receive the same total.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(dpp_i<0xB1>(__float_as_int(x)));
+  x += __int_as_float(dpp_i<0x4E>(__float_as_int(x)));
+  return x;
 }
 
 // Reduce the lane partials of RB rows; lane i (< RB) receives row i's dot product.
@@ -438,6 +426,14 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
     if (lane < RC && r < g.c_row_end) rc_s = W.s_out[r];
   };
 
+  // Phase B's state slice: compute wave w moves chunk w (lane's 4 floats at rows 32p + 4w, column
+  // j, for lane 4j + p) between HBM and LDS: prefetched into LDS one layer ahead by a direct-to-LDS
+  // load, written back from LDS after phase C.
+  const int cwv = tid >> 6;
+  auto s_chunk = [&](int l) {
+    return a.S + (((size_t)l * a.Hv + g.bh) * DK + g.bcb * CB + (lane >> 2)) * DK + 32 * (lane & 3) + 4 * cwv;
+  };
+  if (g.has_b) __builtin_amdgcn_global_load_lds(s_chunk(0), &sm.sbuf[64 * cwv], 16, 0, 0);
   load_a(0);
   load_c(0);
   for (int l = 0; l < a.L; ++l) {
@@ -473,6 +469,15 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       }
       if (lane == 0) bump_counter(&sm.a_done);
       if (tid == 0) DN_MARK(a, l, 3);
+      if (g.has_b) {
+        // this wave's chunk of the slice (prefetched a layer ago, older than its last weight
+        // loads) has landed; the wait also covers the write-back stores
+        DN_WAIT_VMCNT(0);
+        if (lane == 0) bump_counter(&sm.s_ready);
+      }
+      // the next layer's in_proj rows stream in once this workgroup's phase-B inputs have
+      // arrived, so that the u hand-off is not queued behind them
+      wait_counter(&sm.u_done, l + 1, &sm.abort_flag);
       if (l + 1 < a.L) load_a(l + 1);
     }
     __syncthreads();  // (3) gated readout staged
@@ -544,6 +549,16 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       }
       if (lane == 0) bump_counter(&sm.c_done);
       if (tid == 0) DN_MARK(a, l, 8);
+      if (g.has_b) {
+        // write back this wave's chunk of the updated slice (parked in LDS by phase B before
+        // barrier 3), then prefetch the next layer's chunk into the same LDS slots
+        const v4f v = sm.sbuf[64 * cwv + lane];
+        *reinterpret_cast<v4f*>(s_chunk(l)) = v;
+        if (l + 1 < a.L) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS read is done before the slots refill
+          __builtin_amdgcn_global_load_lds(s_chunk(l + 1), &sm.sbuf[64 * cwv], 16, 0, 0);
+        }
+      }
       if (l + 1 < a.L) load_c(l + 1);
     }
   }
@@ -565,16 +580,11 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
   const int C = a.C, QK = a.QK, Hv = a.Hv;
   const int npart = Hv * nblk;
   const unsigned* err = &a.ctl->error;
-  v4f st[2][CB / 4];  // rows lane and lane+64 of the state slice
-  auto s_slice = [&](int l) { return a.S + (((size_t)l * Hv + g.bh) * nblk + g.bcb) * (DK * CB); };
-  auto load_s = [&](int l) {
-    const float* S = s_slice(l);
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf)
-#pragma unroll
-      for (int q = 0; q < CB / 4; ++q)
-        st[hlf][q] = *reinterpret_cast<const v4f*>(S + (size_t)(lane + 64 * hlf) * CB + 4 * q);
-  };
+  // Phase B lane layout: lane 4j + p holds value column j of the slice, key rows 32p .. 32p+31.
+  // The state of each head is stored transposed ([dv][dk]), so those 32 rows are contiguous.
+  const int jc = lane >> 2, pr = lane & 3;
+  // The slice lives in sm.sbuf (lane's chunk q at sbuf[64q + lane]); the compute waves move it
+  // between HBM and LDS (state_traffic), so this wave's polls never queue behind it.
   auto fail = [&]() {
     if (lane == 0) {
       sm.abort_flag = 1;
@@ -590,11 +600,14 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
       sm.gate[l][1] = a.beta[(size_t)l * Hv + g.bh];
     }
     for (int e = lane; e < a.L * CB; e += 64) sm.nw[e / CB][e % CB] = a.layers[e / CB].norm_w[g.bcb * CB + e % CB];
-    load_s(0);
   }
 
   for (int l = 0; l < a.L; ++l) {
     const unsigned tag = base_tag + (unsigned)l;
+    // Buffer bases laundered once per layer: addresses derived from them are recomputed in the
+    // loop (a few scalar and vector adds) instead of being held across it, which would spill.
+    uint64_t *Ub = a.U, *Xb = a.X, *Gb = a.G;
+    asm volatile("" : "+s"(Ub), "+s"(Xb), "+s"(Gb));
     // stage x: this wave polls a quarter of the columns, once this workgroup's phase C of the
     // previous layer is done
     if (cw == 0) DN_MARK(a, l, 0);
@@ -608,7 +621,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
       } else {
         wait_counter(&sm.c_done, NCW * l, &sm.abort_flag);
         unsigned rounds = 0;
-        ok = poll_words<XW, 64>(a.X + rep * D + col0, tag - 1, xv, XW, err, &rounds, cw == 0 ? DN_TS(a, l, 16) : nullptr);
+        ok = poll_words<XW, 64>(Xb + rep * D + col0, tag - 1, xv, XW, err, &rounds, cw == 0 ? DN_TS(a, l, 16) : nullptr);
 
       }
       float ss = 0.f, mx = 0.f;
@@ -635,85 +648,88 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
 
     bool ok = true;
     if (runs_b) {
-      // phase B: recurrence on the 128 x 16 state slice (rows lane and lane+64)
+      // phase B: recurrence on the 128 x 16 state slice
       const int vcol = g.bh * DV + g.bcb * CB;
-      // q and k rows lane and lane+64 of key head bg; lanes < 16 also v and z of column lane
+      // raw q and k rows lane and lane+64 of key head bg; v and z of this lane's column
       const int qo = g.bg * DK + lane;
-      const int off[6] = {qo, qo + 64, QK + qo, QK + qo + 64, 2 * QK + vcol + lane, C + vcol + lane};
+      const int off[6] = {qo, qo + 64, QK + qo, QK + qo + 64, 2 * QK + vcol + jc, C + vcol + jc};
       float val[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
       DN_MARK(a, l, 10);
       unsigned rounds = 0;
-      ok = poll_words_at<6>(a.U, off, tag, val, lane < CB ? 6u : 4u, err, &rounds, DN_TS(a, l, 20));
+      ok = poll_words_at<6>(Ub, off, tag, val, 6u, err, &rounds, DN_TS(a, l, 20));
+      if (lane == 0) bump_counter(&sm.u_done);
       DN_MARK(a, l, 4);
       if (__all(ok)) {
-        double sq = (double)val[0] * val[0] + (double)val[1] * val[1];
-        double sk = (double)val[2] * val[2] + (double)val[3] * val[3];
-        sq = wsum(sq);
-        sk = wsum(sk);
+        // this wave's own LDS writes are visible to its later LDS reads (in-order LDS queue)
+        sm.qk[lane] = val[0];
+        sm.qk[lane + 64] = val[1];
+        sm.qk[DK + lane] = val[2];
+        sm.qk[DK + lane + 64] = val[3];
+        // L2 norms in double, eps inside the sqrt
+        const double sq = wave_total_d((double)val[0] * val[0] + (double)val[1] * val[1]);
+        const double sk = wave_total_d((double)val[2] * val[2] + (double)val[3] * val[3]);
         const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
         const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
-        const float q0 = val[0] * qn, q1 = val[1] * qn, k0 = val[2] * kn, k1 = val[3] * kn;
         DN_MARK(a, l, 11);
         const float alpha = sm.gate[l][0], beta = sm.gate[l][1];
-        float s0[CB], s1v[CB], p[CB];
+        const v4f* Q4 = reinterpret_cast<const v4f*>(sm.qk + 32 * pr);
+        const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DK + 32 * pr);
+        float sv[32];
+        float kvp = 0.f;
+        wait_counter(&sm.s_ready, NCW * (l + 1), &sm.abort_flag);  // the slice has landed in LDS
 #pragma unroll
-        for (int q = 0; q < CB / 4; ++q)
+        for (int q = 0; q < 8; ++q) {
+          const v4f kk = K4[q], st = sm.sbuf[64 * q + lane];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            s0[4 * q + e] = alpha * st[0][q][e];
-            s1v[4 * q + e] = alpha * st[1][q][e];
+            sv[4 * q + e] = alpha * st[e];  // decay
+            kvp = fmaf(sv[4 * q + e], kk[e] * kn, kvp);
           }
-#pragma unroll
-        for (int j = 0; j < CB; ++j) p[j] = fmaf(s0[j], k0, s1v[j] * k1);
-        const float kv = rs16(p, lane);  // column lane >> 2
-        const int jc = lane >> 2;
-        const float vj = __shfl(val[4], jc);
-        const float dl = beta * (vj - kv);
-        float d[CB];
-#pragma unroll
-        for (int j = 0; j < CB; ++j) d[j] = __shfl(dl, 4 * j);
+        }
+        const float kv = quad_sum(kvp);  // (decayed S)^T k of column jc
+        const float dl = beta * (val[4] - kv);
         DN_MARK(a, l, 13);
+        float op = 0.f;
 #pragma unroll
-        for (int j = 0; j < CB; ++j) {
-          s0[j] = fmaf(k0, d[j], s0[j]);
-          s1v[j] = fmaf(k1, d[j], s1v[j]);
-          p[j] = fmaf(s0[j], q0, s1v[j] * q1);
-        }
-        float* S = s_slice(l);
+        for (int q = 0; q < 8; ++q) {
+          const v4f qq = Q4[q], kk = K4[q];
 #pragma unroll
-        for (int q = 0; q < CB / 4; ++q) {
-          *reinterpret_cast<v4f*>(S + (size_t)lane * CB + 4 * q) =
-              v4f{s0[4 * q], s0[4 * q + 1], s0[4 * q + 2], s0[4 * q + 3]};
-          *reinterpret_cast<v4f*>(S + (size_t)(lane + 64) * CB + 4 * q) =
-              v4f{s1v[4 * q], s1v[4 * q + 1], s1v[4 * q + 2], s1v[4 * q + 3]};
+          for (int e = 0; e < 4; ++e) {
+            sv[4 * q + e] = fmaf(kk[e] * kn, dl, sv[4 * q + e]);  // delta rule write
+            op = fmaf(sv[4 * q + e], qq[e] * qn, op);             // readout of the updated state
+          }
         }
+        const float o = quad_sum(op);
+        // park the updated slice in LDS; it is written back while phase C runs
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sm.sbuf[q * 64 + lane] = v4f{sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]};
         DN_MARK(a, l, 14);
-        const float o = rs16(p, lane);  // readout of column lane >> 2
+        const float gt = sm.nw[l][jc] * o * silu(val[5]);
+        const float osq = wave_total_f(pr == 0 ? o * o : 0.f);
         DN_MARK(a, l, 15);
-        const float zj = __shfl(val[5], jc);
-        const float gt = sm.nw[l][jc] * o * silu(zj);
-        const float osq = wsum((lane & 3) == 0 ? o * o : 0.f);
         // G buffer: NCM segments of [V/NCM gated columns | partials of the same heads]
         const int gc = vcol + jc, gw = gc / (V / NCM);
         const int pw = g.bh / (Hv / NCM);
-        // every lane of a column's group of four holds its value: lane l writes replicas
-        // 2(l&3) and 2(l&3)+1; lanes 0..7 write one replica each of the partial sum
+        // the four lanes of column jc hold the same value: lane 4jc+p writes replicas 2p and 2p+1;
+        // lanes 0..7 write one replica each of the partial sum
         {
           const size_t off = (size_t)gw * GSEG + (gc - gw * (V / NCM));
-          const int r0 = 2 * (lane & 3);
-          ll_store(a.G + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
-          ll_store(a.G + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
+          const int r0 = 2 * pr;
+          ll_store(Gb + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
+          ll_store(Gb + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
           if (lane < NREP)
-            ll_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
+            ll_store(Gb + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
         }
         DN_MARK(a, l, 5);
-        if (l + 1 < a.L) load_s(l + 1);
       }
       if (lane == 0) bump_counter(&sm.b_done);
     } else if (cw == 0) {
       wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
-      if (lane == 0) bump_counter(&sm.b_done);
+      if (lane == 0) {
+        bump_counter(&sm.u_done);
+        bump_counter(&sm.b_done);
+      }
     }
     if (__all(ok)) {
       // stage the gated readout: value columns [cw*V/NCM, (cw+1)*V/NCM) and the partials of those
@@ -725,7 +741,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
       const int pn = npart / NCM, pbase = cw * pn;
       if (cw == 0) DN_MARK(a, l, 12);
       unsigned rounds = 0;
-      ok = poll_words<GW + 1, 64>(a.G + rep * (NCM * GSEG) + cw * GSEG + lane, tag, gv, lane < pn ? GW + 1 : GW, err,
+      ok = poll_words<GW + 1, 64>(Gb + rep * (NCM * GSEG) + cw * GSEG + lane, tag, gv, lane < pn ? GW + 1 : GW, err,
                                   &rounds, cw == 0 ? DN_TS(a, l, 24) : nullptr);
       if (cw == 0) DN_MARK(a, l, 6);
       // per-head sums of the partials: head h's nblk partials sit in nblk consecutive lanes
@@ -781,7 +797,7 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
 
   if (tid == 0) {
     sm.abort_flag = 0;
-    sm.a_done = sm.b_done = sm.c_done = 0;
+    sm.a_done = sm.b_done = sm.c_done = sm.u_done = sm.s_ready = 0;
   }
   __syncthreads();
   // The two roles run separate loops with the same sequence of three workgroup barriers per
@@ -847,7 +863,7 @@ hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, 
   return nc == 2 ? go<4, 1, 2>(a, nwg, st) : go<4, 1, 1>(a, nwg, st);
 }
 
-// Canonical state [L][Hv][dk][dv] <-> tiled [L][Hv][dv/16][dk][16].
+// Canonical state [L][Hv][dk][dv] <-> the whole-stack kernel's layout [L][Hv][dv][dk] (each head transposed).
 __global__ void k_state_tile(const float* __restrict__ src, float* __restrict__ dst, int L, int Hv, int dk, int dv,
                              int to_tiled) {
   const size_t n = (size_t)L * Hv * dk * dv;
@@ -856,7 +872,7 @@ __global__ void k_state_tile(const float* __restrict__ src, float* __restrict__ 
     size_t t = e / dv;
     const int i = (int)(t % dk);
     t /= dk;  // l * Hv + h
-    const size_t tiled = ((t * (dv / CB) + j / CB) * dk + i) * CB + (j % CB);
+    const size_t tiled = (t * dv + j) * dk + i;  // each head stored transposed, [dv][dk]
     if (to_tiled) dst[tiled] = src[e];
     else dst[e] = src[tiled];
   }
