@@ -46,7 +46,7 @@ def create_reporting_path(dn, cfg, layers):
             del os.environ["DN_VERBOSE"]
         tf.seek(0)
         text = tf.read().decode(errors="replace")
-    path = "whole-stack kernel" if "whole-stack kernel" in text else "per-layer kernels"
+    path = next((p for p in ("whole-stack kernel", "batched kernels") if p in text), "per-layer kernels")
     return st, path
 
 

@@ -6,6 +6,7 @@
 // dn_set_state / dn_get_state, and dn_get_state still works after a failed step.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -42,6 +43,13 @@ struct dn_layer {
   unsigned* err_host = nullptr;  // pinned host word the whole-stack kernel writes its error flag to
   unsigned* err_dev = nullptr;   // the same word as the device addresses it
   unsigned long long* timers = nullptr;  // instrumented builds: phase timestamps of the last step
+  // batched path (B >= 2, 128 x 128 state tiles): MFMA projections with split-K partial sums
+  bool batched = false;
+  int mf1 = 0, kr1 = 0, mf2 = 0, kr2 = 0;  // rows per workgroup / 64 and K range of in_proj, out_proj
+  float* part = nullptr;                   // split-K partial sums
+  void* xs = nullptr;                      // activations split into int8 terms, fragment order
+  float* sc = nullptr;                     // their per-(sequence, 128-column chunk) scales
+  float* ssq = nullptr;                    // per-(sequence, chunk) sums of squares (input pre-norm)
   bool disabled = false;
   long steps = 0;
   long fault_step = 0;    // 1-based step to fail (0 = never)
@@ -90,6 +98,37 @@ void free_all(dn_layer* h) {
   if (h->err_host) (void)hipHostFree(h->err_host);
   h->err_host = nullptr;
   dfree(h->timers);
+  dfree(h->part);
+  dfree(h->xs);
+  dfree(h->sc);
+  dfree(h->ssq);
+}
+
+// Set up the batched path when the shape allows it: the in_proj GEMM takes 128-row blocks (64 if
+// R is not a multiple of 128) and the largest K range of 1024/512/256 columns that divides
+// d_model; out_proj takes 64-row blocks and 1024/512/256-column K ranges.
+int setup_batched(dn_layer* h) {
+  const dn_config& c = h->cfg;
+  const char* force = std::getenv("DN_LAYER_KERNELS");
+  if ((force && std::atoi(force) != 0) || c.batch < 2 || c.d_k != 128 || c.d_v != 128) return DN_OK;
+  const int D = c.d_model, R = h->R, V = h->V;
+  const int mf1 = R % 128 == 0 ? 2 : 1;
+  int kr1 = 0, kr2 = 0;
+  for (int kr : {1024, 512, 256})
+    if (!kr1 && dn::bgemm_shape_ok(R, D, mf1, kr)) kr1 = kr;
+  for (int kr : {1024, 512, 256})
+    if (!kr2 && dn::bgemm_shape_ok(D, V, 1, kr)) kr2 = kr;
+  if (!kr1 || !kr2) return DN_OK;
+  const size_t B = c.batch, nb = (B + 63) / 64, nc = std::max(D, V) / 128;
+  const size_t part_elems = std::max((size_t)(D / kr1) * B * R, (size_t)(V / kr2) * B * D);
+  bool ok = hipMalloc(&h->part, sizeof(float) * part_elems) == hipSuccess;
+  ok = ok && hipMalloc(&h->xs, (size_t)24576 * nb * nc) == hipSuccess;
+  ok = ok && hipMalloc(&h->sc, sizeof(float) * 64 * nb * nc) == hipSuccess;
+  ok = ok && hipMalloc(&h->ssq, sizeof(float) * B * nc) == hipSuccess;
+  if (!ok) return DN_E_NOMEM;
+  h->mf1 = mf1; h->kr1 = kr1; h->mf2 = 1; h->kr2 = kr2;
+  h->batched = true;
+  return DN_OK;
 }
 
 // Set up the whole-stack kernel when the shape allows it: hand-off buffers, control words,
@@ -194,6 +233,11 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
     delete h;
     return rc;
   }
+  if (int rc = setup_batched(h); rc != DN_OK) {
+    free_all(h);
+    delete h;
+    return rc;
+  }
   if (hipDeviceSynchronize() != hipSuccess) {
     free_all(h);
     delete h;
@@ -203,7 +247,7 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   if (const char* e = std::getenv("DN_SYNC_DEBUG")) h->sync_debug = std::atoi(e) != 0;
   if (const char* e = std::getenv("DN_VERBOSE"); e && std::atoi(e) != 0)
     std::fprintf(stderr, "[dn] handle: %d layer(s), batch %d: %s\n", cfg->n_layers, cfg->batch,
-                 h->persist ? "whole-stack kernel" : "per-layer kernels");
+                 h->persist ? "whole-stack kernel" : h->batched ? "batched kernels" : "per-layer kernels");
   *out = h;
   return DN_OK;
 }
@@ -252,6 +296,27 @@ DN_API int dn_get_state(dn_layer* h, float* S, float* ring) {
   return hipDeviceSynchronize() == hipSuccess ? DN_OK : DN_E_DEVICE;
 }
 
+namespace {
+// One batched projection: split the activations, split-K MFMA GEMM, epilogue.
+int batched_proj(dn_layer* h, const void* W, const float* s, const float* act, int K, int M, int mf, int kr,
+                 bool prenorm, const float* conv_w, float* ring, float* outp, int out_stride, hipStream_t st) {
+  const dn_config& c = h->cfg;
+  dn::BSplitArgs sp{};
+  sp.act = act; sp.act_stride = K; sp.K = K; sp.B = c.batch; sp.xs = h->xs; sp.sc = h->sc; sp.ssq = h->ssq;
+  if (dn::launch_bsplit(sp, st) != hipSuccess) return DN_E_DEVICE;
+  dn::BGemmArgs g{};
+  g.W = W; g.xs = h->xs; g.sc = h->sc; g.part = h->part; g.M = M; g.K = K; g.B = c.batch; g.KR = kr;
+  if (dn::launch_bgemm(g, c.weight_bits, mf, st) != hipSuccess) return DN_E_DEVICE;
+  dn::BEpiArgs e{};
+  e.part = h->part; e.KS = K / kr; e.M = M; e.B = c.batch; e.s = s;
+  e.ssq = h->ssq; e.NC = K / 128; e.K = K; e.prenorm = prenorm ? 1 : 0; e.eps = c.eps_rms;
+  e.conv_w = conv_w; e.ring = ring; e.C = h->C; e.Kc = c.conv_k; e.out = outp; e.out_stride = out_stride;
+  if (dn::launch_bepi(e, st) != hipSuccess) return DN_E_DEVICE;
+  if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return DN_E_DEVICE;
+  return DN_OK;
+}
+}  // namespace
+
 DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float* beta, float* out, void* hip_stream) {
   if (!h || !x || !alpha || !beta || !out) return DN_E_INVAL;
   if (h->disabled) return DN_E_DISABLED;
@@ -274,6 +339,30 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     a.eps_l2 = c.eps_l2; a.eps_rms = c.eps_rms; a.q_scale = c.q_scale;
     if (dn::launch_persist(a, h->ps, h->nwg, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
+    return DN_OK;
+  }
+  if (h->batched) {
+    const int QK = c.n_k_heads * c.d_k;
+    for (size_t l = 0; l < L; ++l) {
+      const dn_weights& w = h->w[l];
+      if (int rc = batched_proj(h, w.w_in, w.s_in, l == 0 ? x : out + (l - 1) * B * D, (int)D, h->R, h->mf1, h->kr1,
+                                (c.flags & DN_X_RMSNORM) != 0, w.conv_w, h->ring + l * h->ring_elems, h->u, h->R, st);
+          rc != DN_OK)
+        return fail(h, rc);
+      dn::BStateArgs bs{};
+      bs.u = h->u; bs.S = h->S + l * h->s_elems;
+      bs.alpha = alpha + l * B * c.n_v_heads; bs.beta = beta + l * B * c.n_v_heads;
+      bs.norm_w = w.norm_w; bs.y = h->y;
+      bs.B = (int)B; bs.Hk = c.n_k_heads; bs.Hv = c.n_v_heads; bs.R = h->R; bs.C = h->C; bs.QK = QK; bs.V = h->V;
+      bs.eps_l2 = c.eps_l2; bs.eps_rms = c.eps_rms; bs.q_scale = c.q_scale;
+      if (dn::launch_bstate(bs, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      if (int rc = batched_proj(h, w.w_out, w.s_out, h->y, h->V, (int)D, h->mf2, h->kr2, false, nullptr, nullptr,
+                                out + l * B * D, (int)D, st);
+          rc != DN_OK)
+        return fail(h, rc);
+      if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    }
     return DN_OK;
   }
   for (size_t l = 0; l < L; ++l) {

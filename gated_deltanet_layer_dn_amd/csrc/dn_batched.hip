@@ -1,0 +1,441 @@
+// Batched decode: B >= 2 independent sequences stepped together through each layer (the
+// per-layer step of page "qwen36: run the DeltaNet layer end to end on the card", section "What
+// the PR does", Backend paragraph, applied to every sequence of the batch).
+//
+// With a batch the two projections are skinny GEMMs (M weight rows x B sequences x K), so they run
+// on the int8 matrix cores (v_mfma_i32_16x16x64_i8); the recurrence is a pure stream over the B x
+// Hv state tiles.
+//
+//  * k_bsplit: the activations of a step split once into three int8 terms per (sequence,
+//    128-column chunk), v ~= s1 (h + (m + l/254)/254) with s1 = max|v|/127 over the chunk, stored
+//    in the GEMM's fragment order.
+//  * k_bgemm: partial sums over a K range of KR columns (split-K across workgroups) for 64*MF
+//    weight rows and 64 sequences. Each MFMA accumulates exact int32 products; a chunk's three sums
+//    are combined in double with the chunk's scale. Fragments reach LDS by direct-to-LDS copies,
+//    double-buffered; weight fragments stream into registers one chunk ahead.
+//  * k_bepi: adds the KS partial sums in a fixed order and finishes each row: row scale, optional
+//    input pre-norm factor, and for in_proj rows r < C the causal conv over the history plus SiLU.
+//  * k_bstate: one workgroup per (value head, sequence): L2 norms of q and k in double, decay,
+//    delta rule against the decayed state, readout over the updated state and the gated RMSNorm
+//    with silu(z). Thread t holds rows 16(t/32)..+15 x columns 4(t%32)..+3 of the 128 x 128 tile
+//    in registers: one coalesced read and one write of the tile.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dn_internal.h"
+
+namespace dn {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// s_waitcnt with vmcnt <= n and the other counters unconstrained
+#define DN_VMCNT_WAIT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
+constexpr int KC = 128;  // activation columns staged per chunk (2 MFMA k-steps of 64)
+constexpr int KSC = KC / 64;  // k-steps per chunk
+constexpr int NT = 64;   // sequences per workgroup: 4 MFMA column fragments of 16
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Two packed 4-bit weights per byte (element 2m low nibble, 2m+1 high) -> four signed bytes
+// holding 16*w in k order, from one 16-bit half.
+__device__ __forceinline__ int nib4(unsigned h16) {
+  const unsigned y = (h16 & 0xFFu) | ((h16 & 0xFF00u) << 8);
+  return (int)(((y << 4) & 0x00F000F0u) | ((y & 0x00F000F0u) << 8));
+}
+
+// Split v (|v| <= 127 s1) into three int8 terms.
+__device__ __forceinline__ void split3(float v, float inv1, float s1, float inv2, float s2, float inv3, int& h,
+                                       int& m, int& l) {
+  const float hf = fminf(fmaxf(rintf(v * inv1), -127.f), 127.f);
+  const float r1 = fmaf(-s1, hf, v);
+  const float mf = fminf(fmaxf(rintf(r1 * inv2), -127.f), 127.f);
+  const float r2 = fmaf(-s2, mf, r1);
+  const float lf = fminf(fmaxf(rintf(r2 * inv3), -127.f), 127.f);
+  h = (int)hf;
+  m = (int)mf;
+  l = (int)lf;
+}
+
+// Three-term int8 split of the activations, once per (sequence, 128-column chunk), written in
+// the order the GEMM's LDS fragments take: for column block nb and chunk c a 24 KB block
+// [term][k-step][column fragment][lane][16 bytes] (lane = sequence % 16 + 16 * (16-column group of
+// the k-step)), the chunk's scale per sequence, and its sum of squares (for the input pre-norm).
+__global__ __launch_bounds__(256) void k_bsplit(const BSplitArgs a) {
+  const int tid = threadIdx.x, c = blockIdx.x, nb = blockIdx.y;
+  const int NC = gridDim.x;
+  const int sb = tid >> 2, sq4 = tid & 3;  // sequence nb*64 + sb, columns 32 sq4 .. +31 of the chunk
+  const int b = nb * NT + sb;
+  const bool valid = b < a.B;
+  const float* arow = a.act + (size_t)(valid ? b : 0) * a.act_stride + c * KC + 32 * sq4;
+  v4f xv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i] = valid ? reinterpret_cast<const v4f*>(arow)[i] : v4f{0.f, 0.f, 0.f, 0.f};
+  float mx = 0.f, ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mx = fmaxf(mx, fabsf(xv[i][e]));
+      ss = fmaf(xv[i][e], xv[i][e], ss);
+    }
+  // the four threads of a sequence are the lanes of one quad
+  mx = fmaxf(mx, dpp_f<0xB1>(mx));
+  mx = fmaxf(mx, dpp_f<0x4E>(mx));
+  ss += dpp_f<0xB1>(ss);
+  ss += dpp_f<0x4E>(ss);
+  float s1 = mx * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+  const size_t blk = (size_t)nb * NC + c;
+  if (sq4 == 0) {
+    a.sc[blk * NT + sb] = s1;
+    if (valid) a.ssq[(size_t)b * NC + c] = ss;
+  }
+  v4i* xs = static_cast<v4i*>(a.xs) + blk * (3 * KSC * 4 * 64);
+  // columns 32 sq4 + 16 gg: k-step sq4 / 2, 16-column group 2 (sq4 % 2) + gg -> lane
+  // (sb % 16) + 16 * group of column fragment sb / 16
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg) {
+    int hw[4], mw[4], lw[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      int h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+      const v4f v = xv[4 * gg + d];
+      split3(v[0], inv1, s1, inv2, s2, inv3, h0, m0, l0);
+      split3(v[1], inv1, s1, inv2, s2, inv3, h1, m1, l1);
+      split3(v[2], inv1, s1, inv2, s2, inv3, h2, m2, l2);
+      split3(v[3], inv1, s1, inv2, s2, inv3, h3, m3, l3);
+      hw[d] = (h0 & 0xFF) | ((h1 & 0xFF) << 8) | ((h2 & 0xFF) << 16) | ((h3 & 0xFF) << 24);
+      mw[d] = (m0 & 0xFF) | ((m1 & 0xFF) << 8) | ((m2 & 0xFF) << 16) | ((m3 & 0xFF) << 24);
+      lw[d] = (l0 & 0xFF) | ((l1 & 0xFF) << 8) | ((l2 & 0xFF) << 16) | ((l3 & 0xFF) << 24);
+    }
+    const int f = sb >> 4, ln = (sb & 15) + 16 * (2 * (sq4 & 1) + gg), ks2 = sq4 >> 1;
+    xs[((0 * KSC + ks2) * 4 + f) * 64 + ln] = v4i{hw[0], hw[1], hw[2], hw[3]};
+    xs[((1 * KSC + ks2) * 4 + f) * 64 + ln] = v4i{mw[0], mw[1], mw[2], mw[3]};
+    xs[((2 * KSC + ks2) * 4 + f) * 64 + ln] = v4i{lw[0], lw[1], lw[2], lw[3]};
+  }
+}
+
+// Split-K GEMM on the pre-split activations: partial sums of one K range for 64 MF rows and 64
+// sequences. Each 128-column chunk (24 KB of fragments + 64 scales) is copied straight into LDS
+// with direct-to-LDS loads, double-buffered, while the next chunk's weight fragments stream into
+// registers.
+template <int BITS, int MF, int NKS>
+__global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
+  constexpr int NCHUNK = NKS / KSC;
+  constexpr int FRAGS = 3 * KSC * 4 * 64;  // v4i per chunk block (24 KB)
+  constexpr int PER_WAVE = FRAGS / 64 / 4;  // 1 KB direct-to-LDS loads per wave per chunk
+  static_assert(NCHUNK % 2 == 0, "chunks run in pairs");
+  __shared__ v4i xs[2][FRAGS];
+  __shared__ float scl[2][NT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = blockIdx.x, ks = blockIdx.y, nb = blockIdx.z;
+  const int M = a.M, K = a.K, B = a.B;
+  const int NC = K / KC;
+  const int k0 = ks * (NKS * 64);
+  const int c0 = k0 / KC;
+  const int r0 = rb * 64 * MF + wave * 16 * MF;
+
+  typedef v4i Frag[KSC][MF];
+  // A fragments (weights): row r0 + 16 mf + lane%16, k = 64 s + 16 (lane/16) + byte
+  auto load_a = [&](int c, Frag& A) {
+#pragma unroll
+    for (int s = 0; s < KSC; ++s)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        const size_t row = (size_t)(r0 + 16 * mf + (lane & 15));
+        const int kk = k0 + 64 * (KSC * c + s) + 16 * (lane >> 4);
+        if (BITS == 8) {
+          A[s][mf] =
+              __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const int8_t*>(a.W) + row * K + kk));
+        } else {
+          const v2u p = __builtin_nontemporal_load(
+              reinterpret_cast<const v2u*>(static_cast<const uint8_t*>(a.W) + row * (K / 2) + kk / 2));
+          A[s][mf] = v4i{nib4(p.x & 0xFFFFu), nib4(p.x >> 16), nib4(p.y & 0xFFFFu), nib4(p.y >> 16)};
+        }
+      }
+  };
+  // copy chunk c's fragments and scales into LDS buffer c % 2
+  auto stage = [&](int c) {
+    const size_t blk = (size_t)nb * NC + c0 + c;
+    const v4i* src = static_cast<const v4i*>(a.xs) + blk * FRAGS;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave * PER_WAVE + i;  // 1 KB piece
+      __builtin_amdgcn_global_load_lds(src + q * 64 + lane, &xs[c & 1][q * 64], 16, 0, 0);
+    }
+    if (wave == 0) __builtin_amdgcn_global_load_lds(a.sc + blk * NT + lane, &scl[c & 1][0], 4, 0, 0);
+  };
+
+  float facc[MF][4][4];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) facc[mf][f][v] = 0.f;
+
+  Frag A0, A1;
+  stage(0);
+  load_a(0, A0);
+  // one chunk: request the next chunk, wait for this one, run its MFMAs
+  auto chunk = [&](int c, const Frag& A, Frag& Anext) {
+    if (c + 1 < NCHUNK) {
+      stage(c + 1);
+      load_a(c + 1, Anext);
+      // loads issued after this chunk's: the next chunk's pieces (+ its scales on wave 0) and weights
+      if (wave == 0) DN_VMCNT_WAIT(PER_WAVE + 1 + KSC * MF);
+      else DN_VMCNT_WAIT(PER_WAVE + KSC * MF);
+    } else {
+      DN_VMCNT_WAIT(0);
+    }
+    __syncthreads();  // every wave's pieces of chunk c are in LDS
+    v4i acc[3][MF][4];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[t][mf][f] = v4i{0, 0, 0, 0};
+    const v4i* X = xs[c & 1];
+#pragma unroll
+    for (int s = 0; s < KSC; ++s)
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const v4i bf = X[((t * KSC + s) * 4 + f) * 64 + lane];
+#pragma unroll
+          for (int mf = 0; mf < MF; ++mf)
+            acc[t][mf][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s][mf], bf, acc[t][mf][f], 0, 0, 0);
+        }
+    // fold the chunk into the float sums with each sequence's scale (column lane % 16 of fragment f)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const double s1b = (double)scl[c & 1][16 * f + (lane & 15)] * (BITS == 4 ? 1.0 / 16.0 : 1.0);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const double d = (double)acc[0][mf][f][v] +
+                           ((double)acc[1][mf][f][v] + (double)acc[2][mf][f][v] * (1.0 / 254.0)) * (1.0 / 254.0);
+          facc[mf][f][v] += (float)(s1b * d);
+        }
+    }
+    __syncthreads();  // buffer c % 2 is refilled two chunks later
+  };
+  // rolled loop over chunk pairs (ping-pong weight buffers), so only two chunks of weights are live
+#pragma clang loop unroll(disable)
+  for (int c = 0; c < NCHUNK; c += 2) {
+    chunk(c, A0, A1);
+    chunk(c + 1, A1, A0);
+  }
+
+  // partial sums: lane holds rows r0 + 16 mf + 4 (lane/16) .. +3 of sequence nb*64 + 16 f + lane%16
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int b = nb * NT + 16 * f + (lane & 15);
+    if (b < B)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf)
+        *reinterpret_cast<v4f*>(a.part + ((size_t)ks * B + b) * M + r0 + 16 * mf + 4 * (lane >> 4)) =
+            v4f{facc[mf][f][0], facc[mf][f][1], facc[mf][f][2], facc[mf][f][3]};
+  }
+}
+
+// Finish the rows: add the K-range partial sums in order, row scale, input pre-norm factor, and for
+// rows r < C the causal conv over the history (oldest first) plus SiLU, advancing the history.
+__global__ __launch_bounds__(256) void k_bepi(const BEpiArgs a) {
+  const int r = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+  if (r >= a.M) return;
+  float sum = 0.f;
+  for (int k = 0; k < a.KS; ++k) sum += a.part[((size_t)k * a.B + b) * a.M + r];
+  float scale = a.s[r];
+  if (a.prenorm) {
+    float ss = 0.f;
+    for (int c = 0; c < a.NC; ++c) ss += a.ssq[(size_t)b * a.NC + c];
+    scale *= rsqrtf(ss / (float)a.K + a.eps);
+  }
+  const float u = scale * sum;
+  float o = u;
+  if (a.conv_w && r < a.C) {
+    const int Kc = a.Kc, C = a.C;
+    const float* cw = a.conv_w + (size_t)r * Kc;
+    float* rg = a.ring + (size_t)b * (Kc - 1) * C + r;
+    float prev[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < Kc - 1) prev[j] = rg[(size_t)j * C];
+    float acc = cw[Kc - 1] * u;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < Kc - 1) acc = fmaf(cw[j], prev[j], acc);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j + 1 < Kc - 1) rg[(size_t)j * C] = prev[j + 1];
+    if (Kc > 1) rg[(size_t)(Kc - 2) * C] = u;
+    o = silu(acc);
+  }
+  a.out[(size_t)b * a.out_stride + r] = o;
+}
+
+// One (value head, sequence) per workgroup; 128 x 128 state tile.
+__global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
+  constexpr int DK = 128, DV = 128;
+  __shared__ float qs[DK], kks[DK], dl[DV];
+  __shared__ float red[8][DV];
+  __shared__ double dred[4][2];
+  __shared__ float fred[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int cg = tid & 31, rg = tid >> 5;
+  float* Sb = a.S + ((size_t)b * a.Hv + h) * DK * DV;
+  v4f s[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(Sb + (size_t)(16 * rg + r) * DV + 4 * cg));
+
+  const float* ub = a.u + (size_t)b * a.R;
+  const int g = h / (a.Hv / a.Hk);
+  float vv = 0.f, zz = 0.f;
+  double sq = 0.0, sk = 0.0;
+  if (tid < DK) {
+    const float q = ub[g * DK + tid], k = ub[a.QK + g * DK + tid];
+    qs[tid] = q;
+    kks[tid] = k;
+    sq = (double)q * q;
+    sk = (double)k * k;
+    vv = ub[2 * a.QK + h * DV + tid];
+    zz = ub[a.C + h * DV + tid];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sq += __shfl_xor(sq, o);
+    sk += __shfl_xor(sk, o);
+  }
+  if (lane == 0) {
+    dred[wave][0] = sq;
+    dred[wave][1] = sk;
+  }
+  __syncthreads();
+  // L2 norms in double, eps inside the sqrt (waves 0 and 1 hold the 128 rows)
+  const float qn = (float)((double)a.q_scale / sqrt((dred[0][0] + dred[1][0]) + (double)a.eps_l2));
+  const float kn = (float)(1.0 / sqrt((dred[0][1] + dred[1][1]) + (double)a.eps_l2));
+  const float alpha = a.alpha[(size_t)b * a.Hv + h], beta = a.beta[(size_t)b * a.Hv + h];
+
+  // decay, then (decayed S)^T k for this thread's 4 columns over its 16 rows
+  float kvp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float kr = kks[16 * rg + r] * kn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[r][j] *= alpha;
+      kvp[j] = fmaf(s[r][j], kr, kvp[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[rg][4 * cg + j] = kvp[j];
+  __syncthreads();
+  if (tid < DV) {
+    float kv = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kv += red[i][tid];
+    dl[tid] = beta * (vv - kv);
+  }
+  __syncthreads();
+  // delta rule write, then the readout over the updated state
+  float op[4] = {0.f, 0.f, 0.f, 0.f};
+  float d4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) d4[j] = dl[4 * cg + j];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float kr = kks[16 * rg + r] * kn, qr = qs[16 * rg + r] * qn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[r][j] = fmaf(kr, d4[j], s[r][j]);
+      op[j] = fmaf(s[r][j], qr, op[j]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(s[r], reinterpret_cast<v4f*>(Sb + (size_t)(16 * rg + r) * DV + 4 * cg));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[rg][4 * cg + j] = op[j];
+  __syncthreads();
+  float o = 0.f, o2 = 0.f;
+  if (tid < DV) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o += red[i][tid];
+    o2 = o * o;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) o2 += __shfl_xor(o2, off);
+  if (lane == 0 && wave < 2) fred[wave] = o2;
+  __syncthreads();
+  if (tid < DV) {
+    const float inv = rsqrtf((fred[0] + fred[1]) / (float)DV + a.eps_rms);
+    a.y[(size_t)b * a.V + h * DV + tid] = a.norm_w[tid] * o * inv * silu(zz);
+  }
+}
+
+template <int BITS, int MF, int NKS>
+hipError_t go_bgemm(const BGemmArgs& a, hipStream_t st) {
+  const dim3 grid(a.M / (64 * MF), a.K / (NKS * 64), (a.B + NT - 1) / NT);
+  hipLaunchKernelGGL((k_bgemm<BITS, MF, NKS>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t bgemm_bits(const BGemmArgs& a, int mf, hipStream_t st) {
+  const int nks = a.KR / 64;
+  if (mf == 2) {
+    if (nks == 16) return go_bgemm<BITS, 2, 16>(a, st);
+    if (nks == 8) return go_bgemm<BITS, 2, 8>(a, st);
+    if (nks == 4) return go_bgemm<BITS, 2, 4>(a, st);
+  } else if (mf == 1) {
+    if (nks == 16) return go_bgemm<BITS, 1, 16>(a, st);
+    if (nks == 8) return go_bgemm<BITS, 1, 8>(a, st);
+    if (nks == 4) return go_bgemm<BITS, 1, 4>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool bgemm_shape_ok(int M, int K, int mf, int kr) {
+  return M > 0 && K > 0 && (mf == 1 || mf == 2) && M % (64 * mf) == 0 && (kr == 256 || kr == 512 || kr == 1024) &&
+         K % kr == 0;
+}
+
+hipError_t launch_bsplit(const BSplitArgs& a, hipStream_t st) {
+  if (a.K % KC) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bsplit, dim3(a.K / KC, (a.B + NT - 1) / NT), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bgemm(const BGemmArgs& a, int bits, int mf, hipStream_t st) {
+  if (!bgemm_shape_ok(a.M, a.K, mf, a.KR)) return hipErrorInvalidValue;
+  return bits == 8 ? bgemm_bits<8>(a, mf, st) : bgemm_bits<4>(a, mf, st);
+}
+
+hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_bepi, dim3((a.M + 255) / 256, a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bstate(const BStateArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_bstate, dim3(a.Hv, a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dn

@@ -40,6 +40,54 @@ struct HeadArgs {
 hipError_t launch_gemv(const GemvArgs& a, int bits, hipStream_t st);
 hipError_t launch_head(const HeadArgs& a, hipStream_t st);
 
+// ---- batched path (B >= 2): int8-MFMA projections and a streaming state kernel ----
+// act[b][k] split into three int8 terms per (sequence, 128-column chunk), in the GEMM's fragment order.
+struct BSplitArgs {
+  const float* act;      // [B][act_stride], K columns used
+  int act_stride;
+  int K, B;
+  void* xs;              // [ceil(B/64)][K/128] blocks of 24 KB
+  float* sc;             // [ceil(B/64)][K/128][64] split scales
+  float* ssq;            // [B][K/128] sums of squares
+};
+// part[ks][b][r] = sum over the ks-th K range of W[r][k] * act[b][k], for M rows.
+struct BGemmArgs {
+  const void* W;         // [M][K] int8 or [M][K/2] packed int4
+  const void* xs;        // split activations (BSplitArgs::xs)
+  const float* sc;       // their scales (BSplitArgs::sc)
+  float* part;           // [K/KR][B][M]
+  int M, K, B, KR;
+};
+// out[b][r] = epilogue(s[r] * sum_ks part[ks][b][r]).
+struct BEpiArgs {
+  const float* part;
+  int KS, M, B;
+  const float* s;        // [M]
+  const float* ssq;      // [B][NC] (pre-norm only)
+  int NC, K, prenorm;    // the pre-norm factor is 1/sqrt(sum ssq / K + eps)
+  float eps;
+  const float* conv_w;   // [C][Kc] or nullptr: rows r < C get the causal conv + SiLU
+  float* ring;           // [B][Kc-1][C], oldest first
+  int C, Kc;
+  float* out;            // [B][out_stride]
+  int out_stride;
+};
+struct BStateArgs {
+  const float* u;        // [B][R]: post-conv q | k | v, then raw z
+  float* S;              // [B][Hv][128][128]
+  const float* alpha;    // [B][Hv]
+  const float* beta;     // [B][Hv]
+  const float* norm_w;   // [128]
+  float* y;              // [B][V]
+  int B, Hk, Hv, R, C, QK, V;
+  float eps_l2, eps_rms, q_scale;
+};
+bool bgemm_shape_ok(int M, int K, int mf, int kr);
+hipError_t launch_bsplit(const BSplitArgs& a, hipStream_t st);
+hipError_t launch_bgemm(const BGemmArgs& a, int bits, int mf, hipStream_t st);
+hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st);
+hipError_t launch_bstate(const BStateArgs& a, hipStream_t st);
+
 // ---- whole-stack kernel (single sequence, 128 x 128 state tiles) ----
 struct LayerW {
   const void* w_in;

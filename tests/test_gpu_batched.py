@@ -1,0 +1,99 @@
+"""The batched path (B >= 2 sequences with 128 x 128 state tiles: int8-MFMA projections with
+split-K partial sums, streaming state kernel): parity with the oracle per sequence, ragged
+batches (a partial block of 64 sequences), int4 weights, conv widths, a pre-normed stack, K ranges
+of 1024 / 512 / 256 columns, agreement with the per-layer kernels and bitwise reruns."""
+import numpy as np
+import pytest
+
+import dn_inputs as gi
+import oracle as orc
+
+from gpu_util import OUT_TOL, STATE_TOL, make_stack, out_err, run_gpu, state_err
+
+pytestmark = pytest.mark.gpu
+
+BATCHED = {
+    # d_model 1024: in_proj K range 1024 (one split), out_proj 512
+    "b_small": gi.custom("b_small", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=8,
+                         n_tokens=6, ring_std=1.0),
+    # 70 sequences: a full block of 64 and a ragged block of 6
+    "b_ragged": gi.custom("b_ragged", d_model=512, n_k_heads=2, d_k=128, n_v_heads=4, d_v=128, batch=70,
+                          n_tokens=4, ring_std=1.0),
+    "b_int4": gi.custom("b_int4", d_model=2048, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=16,
+                        n_tokens=5, weight_bits=4, ring_std=1.0),
+    "b_conv1": gi.custom("b_conv1", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=4,
+                         conv_k=1, n_tokens=4),
+    "b_conv2": gi.custom("b_conv2", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=3,
+                         conv_k=2, n_tokens=4, ring_std=1.0),
+    # 768-wide model and 768 value columns: 256-column K ranges; in_proj rows 2304 (18 blocks of 128)
+    "b_odd": gi.custom("b_odd", d_model=768, n_k_heads=3, d_k=128, n_v_heads=6, d_v=128, batch=5,
+                       n_tokens=4, q_scale=0.0883883),
+    # three pre-normed layers, each output feeding the next layer
+    "b_stack": gi.custom("b_stack", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=6,
+                         n_layers=3, n_tokens=5, flags=gi.DN_X_RMSNORM, ring_std=1.0),
+}
+
+
+def _path_of(cfg, layers, capfd, monkeypatch):
+    monkeypatch.setenv("DN_VERBOSE", "1")
+    st = make_stack(cfg, layers)
+    monkeypatch.delenv("DN_VERBOSE")
+    return st, capfd.readouterr().err
+
+
+def _per_seq_out_err(gout, ref):
+    """max over layers and sequences of the per-token error relative to that sequence's RMS."""
+    T, L, B, D = ref.shape
+    return max(out_err(gout[:, l, b], ref[:, l, b]) for l in range(L) for b in range(B))
+
+
+@pytest.mark.parametrize("name", list(BATCHED))
+def test_batched_parity(name, capfd, monkeypatch):
+    cfg = BATCHED[name]
+    layers, stream = gi.generate(cfg)
+    print(f"[batched] {name}", flush=True)
+    st, err = _path_of(cfg, layers, capfd, monkeypatch)
+    try:
+        assert "batched kernels" in err, err
+        gout = run_gpu(st, stream)
+        gS, gH = st.get_state()
+    finally:
+        st.close()
+    ref_out, ref_S, ref_H = orc.run(cfg, layers, stream)
+    e = _per_seq_out_err(gout, ref_out)
+    es = state_err(gS.cpu().numpy(), ref_S)
+    eh = state_err(gH.cpu().numpy(), ref_H) if cfg.conv_k > 1 else 0.0
+    print(f"[batched] {name}: out {e:.2e} state {es:.2e} ring {eh:.2e}", flush=True)
+    assert e <= OUT_TOL and es <= STATE_TOL and eh <= STATE_TOL
+
+
+def test_batched_agrees_with_layer_kernels(monkeypatch):
+    cfg = BATCHED["b_stack"]
+    layers, stream = gi.generate(cfg)
+    a = make_stack(cfg, layers)
+    out_a = run_gpu(a, stream)
+    Sa, Ra = a.get_state()
+    a.close()
+    monkeypatch.setenv("DN_LAYER_KERNELS", "1")
+    b = make_stack(cfg, layers)
+    monkeypatch.delenv("DN_LAYER_KERNELS")
+    out_b = run_gpu(b, stream)
+    Sb, Rb = b.get_state()
+    b.close()
+    assert _per_seq_out_err(out_a, out_b.astype(np.float64)) <= 1e-4
+    assert state_err(Sa.cpu().numpy(), Sb.cpu().numpy()) <= 1e-5
+    assert state_err(Ra.cpu().numpy(), Rb.cpu().numpy()) <= 1e-5
+
+
+def test_batched_rerun_bitwise():
+    """Split-K partial sums are added in a fixed order: two runs are byte-identical."""
+    cfg = BATCHED["b_ragged"]
+    layers, stream = gi.generate(cfg)
+    outs, states = [], []
+    for _ in range(2):
+        st = make_stack(cfg, layers)
+        outs.append(run_gpu(st, stream))
+        states.append(st.get_state()[0].cpu().numpy())
+        st.close()
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(states[0], states[1])
