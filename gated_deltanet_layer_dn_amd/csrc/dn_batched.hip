@@ -17,7 +17,7 @@
 //    input pre-norm factor, and for in_proj rows r < C the causal conv over the history plus SiLU.
 //  * k_bstate: one workgroup per (value head, sequence): L2 norms of q and k in double, decay,
 //    delta rule against the decayed state, readout over the updated state and the gated RMSNorm
-//    with silu(z). Thread t holds rows 16(t/32)..+15 x columns 4(t%32)..+3 of the 128 x 128 tile
+//    with silu(z); the head's 128 outputs are one chunk of out_proj's input, split in place. Thread t holds rows 16(t/32)..+15 x columns 4(t%32)..+3 of the 128 x 128 tile
 //    in registers: one coalesced read and one write of the tile.
 #include <hip/hip_runtime.h>
 
@@ -296,6 +296,7 @@ __global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
   __shared__ float red[8][DV];
   __shared__ double dred[4][2];
   __shared__ float fred[2];
+  __shared__ __attribute__((aligned(16))) int8_t ybytes[3][DV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   const int cg = tid & 31, rg = tid >> 5;
@@ -382,10 +383,40 @@ __global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
   for (int off = 32; off > 0; off >>= 1) o2 += __shfl_xor(o2, off);
   if (lane == 0 && wave < 2) fred[wave] = o2;
   __syncthreads();
+  float yv = 0.f;
   if (tid < DV) {
     const float inv = rsqrtf((fred[0] + fred[1]) / (float)DV + a.eps_rms);
-    a.y[(size_t)b * a.V + h * DV + tid] = a.norm_w[tid] * o * inv * silu(zz);
+    yv = a.norm_w[tid] * o * inv * silu(zz);
   }
+  // This head's 128 readout columns are one 128-column chunk of the out_proj input of sequence b:
+  // split it into three int8 terms in the GEMM's fragment order (as k_bsplit does).
+  float mx = fabsf(yv);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  __syncthreads();  // fred is reused
+  if (lane == 0 && wave < 2) fred[wave] = mx;
+  __syncthreads();
+  float s1 = fmaxf(fred[0], fred[1]) * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  if (tid < DV) {
+    const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+    int hq, mq, lq;
+    split3(yv, inv1, s1, inv2, s2, inv3, hq, mq, lq);
+    ybytes[0][tid] = (int8_t)hq;
+    ybytes[1][tid] = (int8_t)mq;
+    ybytes[2][tid] = (int8_t)lq;
+  }
+  __syncthreads();
+  const int sb = b % NT;
+  const size_t blk = (size_t)(b / NT) * a.Hv + h;  // column block of 64 sequences, chunk h
+  if (tid < 3 * 8) {
+    // 16 columns 16 p .. +15 of term t: k-step p / 4, 16-column group p % 4
+    const int t = tid >> 3, p = tid & 7;
+    const int ln = (sb & 15) + 16 * (p & 3), f = sb >> 4, ks2 = p >> 2;
+    static_cast<v4i*>(a.xs)[blk * (3 * KSC * 4 * 64) + ((t * KSC + ks2) * 4 + f) * 64 + ln] =
+        *reinterpret_cast<const v4i*>(&ybytes[t][16 * p]);
+  }
+  if (tid == 0) a.sc[blk * NT + sb] = s1;
 }
 
 template <int BITS, int MF, int NKS>
@@ -398,11 +429,7 @@ hipError_t go_bgemm(const BGemmArgs& a, hipStream_t st) {
 template <int BITS>
 hipError_t bgemm_bits(const BGemmArgs& a, int mf, hipStream_t st) {
   const int nks = a.KR / 64;
-  if (mf == 2) {
-    if (nks == 16) return go_bgemm<BITS, 2, 16>(a, st);
-    if (nks == 8) return go_bgemm<BITS, 2, 8>(a, st);
-    if (nks == 4) return go_bgemm<BITS, 2, 4>(a, st);
-  } else if (mf == 1) {
+  if (mf == 1) {
     if (nks == 16) return go_bgemm<BITS, 1, 16>(a, st);
     if (nks == 8) return go_bgemm<BITS, 1, 8>(a, st);
     if (nks == 4) return go_bgemm<BITS, 1, 4>(a, st);
@@ -413,8 +440,7 @@ hipError_t bgemm_bits(const BGemmArgs& a, int mf, hipStream_t st) {
 }  // namespace
 
 bool bgemm_shape_ok(int M, int K, int mf, int kr) {
-  return M > 0 && K > 0 && (mf == 1 || mf == 2) && M % (64 * mf) == 0 && (kr == 256 || kr == 512 || kr == 1024) &&
-         K % kr == 0;
+  return M > 0 && K > 0 && mf == 1 && M % (64 * mf) == 0 && (kr == 256 || kr == 512 || kr == 1024) && K % kr == 0;
 }
 
 hipError_t launch_bsplit(const BSplitArgs& a, hipStream_t st) {

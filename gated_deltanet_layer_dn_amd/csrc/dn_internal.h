@@ -78,7 +78,8 @@ struct BStateArgs {
   const float* alpha;    // [B][Hv]
   const float* beta;     // [B][Hv]
   const float* norm_w;   // [128]
-  float* y;              // [B][V]
+  void* xs;              // out: the gated readout split for out_proj (BSplitArgs::xs layout, K = V)
+  float* sc;             // out: its scales
   int B, Hk, Hv, R, C, QK, V;
   float eps_l2, eps_rms, q_scale;
 };
