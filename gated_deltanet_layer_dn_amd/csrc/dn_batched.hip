@@ -253,6 +253,102 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
   }
 }
 
+// Split-K GEMM, all loads up front. A workgroup of 4*NRB waves owns one K range of KR columns, 64
+// sequences and NRB blocks of 64 weight rows (wave w: 16 rows of block w/4). It first copies the K
+// range's split activations (3 x 64 x KR bytes) into LDS with direct-to-LDS loads and waits for
+// them alone (the compiler orders every later LDS read after all loads that precede it, so no
+// weight load may be in flight at that point); then each wave requests its whole K range of
+// weight fragments at once and runs the MFMAs as they arrive.
+template <int BITS, int NRB, int KR>
+__global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
+  constexpr int NW = 4 * NRB;              // waves
+  constexpr int NKS = KR / 64;             // k-steps
+  constexpr int NCHUNK = KR / KC;          // 128-column chunks (one split scale each)
+  constexpr int FRAGS = 3 * KSC * 4 * 64;  // v4i per chunk block (24 KB)
+  constexpr int PIECES = NCHUNK * FRAGS / 64;  // 1 KB direct-to-LDS copies
+  static_assert(PIECES % NW == 0, "");
+  __shared__ v4i xs[NCHUNK][FRAGS];
+  __shared__ float scl[NCHUNK][NT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = blockIdx.x, ks = blockIdx.y, nb = blockIdx.z;
+  const int M = a.M, K = a.K, B = a.B;
+  const int NC = K / KC;
+  const int k0 = ks * KR, c0 = k0 / KC;
+  const int row0 = (rg * NRB + wave / 4) * 64 + 16 * (wave & 3);
+
+  {
+    const v4i* src = static_cast<const v4i*>(a.xs) + ((size_t)nb * NC + c0) * FRAGS;
+    v4i* dst = &xs[0][0];
+#pragma unroll
+    for (int i = 0; i < PIECES / NW; ++i) {
+      const int q = wave * (PIECES / NW) + i;  // 1 KB piece of the K range's contiguous blocks
+      __builtin_amdgcn_global_load_lds(src + q * 64 + lane, dst + q * 64, 16, 0, 0);
+    }
+    if (wave == 0)
+#pragma unroll
+      for (int c = 0; c < NCHUNK; ++c)
+        __builtin_amdgcn_global_load_lds(a.sc + ((size_t)nb * NC + c0 + c) * NT + lane, &scl[c][0], 4, 0, 0);
+  }
+  DN_VMCNT_WAIT(0);
+  __syncthreads();
+  v4i A[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const size_t row = (size_t)(row0 + (lane & 15));
+    const int kk = k0 + 64 * s + 16 * (lane >> 4);
+    if (BITS == 8) {
+      A[s] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const int8_t*>(a.W) + row * K + kk));
+    } else {
+      const v2u p = __builtin_nontemporal_load(
+          reinterpret_cast<const v2u*>(static_cast<const uint8_t*>(a.W) + row * (K / 2) + kk / 2));
+      A[s] = v4i{nib4(p.x & 0xFFFFu), nib4(p.x >> 16), nib4(p.y & 0xFFFFu), nib4(p.y >> 16)};
+    }
+  }
+
+  float facc[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) facc[f][v] = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCHUNK; ++c) {
+    v4i acc[3][4];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[t][f] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[t][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[KSC * c + s], xs[c][((t * KSC + s) * 4 + f) * 64 + lane],
+                                                            acc[t][f], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // one k-step's fragments in registers at a time
+    }
+    // a chunk's sums are below 2^22 in magnitude: exact in fp32, combined in fp32
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const float s1b = scl[c][16 * f + (lane & 15)] * (BITS == 4 ? 1.0f / 16.0f : 1.0f);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float d = (float)acc[0][f][v] +
+                         fmaf((float)acc[2][f][v], 1.0f / 254.0f, (float)acc[1][f][v]) * (1.0f / 254.0f);
+        facc[f][v] = fmaf(s1b, d, facc[f][v]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one chunk's accumulators live at a time
+  }
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int b = nb * NT + 16 * f + (lane & 15);
+    if (b < B)
+      *reinterpret_cast<v4f*>(a.part + ((size_t)ks * B + b) * M + row0 + 4 * (lane >> 4)) =
+          v4f{facc[f][0], facc[f][1], facc[f][2], facc[f][3]};
+  }
+}
+
 // Finish the rows: add the K-range partial sums in order, row scale, input pre-norm factor, and for
 // rows r < C the causal conv over the history (oldest first) plus SiLU, advancing the history.
 __global__ __launch_bounds__(256) void k_bepi(const BEpiArgs a) {
@@ -452,6 +548,37 @@ hipError_t launch_bsplit(const BSplitArgs& a, hipStream_t st) {
 hipError_t launch_bgemm(const BGemmArgs& a, int bits, int mf, hipStream_t st) {
   if (!bgemm_shape_ok(a.M, a.K, mf, a.KR)) return hipErrorInvalidValue;
   return bits == 8 ? bgemm_bits<8>(a, mf, st) : bgemm_bits<4>(a, mf, st);
+}
+
+template <int BITS, int NRB, int KR>
+hipError_t go_bgemm2(const BGemmArgs& a, hipStream_t st) {
+  const dim3 grid(a.M / (64 * NRB), a.K / KR, (a.B + NT - 1) / NT);
+  hipLaunchKernelGGL((k_bgemm2<BITS, NRB, KR>), grid, dim3(256 * NRB), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int KR>
+hipError_t bgemm2_kr(const BGemmArgs& a, int nrb, hipStream_t st) {
+  if (nrb == 3) return go_bgemm2<BITS, 3, KR>(a, st);
+  if (nrb == 2) return go_bgemm2<BITS, 2, KR>(a, st);
+  if (nrb == 1) return go_bgemm2<BITS, 1, KR>(a, st);
+  return hipErrorInvalidValue;
+}
+
+template <int BITS>
+hipError_t bgemm2_bits(const BGemmArgs& a, int nrb, hipStream_t st) {
+  if (a.KR == 512) return bgemm2_kr<BITS, 512>(a, nrb, st);
+  if (a.KR == 256) return bgemm2_kr<BITS, 256>(a, nrb, st);
+  return hipErrorInvalidValue;
+}
+
+bool bgemm2_shape_ok(int M, int K, int nrb, int kr) {
+  return M > 0 && K > 0 && nrb >= 1 && nrb <= 3 && M % (64 * nrb) == 0 && (kr == 256 || kr == 512) && K % kr == 0;
+}
+
+hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st) {
+  if (!bgemm2_shape_ok(a.M, a.K, nrb, a.KR)) return hipErrorInvalidValue;
+  return bits == 8 ? bgemm2_bits<8>(a, nrb, st) : bgemm2_bits<4>(a, nrb, st);
 }
 
 hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st) {

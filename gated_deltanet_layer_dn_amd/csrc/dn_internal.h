@@ -86,6 +86,9 @@ struct BStateArgs {
 bool bgemm_shape_ok(int M, int K, int mf, int kr);
 hipError_t launch_bsplit(const BSplitArgs& a, hipStream_t st);
 hipError_t launch_bgemm(const BGemmArgs& a, int bits, int mf, hipStream_t st);
+// all loads up front: K range KR (256 or 512), NRB (1..3) blocks of 64 rows per workgroup
+bool bgemm2_shape_ok(int M, int K, int nrb, int kr);
+hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st);
 hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st);
 hipError_t launch_bstate(const BStateArgs& a, hipStream_t st);
 
