@@ -479,6 +479,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       // arrived, so that the u hand-off is not queued behind them
       wait_counter(&sm.u_done, l + 1, &sm.abort_flag);
       if (l + 1 < a.L) load_a(l + 1);
+      if (tid == 0) DN_MARK(a, l, 28);
     }
     __syncthreads();  // (3) gated readout staged
     if (sm.abort_flag) break;
