@@ -31,6 +31,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 DN_X_RMSNORM = 1  # flag bit: RMS-normalise each layer's input (stack pre-norm)
+DN_ALPHA_PER_KEY = 2  # flag bit: one decay per key channel, alpha [T][L][B][Hv][dk]
 
 
 @dataclass(frozen=True)
@@ -144,7 +145,7 @@ class Layer:
 @dataclass
 class Stream:
     x: np.ndarray      # [T][B][D]
-    alpha: np.ndarray  # [T][L][B][Hv]
+    alpha: np.ndarray  # [T][L][B][Hv] ([T][L][B][Hv][dk] with DN_ALPHA_PER_KEY)
     beta: np.ndarray   # [T][L][B][Hv]
 
 
@@ -183,7 +184,8 @@ def gen_stream(cfg: Config, rng: np.random.Generator, n_tokens: int | None = Non
     T = cfg.n_tokens if n_tokens is None else n_tokens
     B, D, L, Hv = cfg.batch, cfg.d_model, cfg.n_layers, cfg.n_v_heads
     x = rng.standard_normal((T, B, D)).astype(np.float32)
-    alpha = np.exp(-rng.uniform(0.0, 0.1, size=(T, L, B, Hv))).astype(np.float32)
+    ashape = (T, L, B, Hv, cfg.d_k) if cfg.flags & DN_ALPHA_PER_KEY else (T, L, B, Hv)
+    alpha = np.exp(-rng.uniform(0.0, 0.1, size=ashape)).astype(np.float32)
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, L, B, Hv))))).astype(np.float32)
     return Stream(x, alpha, beta)
 

@@ -65,6 +65,7 @@ def lib():
             L.dno_conv_silu.argtypes = [I, I, P, P, P, P]; L.dno_conv_silu.restype = None
             L.dno_l2norm.argtypes = [I, P, Dd, P]; L.dno_l2norm.restype = None
             L.dno_delta_head.argtypes = [I, I, P, P, P, P, Dd, Dd, Dd, P]; L.dno_delta_head.restype = None
+            L.dno_delta_head_vec.argtypes = [I, I, P, P, P, P, P, Dd, Dd, P]; L.dno_delta_head_vec.restype = None
             L.dno_gated_rmsnorm.argtypes = [I, P, P, P, Dd, P]; L.dno_gated_rmsnorm.restype = None
             L.dno_layer_step.argtypes = [P, P, P, P, P, P, P, P]; L.dno_layer_step.restype = I
             L.dno_run.argtypes = [P, P, P, P, I, P, P, P, P]; L.dno_run.restype = I
@@ -135,6 +136,15 @@ def delta_head(S, k, v, q, alpha, beta, q_scale=1.0):
     S = _f64(S).copy(); dk, dv = S.shape
     k = _f64(k); v = _f64(v); q = _f64(q); o = np.zeros(dv, np.float64)
     lib().dno_delta_head(dk, dv, _p(S), _p(k), _p(v), _p(q), float(alpha), float(beta), float(q_scale), _p(o))
+    return S, o
+
+
+def delta_head_vec(S, k, v, q, alpha, beta, q_scale=1.0):
+    """The recurrence with a decay per key channel: alpha [dk] scales key row i. Returns (S_new, o)."""
+    S = _f64(S).copy(); dk, dv = S.shape
+    k = _f64(k); v = _f64(v); q = _f64(q); a = _f64(alpha); o = np.zeros(dv, np.float64)
+    assert a.shape == (dk,)
+    lib().dno_delta_head_vec(dk, dv, _p(S), _p(k), _p(v), _p(q), _p(a), float(beta), float(q_scale), _p(o))
     return S, o
 
 

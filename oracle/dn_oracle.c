@@ -28,6 +28,7 @@
 #include <string.h>
 
 #define DNO_X_RMSNORM 1u
+#define DNO_ALPHA_PER_KEY 2u
 
 typedef struct {
   int d_model, n_k_heads, d_k, n_v_heads, d_v;
@@ -140,6 +141,31 @@ void dno_delta_head(int dk, int dv, double *S, const double *k, const double *v,
   free(d);
 }
 
+/* The same recurrence with a decay per key channel, the form the linear-attention layers of the
+ * other engines use ([DN-GPU], "Where this goes next": the same gated delta step, only the
+ * dimensions and the gate differ). alpha[i] scales key row i of the state:
+ *   S'[i][j] = alpha[i] * S[i][j]
+ * and the delta, write-back and readout follow as in dno_delta_head. */
+void dno_delta_head_vec(int dk, int dv, double *S, const double *k, const double *v, const double *q,
+                        const double *alpha, double beta, double q_scale, double *o) {
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] *= alpha[i];
+  double *d = (double *)malloc(sizeof(double) * dv);
+  for (int j = 0; j < dv; ++j) {
+    double kv = 0.0;
+    for (int i = 0; i < dk; ++i) kv += S[(long)i * dv + j] * k[i];
+    d[j] = beta * (v[j] - kv);
+  }
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(long)i * dv + j] += k[i] * d[j];
+  for (int j = 0; j < dv; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * q[i];
+    o[j] = q_scale * acc;
+  }
+  free(d);
+}
+
 /* Gated RMSNorm with silu(z) [DN-GPU], per value head over dv:
  *   y[j] = w[j] * o[j] / sqrt(mean(o^2) + eps) * silu(z[j]). */
 void dno_gated_rmsnorm(int n, const double *o, const double *z, const float *w, double eps, double *y) {
@@ -155,7 +181,8 @@ void dno_gated_rmsnorm(int n, const double *o, const double *z, const float *w, 
  * in_proj rows: q (Hk*dk) | k (Hk*dk) | v (Hv*dv) | z (Hv*dv) [TRUNK]; q, k, v are
  * convolved, z is not. Value head h reads key head h / (Hv/Hk).
  *   S    [B][Hv][dk][dv]  (in/out)     hist [B][K-1][C] (in/out)
- *   x    [B][D]  alpha, beta [B][Hv]   out  [B][D]                               */
+ *   x    [B][D]  alpha, beta [B][Hv]   out  [B][D]
+ *   (with DNO_ALPHA_PER_KEY, alpha is [B][Hv][dk])                               */
 int dno_layer_step(const dno_dims *d, const dno_layer_weights *W, double *S, double *hist,
                    const double *x, const float *alpha, const float *beta, double *out) {
   const int D = d->d_model, Hk = d->n_k_heads, dk = d->d_k, Hv = d->n_v_heads, dv = d->d_v;
@@ -183,8 +210,15 @@ int dno_layer_step(const dno_dims *d, const dno_layer_weights *W, double *S, dou
       dno_l2norm(dk, c + QK + (long)g * dk, d->eps_l2, kh);
       const double *v = c + 2 * QK + (long)h * dv;
       double *Sh = S + ((long)b * Hv + h) * dk * dv;
-      dno_delta_head(dk, dv, Sh, kh, v, qh, (double)alpha[(long)b * Hv + h], (double)beta[(long)b * Hv + h],
-                     d->q_scale, o);
+      if (d->flags & DNO_ALPHA_PER_KEY) {
+        double *av = (double *)malloc(sizeof(double) * dk);
+        for (int i = 0; i < dk; ++i) av[i] = (double)alpha[((long)b * Hv + h) * dk + i];
+        dno_delta_head_vec(dk, dv, Sh, kh, v, qh, av, (double)beta[(long)b * Hv + h], d->q_scale, o);
+        free(av);
+      } else {
+        dno_delta_head(dk, dv, Sh, kh, v, qh, (double)alpha[(long)b * Hv + h], (double)beta[(long)b * Hv + h],
+                       d->q_scale, o);
+      }
       dno_gated_rmsnorm(dv, o, z + (long)h * dv, W->norm_w, d->eps_rms, y + (long)h * dv);
       free(qh); free(kh); free(o);
     }
@@ -197,7 +231,7 @@ int dno_layer_step(const dno_dims *d, const dno_layer_weights *W, double *S, dou
 /* A run of T tokens through a stack of L layers: the output of layer l is the
  * input of layer l+1; x feeds layer 0.
  *   S    [L][B][Hv][dk][dv]   hist [L][B][K-1][C]   (in/out, double)
- *   x    [T][B][D] fp32       alpha, beta [T][L][B][Hv] fp32
+ *   x    [T][B][D] fp32       alpha, beta [T][L][B][Hv] fp32 (alpha [T][L][B][Hv][dk] per key)
  *   out  [T][L][B][D] double (every layer's output, so a stack can be checked per layer) */
 int dno_run(const dno_dims *d, const dno_layer_weights *W, double *S, double *hist, int T,
             const float *x, const float *alpha, const float *beta, double *out) {
@@ -210,7 +244,8 @@ int dno_run(const dno_dims *d, const dno_layer_weights *W, double *S, double *hi
     for (int l = 0; l < L; ++l) {
       double *o = out + ((long)t * L + l) * B * D;
       const long ab = ((long)t * L + l) * B * Hv;
-      int rc = dno_layer_step(d, W + l, S + l * s_stride, hist + l * h_stride, xin, alpha + ab, beta + ab, o);
+      const long aa = (d->flags & DNO_ALPHA_PER_KEY) ? ab * d->d_k : ab;
+      int rc = dno_layer_step(d, W + l, S + l * s_stride, hist + l * h_stride, xin, alpha + aa, beta + ab, o);
       if (rc) { free(xin); return rc; }
       memcpy(xin, o, sizeof(double) * B * D);
     }

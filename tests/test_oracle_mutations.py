@@ -35,6 +35,11 @@ MUTATIONS = [
     ("prenorm_missing", "if (d->flags & DNO_X_RMSNORM)", "if (0)", 0),
     ("chain_broken", "memcpy(xin, o, sizeof(double) * B * D);", "(void)o;", 0),
     ("q_scale_ignored", "o[j] = q_scale * acc;", "o[j] = acc;", 0),
+    ("per_key_decay_on_columns", "S[(long)i * dv + j] *= alpha[i];", "S[(long)i * dv + j] *= alpha[j % dk];", 0),
+    ("per_key_alpha_head_index", "av[i] = (double)alpha[((long)b * Hv + h) * dk + i];",
+     "av[i] = (double)alpha[((long)h * B + b) * dk + i];", 0),
+    ("per_key_alpha_layer_stride", "const long aa = (d->flags & DNO_ALPHA_PER_KEY) ? ab * d->d_k : ab;",
+     "const long aa = ab;", 0),
 ]
 
 

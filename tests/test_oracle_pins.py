@@ -323,3 +323,68 @@ def test_stack_without_prenorm_grows_per_layer():
     out, _, _ = orc.run(cfg, layers, stream)
     r = [np.sqrt(np.mean(out[0, l] ** 2)) for l in range(3)]
     assert r[1] / r[0] > 50 and r[2] / r[1] > 50
+
+
+# --------------------------------------------------------------------------- decay per key channel
+
+def test_per_key_decay_with_equal_entries_is_the_scalar_step_bitwise():
+    dk, dv = 32, 24
+    S = RNG.standard_normal((dk, dv)); k = _unit(RNG.standard_normal(dk)); v = RNG.standard_normal(dv)
+    q = _unit(RNG.standard_normal(dk))
+    S1, o1 = orc.delta_head(S, k, v, q, 0.93, 0.6, q_scale=0.7)
+    S2, o2 = orc.delta_head_vec(S, k, v, q, np.full(dk, 0.93), 0.6, q_scale=0.7)
+    assert np.array_equal(S1, S2) and np.array_equal(o1, o2)
+
+
+def test_per_key_decay_scales_key_rows():
+    """beta = 0: the step is the decay alone, S'[i][j] = alpha[i] S[i][j]; a one-hot alpha keeps one
+    key row and zeroes the rest (rows, not columns)."""
+    dk, dv = 16, 24
+    S = RNG.standard_normal((dk, dv)); k = _unit(RNG.standard_normal(dk)); v = RNG.standard_normal(dv)
+    a = np.zeros(dk); a[5] = 1.0
+    S1, o = orc.delta_head_vec(S, k, v, k, a, 0.0)
+    assert np.array_equal(S1[5], S[5]) and not np.any(np.delete(S1, 5, axis=0))
+    np.testing.assert_allclose(o, k[5] * S[5], rtol=1e-14, atol=1e-15)
+    S1, _ = orc.delta_head_vec(S, k, v, k, np.ones(dk), 0.0)
+    assert np.array_equal(S1, S)
+    S1, _ = orc.delta_head_vec(S, k, v, k, np.zeros(dk), 1.0)
+    np.testing.assert_allclose(S1, np.outer(k, v), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (128, 128), (64, 32)])
+def test_per_key_delta_rule_retrieval_identity(dk, dv):
+    for _ in range(5):
+        S = RNG.standard_normal((dk, dv)) * 0.3
+        k = RNG.standard_normal(dk); k = k / np.sqrt(k @ k + 1e-6)
+        v = RNG.standard_normal(dv)
+        a = np.exp(-RNG.uniform(0, 0.5, size=dk)); beta = float(1 / (1 + np.exp(-RNG.standard_normal())))
+        S1, o = orc.delta_head_vec(S, k, v, k, a, beta)
+        kk = float(k @ k)
+        Sd = S * a[:, None]
+        np.testing.assert_allclose(S1.T @ k, (1 - beta * kk) * (Sd.T @ k) + beta * kk * v, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(o, S1.T @ k, rtol=1e-12, atol=1e-12)
+
+
+def test_per_key_run_with_constant_rows_equals_scalar_run():
+    base = gi.custom("pk_eq", d_model=64, n_k_heads=2, d_k=16, n_v_heads=4, d_v=16, n_layers=2, n_tokens=3,
+                     flags=gi.DN_X_RMSNORM, ring_std=1.0)
+    layers, stream = gi.generate(base)
+    out1, S1, H1 = orc.run(base, layers, stream)
+    pk = base.replace(flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
+    a = np.ascontiguousarray(np.repeat(stream.alpha[..., None], base.d_k, axis=-1))
+    out2, S2, H2 = orc.run(pk, layers, gi.Stream(stream.x, a, stream.beta))
+    assert np.array_equal(out1, out2) and np.array_equal(S1, S2) and np.array_equal(H1, H2)
+
+
+def test_per_key_run_decay_only_closed_form():
+    """beta = 0 at every token: each key row of every (layer, sequence, head) state is multiplied by
+    the product over tokens of its own alpha, so any slip in the [T][L][B][Hv][dk] indexing shows."""
+    cfg = gi.custom("pk_idx", d_model=64, n_k_heads=2, d_k=16, n_v_heads=4, d_v=8, n_layers=2, batch=3,
+                    n_tokens=3, flags=gi.DN_ALPHA_PER_KEY, ring_std=1.0)
+    layers, stream = gi.generate(cfg)
+    a = np.exp(-RNG.uniform(0.0, 1.0, size=stream.alpha.shape)).astype(np.float32)
+    zero = np.zeros_like(stream.beta)
+    S0, H0 = orc.initial_state(layers)
+    _, S, _ = orc.run(cfg, layers, gi.Stream(stream.x, a, zero), S=S0, hist=H0)
+    want = S0 * np.prod(a.astype(np.float64), axis=0)[..., None]
+    np.testing.assert_allclose(S, want, rtol=1e-14, atol=0)
