@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("DN_LIB") or os.path.join(_PKG, "libdn.so")
 
 DN_OK, DN_E_INVAL, DN_E_NOMEM, DN_E_DEVICE, DN_E_DISABLED, DN_E_FAULT = 0, -1, -2, -3, -4, -5
 DN_X_RMSNORM = 1
+DN_ALPHA_PER_KEY = 2  # alpha [L][B][Hv][dk]: one decay per key channel
 EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy")
 
 _ERR = {DN_OK: "ok", DN_E_INVAL: "invalid argument", DN_E_NOMEM: "out of device memory",

@@ -74,7 +74,7 @@ int validate(const dn_config* c) {
   if (c->conv_k < 1 || c->conv_k > 4) return DN_E_INVAL;
   if (c->batch < 1 || c->batch > 1024) return DN_E_INVAL;
   if (c->n_layers < 1 || c->n_layers > 256) return DN_E_INVAL;
-  if (c->flags & ~DN_X_RMSNORM) return DN_E_INVAL;
+  if (c->flags & ~(DN_X_RMSNORM | DN_ALPHA_PER_KEY)) return DN_E_INVAL;
   if (!(c->eps_l2 >= 0.f) || !(c->eps_rms >= 0.f)) return DN_E_INVAL;
   return DN_OK;
 }
@@ -158,7 +158,8 @@ int setup_persist(dn_layer* h) {
   ps.batch = c.batch; ps.D = c.d_model; ps.V = h->V; ps.R = h->R; ps.dk = c.d_k; ps.dv = c.d_v;
   ps.Hv = c.n_v_heads; ps.K = c.conv_k; ps.bits = c.weight_bits;
   const char* force = std::getenv("DN_LAYER_KERNELS");
-  if ((force && std::atoi(force) != 0) || !dn::persist_supported(ps, h->nwg)) return DN_OK;
+  if ((force && std::atoi(force) != 0) || (c.flags & DN_ALPHA_PER_KEY) || !dn::persist_supported(ps, h->nwg))
+    return DN_OK;
   int per_cu = 0;
   if (dn::persist_occupancy(ps, &per_cu) != hipSuccess || per_cu < 1) return DN_OK;
   const size_t L = c.n_layers;
@@ -361,6 +362,8 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
     return DN_OK;
   }
+  const int pk = (c.flags & DN_ALPHA_PER_KEY) ? 1 : 0;
+  const size_t a_layer = B * c.n_v_heads * (pk ? (size_t)c.d_k : 1);  // alpha elements per layer
   if (h->batched) {
     const int QK = c.n_k_heads * c.d_k;
     for (size_t l = 0; l < L; ++l) {
@@ -371,7 +374,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
         return fail(h, rc);
       dn::BStateArgs bs{};
       bs.u = h->u; bs.S = h->S + l * h->s_elems;
-      bs.alpha = alpha + l * B * c.n_v_heads; bs.beta = beta + l * B * c.n_v_heads;
+      bs.alpha = alpha + l * a_layer; bs.beta = beta + l * B * c.n_v_heads; bs.alpha_per_key = pk;
       bs.norm_w = w.norm_w; bs.xs = h->xs; bs.sc = h->sc;
       bs.B = (int)B; bs.Hk = c.n_k_heads; bs.Hv = c.n_v_heads; bs.R = h->R; bs.C = h->C; bs.QK = QK; bs.V = h->V;
       bs.eps_l2 = c.eps_l2; bs.eps_rms = c.eps_rms; bs.q_scale = c.q_scale;
@@ -399,7 +402,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
 
     dn::HeadArgs ha{};
     ha.u = h->u; ha.S = h->S + l * h->s_elems;
-    ha.alpha = alpha + l * B * c.n_v_heads; ha.beta = beta + l * B * c.n_v_heads;
+    ha.alpha = alpha + l * a_layer; ha.beta = beta + l * B * c.n_v_heads; ha.alpha_per_key = pk;
     ha.norm_w = w.norm_w; ha.y = h->y;
     ha.Hk = c.n_k_heads; ha.Hv = c.n_v_heads; ha.dk = c.d_k; ha.dv = c.d_v;
     ha.R = h->R; ha.C = h->C; ha.batch = (int)B;

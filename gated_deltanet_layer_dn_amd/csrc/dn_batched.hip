@@ -385,10 +385,11 @@ __global__ __launch_bounds__(256) void k_bepi(const BEpiArgs a) {
   a.out[(size_t)b * a.out_stride + r] = o;
 }
 
-// One (value head, sequence) per workgroup; 128 x 128 state tile.
+// One (value head, sequence) per workgroup; 128 x 128 state tile. PK: one decay per key row.
+template <bool PK>
 __global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
   constexpr int DK = 128, DV = 128;
-  __shared__ float qs[DK], kks[DK], dl[DV];
+  __shared__ float qs[DK], kks[DK], dl[DV], als[PK ? DK : 1];
   __shared__ float red[8][DV];
   __shared__ double dred[4][2];
   __shared__ float fred[2];
@@ -413,6 +414,7 @@ __global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
     sk = (double)k * k;
     vv = ub[2 * a.QK + h * DV + tid];
     zz = ub[a.C + h * DV + tid];
+    if constexpr (PK) als[tid] = a.alpha[((size_t)b * a.Hv + h) * DK + tid];
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -427,16 +429,17 @@ __global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
   // L2 norms in double, eps inside the sqrt (waves 0 and 1 hold the 128 rows)
   const float qn = (float)((double)a.q_scale / sqrt((dred[0][0] + dred[1][0]) + (double)a.eps_l2));
   const float kn = (float)(1.0 / sqrt((dred[0][1] + dred[1][1]) + (double)a.eps_l2));
-  const float alpha = a.alpha[(size_t)b * a.Hv + h], beta = a.beta[(size_t)b * a.Hv + h];
+  const float alpha = PK ? 0.f : a.alpha[(size_t)b * a.Hv + h], beta = a.beta[(size_t)b * a.Hv + h];
 
   // decay, then (decayed S)^T k for this thread's 4 columns over its 16 rows
   float kvp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const float kr = kks[16 * rg + r] * kn;
+    const float ar = PK ? als[16 * rg + r] : alpha;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      s[r][j] *= alpha;
+      s[r][j] *= ar;
       kvp[j] = fmaf(s[r][j], kr, kvp[j]);
     }
   }
@@ -587,7 +590,10 @@ hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bstate(const BStateArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_bstate, dim3(a.Hv, a.B), dim3(256), 0, st, a);
+  if (a.alpha_per_key)
+    hipLaunchKernelGGL(k_bstate<true>, dim3(a.Hv, a.B), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_bstate<false>, dim3(a.Hv, a.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

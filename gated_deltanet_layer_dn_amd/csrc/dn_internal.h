@@ -29,11 +29,12 @@ struct GemvArgs {
 struct HeadArgs {
   const float* u;       // [B][R]: post-conv q | k | v, then raw z
   float* S;             // [B][Hv][dk][dv]
-  const float* alpha;   // [B][Hv]
+  const float* alpha;   // [B][Hv], or [B][Hv][dk] with alpha_per_key
   const float* beta;    // [B][Hv]
   const float* norm_w;  // [dv]
   float* y;             // [B][Hv*dv]
   int Hk, Hv, dk, dv, R, C, batch;
+  int alpha_per_key;    // 1: key row i of head h decays by alpha[b][h][i]
   float eps_l2, eps_rms, q_scale;
 };
 
@@ -75,13 +76,14 @@ struct BEpiArgs {
 struct BStateArgs {
   const float* u;        // [B][R]: post-conv q | k | v, then raw z
   float* S;              // [B][Hv][128][128]
-  const float* alpha;    // [B][Hv]
+  const float* alpha;    // [B][Hv], or [B][Hv][128] with alpha_per_key
   const float* beta;     // [B][Hv]
   const float* norm_w;   // [128]
   void* xs;              // out: the gated readout split for out_proj (BSplitArgs::xs layout, K = V)
   float* sc;             // out: its scales
   int B, Hk, Hv, R, C, QK, V;
   float eps_l2, eps_rms, q_scale;
+  int alpha_per_key;     // 1: key row i of head h decays by alpha[b][h][i]
 };
 bool bgemm_shape_ok(int M, int K, int mf, int kr);
 hipError_t launch_bsplit(const BSplitArgs& a, hipStream_t st);

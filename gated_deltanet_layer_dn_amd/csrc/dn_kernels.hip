@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
 template <int DKMAX>
 __global__ __launch_bounds__(256) void k_head(const HeadArgs a) {
   constexpr int TPR = DKMAX / 4;  // key rows per thread
-  __shared__ float qs[256], ks[256], os[256];
+  __shared__ float qs[256], ks[256], os[256], als[256];
   __shared__ float red[4][64];
   __shared__ double redd[4];
   __shared__ float redf[4];
@@ -243,10 +243,12 @@ __global__ __launch_bounds__(256) void k_head(const HeadArgs a) {
 
   // L2 norms in double, eps inside the sqrt
   double sq = 0.0, sk = 0.0;
+  const float* ah = a.alpha + ((size_t)b * a.Hv + h) * (a.alpha_per_key ? dk : 1);
   for (int i = tid; i < dk; i += 256) {
     const float qv = q[i], kv = k[i];
     qs[i] = qv;
     ks[i] = kv;
+    als[i] = ah[a.alpha_per_key ? i : 0];
     sq += (double)qv * qv;
     sk += (double)kv * kv;
   }
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(256) void k_head(const HeadArgs a) {
   }
   __syncthreads();
 
-  const float alpha = a.alpha[(size_t)b * a.Hv + h], beta = a.beta[(size_t)b * a.Hv + h];
+  const float beta = a.beta[(size_t)b * a.Hv + h];
   float* S = a.S + ((size_t)b * a.Hv + h) * dk * dv;
   for (int j0 = 0; j0 < dv; j0 += 64) {
     const int j = j0 + lane;
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(256) void k_head(const HeadArgs a) {
       const int i = wave + 4 * t;
       s[t] = 0.f;
       if (i < dk && jv) {
-        s[t] = alpha * S[(size_t)i * dv + j];
+        s[t] = als[i] * S[(size_t)i * dv + j];
         kvp = fmaf(s[t], ks[i], kvp);
       }
     }

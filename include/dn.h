@@ -45,6 +45,13 @@ extern "C" {
 
 /* dn_config.flags */
 #define DN_X_RMSNORM 1u   /* RMS-normalise each layer's input, x / sqrt(mean(x^2) + eps_rms) (stack pre-norm) */
+/* One decay per key channel instead of one per head: key row i of value head h's state is
+ * multiplied by alpha[l][b][h][i] before the delta step. This is the gate of the other engines'
+ * linear-attention layers, which run the same gated delta step with other dimensions and gates
+ * (page "qwen36: run the DeltaNet layer end to end on the card", section "Where this goes next").
+ * alpha becomes [L][B][Hv][dk]. Single-sequence handles then run the per-layer kernels instead
+ * of the whole-stack kernel. */
+#define DN_ALPHA_PER_KEY 2u
 
 typedef struct dn_layer dn_layer; /* opaque */
 
@@ -58,7 +65,7 @@ typedef struct {
   int batch;        /* B: independent sequences stepped together, 1..1024 */
   int n_layers;     /* L: layers in the stack, 1..256 */
   int weight_bits;  /* 8 (int8) or 4 (packed signed int4) */
-  unsigned flags;   /* DN_X_RMSNORM or 0 */
+  unsigned flags;   /* DN_X_RMSNORM | DN_ALPHA_PER_KEY, or 0 */
   float eps_l2;     /* eps inside the sqrt of the q/k L2 norms (1e-6) */
   float eps_rms;    /* eps of the gated RMSNorm and of the input pre-norm (1e-6) */
   float q_scale;    /* multiplies the readout q^T S (1.0) */
@@ -105,7 +112,8 @@ int dn_get_state(dn_layer *h, float *S, float *ring);
  * out = q^T S over the updated state, gated RMSNorm with silu(z), out_proj GEMV).
  * DEVICE pointers:
  *   x            [B][D]        input of layer 0
- *   alpha, beta  [L][B][Hv]    per-head decay (multiplies S) and delta-rule step size
+ *   alpha, beta  [L][B][Hv]    per-head decay (multiplies S) and delta-rule step size;
+ *                              alpha is [L][B][Hv][dk] with DN_ALPHA_PER_KEY
  *   out          [L][B][D]     out[l] is layer l's output and layer l+1's input;
  *                              out[L-1] is the stack's output. Must not overlap x.
  * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only: returns

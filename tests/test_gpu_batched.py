@@ -31,6 +31,9 @@ BATCHED = {
     # three pre-normed layers, each output feeding the next layer
     "b_stack": gi.custom("b_stack", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=6,
                          n_layers=3, n_tokens=5, flags=gi.DN_X_RMSNORM, ring_std=1.0),
+    # one decay per key channel, alpha [B][Hv][128]
+    "b_perkey": gi.custom("b_perkey", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=5,
+                          n_tokens=5, flags=gi.DN_ALPHA_PER_KEY, ring_std=1.0),
 }
 
 

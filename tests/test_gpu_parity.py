@@ -42,6 +42,13 @@ SMALL = {
     "maxD": gi.custom("maxD", d_model=16384, n_k_heads=1, d_k=16, n_v_heads=1, d_v=16, n_tokens=3),
     "qscale": gi.custom("qscale", d_model=128, n_k_heads=2, d_k=32, n_v_heads=4, d_v=32, n_tokens=6,
                         q_scale=0.125),
+    # one decay per key channel (alpha [Hv][dk]): a ragged single-sequence shape and a
+    # pre-normed 3-layer stack at the 128-wide head shape
+    "perkey": gi.custom("perkey", d_model=80, n_k_heads=3, d_k=24, n_v_heads=6, d_v=40, conv_k=3,
+                        n_tokens=8, flags=gi.DN_ALPHA_PER_KEY, ring_std=1.0),
+    "perkey_stack": gi.custom("perkey_stack", d_model=512, n_k_heads=2, d_k=128, n_v_heads=4, d_v=128,
+                              n_layers=3, n_tokens=6, flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY,
+                              ring_std=1.0),
 }
 
 
