@@ -35,9 +35,10 @@ struct dn_layer {
   int nwg = 0;
   dn::PersistShape ps{};
   dn::LayerW* d_layers = nullptr;
-  uint64_t* X = nullptr;    // tagged hand-off buffers
+  unsigned* X = nullptr;    // hand-off buffers: layer output and gated readout in self-tagged
+                            // 32-bit words, in_proj output in 64-bit tagged words
   uint64_t* U = nullptr;
-  uint64_t* G = nullptr;
+  unsigned* G = nullptr;
   dn::Ctl* ctl = nullptr;
   float* stage = nullptr;   // canonical-layout staging of the state for set/get
   unsigned* err_host = nullptr;  // pinned host word the whole-stack kernel writes its error flag to
@@ -164,9 +165,9 @@ int setup_persist(dn_layer* h) {
   if (dn::persist_occupancy(ps, &per_cu) != hipSuccess || per_cu < 1) return DN_OK;
   const size_t L = c.n_layers;
   bool ok = hipMalloc(&h->d_layers, sizeof(dn::LayerW) * L) == hipSuccess;
-  ok = ok && hipMalloc(&h->X, sizeof(uint64_t) * 8 * c.d_model) == hipSuccess;
+  ok = ok && hipMalloc(&h->X, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
   ok = ok && hipMalloc(&h->U, sizeof(uint64_t) * h->R) == hipSuccess;
-  ok = ok && hipMalloc(&h->G, sizeof(uint64_t) * 8 * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMalloc(&h->G, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
   ok = ok && hipMalloc(&h->ctl, sizeof(dn::Ctl)) == hipSuccess;
   ok = ok && hipMalloc(&h->stage, sizeof(float) * L * h->s_elems) == hipSuccess;
   ok = ok && hipHostMalloc(&h->err_host, sizeof(unsigned), hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
@@ -181,9 +182,9 @@ int setup_persist(dn_layer* h) {
     lw[l] = dn::LayerW{h->w[l].w_in, h->w[l].s_in, h->w[l].conv_w, h->w[l].norm_w, h->w[l].w_out, h->w[l].s_out};
   const dn::Ctl ctl0{1u, 0u, 0u, 0u};
   ok = hipMemcpy(h->d_layers, lw.data(), sizeof(dn::LayerW) * L, hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemset(h->X, 0, sizeof(uint64_t) * 8 * c.d_model) == hipSuccess;
+  ok = ok && hipMemset(h->X, 0, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
   ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * h->R) == hipSuccess;
-  ok = ok && hipMemset(h->G, 0, sizeof(uint64_t) * 8 * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMemset(h->G, 0, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
   ok = ok && hipMemcpy(h->ctl, &ctl0, sizeof(ctl0), hipMemcpyHostToDevice) == hipSuccess;
   if (!ok) return DN_E_DEVICE;
   *h->err_host = 0;

@@ -121,11 +121,11 @@ struct PersistArgs {
   const float* alpha;    // [L][Hv]
   const float* beta;     // [L][Hv]
   float* out;            // [L][D]
-  uint64_t* X;           // [8][D]  tagged layer output, one copy per XCD
+  unsigned* X;           // [8][D]  layer output, self-tagged 32-bit words, one copy per XCD
   uint64_t* U;           // [R]  tagged in_proj output (post-conv q|k|v, raw z)
-  uint64_t* G;           // [8][V + 256] tagged gated readout and partial sums of squares of the
-                         // readout, in four segments [V/4 columns | partials of those heads | pad],
-                         // one copy per XCD
+  unsigned* G;           // [8][V + 256] gated readout and partial sums of squares of the readout,
+                         // self-tagged 32-bit words, in four segments [V/4 columns | partials of
+                         // those heads], one copy per XCD
   Ctl* ctl;
   unsigned* err_host;          // host-mapped pinned word: the launch's error flag, written by the last workgroup
   unsigned long long* timers;  // instrumented builds only: [NWG][L][32] phase timestamps

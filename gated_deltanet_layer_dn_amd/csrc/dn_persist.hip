@@ -17,10 +17,13 @@
 //    j, key rows 32p..32p+31), prefetched one layer ahead, and performs decay, delta rule, readout
 //    and the gate for those columns; sums over the key rows are in-lane plus two DPP steps.
 //  * Phase C (gated RMSNorm finish + out_proj): each workgroup owns D/NWG out_proj rows.
-// Hand-offs between workgroups carry no fences: every cross-workgroup value travels as a 64-bit
-// word (fp32 value, 32-bit tag) stored and loaded with device-coherent (sc1) accesses; a reader
-// spins until each word carries the tag of the current layer and token. Tags grow by one per
-// layer and never repeat within 2^32 layer steps, so buffers need no reset.
+// Hand-offs between workgroups carry no fences: every cross-workgroup value travels in a tagged
+// word stored and loaded with device-coherent (sc1) accesses, and a reader spins until each word
+// carries the tag of the current layer and token. The in_proj output, which each reader gathers
+// only in part, uses 64-bit words (fp32 value, 32-bit tag); the layer output and the gated readout,
+// which every workgroup reads whole, use 32-bit words whose two low mantissa bits hold the tag mod
+// 4, read four at a time. Tags grow by one per layer and never repeat within 2^32 layer steps, so
+// buffers need no reset.
 // Compute waves never poll, so their outstanding weight prefetches never delay a hand-off (a
 // wave's loads complete in order); the communication waves poll, stage activations into LDS, and
 // run phase B. The next layer's in_proj rows are requested only after phase B's inputs arrived.
@@ -38,6 +41,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int NCW = 8;                 // compute waves per workgroup
 constexpr int NCM = 4;                 // communication waves per workgroup
@@ -53,6 +57,7 @@ constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
 #define DN_PREFETCH_INFLIGHT 2
 #endif
 static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
+
 // s_waitcnt with vmcnt <= n and the other counters unconstrained
 #define DN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
@@ -94,6 +99,27 @@ __device__ __forceinline__ unsigned coherent_load_u32(const unsigned* p) {
 __device__ __forceinline__ void coherent_store_u32(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Self-tagged 32-bit hand-off words: the fp32 value rounded to nearest at 21 mantissa bits (relative
+// change at most 2^-22), its two lowest bits replaced by the layer tag mod 4. Every reader of these
+// buffers reads every word each layer, and no producer runs more than one layer ahead of a reader,
+// so a word holds either the previous layer's tag or the current one: two bits tell them apart.
+// Tearing between the words of a 16-byte load is harmless since each word carries its own tag.
+__device__ __forceinline__ unsigned st_pack(float v, unsigned tag) {
+  return ((__float_as_uint(v) + 2u) & ~3u) | (tag & 3u);
+}
+__device__ __forceinline__ float st_value(unsigned w) { return __uint_as_float(w & ~3u); }
+__device__ __forceinline__ void st_store(unsigned* p, float v, unsigned tag) {
+  __hip_atomic_store(p, st_pack(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool st_tagged(const v4u& q, unsigned t) {
+  return ((q[0] & 3u) == t) & ((q[1] & 3u) == t) & ((q[2] & 3u) == t) & ((q[3] & 3u) == t);
+}
+// Buffer resource over `bytes` bytes at p (raw, untyped 32-bit accesses).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;  // cache policy of a device-coherent load
 
 template <typename T>
 __device__ __forceinline__ T wsum(T v) {
@@ -273,42 +299,11 @@ __device__ __forceinline__ float reduce_rows(int (&acc)[RB][3], float s1, int la
   return mine;
 }
 
-// Poll N tagged words per lane, word i at base + i * STRIDE, until every one carries `want`;
-// values go to v[]. Returns false if the spin cap is hit or another workgroup reported an error.
-// The base pointer is laundered through an empty asm statement each round so that the compiler
-// rebuilds the addresses from one register pair with immediate offsets instead of keeping N
-// 64-bit addresses alive across the loop.
-template <int N, int STRIDE>
-__device__ __forceinline__ bool poll_words(const uint64_t* base, unsigned want, float (&v)[N], unsigned nvalid,
-                                           const unsigned* err, unsigned* rounds = nullptr,
-                                           unsigned long long* round_ts = nullptr) {
-  static_assert(N <= 32, "at most 32 words per lane per poll");
-  unsigned pend = N == 32 ? 0xFFFFFFFFu : ((1u << N) - 1u);
-  pend &= nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
-  unsigned it = 0;
-  while (__any(pend != 0)) {
-    const uint64_t* b = base;
-    asm volatile("" : "+v"(b));
-    uint64_t w[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      if ((pend >> i) & 1) w[i] = ll_load(b + i * STRIDE);
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      if (((pend >> i) & 1) && (unsigned)(w[i] >> 32) == want) {
-        v[i] = __uint_as_float((unsigned)w[i]);
-        pend &= ~(1u << i);
-      }
-#ifdef DN_PHASE_TIMERS
-    if (round_ts && it < 4 && (threadIdx.x & 63) == 0) round_ts[it] = wall_clock64();
-#endif
-    if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
-  }
-  if (rounds) *rounds = it;
-  return true;
-}
-
-// As poll_words, with word i at base + off[i] (element offsets).
+// Poll N 64-bit tagged words per lane, word i at base + off[i] (element offsets), until every one
+// carries `want`; values go to v[]. Returns false if the spin cap is hit or another workgroup
+// reported an error. The base pointer is laundered through an empty asm statement each round so
+// that the compiler rebuilds the addresses from one register pair with immediate offsets instead
+// of keeping N 64-bit addresses alive across the loop.
 template <int N>
 __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&off)[N], unsigned want, float (&v)[N],
                                               unsigned nvalid, const unsigned* err, unsigned* rounds = nullptr,
@@ -335,6 +330,32 @@ __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&
     if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
   }
   if (rounds) *rounds = it;
+  return true;
+}
+
+// Poll NQ 16-byte quads of self-tagged words per lane, quad i at byte offset boff + i * QSTRIDE of
+// the buffer, with device-coherent loads until every word carries `want` mod 4; quads i >= nvalid
+// are not polled. When ONE is set, the single word at byte offset boff1 is polled as well. Returns
+// false if the spin cap is hit or another workgroup reported an error.
+template <int NQ, int QSTRIDE, bool ONE>
+__device__ __forceinline__ bool poll_quads(__amdgpu_buffer_rsrc_t rs, int boff, int boff1, unsigned want, v4u (&q)[NQ],
+                                           unsigned& w1, const unsigned* err) {
+  const unsigned t = want & 3u;
+  unsigned pend = (1u << NQ) - 1u;
+  bool pend1 = ONE;
+  unsigned it = 0;
+  while (__any((pend != 0) | pend1)) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+      if ((pend >> i) & 1)
+        q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, boff + i * QSTRIDE, 0, CPOL_SC1);
+    if (ONE && pend1) w1 = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1, 0, CPOL_SC1);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+      if (((pend >> i) & 1) && st_tagged(q[i], t)) pend &= ~(1u << i);
+    if (ONE && pend1 && (w1 & 3u) == t) pend1 = false;
+    if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
+  }
   return true;
 }
 
@@ -545,7 +566,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
         for (int i = 0; i < RC; ++i) {
           const float oi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o), i));
           const int ri = g.c_row0 + i;
-          if (lane < NREP && ri < g.c_row_end) ll_store(a.X + (size_t)lane * D + ri, oi, tag);
+          if (lane < NREP && ri < g.c_row_end) st_store(a.X + (size_t)lane * D + ri, oi, tag);
         }
       }
       if (lane == 0) bump_counter(&sm.c_done);
@@ -577,7 +598,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
   constexpr int GW = V / (64 * NCM);  // gated readout words per lane
   constexpr int nblk = DV / CB;
   constexpr int GSEG = V / NCM + 64;  // words per communication wave segment of the G buffer
-  static_assert(XW <= 32 && GW < 32, "");
+  constexpr int XQ = XW / 4, GQ = GW / 4;  // 16-byte quads per lane
+  static_assert(XW % 4 == 0 && GW % 4 == 0 && XQ <= 4 && GQ <= 4, "");
   const int C = a.C, QK = a.QK, Hv = a.Hv;
   const int npart = Hv * nblk;
   const unsigned* err = &a.ctl->error;
@@ -593,6 +615,9 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
     }
   };
   const int rep = xcd_id();
+  // this XCD's copies of the broadcast buffers
+  const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(a.X + (size_t)rep * D, 4u * D);
+  const __amdgpu_buffer_rsrc_t grs = buf_rsrc(a.G + (size_t)rep * (NCM * GSEG), 4u * NCM * GSEG);
   const bool runs_b = cw == 0 && g.has_b;
   if (runs_b) {
     // the per-layer gates and norm weights this workgroup needs, fetched once per launch
@@ -605,30 +630,38 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
 
   for (int l = 0; l < a.L; ++l) {
     const unsigned tag = base_tag + (unsigned)l;
-    // Buffer bases laundered once per layer: addresses derived from them are recomputed in the
-    // loop (a few scalar and vector adds) instead of being held across it, which would spill.
-    uint64_t *Ub = a.U, *Xb = a.X, *Gb = a.G;
-    asm volatile("" : "+s"(Ub), "+s"(Xb), "+s"(Gb));
-    // stage x: this wave polls a quarter of the columns, once this workgroup's phase C of the
-    // previous layer is done
+    // Buffer base laundered once per layer: addresses derived from it are recomputed in the loop
+    // (a few scalar and vector adds) instead of being held across it, which would spill.
+    uint64_t* Ub = a.U;
+    asm volatile("" : "+s"(Ub));
+    // stage x: this wave polls a quarter of the columns (quad h of lane: columns
+    // col0 + 256 h .. +3), once this workgroup's phase C of the previous layer is done
     if (cw == 0) DN_MARK(a, l, 0);
     {
       float xv[XW];
-      const int col0 = cw * (D / NCM) + lane;
+      const int col0 = cw * (D / NCM) + 4 * lane;
       bool ok = true;
       if (l == 0) {
 #pragma unroll
-        for (int i = 0; i < XW; ++i) xv[i] = a.x[col0 + 64 * i];
+        for (int h = 0; h < XQ; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[4 * h + e] = a.x[col0 + 256 * h + e];
       } else {
         wait_counter(&sm.c_done, NCW * l, &sm.abort_flag);
-        unsigned rounds = 0;
-        ok = poll_words<XW, 64>(Xb + rep * D + col0, tag - 1, xv, XW, err, &rounds, cw == 0 ? DN_TS(a, l, 16) : nullptr);
-
+        v4u q[XQ];
+        unsigned w1 = 0;
+        ok = poll_quads<XQ, 1024, false>(xrs, 4 * col0, 0, tag - 1, q, w1, err);
+#pragma unroll
+        for (int h = 0; h < XQ; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[4 * h + e] = st_value(q[h][e]);
       }
       float ss = 0.f, mx = 0.f;
 #pragma unroll
+      for (int h = 0; h < XQ; ++h)
+        *reinterpret_cast<v4f*>(sm.raw + col0 + 256 * h) = v4f{xv[4 * h], xv[4 * h + 1], xv[4 * h + 2], xv[4 * h + 3]};
+#pragma unroll
       for (int i = 0; i < XW; ++i) {
-        sm.raw[col0 + 64 * i] = xv[i];
         ss = fmaf(xv[i], xv[i], ss);
         mx = fmaxf(mx, fabsf(xv[i]));
       }
@@ -717,10 +750,10 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
         {
           const size_t off = (size_t)gw * GSEG + (gc - gw * (V / NCM));
           const int r0 = 2 * pr;
-          ll_store(Gb + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
-          ll_store(Gb + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
+          st_store(a.G + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
+          st_store(a.G + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
           if (lane < NREP)
-            ll_store(Gb + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
+            st_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
         }
         DN_MARK(a, l, 5);
       }
@@ -737,13 +770,23 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
       // heads, which follow them in this wave's segment of the buffer
       wait_counter(&sm.b_done, l + 1, &sm.abort_flag);
       float gv[GW + 1];
-#pragma unroll
-      for (int i = 0; i <= GW; ++i) gv[i] = 0.f;
       const int pn = npart / NCM, pbase = cw * pn;
       if (cw == 0) DN_MARK(a, l, 12);
-      unsigned rounds = 0;
-      ok = poll_words<GW + 1, 64>(Gb + rep * (NCM * GSEG) + cw * GSEG + lane, tag, gv, lane < pn ? GW + 1 : GW, err,
-                                  &rounds, cw == 0 ? DN_TS(a, l, 24) : nullptr);
+      {
+        // quad h of lane: columns cw V/4 + 256 h + 4 lane .. +3; then the partial of lane (< pn)
+        v4u q[GQ];
+        unsigned w1 = 0;
+        const int w0 = cw * GSEG + 4 * lane;
+        if (lane < pn)
+          ok = poll_quads<GQ, 1024, true>(grs, 4 * w0, 4 * (cw * GSEG + V / NCM + lane), tag, q, w1, err);
+        else
+          ok = poll_quads<GQ, 1024, false>(grs, 4 * w0, 0, tag, q, w1, err);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gv[4 * h + e] = st_value(q[h][e]);
+        gv[GW] = lane < pn ? st_value(w1) : 0.f;
+      }
       if (cw == 0) DN_MARK(a, l, 6);
       // per-head sums of the partials: head h's nblk partials sit in nblk consecutive lanes
       {
@@ -754,13 +797,14 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
       }
       // y = g / rms(head), staged for phase C, and the sum of this quarter of y
       float sy = 0.f;
-      const int gcol0 = cw * (V / NCM) + lane;
+      const int gcol0 = cw * (V / NCM) + 4 * lane;
 #pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        const int c = gcol0 + 64 * i;
-        const float y = gv[i] * sm.inv[c / DV];
-        sm.yf[c] = y;
-        sy += y;
+      for (int h = 0; h < GQ; ++h) {
+        const int c = gcol0 + 256 * h;  // the four columns of a quad belong to one head
+        const float iv = sm.inv[c / DV];
+        const v4f y = v4f{gv[4 * h], gv[4 * h + 1], gv[4 * h + 2], gv[4 * h + 3]} * iv;
+        *reinterpret_cast<v4f*>(sm.yf + c) = y;
+        sy += (y[0] + y[1]) + (y[2] + y[3]);
       }
       sy = wave_total_f(sy);
       if (lane == 0) sm.stat[9 + cw] = sy;
