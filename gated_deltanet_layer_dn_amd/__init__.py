@@ -19,7 +19,7 @@ LIB_PATH = os.environ.get("DN_LIB") or os.path.join(_PKG, "libdn.so")
 DN_OK, DN_E_INVAL, DN_E_NOMEM, DN_E_DEVICE, DN_E_DISABLED, DN_E_FAULT = 0, -1, -2, -3, -4, -5
 DN_X_RMSNORM = 1
 DN_ALPHA_PER_KEY = 2  # alpha [L][B][Hv][dk]: one decay per key channel
-EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy")
+EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy", "dn_prefill")
 
 _ERR = {DN_OK: "ok", DN_E_INVAL: "invalid argument", DN_E_NOMEM: "out of device memory",
         DN_E_DEVICE: "device error", DN_E_DISABLED: "layer disabled after a failed step",
@@ -62,6 +62,7 @@ def lib():
         L.dn_get_state.argtypes = [P, P, P]; L.dn_get_state.restype = ctypes.c_int
         L.dn_step.argtypes = [P, P, P, P, P, P]; L.dn_step.restype = ctypes.c_int
         L.dn_destroy.argtypes = [P]; L.dn_destroy.restype = None
+        L.dn_prefill.argtypes = [P, P, ctypes.c_int, P, P, P, P]; L.dn_prefill.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -102,6 +103,14 @@ def dn_step(h: int, x, alpha, beta, out, stream=None) -> int:
     s = torch.cuda.current_stream().cuda_stream if stream is None else (
         stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
     return lib().dn_step(h, _ptr(x), _ptr(alpha), _ptr(beta), _ptr(out), s)
+
+
+def dn_prefill(h: int, x, n_tokens: int, alpha, beta, out, stream=None) -> int:
+    """Enqueue a prompt of n_tokens tokens (x [T][D], alpha/beta [T][L][Hv], out [L][T][D]);
+    returns the C return code."""
+    s = torch.cuda.current_stream().cuda_stream if stream is None else (
+        stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return lib().dn_prefill(h, _ptr(x), int(n_tokens), _ptr(alpha), _ptr(beta), _ptr(out), s)
 
 
 def dn_destroy(h: int) -> None:
@@ -172,6 +181,16 @@ class DeltaNetStack:
         rc = dn_step(self.h, x, alpha, beta, out, stream)
         if check:
             _check(rc, "dn_step")
+        return out if check else rc
+
+    def prefill(self, x, alpha, beta, out=None, stream=None, check=True):
+        """Run a prompt through every layer: x [T][D], alpha/beta [T][L][Hv]; returns out [L][T][D]."""
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((self.L, T, self.D), dtype=torch.float32, device=self.device)
+        rc = dn_prefill(self.h, x, T, alpha, beta, out, stream)
+        if check:
+            _check(rc, "dn_prefill")
         return out if check else rc
 
     def close(self):

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dn_kernels.hip", "dn_persist.hip", "dn_batched.hip", "dn_api.cpp"]
+SOURCES = ["dn_kernels.hip", "dn_persist.hip", "dn_batched.hip", "dn_prefill.hip", "dn_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",

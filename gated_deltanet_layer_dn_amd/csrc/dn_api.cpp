@@ -52,6 +52,16 @@ struct dn_layer {
   void* xs = nullptr;                      // activations split into int8 terms, fragment order
   float* sc = nullptr;                     // their per-(sequence, 128-column chunk) scales
   float* ssq = nullptr;                    // per-(sequence, chunk) sums of squares (input pre-norm)
+  // prefill scratch, sized for the longest prompt so far (pf_cap tokens)
+  int pf_cap = 0;
+  void* pf_xs = nullptr;                   // split activations of the prompt
+  float* pf_sc = nullptr;                  // their scales
+  float* pf_ssq = nullptr;                 // their per-chunk sums of squares
+  float* pf_part = nullptr;                // GEMM K-range partial sums [KS][T][M]
+  float* pf_u = nullptr;                   // [T][R] post-conv in_proj output
+  float* pf_cw = nullptr;                  // chunk terms of the recurrence
+  float* pf_o = nullptr;                   // [T][V] readout, then gated output
+  float* pf_ring = nullptr;                // the new conv history of a layer
   bool disabled = false;
   long steps = 0;
   long fault_step = 0;    // 1-based step to fail (0 = never)
@@ -104,6 +114,15 @@ void free_all(dn_layer* h) {
   dfree(h->xs);
   dfree(h->sc);
   dfree(h->ssq);
+  dfree(h->pf_xs);
+  dfree(h->pf_sc);
+  dfree(h->pf_ssq);
+  dfree(h->pf_part);
+  dfree(h->pf_u);
+  dfree(h->pf_cw);
+  dfree(h->pf_o);
+  dfree(h->pf_ring);
+  h->pf_cap = 0;
 }
 
 // GEMM shape for an M x K projection: the all-loads-up-front kernel with 256-column K ranges and
@@ -419,6 +438,107 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     go.conv_w = nullptr; go.ring = nullptr; go.C = 0; go.K = 0;
     if (dn::launch_gemv(go, c.weight_bits, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
+  }
+  return DN_OK;
+}
+
+namespace {
+// K range of a prefill GEMM: the widest of 1024, 512, 256 columns that divides K.
+int pf_kr(int K) { return K % 1024 == 0 ? 1024 : K % 512 == 0 ? 512 : 256; }
+
+// Prefill scratch for prompts of up to T tokens (grown, never shrunk).
+int pf_reserve(dn_layer* h, int T) {
+  if (T <= h->pf_cap) return DN_OK;
+  const dn_config& c = h->cfg;
+  const size_t D = c.d_model, V = h->V, R = h->R;
+  const size_t nb = ((size_t)T + 63) / 64, nch = ((size_t)T + dn::PF_CT - 1) / dn::PF_CT;
+  const size_t ncmax = std::max(D, V) / 128;
+  const size_t part = (size_t)T * std::max((D / pf_kr((int)D)) * R, (V / pf_kr((int)V)) * D);
+  const size_t ring = std::max<size_t>(1, (size_t)(c.conv_k - 1) * h->C);
+  for (void** p : {&h->pf_xs, reinterpret_cast<void**>(&h->pf_sc), reinterpret_cast<void**>(&h->pf_ssq),
+                   reinterpret_cast<void**>(&h->pf_part), reinterpret_cast<void**>(&h->pf_u),
+                   reinterpret_cast<void**>(&h->pf_cw), reinterpret_cast<void**>(&h->pf_o),
+                   reinterpret_cast<void**>(&h->pf_ring)})
+    if (*p) {
+      (void)hipFree(*p);
+      *p = nullptr;
+    }
+  h->pf_cap = 0;
+  bool ok = hipMalloc(&h->pf_xs, nb * ncmax * 24576) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_sc, sizeof(float) * nb * ncmax * 64) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_ssq, sizeof(float) * T * ncmax) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_part, sizeof(float) * part) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_u, sizeof(float) * T * R) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_cw, sizeof(float) * c.n_v_heads * nch * dn::PF_CHUNK_FLOATS) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_o, sizeof(float) * T * V) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_ring, sizeof(float) * ring) == hipSuccess;
+  if (!ok) return DN_E_NOMEM;
+  h->pf_cap = T;
+  return DN_OK;
+}
+}  // namespace
+
+DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* alpha, const float* beta, float* out,
+                      void* hip_stream) {
+  if (!h || !x || !alpha || !beta || !out || n_tokens < 1) return DN_E_INVAL;
+  if (h->disabled) return DN_E_DISABLED;
+  const dn_config& c = h->cfg;
+  const size_t L = c.n_layers, D = c.d_model, T = n_tokens;
+  if (c.batch != 1 || c.d_k != 128 || c.d_v != 128 || (c.flags & DN_ALPHA_PER_KEY) || D % 256 || h->V % 256)
+    return DN_E_INVAL;
+  const char* xb = reinterpret_cast<const char*>(x);
+  const char* ob = reinterpret_cast<const char*>(out);
+  if (ob < xb + sizeof(float) * T * D && xb < ob + sizeof(float) * L * T * D) return DN_E_INVAL;
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, DN_E_DEVICE);
+  if (h->persist && host_err(h)) return fail(h, DN_E_DEVICE);
+  if (int rc = pf_reserve(h, n_tokens); rc != DN_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const int QK = c.n_k_heads * c.d_k, V = h->V, R = h->R, K = c.conv_k;
+  const int nch = (n_tokens + dn::PF_CT - 1) / dn::PF_CT;
+  const int kr_in = pf_kr((int)D), kr_out = pf_kr(V);
+  auto check = [&]() { return !h->sync_debug || hipStreamSynchronize(st) == hipSuccess; };
+  for (size_t l = 0; l < L; ++l) {
+    const dn_weights& w = h->w[l];
+    const float* xl = l == 0 ? x : out + (l - 1) * T * D;
+    // in_proj: split the prompt's inputs, int8 GEMM over the tokens, conv along the tokens
+    dn::BSplitArgs sp{xl, (int)D, (int)D, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
+    if (dn::launch_bsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    dn::BGemmArgs gi{w.w_in, h->pf_xs, h->pf_sc, h->pf_part, R, (int)D, n_tokens, kr_in};
+    if (dn::launch_bgemm(gi, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    dn::PConvArgs pc{};
+    pc.part = h->pf_part; pc.KS = (int)D / kr_in; pc.T = n_tokens; pc.M = R;
+    pc.s = w.s_in; pc.ssq = h->pf_ssq; pc.NC = (int)D / 128; pc.K = (int)D;
+    pc.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; pc.eps = c.eps_rms;
+    pc.conv_w = w.conv_w; pc.ring_in = h->ring + l * h->ring_elems; pc.ring_out = h->pf_ring;
+    pc.C = h->C; pc.Kc = K; pc.out = h->pf_u;
+    if (dn::launch_pconv(pc, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (K > 1 && hipMemcpyAsync(h->ring + l * h->ring_elems, h->pf_ring, sizeof(float) * h->ring_elems,
+                                hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return fail(h, DN_E_DEVICE);
+    if (!check()) return fail(h, DN_E_DEVICE);
+    // recurrence in chunks, then the gated RMSNorm
+    dn::PIntraArgs pi{};
+    pi.u = h->pf_u; pi.T = n_tokens; pi.R = R; pi.QK = QK; pi.Hv = c.n_v_heads; pi.Hk = c.n_k_heads;
+    pi.alpha = alpha + l * c.n_v_heads; pi.beta = beta + l * c.n_v_heads; pi.gstride = (int)L * c.n_v_heads;
+    pi.eps_l2 = c.eps_l2; pi.q_scale = c.q_scale; pi.NCH = nch; pi.cw = h->pf_cw;
+    if (dn::launch_pintra(pi, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    dn::PScanArgs ps{};
+    ps.cw = h->pf_cw; ps.S = h->S + l * h->s_elems; ps.transposed = h->persist ? 1 : 0;
+    ps.T = n_tokens; ps.Hv = c.n_v_heads; ps.NCH = nch; ps.V = V; ps.o = h->pf_o;
+    if (dn::launch_pscan(ps, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    dn::PNormArgs pn{h->pf_o, h->pf_u, w.norm_w, n_tokens, R, h->C, V, c.eps_rms};
+    if (dn::launch_pnorm(pn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (!check()) return fail(h, DN_E_DEVICE);
+    // out_proj
+    dn::BSplitArgs so{h->pf_o, V, V, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
+    if (dn::launch_bsplit(so, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    dn::BGemmArgs go{w.w_out, h->pf_xs, h->pf_sc, h->pf_part, (int)D, V, n_tokens, kr_out};
+    if (dn::launch_bgemm(go, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    dn::BEpiArgs e{};
+    e.part = h->pf_part; e.KS = V / kr_out; e.M = (int)D; e.B = n_tokens; e.s = w.s_out;
+    e.out = out + l * T * D; e.out_stride = (int)D;
+    if (dn::launch_bepi(e, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (!check()) return fail(h, DN_E_DEVICE);
   }
   return DN_OK;
 }

@@ -94,6 +94,56 @@ hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st);
 hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st);
 hipError_t launch_bstate(const BStateArgs& a, hipStream_t st);
 
+// ---- prefill: T tokens of one sequence through a layer, chunkwise (128 x 128 state tiles) ----
+// in_proj epilogue along the tokens: u[t][r] = s[r] * prenorm(t) * sum_ks part[ks][t][r], then for
+// rows r < C the causal conv over the history (ring_in, oldest first) and the previous tokens, SiLU.
+struct PConvArgs {
+  const float* part;     // [KS][T][M]
+  int KS, T, M;
+  const float* s;        // [M]
+  const float* ssq;      // [T][NC] sums of squares of the layer input per 128-column chunk
+  int NC, K, prenorm;    // pre-norm factor 1/sqrt(sum ssq / K + eps)
+  float eps;
+  const float* conv_w;   // [C][Kc]
+  const float* ring_in;  // [Kc-1][C]
+  float* ring_out;       // [Kc-1][C]: the last Kc-1 pre-conv values after token T-1
+  int C, Kc;
+  float* out;            // [T][M]: post-conv q | k | v, raw z
+};
+// Chunk-local terms of the gated delta rule for (value head, chunk of 64 tokens).
+struct PIntraArgs {
+  const float* u;        // [T][R] post-conv q | k | v, raw z
+  int T, R, QK, Hv, Hk;
+  const float* alpha;    // token t, head h at alpha[t * gstride + h]
+  const float* beta;
+  int gstride;
+  float eps_l2, q_scale;
+  int NCH;               // chunks: ceil(T / 64)
+  float* cw;             // per (h, chunk): W, Uv, Qg, Kt [64][128] each, P [64][64], gamma
+};
+// Sequential pass over the chunks for (value head, block of 16 value columns).
+struct PScanArgs {
+  const float* cw;       // PIntraArgs::cw
+  float* S;              // the layer's state: [Hv][128][128] ([dk][dv]), or [Hv][dv][dk] if transposed
+  int transposed;
+  int T, Hv, NCH, V;
+  float* o;              // [T][V] readout
+};
+// Gated RMSNorm per (token, value head): y = w * o / rms(o) * silu(z), in place over o.
+struct PNormArgs {
+  float* o;              // [T][V] readout in, gated output out
+  const float* u;        // [T][R] (z at column C + h * 128)
+  const float* norm_w;   // [128]
+  int T, R, C, V;
+  float eps_rms;
+};
+constexpr int PF_CT = 64;                                   // tokens per chunk
+constexpr size_t PF_CHUNK_FLOATS = 4 * 64 * 128 + 64 * 64 + 4;  // per (head, chunk) in PIntraArgs::cw
+hipError_t launch_pconv(const PConvArgs& a, hipStream_t st);
+hipError_t launch_pintra(const PIntraArgs& a, hipStream_t st);
+hipError_t launch_pscan(const PScanArgs& a, hipStream_t st);
+hipError_t launch_pnorm(const PNormArgs& a, hipStream_t st);
+
 // ---- whole-stack kernel (single sequence, 128 x 128 state tiles) ----
 struct LayerW {
   const void* w_in;

@@ -1,0 +1,383 @@
+// Prefill: a prompt of T tokens of one sequence through a layer, with the recurrence taken in
+// chunks of 64 tokens. The per-token step is the one of page "qwen36: run the DeltaNet layer end to
+// end on the card", section "What the PR does", Backend paragraph (in_proj, conv + SiLU with the
+// history advancing, L2 norms of q and k with eps inside the sqrt, decay, delta rule against the
+// decayed state, readout over the updated state, gated RMSNorm with silu(z), out_proj); the page
+// keeps a prompt (more than one token) on the CPU, and this file is that prompt pass on the card.
+//
+// The projections are the batched path's int8 GEMMs with the tokens as the columns. This file
+// holds the parts that differ from decode:
+//  * k_pconv: the in_proj epilogue, with the causal conv running along the tokens (the history
+//    supplies the values before token 0).
+//  * k_pintra + k_pscan: the gated delta rule over a chunk of tokens j = 0..63 with the state S0
+//    at its start. With g_j the product of the decays up to token j of the chunk, the step's
+//    corrections d_j = beta_j (v_j - (decayed state)^T k_j) satisfy
+//        d_j + sum_{m<j} beta_j (g_j / g_m) (k_j . k_m) d_m = beta_j (v_j - g_j S0^T k_j),
+//    a unit lower-triangular system (I + A) D = diag(beta) (V - diag(g) K S0). With
+//    Tm = (I + A)^-1, W = Tm diag(beta g) K and Uv = Tm diag(beta) V, D = Uv - W S0. The readout
+//    over the updated state is o_j = g_j S0^T q_j + sum_{m<=j} (g_j / g_m) (q_j . k_m) d_m, and the
+//    state after the chunk is g_last S0 + sum_m (g_last / g_m) k_m d_m^T. This is the per-token
+//    step rewritten, not an approximation: it agrees with it up to rounding.
+//    k_pintra computes the parts that do not depend on S0 (Tm, W, Uv, the decayed q and k, the
+//    masked q.k products) for every (head, chunk) in parallel; k_pscan carries the state through
+//    the chunks for one (head, 16 value columns), the columns of S being independent.
+//  * k_pnorm: the gated RMSNorm of every (token, head).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dn_internal.h"
+
+namespace dn {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int DK = 128, DV = 128, CT = PF_CT;
+constexpr int OFF_W = 0, OFF_UV = CT * DK, OFF_QG = 2 * CT * DK, OFF_KT = 3 * CT * DK, OFF_P = 4 * CT * DK,
+              OFF_G = 4 * CT * DK + CT * CT;
+constexpr int TR = 32;  // tokens per thread in k_pconv
+constexpr int LD = DK + 4;  // padded LDS row of 128 floats (keeps 16-byte alignment)
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+__device__ __forceinline__ float prenorm_of(const PConvArgs& a, int t) {
+  if (!a.prenorm) return 1.0f;
+  float ss = 0.f;
+  for (int c = 0; c < a.NC; ++c) ss += a.ssq[(size_t)t * a.NC + c];
+  return rsqrtf(ss / (float)a.K + a.eps);
+}
+
+// One thread per (row, run of TR tokens): pre-conv values from the K-range partial sums in a fixed
+// order, the conv over a window slid along the run, SiLU; the thread whose run ends the prompt
+// writes the new history.
+__global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
+  __shared__ float pn[TR];
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int t0 = blockIdx.y * TR, nt = min(TR, a.T - t0);
+  if ((int)threadIdx.x < nt) pn[threadIdx.x] = prenorm_of(a, t0 + threadIdx.x);
+  __syncthreads();
+  if (r >= a.M) return;
+  const float sr = a.s[r];
+  auto pre = [&](int t, float f) {
+    float sum = 0.f;
+    for (int k = 0; k < a.KS; ++k) sum += a.part[((size_t)k * a.T + t) * a.M + r];
+    return sr * f * sum;
+  };
+  if (r >= a.C) {  // z rows: no conv
+    for (int i = 0; i < nt; ++i) a.out[(size_t)(t0 + i) * a.M + r] = pre(t0 + i, pn[i]);
+    return;
+  }
+  const int K = a.Kc;
+  float w[4], hist[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = j < K ? a.conv_w[(size_t)r * K + j] : 0.f;
+  // hist[j]: pre-conv value of token t0 - (K-1) + j (oldest first); negative tokens from the history
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < K - 1) {
+      const int tok = t0 - (K - 1) + j;
+      hist[j] = tok >= 0 ? pre(tok, prenorm_of(a, tok)) : a.ring_in[(size_t)(tok + K - 1) * a.C + r];
+    }
+  for (int i = 0; i < nt; ++i) {
+    const float u = pre(t0 + i, pn[i]);
+    float acc = w[K - 1] * u;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < K - 1) acc = fmaf(w[j], hist[j], acc);
+    a.out[(size_t)(t0 + i) * a.M + r] = silu(acc);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j + 1 < K - 1) hist[j] = hist[j + 1];
+    if (K > 1) hist[K - 2] = u;
+  }
+  if (t0 + nt == a.T)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < K - 1) a.ring_out[(size_t)j * a.C + r] = hist[j];
+}
+
+// One workgroup per (value head, chunk): the chunk terms that do not depend on the incoming state.
+__global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
+  __shared__ __attribute__((aligned(16))) float sQ[CT][LD], sK[CT][LD], sV[CT][LD];
+  __shared__ float sA[CT][CT + 1], sT[CT][CT + 1];
+  __shared__ float slg[CT], sb[CT], sbg[CT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, c = blockIdx.y;
+  const int g = h / (a.Hv / a.Hk);
+  const int t0 = c * CT, nj = min(CT, a.T - t0);
+  float* out = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
+
+  // q, k (L2-normalised, norms accumulated in double, eps inside the sqrt) and v of the chunk's
+  // tokens; four threads per token, rows of tokens past the prompt are zero
+  {
+    const int j = tid >> 2, p = tid & 3;
+    const bool live = j < nj;
+    const float* ur = a.u + (size_t)(t0 + (live ? j : 0)) * a.R;
+    v4f qv[8], kv[8], vv[8];
+    double sq = 0.0, sk = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 4 * (p + 4 * e);
+      const v4f z4 = {0.f, 0.f, 0.f, 0.f};
+      qv[e] = live ? *reinterpret_cast<const v4f*>(ur + g * DK + col) : z4;
+      kv[e] = live ? *reinterpret_cast<const v4f*>(ur + a.QK + g * DK + col) : z4;
+      vv[e] = live ? *reinterpret_cast<const v4f*>(ur + 2 * a.QK + h * DV + col) : z4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sq += (double)qv[e][q] * qv[e][q];
+        sk += (double)kv[e][q] * kv[e][q];
+      }
+    }
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    sk += __shfl_xor(sk, 1);
+    sk += __shfl_xor(sk, 2);
+    const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
+    const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 4 * (p + 4 * e);
+      *reinterpret_cast<v4f*>(&sQ[j][col]) = qv[e] * qn;
+      *reinterpret_cast<v4f*>(&sK[j][col]) = kv[e] * kn;
+      *reinterpret_cast<v4f*>(&sV[j][col]) = vv[e];
+    }
+  }
+  // gates; slg = running sum of log decay within the chunk (a decay of 0 is clamped to e^-80)
+  if (wave == 0) {
+    const bool live = lane < nj;
+    const size_t gi = (size_t)(t0 + lane) * a.gstride + h;
+    const float al = live ? a.alpha[gi] : 1.0f;
+    const float be = live ? a.beta[gi] : 0.0f;
+    float lg = fmaxf(logf(al), -80.0f);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(lg, o);
+      if (lane >= o) lg += v;
+    }
+    slg[lane] = lg;
+    sb[lane] = be;
+    sbg[lane] = be * expf(lg);
+  }
+  __syncthreads();
+
+  // A = strictly lower part of diag(beta) (g_j/g_m) K K^T; P = lower part (with the diagonal) of
+  // (g_j/g_m) Q K^T. Thread: a 4 x 4 block of (j, m).
+  {
+    const int jb = (tid >> 4) * 4, mb = (tid & 15) * 4;
+    float ga[4][4], qa[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ga[r][s] = qa[r][s] = 0.f;
+    if (mb <= jb + 3) {
+      for (int i = 0; i < DK; i += 4) {
+        v4f kj[4], qj[4], km[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          kj[r] = *reinterpret_cast<const v4f*>(&sK[jb + r][i]);
+          qj[r] = *reinterpret_cast<const v4f*>(&sQ[jb + r][i]);
+          km[r] = *reinterpret_cast<const v4f*>(&sK[mb + r][i]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ga[r][s] = fmaf(kj[r][e], km[s][e], ga[r][s]);
+              qa[r][s] = fmaf(qj[r][e], km[s][e], qa[r][s]);
+            }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int j = jb + r, m = mb + s;
+        const float dec = m <= j ? expf(slg[j] - slg[m]) : 0.f;
+        sA[j][m] = m < j ? sb[j] * dec * ga[r][s] : 0.f;
+        out[OFF_P + j * CT + m] = m <= j ? dec * qa[r][s] : 0.f;
+      }
+  }
+  __syncthreads();
+
+  // Tm = (I + A)^-1 by forward substitution; lane `col` of the first wave solves column col
+  if (wave == 0) {
+    const int col = lane;
+    float tc[CT];
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+      float v = j == col ? 1.0f : 0.0f;
+#pragma unroll
+      for (int m = 0; m < j; ++m) v = fmaf(-sA[j][m], tc[m], v);
+      tc[j] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < CT; ++j) sT[j][col] = tc[j];
+  }
+  __syncthreads();
+
+  // W = Tm diag(beta g) K and Uv = Tm diag(beta) V; thread: rows jb..jb+3, columns ib..ib+7
+  {
+    const int jb = (tid >> 4) * 4, ib = (tid & 15) * 8;
+    v4f w0[4], w1[4], u0[4], u1[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w0[r] = w1[r] = u0[r] = u1[r] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m <= jb + 3; ++m) {
+      const v4f k0 = *reinterpret_cast<const v4f*>(&sK[m][ib]), k1 = *reinterpret_cast<const v4f*>(&sK[m][ib + 4]);
+      const v4f v0 = *reinterpret_cast<const v4f*>(&sV[m][ib]), v1 = *reinterpret_cast<const v4f*>(&sV[m][ib + 4]);
+      const float bg = sbg[m], bb = sb[m];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float tj = sT[jb + r][m];
+        const float tw = tj * bg, tu = tj * bb;
+        w0[r] += tw * k0;
+        w1[r] += tw * k1;
+        u0[r] += tu * v0;
+        u1[r] += tu * v1;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* wr = out + OFF_W + (jb + r) * DK + ib;
+      float* ur = out + OFF_UV + (jb + r) * DV + ib;
+      *reinterpret_cast<v4f*>(wr) = w0[r];
+      *reinterpret_cast<v4f*>(wr + 4) = w1[r];
+      *reinterpret_cast<v4f*>(ur) = u0[r];
+      *reinterpret_cast<v4f*>(ur + 4) = u1[r];
+    }
+  }
+  // decayed q rows, k rows weighted by the decay to the chunk's end, the chunk's total decay
+  {
+    const float lgl = slg[nj - 1];
+    for (int e = tid; e < CT * (DK / 4); e += 256) {
+      const int j = e / (DK / 4), i4 = (e % (DK / 4)) * 4;
+      const v4f q = *reinterpret_cast<const v4f*>(&sQ[j][i4]), k = *reinterpret_cast<const v4f*>(&sK[j][i4]);
+      *reinterpret_cast<v4f*>(out + OFF_QG + j * DK + i4) = q * expf(slg[j]);
+      *reinterpret_cast<v4f*>(out + OFF_KT + j * DK + i4) = j < nj ? k * expf(lgl - slg[j]) : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    if (tid == 0) out[OFF_G] = expf(lgl);
+  }
+}
+
+// One workgroup per (value head, block of 16 value columns): the state block is carried through
+// the chunks in order; each chunk gives D = Uv - W S, the readout Qg S + P D and the next state.
+__global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
+  __shared__ __attribute__((aligned(16))) float sW[CT][LD], sQg[CT][LD], sKt[CT][LD];
+  __shared__ __attribute__((aligned(16))) float sP[CT][CT + 4];
+  __shared__ __attribute__((aligned(16))) float sU[CT][16], sD[CT][16], sS[DK][16];
+  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  float* Sh = a.S + (size_t)h * DK * DV;
+  for (int e = tid; e < DK * 16; e += 256) {
+    if (a.transposed) {
+      const int cc = e / DK, i = e % DK;  // stored [dv][dk]
+      sS[i][cc] = Sh[(size_t)(16 * b + cc) * DK + i];
+    } else {
+      const int i = e / 16, cc = e % 16;
+      sS[i][cc] = Sh[(size_t)i * DV + 16 * b + cc];
+    }
+  }
+  for (int c = 0; c < a.NCH; ++c) {
+    const float* cw = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
+    const int t0 = c * CT, nj = min(CT, a.T - t0);
+    for (int e = tid; e < CT * (DK / 4); e += 256) {
+      const int j = e / (DK / 4), i4 = (e % (DK / 4)) * 4;
+      *reinterpret_cast<v4f*>(&sW[j][i4]) = *reinterpret_cast<const v4f*>(cw + OFF_W + j * DK + i4);
+      *reinterpret_cast<v4f*>(&sQg[j][i4]) = *reinterpret_cast<const v4f*>(cw + OFF_QG + j * DK + i4);
+      *reinterpret_cast<v4f*>(&sKt[j][i4]) = *reinterpret_cast<const v4f*>(cw + OFF_KT + j * DK + i4);
+    }
+    for (int e = tid; e < CT * (CT / 4); e += 256) {
+      const int j = e / (CT / 4), m4 = (e % (CT / 4)) * 4;
+      *reinterpret_cast<v4f*>(&sP[j][m4]) = *reinterpret_cast<const v4f*>(cw + OFF_P + j * CT + m4);
+    }
+    {
+      const int j = tid >> 2, q4 = (tid & 3) * 4;
+      *reinterpret_cast<v4f*>(&sU[j][q4]) = *reinterpret_cast<const v4f*>(cw + OFF_UV + j * DV + 16 * b + q4);
+    }
+    const float gl = cw[OFF_G];
+    __syncthreads();
+    const int j = tid >> 2, c4 = (tid & 3) * 4;
+    {  // D = Uv - W S
+      v4f d = *reinterpret_cast<const v4f*>(&sU[j][c4]);
+      for (int i = 0; i < DK; i += 4) {
+        const v4f w = *reinterpret_cast<const v4f*>(&sW[j][i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d -= w[e] * *reinterpret_cast<const v4f*>(&sS[i + e][c4]);
+      }
+      *reinterpret_cast<v4f*>(&sD[j][c4]) = d;
+    }
+    __syncthreads();
+    {  // readout: Qg S + P D
+      v4f o = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < DK; i += 4) {
+        const v4f q = *reinterpret_cast<const v4f*>(&sQg[j][i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o += q[e] * *reinterpret_cast<const v4f*>(&sS[i + e][c4]);
+      }
+      for (int m = 0; m <= j; ++m) o += sP[j][m] * *reinterpret_cast<const v4f*>(&sD[m][c4]);
+      if (j < nj) *reinterpret_cast<v4f*>(a.o + (size_t)(t0 + j) * a.V + h * DV + 16 * b + c4) = o;
+    }
+    // next state: gl S + Kt^T D; thread: row i, columns c8..c8+7
+    const int i = tid >> 1, c8 = (tid & 1) * 8;
+    v4f s0 = gl * *reinterpret_cast<const v4f*>(&sS[i][c8]), s1 = gl * *reinterpret_cast<const v4f*>(&sS[i][c8 + 4]);
+    for (int m = 0; m < nj; ++m) {
+      const float k = sKt[m][i];
+      s0 += k * *reinterpret_cast<const v4f*>(&sD[m][c8]);
+      s1 += k * *reinterpret_cast<const v4f*>(&sD[m][c8 + 4]);
+    }
+    __syncthreads();  // every read of the old state and of this chunk's terms is done
+    *reinterpret_cast<v4f*>(&sS[i][c8]) = s0;
+    *reinterpret_cast<v4f*>(&sS[i][c8 + 4]) = s1;
+    __syncthreads();
+  }
+  for (int e = tid; e < DK * 16; e += 256) {
+    if (a.transposed) {
+      const int cc = e / DK, ii = e % DK;
+      Sh[(size_t)(16 * b + cc) * DK + ii] = sS[ii][cc];
+    } else {
+      const int ii = e / 16, cc = e % 16;
+      Sh[(size_t)ii * DV + 16 * b + cc] = sS[ii][cc];
+    }
+  }
+}
+
+// Gated RMSNorm of one (token, value head), in place.
+__global__ __launch_bounds__(128) void k_pnorm(const PNormArgs a) {
+  __shared__ float red[2];
+  const int t = blockIdx.x, h = blockIdx.y, j = threadIdx.x;
+  float* op = a.o + (size_t)t * a.V + h * DV + j;
+  const float o = *op;
+  const float z = a.u[(size_t)t * a.R + a.C + h * DV + j];
+  float s = o * o;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if ((j & 63) == 0) red[j >> 6] = s;
+  __syncthreads();
+  const float inv = rsqrtf((red[0] + red[1]) / (float)DV + a.eps_rms);
+  *op = a.norm_w[j] * o * inv * silu(z);
+}
+
+}  // namespace
+
+hipError_t launch_pconv(const PConvArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_pconv, dim3((a.M + 255) / 256, (a.T + TR - 1) / TR), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pintra(const PIntraArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_pintra, dim3(a.Hv, a.NCH), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pscan(const PScanArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_pscan, dim3(a.Hv, DV / 16), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pnorm(const PNormArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_pnorm, dim3(a.T, a.V / DV), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dn

@@ -10,9 +10,11 @@
  * page's object); dn_step then runs one decode token through all of them, the
  * output of layer l feeding layer l+1 on the device.
  *
- * The five entry points mirror the page's five optional backend calls (the
+ * Five entry points mirror the page's five optional backend calls (the
  * "Verified" section counts them): create, set_state, get_state, step, destroy.
- * dn_strerror is static inline, so the library exports exactly these five.
+ * A sixth, dn_prefill, runs a whole prompt through the handle on the card (the page
+ * leaves prompts to the CPU). dn_strerror is static inline, so the library exports
+ * exactly these six.
  *
  * All sizes are element counts. All matrices are row-major and C-contiguous.
  * The library never synchronises the device inside dn_step.
@@ -123,6 +125,29 @@ int dn_get_state(dn_layer *h, float *S, float *ring);
  * token and records an error in host memory at its end; the first dn_step after that
  * launch has completed returns DN_E_DEVICE. */
 int dn_step(dn_layer *h, const float *x, const float *alpha, const float *beta, float *out, void *hip_stream);
+
+/* Prefill: run a prompt of T tokens of ONE sequence through every layer (all T tokens
+ * through layer 0, then layer 1, ...), starting from the state and conv history the
+ * handle holds and leaving them after the last prompt token, so that dn_step continues
+ * the sequence. Each token gets exactly the decode step of dn_step (page "qwen36: run
+ * the DeltaNet layer end to end on the card", section "What the PR does"; the page
+ * keeps prompts on the CPU, this is the same computation on the card): the recurrence
+ * is evaluated in chunks of 64 tokens, which is the per-token step rewritten and
+ * agrees with it up to rounding.
+ * Requires batch == 1, d_k == d_v == 128, a scalar decay (no DN_ALPHA_PER_KEY),
+ * d_model and n_v_heads * d_v multiples of 256.
+ * DEVICE pointers:
+ *   x            [T][D]        the prompt's inputs of layer 0
+ *   alpha, beta  [T][L][Hv]    per token, the gates of dn_step
+ *   out          [L][T][D]     out[l] is layer l's output for every token and layer
+ *                              l+1's input. Must not overlap x.
+ * T = n_tokens >= 1. The handle keeps scratch memory sized for the longest prompt
+ * seen so far (allocated here, freed by dn_destroy).
+ * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only. Returns DN_OK,
+ * DN_E_INVAL (shape or arguments not supported; the handle stays usable), DN_E_NOMEM,
+ * DN_E_DISABLED or DN_E_DEVICE (latches the handle off, as a failed dn_step does). */
+int dn_prefill(dn_layer *h, const float *x, int n_tokens, const float *alpha, const float *beta, float *out,
+               void *hip_stream);
 
 /* Free everything the handle owns (waits for the device first). NULL-safe. */
 void dn_destroy(dn_layer *h);

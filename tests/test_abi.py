@@ -27,8 +27,8 @@ def built():
     return LIB
 
 
-def test_header_declares_the_five_calls():
-    assert _declared() == {"dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy"}
+def test_header_declares_the_six_calls():
+    assert _declared() == {"dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy", "dn_prefill"}
 
 
 def test_library_exports_exactly_the_declared_symbols(built):
