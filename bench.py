@@ -87,7 +87,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="stack", choices=["stack", "stack_int4", "layer", "batched"])
+    ap.add_argument("--config", default="stack", choices=["stack", "stack_int4", "layer", "batched", "prefill"])
+    ap.add_argument("--prompt", type=int, default=2048, help="prompt length of --config prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -116,6 +117,8 @@ def main():
     import dn_inputs as gi
     import gated_deltanet_layer_dn_amd as dn
 
+    if args.config == "prefill":
+        return bench_prefill(args, gi, dn)
     cfg = gi.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
@@ -219,6 +222,81 @@ def main():
         "hbm_gbs": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": f"{props.name} {getattr(props, 'gcnArchName', '')}".strip(),
+    }
+    st.close()
+    print(json.dumps(rec), flush=True)
+
+
+def bench_prefill(args, gi, dn):
+    """Prompt throughput: one step is a prompt of --prompt tokens through the 30-layer stack
+    (dn_prefill), starting from the seeded initial states each time (the reset is outside the
+    timed region). Synthetic inputs of the stack workload's distributions."""
+    import numpy as np
+    import torch
+
+    base = gi.CONFIGS["stack"]
+    T = args.prompt
+    cfg = base.replace(name="prefill", n_tokens=T)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    t0 = time.time()
+    layers, stream = gi.generate(cfg)
+    log(f"[bench] generated prefill workload: L={cfg.n_layers} prompt {T} tokens in {time.time() - t0:.1f}s")
+    st, path = create_reporting_path(dn, cfg, layers)
+    S0d = torch.from_numpy(np.ascontiguousarray(np.stack([l.S0 for l in layers]))).to(dev)
+    R0d = torch.from_numpy(np.ascontiguousarray(np.stack([l.ring0 for l in layers]))).to(dev)
+    x = torch.from_numpy(np.ascontiguousarray(stream.x[:, 0])).to(dev)
+    al = torch.from_numpy(np.ascontiguousarray(stream.alpha[:, :, 0])).to(dev)
+    be = torch.from_numpy(np.ascontiguousarray(stream.beta[:, :, 0])).to(dev)
+    out = torch.empty((cfg.n_layers, T, cfg.d_model), dtype=torch.float32, device=dev)
+    stream_t = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        st.set_state(S0d, R0d)
+        st.prefill(x, al, be, out, stream=stream_t)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        st.set_state(S0d, R0d)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream_t)
+        st.prefill(x, al, be, out, stream=stream_t)
+        e1.record(stream_t)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    assert torch.isfinite(out).all().item(), "non-finite output"
+    ms = float(np.sum(times))
+    per = float(np.mean(times))
+    tok_s = T / (per / 1e3)
+    # algorithmic work of the two projections: 2 flops per weight per token
+    w_per_layer = cfg.d_model * (2 * cfg.qk_dim + 2 * cfg.v_dim) + cfg.v_dim * cfg.d_model
+    proj_flops = 2.0 * w_per_layer * T * cfg.n_layers
+    log(f"[bench] prefill of {T} tokens x {cfg.n_layers} layers: {per:.3f} ms ({tok_s:.0f} prompt tokens/s); "
+        f"projections {proj_flops / (per * 1e-3) / 1e12:.1f} TFLOP/s algorithmic")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        orc.lib()
+        c0 = time.time()
+        orc.run(cfg, layers, stream, n_tokens=1)
+        per_tok = max(time.time() - c0, 1e-3)
+        n = int(max(1, min(T, args.cpu_seconds / per_tok)))
+        c0 = time.time()
+        orc.run(cfg, layers, stream, n_tokens=n)
+        csec = time.time() - c0
+        cpu = {"value": round(n / csec, 3), "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
+               "sample": f"first {n} of {T} prompt tokens of the same workload, token by token (fp64 oracle, "
+                         f"{csec:.1f} s)"}
+    rec = {
+        "metric": "DeltaNet prefill prompt tokens/s (30-layer stack)",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(per, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"prefill: a {T}-token prompt through 30 layers x d_model {cfg.d_model}, "
+                               f"{cfg.n_k_heads}x{cfg.d_k} key / {cfg.n_v_heads}x{cfg.d_v} value heads, 8-bit weights",
+                   "layers": cfg.n_layers, "prompt_tokens": T},
+        "projection_tflops_algorithmic": round(proj_flops / (per * 1e-3) / 1e12, 2),
         "cpu_baseline": cpu,
         "device": f"{props.name} {getattr(props, 'gcnArchName', '')}".strip(),
     }

@@ -262,12 +262,17 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
 }
 
 // One workgroup per (value head, block of 16 value columns): the state block is carried through
-// the chunks in order; each chunk gives D = Uv - W S, the readout Qg S + P D and the next state.
+// the chunks in order; each chunk gives D = Uv - W S, the readout Qg S + P D and the next state
+// g_last S + Kt^T D. The products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane l
+// holds A[l%16][k] and B[k][l%16] with k = l/16, and D[4(l/16)+v][l%16]). The sum index is
+// permuted so that every lane reads contiguous runs: at step s, lane group k = l/16 covers column
+// 32k + s of a 128-long sum and 16k + s of a 64-long one, on both operands. Wave w owns rows
+// 16w..16w+15 of D and of the readout, and rows 32w..32w+31 of the next state; the state block
+// also sits in every wave's registers as the B operand, refreshed through LDS after each chunk.
 __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
-  __shared__ __attribute__((aligned(16))) float sW[CT][LD], sQg[CT][LD], sKt[CT][LD];
-  __shared__ __attribute__((aligned(16))) float sP[CT][CT + 4];
-  __shared__ __attribute__((aligned(16))) float sU[CT][16], sD[CT][16], sS[DK][16];
-  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) float sS[DK][16], sD[CT][16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = blockIdx.x, b = blockIdx.y;
+  const int li = lane & 15, lk = lane >> 4;
   float* Sh = a.S + (size_t)h * DK * DV;
   for (int e = tid; e < DK * 16; e += 256) {
     if (a.transposed) {
@@ -278,58 +283,81 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
       sS[i][cc] = Sh[(size_t)i * DV + 16 * b + cc];
     }
   }
+  __syncthreads();
+  float bS[32];
+#pragma unroll
+  for (int st = 0; st < 32; ++st) bS[st] = sS[32 * lk + st][li];
   for (int c = 0; c < a.NCH; ++c) {
     const float* cw = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
     const int t0 = c * CT, nj = min(CT, a.T - t0);
-    for (int e = tid; e < CT * (DK / 4); e += 256) {
-      const int j = e / (DK / 4), i4 = (e % (DK / 4)) * 4;
-      *reinterpret_cast<v4f*>(&sW[j][i4]) = *reinterpret_cast<const v4f*>(cw + OFF_W + j * DK + i4);
-      *reinterpret_cast<v4f*>(&sQg[j][i4]) = *reinterpret_cast<const v4f*>(cw + OFF_QG + j * DK + i4);
-      *reinterpret_cast<v4f*>(&sKt[j][i4]) = *reinterpret_cast<const v4f*>(cw + OFF_KT + j * DK + i4);
-    }
-    for (int e = tid; e < CT * (CT / 4); e += 256) {
-      const int j = e / (CT / 4), m4 = (e % (CT / 4)) * 4;
-      *reinterpret_cast<v4f*>(&sP[j][m4]) = *reinterpret_cast<const v4f*>(cw + OFF_P + j * CT + m4);
-    }
+    // A operands of this wave: rows 16w + li of W, Qg, P; columns 32w + 16tau + li of Kt^T
+    float aW[32], aQ[32], aP[16], aK[2][16];
     {
-      const int j = tid >> 2, q4 = (tid & 3) * 4;
-      *reinterpret_cast<v4f*>(&sU[j][q4]) = *reinterpret_cast<const v4f*>(cw + OFF_UV + j * DV + 16 * b + q4);
+      const float* wr = cw + OFF_W + (16 * w + li) * DK + 32 * lk;
+      const float* qr = cw + OFF_QG + (16 * w + li) * DK + 32 * lk;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const v4f x = *reinterpret_cast<const v4f*>(wr + 4 * q), y = *reinterpret_cast<const v4f*>(qr + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          aW[4 * q + e] = -x[e];
+          aQ[4 * q + e] = y[e];
+        }
+      }
+      const float* pr = cw + OFF_P + (16 * w + li) * CT + 16 * lk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f x = *reinterpret_cast<const v4f*>(pr + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) aP[4 * q + e] = x[e];
+      }
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int st = 0; st < 16; ++st) aK[tau][st] = cw[OFF_KT + (16 * lk + st) * DK + 32 * w + 16 * tau + li];
     }
     const float gl = cw[OFF_G];
-    __syncthreads();
-    const int j = tid >> 2, c4 = (tid & 3) * 4;
-    {  // D = Uv - W S
-      v4f d = *reinterpret_cast<const v4f*>(&sU[j][c4]);
-      for (int i = 0; i < DK; i += 4) {
-        const v4f w = *reinterpret_cast<const v4f*>(&sW[j][i]);
+    // D = Uv - W S for rows 16w.., started from Uv
+    v4f dacc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d -= w[e] * *reinterpret_cast<const v4f*>(&sS[i + e][c4]);
-      }
-      *reinterpret_cast<v4f*>(&sD[j][c4]) = d;
-    }
-    __syncthreads();
-    {  // readout: Qg S + P D
-      v4f o = {0.f, 0.f, 0.f, 0.f};
-      for (int i = 0; i < DK; i += 4) {
-        const v4f q = *reinterpret_cast<const v4f*>(&sQg[j][i]);
+    for (int v = 0; v < 4; ++v) dacc[v] = cw[OFF_UV + (16 * w + 4 * lk + v) * DV + 16 * b + li];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o += q[e] * *reinterpret_cast<const v4f*>(&sS[i + e][c4]);
-      }
-      for (int m = 0; m <= j; ++m) o += sP[j][m] * *reinterpret_cast<const v4f*>(&sD[m][c4]);
-      if (j < nj) *reinterpret_cast<v4f*>(a.o + (size_t)(t0 + j) * a.V + h * DV + 16 * b + c4) = o;
-    }
-    // next state: gl S + Kt^T D; thread: row i, columns c8..c8+7
-    const int i = tid >> 1, c8 = (tid & 1) * 8;
-    v4f s0 = gl * *reinterpret_cast<const v4f*>(&sS[i][c8]), s1 = gl * *reinterpret_cast<const v4f*>(&sS[i][c8 + 4]);
-    for (int m = 0; m < nj; ++m) {
-      const float k = sKt[m][i];
-      s0 += k * *reinterpret_cast<const v4f*>(&sD[m][c8]);
-      s1 += k * *reinterpret_cast<const v4f*>(&sD[m][c8 + 4]);
-    }
-    __syncthreads();  // every read of the old state and of this chunk's terms is done
-    *reinterpret_cast<v4f*>(&sS[i][c8]) = s0;
-    *reinterpret_cast<v4f*>(&sS[i][c8 + 4]) = s1;
+    for (int st = 0; st < 32; ++st) dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aW[st], bS[st], dacc, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sD[16 * w + 4 * lk + v][li] = dacc[v];
     __syncthreads();
+    float bD[16];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) bD[st] = sD[16 * lk + st][li];
+    // readout Qg S + P D
+    v4f oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 32; ++st) oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aQ[st], bS[st], oacc, 0, 0, 0);
+#pragma unroll
+    for (int st = 0; st < 16; ++st) oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aP[st], bD[st], oacc, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * w + 4 * lk + v;
+      if (j < nj) a.o[(size_t)(t0 + j) * a.V + h * DV + 16 * b + li] = oacc[v];
+    }
+    // next state, rows 32w + 16tau + 4lk + v
+    v4f sacc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sacc[tau][v] = gl * sS[32 * w + 16 * tau + 4 * lk + v][li];
+#pragma unroll
+      for (int st = 0; st < 16; ++st)
+        sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(aK[tau][st], bD[st], sacc[tau], 0, 0, 0);
+    }
+    __syncthreads();  // every read of the old state block and of D is done
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sS[32 * w + 16 * tau + 4 * lk + v][li] = sacc[tau][v];
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 32; ++st) bS[st] = sS[32 * lk + st][li];
   }
   for (int e = tid; e < DK * 16; e += 256) {
     if (a.transposed) {
