@@ -49,8 +49,8 @@ __device__ __forceinline__ float prenorm_of(const PConvArgs& a, int t) {
 }
 
 // One thread per (row, run of TR tokens): pre-conv values from the K-range partial sums in a fixed
-// order, the conv over a window slid along the run, SiLU; the thread whose run ends the prompt
-// writes the new history.
+// order (all of the run's loads issued before any store), the conv over a window slid along the
+// run, SiLU; the thread whose run ends the prompt writes the new history.
 __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
   __shared__ float pn[TR];
   const int r = blockIdx.x * 256 + threadIdx.x;
@@ -59,13 +59,20 @@ __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
   __syncthreads();
   if (r >= a.M) return;
   const float sr = a.s[r];
+  const float* __restrict__ part = a.part;
+  float* __restrict__ out = a.out;
   auto pre = [&](int t, float f) {
     float sum = 0.f;
-    for (int k = 0; k < a.KS; ++k) sum += a.part[((size_t)k * a.T + t) * a.M + r];
+    for (int k = 0; k < a.KS; ++k) sum += part[((size_t)k * a.T + t) * a.M + r];
     return sr * f * sum;
   };
+  float u[TR];
+#pragma unroll
+  for (int i = 0; i < TR; ++i) u[i] = i < nt ? pre(t0 + i, pn[i]) : 0.f;
   if (r >= a.C) {  // z rows: no conv
-    for (int i = 0; i < nt; ++i) a.out[(size_t)(t0 + i) * a.M + r] = pre(t0 + i, pn[i]);
+#pragma unroll
+    for (int i = 0; i < TR; ++i)
+      if (i < nt) out[(size_t)(t0 + i) * a.M + r] = u[i];
     return;
   }
   const int K = a.Kc;
@@ -79,17 +86,19 @@ __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
       const int tok = t0 - (K - 1) + j;
       hist[j] = tok >= 0 ? pre(tok, prenorm_of(a, tok)) : a.ring_in[(size_t)(tok + K - 1) * a.C + r];
     }
-  for (int i = 0; i < nt; ++i) {
-    const float u = pre(t0 + i, pn[i]);
-    float acc = w[K - 1] * u;
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < K - 1) acc = fmaf(w[j], hist[j], acc);
-    a.out[(size_t)(t0 + i) * a.M + r] = silu(acc);
+  for (int i = 0; i < TR; ++i) {
+    if (i < nt) {
+      float acc = w[K - 1] * u[i];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (j + 1 < K - 1) hist[j] = hist[j + 1];
-    if (K > 1) hist[K - 2] = u;
+      for (int j = 0; j < 3; ++j)
+        if (j < K - 1) acc = fmaf(w[j], hist[j], acc);
+      out[(size_t)(t0 + i) * a.M + r] = silu(acc);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (j + 1 < K - 1) hist[j] = hist[j + 1];
+      if (K > 1) hist[K - 2] = u[i];
+    }
   }
   if (t0 + nt == a.T)
 #pragma unroll
@@ -98,11 +107,15 @@ __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
 }
 
 // One workgroup per (value head, chunk): the chunk terms that do not depend on the incoming state.
+// The 64 x 64 and 64 x 128 products run on the fp32 matrix cores (lane layout and permuted sum
+// index as in k_pscan); the unit lower-triangular solve runs in the first wave (lane = column)
+// while the other three form the masked q.k products.
 __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
   __shared__ __attribute__((aligned(16))) float sQ[CT][LD], sK[CT][LD], sV[CT][LD];
-  __shared__ float sA[CT][CT + 1], sT[CT][CT + 1];
+  __shared__ float sA[CT][CT + 1];  // A, then Tm = (I + A)^-1 in place
   __shared__ float slg[CT], sb[CT], sbg[CT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
   const int h = blockIdx.x, c = blockIdx.y;
   const int g = h / (a.Hv / a.Hk);
   const int t0 = c * CT, nj = min(CT, a.T - t0);
@@ -161,93 +174,6 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
   }
   __syncthreads();
 
-  // A = strictly lower part of diag(beta) (g_j/g_m) K K^T; P = lower part (with the diagonal) of
-  // (g_j/g_m) Q K^T. Thread: a 4 x 4 block of (j, m).
-  {
-    const int jb = (tid >> 4) * 4, mb = (tid & 15) * 4;
-    float ga[4][4], qa[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ga[r][s] = qa[r][s] = 0.f;
-    if (mb <= jb + 3) {
-      for (int i = 0; i < DK; i += 4) {
-        v4f kj[4], qj[4], km[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          kj[r] = *reinterpret_cast<const v4f*>(&sK[jb + r][i]);
-          qj[r] = *reinterpret_cast<const v4f*>(&sQ[jb + r][i]);
-          km[r] = *reinterpret_cast<const v4f*>(&sK[mb + r][i]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ga[r][s] = fmaf(kj[r][e], km[s][e], ga[r][s]);
-              qa[r][s] = fmaf(qj[r][e], km[s][e], qa[r][s]);
-            }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int j = jb + r, m = mb + s;
-        const float dec = m <= j ? expf(slg[j] - slg[m]) : 0.f;
-        sA[j][m] = m < j ? sb[j] * dec * ga[r][s] : 0.f;
-        out[OFF_P + j * CT + m] = m <= j ? dec * qa[r][s] : 0.f;
-      }
-  }
-  __syncthreads();
-
-  // Tm = (I + A)^-1 by forward substitution; lane `col` of the first wave solves column col
-  if (wave == 0) {
-    const int col = lane;
-    float tc[CT];
-#pragma unroll
-    for (int j = 0; j < CT; ++j) {
-      float v = j == col ? 1.0f : 0.0f;
-#pragma unroll
-      for (int m = 0; m < j; ++m) v = fmaf(-sA[j][m], tc[m], v);
-      tc[j] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < CT; ++j) sT[j][col] = tc[j];
-  }
-  __syncthreads();
-
-  // W = Tm diag(beta g) K and Uv = Tm diag(beta) V; thread: rows jb..jb+3, columns ib..ib+7
-  {
-    const int jb = (tid >> 4) * 4, ib = (tid & 15) * 8;
-    v4f w0[4], w1[4], u0[4], u1[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w0[r] = w1[r] = u0[r] = u1[r] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int m = 0; m <= jb + 3; ++m) {
-      const v4f k0 = *reinterpret_cast<const v4f*>(&sK[m][ib]), k1 = *reinterpret_cast<const v4f*>(&sK[m][ib + 4]);
-      const v4f v0 = *reinterpret_cast<const v4f*>(&sV[m][ib]), v1 = *reinterpret_cast<const v4f*>(&sV[m][ib + 4]);
-      const float bg = sbg[m], bb = sb[m];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float tj = sT[jb + r][m];
-        const float tw = tj * bg, tu = tj * bb;
-        w0[r] += tw * k0;
-        w1[r] += tw * k1;
-        u0[r] += tu * v0;
-        u1[r] += tu * v1;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float* wr = out + OFF_W + (jb + r) * DK + ib;
-      float* ur = out + OFF_UV + (jb + r) * DV + ib;
-      *reinterpret_cast<v4f*>(wr) = w0[r];
-      *reinterpret_cast<v4f*>(wr + 4) = w1[r];
-      *reinterpret_cast<v4f*>(ur) = u0[r];
-      *reinterpret_cast<v4f*>(ur + 4) = u1[r];
-    }
-  }
   // decayed q rows, k rows weighted by the decay to the chunk's end, the chunk's total decay
   {
     const float lgl = slg[nj - 1];
@@ -258,6 +184,81 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
       *reinterpret_cast<v4f*>(out + OFF_KT + j * DK + i4) = j < nj ? k * expf(lgl - slg[j]) : v4f{0.f, 0.f, 0.f, 0.f};
     }
     if (tid == 0) out[OFF_G] = expf(lgl);
+  }
+
+  // 64 x 64 tile (rt, ct) of X K^T for X = sQ or sK (sum over 128 columns, permuted)
+  auto tile_xk = [&](const float (*X)[LD], int rt, int ct) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 32; ++st)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[16 * rt + li][32 * lk + st], sK[16 * ct + li][32 * lk + st], acc,
+                                                 0, 0, 0);
+    return acc;
+  };
+  // A = strictly lower part of diag(beta) (g_j/g_m) K K^T: wave w forms row tile w
+  for (int ct = 0; ct < 4; ++ct) {
+    const v4f gt = ct <= wave ? tile_xk(sK, wave, ct) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * wave + 4 * lk + v, m = 16 * ct + li;
+      sA[j][m] = m < j ? sb[j] * expf(slg[j] - slg[m]) * gt[v] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // Tm = (I + A)^-1 by forward substitution; lane `col` solves column col, then Tm overwrites A
+    const int col = lane;
+    float tc[CT];
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+      float v = j == col ? 1.0f : 0.0f;
+#pragma unroll
+      for (int m = 0; m < j; ++m) v = fmaf(-sA[j][m], tc[m], v);
+      tc[j] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < CT; ++j) sA[j][col] = tc[j];
+  } else {
+    // P = lower part (with the diagonal) of (g_j/g_m) Q K^T; the 10 tiles with ct <= rt over the
+    // three other waves, zeros above
+    for (int t = wave - 1; t < 16; t += 3) {
+      const int rt = t >> 2, ct = t & 3;
+      const v4f qt = ct <= rt ? tile_xk(sQ, rt, ct) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 16 * rt + 4 * lk + v, m = 16 * ct + li;
+        out[OFF_P + j * CT + m] = m <= j ? expf(slg[j] - slg[m]) * qt[v] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // W = Tm diag(beta g) K and Uv = Tm diag(beta) V: wave w forms rows 16w..16w+15, all columns
+  {
+    float aw[16], au[16];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int m = 16 * lk + st;
+      const float tm = sA[16 * wave + li][m];
+      aw[st] = tm * sbg[m];
+      au[st] = tm * sb[m];
+    }
+    for (int ct = 0; ct < 8; ++ct) {
+      v4f wacc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const int m = 16 * lk + st;
+        wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[st], sK[m][16 * ct + li], wacc, 0, 0, 0);
+        uacc = __builtin_amdgcn_mfma_f32_16x16x4f32(au[st], sV[m][16 * ct + li], uacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 16 * wave + 4 * lk + v;
+        out[OFF_W + j * DK + 16 * ct + li] = wacc[v];
+        out[OFF_UV + j * DV + 16 * ct + li] = uacc[v];
+      }
+    }
   }
 }
 
