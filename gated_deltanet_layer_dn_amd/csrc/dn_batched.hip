@@ -354,12 +354,27 @@ __global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
 __global__ __launch_bounds__(256) void k_bepi(const BEpiArgs a) {
   const int r = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   if (r >= a.M) return;
+  // partials are requested sixteen at a time before they are added (in a fixed order)
   float sum = 0.f;
-  for (int k = 0; k < a.KS; ++k) sum += a.part[((size_t)k * a.B + b) * a.M + r];
+  for (int k0 = 0; k0 < a.KS; k0 += 16) {
+    float pv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) pv[k] = k0 + k < a.KS ? a.part[((size_t)(k0 + k) * a.B + b) * a.M + r] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k0 + k < a.KS) sum += pv[k];
+  }
   float scale = a.s[r];
   if (a.prenorm) {
     float ss = 0.f;
-    for (int c = 0; c < a.NC; ++c) ss += a.ssq[(size_t)b * a.NC + c];
+    for (int c0 = 0; c0 < a.NC; c0 += 16) {
+      float sv[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) sv[c] = c0 + c < a.NC ? a.ssq[(size_t)b * a.NC + c0 + c] : 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        if (c0 + c < a.NC) ss += sv[c];
+    }
     scale *= rsqrtf(ss / (float)a.K + a.eps);
   }
   const float u = scale * sum;

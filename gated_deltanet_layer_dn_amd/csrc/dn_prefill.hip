@@ -62,8 +62,14 @@ __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
   const float* __restrict__ part = a.part;
   float* __restrict__ out = a.out;
   auto pre = [&](int t, float f) {
+    float pv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pv[k] = k < a.KS ? part[((size_t)k * a.T + t) * a.M + r] : 0.f;
     float sum = 0.f;
-    for (int k = 0; k < a.KS; ++k) sum += part[((size_t)k * a.T + t) * a.M + r];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < a.KS) sum += pv[k];
+    for (int k = 4; k < a.KS; ++k) sum += part[((size_t)k * a.T + t) * a.M + r];
     return sr * f * sum;
   };
   float u[TR];
