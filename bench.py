@@ -87,7 +87,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="stack", choices=["stack", "stack_int4", "layer", "batched", "prefill"])
+    ap.add_argument("--config", default="stack",
+                    choices=["stack", "stack_int4", "stack_perkey", "layer", "batched", "prefill"])
     ap.add_argument("--prompt", type=int, default=2048, help="prompt length of --config prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -119,7 +120,10 @@ def main():
 
     if args.config == "prefill":
         return bench_prefill(args, gi, dn)
-    cfg = gi.CONFIGS[args.config]
+    if args.config == "stack_perkey":  # the stack workload with one decay per key channel
+        cfg = gi.CONFIGS["stack"].replace(name="stack_perkey", flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
+    else:
+        cfg = gi.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     t0 = time.time()

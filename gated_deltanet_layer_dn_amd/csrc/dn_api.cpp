@@ -177,9 +177,9 @@ int setup_persist(dn_layer* h) {
   dn::PersistShape& ps = h->ps;
   ps.batch = c.batch; ps.D = c.d_model; ps.V = h->V; ps.R = h->R; ps.dk = c.d_k; ps.dv = c.d_v;
   ps.Hv = c.n_v_heads; ps.K = c.conv_k; ps.bits = c.weight_bits;
+  ps.L = c.n_layers; ps.alpha_per_key = (c.flags & DN_ALPHA_PER_KEY) ? 1 : 0;
   const char* force = std::getenv("DN_LAYER_KERNELS");
-  if ((force && std::atoi(force) != 0) || (c.flags & DN_ALPHA_PER_KEY) || !dn::persist_supported(ps, h->nwg))
-    return DN_OK;
+  if ((force && std::atoi(force) != 0) || !dn::persist_supported(ps, h->nwg)) return DN_OK;
   int per_cu = 0;
   if (dn::persist_occupancy(ps, &per_cu) != hipSuccess || per_cu < 1) return DN_OK;
   const size_t L = c.n_layers;
@@ -378,6 +378,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     a.L = (int)L; a.R = h->R; a.C = h->C; a.QK = c.n_k_heads * c.d_k; a.K = c.conv_k;
     a.Hk = c.n_k_heads; a.Hv = c.n_v_heads; a.flags = c.flags;
     a.eps_l2 = c.eps_l2; a.eps_rms = c.eps_rms; a.q_scale = c.q_scale;
+    a.alpha_per_key = (c.flags & DN_ALPHA_PER_KEY) ? 1 : 0;
     if (dn::launch_persist(a, h->ps, h->nwg, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
     return DN_OK;

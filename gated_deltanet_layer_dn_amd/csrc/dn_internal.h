@@ -168,7 +168,7 @@ struct PersistArgs {
   float* S;              // [L][Hv][dv][dk]: each head's state stored transposed
   float* ring;           // [L][K-1][C], oldest first
   const float* x;        // [D]
-  const float* alpha;    // [L][Hv]
+  const float* alpha;    // [L][Hv], or [L][Hv][128] with alpha_per_key
   const float* beta;     // [L][Hv]
   float* out;            // [L][D]
   unsigned* X;           // [8][D]  layer output, self-tagged 32-bit words, one copy per XCD
@@ -182,10 +182,13 @@ struct PersistArgs {
   int L, R, C, QK, K, Hk, Hv;
   unsigned flags;
   float eps_l2, eps_rms, q_scale;
+  int alpha_per_key;     // 1: key row i of head h decays by alpha[l][h][i] (at most PK_MAXL layers)
 };
+constexpr int PK_MAXL = 32;  // layers of a whole-stack launch with one decay per key channel
 
 struct PersistShape {
   int batch, D, V, R, dk, dv, Hv, K, bits;
+  int L, alpha_per_key;
 };
 
 bool persist_supported(const PersistShape& s, int nwg);

@@ -386,8 +386,10 @@ __device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid)
   if (tid == 0) sm.stat[8] = s1;
 }
 
-// Compute waves: phase A and phase C, weights prefetched one layer ahead in registers.
-template <int BITS, int NCHA, int NCHC, int RA, int RC>
+// Compute waves: phase A and phase C, weights prefetched one layer ahead in registers. (PK does
+// not change this role; it keeps one specialisation per kernel instantiation, which the host
+// compiler pass needs when both instantiations of the kernel are referenced.)
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK>
 __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
                                              int tid, int lane) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
@@ -589,9 +591,10 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 // Communication waves: poll and stage x and the gated readout; the first one also runs phase B.
 // Each poll starts only once this workgroup's own share of the data it waits for is done, so
 // that the rounds that are bound to miss are not issued.
-template <int BITS, int NCHA, int NCHC>
-__device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
-                                          int tid, int lane, int cw, int wg) {
+// PK: one decay per key channel; apk [L][128] holds this head's decays (LDS).
+template <int BITS, int NCHA, int NCHC, bool PK>
+__device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const PersistArgs& a, const Geo& g,
+                                          unsigned base_tag, int tid, int lane, int cw, int wg) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
   constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC, DV = 128;
   constexpr int XW = D / (64 * NCM);  // x words per lane
@@ -622,9 +625,12 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
   if (runs_b) {
     // the per-layer gates and norm weights this workgroup needs, fetched once per launch
     for (int l = lane; l < a.L; l += 64) {
-      sm.gate[l][0] = a.alpha[(size_t)l * Hv + g.bh];
+      sm.gate[l][0] = PK ? 0.f : a.alpha[(size_t)l * Hv + g.bh];
       sm.gate[l][1] = a.beta[(size_t)l * Hv + g.bh];
     }
+    if constexpr (PK)
+      for (int e = lane; e < a.L * DK; e += 64)
+        apk[e / DK][e % DK] = a.alpha[((size_t)(e / DK) * Hv + g.bh) * DK + e % DK];
     for (int e = lane; e < a.L * CB; e += 64) sm.nw[e / CB][e % CB] = a.layers[e / CB].norm_w[g.bcb * CB + e % CB];
   }
 
@@ -709,15 +715,18 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
         const float alpha = sm.gate[l][0], beta = sm.gate[l][1];
         const v4f* Q4 = reinterpret_cast<const v4f*>(sm.qk + 32 * pr);
         const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DK + 32 * pr);
+        const v4f* A4 = reinterpret_cast<const v4f*>(&apk[PK ? l : 0][32 * pr]);
         float sv[32];
         float kvp = 0.f;
         wait_counter(&sm.s_ready, NCW * (l + 1), &sm.abort_flag);  // the slice has landed in LDS
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const v4f kk = K4[q], st = sm.sbuf[64 * q + lane];
+          v4f av = {alpha, alpha, alpha, alpha};  // decay of rows 32 pr + 4 q ..
+          if constexpr (PK) av = A4[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sv[4 * q + e] = alpha * st[e];  // decay
+            sv[4 * q + e] = av[e] * st[e];  // decay
             kvp = fmaf(sv[4 * q + e], kk[e] * kn, kvp);
           }
         }
@@ -815,12 +824,13 @@ __device__ __forceinline__ void comm_role(Smem& sm, const PersistArgs& a, const 
   }
 }
 
-template <int BITS, int NCHA, int NCHC, int RA, int RC>
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK>
 __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
   constexpr int D = COLS_PER_CHUNK * NCHA;
   constexpr int nblk = 128 / CB;
   __shared__ Smem sm;
+  __shared__ float apk[PK ? PK_MAXL : 1][DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NWG = gridDim.x, wg = blockIdx.x;
   const unsigned base_tag = coherent_load_u32(&a.ctl->epoch);
@@ -847,8 +857,8 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   __syncthreads();
   // The two roles run separate loops with the same sequence of three workgroup barriers per
   // layer, so each role's registers are its own.
-  if (wave < NCW) compute_role<BITS, NCHA, NCHC, RA, RC>(sm, a, g, base_tag, tid, lane);
-  else comm_role<BITS, NCHA, NCHC>(sm, a, g, base_tag, tid, lane, wave - NCW, wg);
+  if (wave < NCW) compute_role<BITS, NCHA, NCHC, RA, RC, PK>(sm, a, g, base_tag, tid, lane);
+  else comm_role<BITS, NCHA, NCHC, PK>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
 
   // the last workgroup to finish advances the tag base for the next launch
   __syncthreads();
@@ -865,13 +875,17 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
 
 template <int BITS, int NCHA, int NCHC>
 hipError_t go(const PersistArgs& a, int nwg, hipStream_t st) {
-  hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1>), dim3(nwg), dim3(NTHR), 0, st, a);
+  if (a.alpha_per_key)
+    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, true>), dim3(nwg), dim3(NTHR), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, false>), dim3(nwg), dim3(NTHR), 0, st, a);
   return hipGetLastError();
 }
 
 template <int BITS, int NCHA, int NCHC>
-hipError_t occ(int* blocks) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1>, NTHR, 0);
+hipError_t occ(int* blocks, bool pk) {
+  return pk ? hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, true>, NTHR, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false>, NTHR, 0);
 }
 
 }  // namespace
@@ -885,6 +899,7 @@ static int chunks(int cols, int bits) {
 
 bool persist_supported(const PersistShape& s, int nwg) {
   if (s.batch != 1 || s.dk != DK || s.dv != 128 || s.K < 1 || s.K > 4) return false;
+  if (s.alpha_per_key && s.L > PK_MAXL) return false;
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
   const bool inst = s.bits == 8 ? ((na == 2 && nc == 4) || (na == 1 && nc == 1))
                                 : ((na == 1 && nc == 2) || (na == 1 && nc == 1));
@@ -898,8 +913,9 @@ bool persist_supported(const PersistShape& s, int nwg) {
 
 hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu) {
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
-  if (s.bits == 8) return na == 2 ? occ<8, 2, 4>(blocks_per_cu) : occ<8, 1, 1>(blocks_per_cu);
-  return nc == 2 ? occ<4, 1, 2>(blocks_per_cu) : occ<4, 1, 1>(blocks_per_cu);
+  const bool pk = s.alpha_per_key != 0;
+  if (s.bits == 8) return na == 2 ? occ<8, 2, 4>(blocks_per_cu, pk) : occ<8, 1, 1>(blocks_per_cu, pk);
+  return nc == 2 ? occ<4, 1, 2>(blocks_per_cu, pk) : occ<4, 1, 1>(blocks_per_cu, pk);
 }
 
 hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, hipStream_t st) {

@@ -27,6 +27,12 @@ PERSIST = {
                          q_scale=0.0883883),
     "p_full_shape": gi.custom("p_full", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=32, d_v=128,
                               n_layers=2, n_tokens=6, flags=gi.DN_X_RMSNORM, ring_std=1.0),
+    # one decay per key channel (alpha [L][Hv][128]), int8 and int4
+    "p_perkey": gi.custom("p_pk", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, n_layers=3,
+                          n_tokens=7, flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY, ring_std=1.0),
+    "p_perkey_full_int4": gi.custom("p_pk4", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=32, d_v=128,
+                                    n_layers=2, n_tokens=5, weight_bits=4,
+                                    flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY, ring_std=1.0),
 }
 
 
