@@ -6,13 +6,16 @@ numbers and lays them out in memory; it holds none of the layer's arithmetic.
 Layouts (all C-contiguous, little-endian):
 
 * ``w_in``   int8  [R_in][D]      rows ordered q (Hk*dk) | k (Hk*dk) | v (Hv*dv) | z (Hv*dv),
-                                   each block head-major with the head dimension contiguous.
+                                   each block head-major with the head dimension contiguous;
+                                   with DN_GATES_ON_DEVICE two more blocks a (Hv) | b (Hv).
                                    For 4-bit weights: uint8 [R_in][D/2], element 2c in the low
                                    nibble and 2c+1 in the high nibble, 4-bit two's complement.
 * ``s_in``   fp32  [R_in]         one scale per in_proj row.
 * ``conv_w`` fp32  [C][K]         depthwise causal conv taps; tap K-1 multiplies the current token.
 * ``norm_w`` fp32  [dv]           gated RMSNorm weight, shared by all value heads.
 * ``w_out``  int8  [D][Hv*dv]     (or packed uint8 [D][Hv*dv/2]), ``s_out`` fp32 [D].
+* ``a_log``, ``a_bias`` fp32 [Hv] (DN_GATES_ON_DEVICE only): per value head parameters of the
+                                   decay gate.
 * ``S0``     fp32  [B][Hv][dk][dv] initial recurrent state.
 * ``ring0``  fp32  [B][K-1][C]    conv history, oldest token first.
 * stream: ``x`` fp32 [T][B][D] (input of layer 0), ``alpha``/``beta`` fp32 [T][L][B][Hv].
@@ -21,7 +24,11 @@ Distributions follow the workload description of the layer: integer weights
 uniform over the symmetric int8 (or int4) range, per-row scales U[0.005, 0.02],
 x ~ N(0, 1), alpha = exp(-U[0, 0.1]), beta = sigmoid(N(0, 1)), state N(0, 0.02).
 Conv taps U[-0.5, 0.5] and norm weights U[0.5, 1.5] are this module's choice
-(the pages give no values for them).
+(the pages give no values for them). With DN_GATES_ON_DEVICE the gate rows a, b take
+the same integer range with row scales U[0.5, 1.5] / (rms of the integers * sqrt(D)),
+so that a and b are of order one for a unit-rms input; a_log = log U[1, 16] and
+a_bias ~ U[-7, -2]. These are drawn after everything else of the layer, so every other
+array equals that of the same seed without the flag.
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ import numpy as np
 
 DN_X_RMSNORM = 1  # flag bit: RMS-normalise each layer's input (stack pre-norm)
 DN_ALPHA_PER_KEY = 2  # flag bit: one decay per key channel, alpha [T][L][B][Hv][dk]
+DN_GATES_ON_DEVICE = 4  # flag bit: alpha and beta computed from two more in_proj rows per value head
 
 
 @dataclass(frozen=True)
@@ -71,8 +79,12 @@ class Config:
         return 2 * self.qk_dim + self.v_dim
 
     @property
+    def gate_rows(self) -> int:
+        return 2 * self.n_v_heads if self.flags & DN_GATES_ON_DEVICE else 0
+
+    @property
     def in_rows(self) -> int:
-        return self.conv_channels + self.v_dim
+        return self.conv_channels + self.v_dim + self.gate_rows
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -84,7 +96,8 @@ class Config:
             mat = R * D + D * V
         else:
             mat = R * D // 2 + D * V // 2
-        return mat + 4 * (R + D) + 4 * C * K + 4 * self.d_v
+        gates = 8 * self.n_v_heads if self.flags & DN_GATES_ON_DEVICE else 0
+        return mat + 4 * (R + D) + 4 * C * K + 4 * self.d_v + gates
 
     def state_bytes_per_layer(self) -> int:
         return 4 * self.batch * self.n_v_heads * self.d_k * self.d_v
@@ -140,6 +153,8 @@ class Layer:
     ring0: np.ndarray
     w_in_vals: np.ndarray = field(repr=False, default=None)   # int8 values (for 4-bit configs)
     w_out_vals: np.ndarray = field(repr=False, default=None)
+    a_log: np.ndarray = None   # [Hv] (DN_GATES_ON_DEVICE)
+    a_bias: np.ndarray = None  # [Hv] (DN_GATES_ON_DEVICE)
 
 
 @dataclass
@@ -156,7 +171,8 @@ def _ints(rng, shape, bits):
 
 def gen_layer(cfg: Config, seed: int, rng=None) -> tuple[Layer, np.random.Generator]:
     rng = np.random.default_rng(seed) if rng is None else rng
-    D, R, V, C, K = cfg.d_model, cfg.in_rows, cfg.v_dim, cfg.conv_channels, cfg.conv_k
+    D, V, C, K = cfg.d_model, cfg.v_dim, cfg.conv_channels, cfg.conv_k
+    R = C + V  # rows q | k | v | z; gate rows are drawn last
     B, Hv, dk, dv = cfg.batch, cfg.n_v_heads, cfg.d_k, cfg.d_v
     w_in_v = _ints(rng, (R, D), cfg.weight_bits)
     s_in = rng.uniform(0.005, 0.02, size=R).astype(np.float32)
@@ -172,11 +188,20 @@ def gen_layer(cfg: Config, seed: int, rng=None) -> tuple[Layer, np.random.Genera
         ring0 = (rng.standard_normal((B, K - 1, C)) * cfg.ring_std).astype(np.float32)
     else:
         ring0 = np.zeros((B, K - 1, C), np.float32)
+    a_log = a_bias = None
+    if cfg.flags & DN_GATES_ON_DEVICE:
+        hi = 127 if cfg.weight_bits == 8 else 7
+        rms_int = np.sqrt(hi * (hi + 1) / 3.0)
+        G = cfg.gate_rows
+        w_in_v = np.concatenate([w_in_v, _ints(rng, (G, D), cfg.weight_bits)])
+        s_in = np.concatenate([s_in, (rng.uniform(0.5, 1.5, size=G) / (rms_int * np.sqrt(D))).astype(np.float32)])
+        a_log = np.log(rng.uniform(1.0, 16.0, size=Hv)).astype(np.float32)
+        a_bias = rng.uniform(-7.0, -2.0, size=Hv).astype(np.float32)
     if cfg.weight_bits == 8:
-        lay = Layer(w_in_v, s_in, conv_w, norm_w, w_out_v, s_out, S0, ring0, w_in_v, w_out_v)
+        lay = Layer(w_in_v, s_in, conv_w, norm_w, w_out_v, s_out, S0, ring0, w_in_v, w_out_v, a_log, a_bias)
     else:
         lay = Layer(pack_int4(w_in_v), s_in, conv_w, norm_w, pack_int4(w_out_v), s_out, S0, ring0,
-                    w_in_v, w_out_v)
+                    w_in_v, w_out_v, a_log, a_bias)
     return lay, rng
 
 

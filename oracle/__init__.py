@@ -20,6 +20,7 @@ _lock = threading.Lock()
 _lib = None
 
 X_RMSNORM = 1
+GATES_ON_DEVICE = 4
 
 
 def build(force: bool = True) -> str:
@@ -42,7 +43,8 @@ class _Dims(ctypes.Structure):
 
 class _LayerW(ctypes.Structure):
     _fields_ = [("w_in", ctypes.c_void_p), ("s_in", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
-                ("norm_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("s_out", ctypes.c_void_p)]
+                ("norm_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("s_out", ctypes.c_void_p),
+                ("a_log", ctypes.c_void_p), ("a_bias", ctypes.c_void_p)]
 
 
 def lib():
@@ -67,6 +69,8 @@ def lib():
             L.dno_delta_head.argtypes = [I, I, P, P, P, P, Dd, Dd, Dd, P]; L.dno_delta_head.restype = None
             L.dno_delta_head_vec.argtypes = [I, I, P, P, P, P, P, Dd, Dd, P]; L.dno_delta_head_vec.restype = None
             L.dno_gated_rmsnorm.argtypes = [I, P, P, P, Dd, P]; L.dno_gated_rmsnorm.restype = None
+            L.dno_softplus.argtypes = [Dd]; L.dno_softplus.restype = Dd
+            L.dno_gates.argtypes = [Dd, Dd, Dd, Dd, P, P]; L.dno_gates.restype = None
             L.dno_layer_step.argtypes = [P, P, P, P, P, P, P, P]; L.dno_layer_step.restype = I
             L.dno_run.argtypes = [P, P, P, P, I, P, P, P, P]; L.dno_run.restype = I
             L.dno_threads.argtypes = []; L.dno_threads.restype = I
@@ -148,6 +152,17 @@ def delta_head_vec(S, k, v, q, alpha, beta, q_scale=1.0):
     return S, o
 
 
+def softplus(y: float) -> float:
+    return lib().dno_softplus(float(y))
+
+
+def gates(a: float, b: float, a_log: float, a_bias: float):
+    """(alpha, beta) of a value head from its gate rows a, b and parameters a_log, a_bias."""
+    al = ctypes.c_double(); be = ctypes.c_double()
+    lib().dno_gates(float(a), float(b), float(a_log), float(a_bias), ctypes.byref(al), ctypes.byref(be))
+    return al.value, be.value
+
+
 def gated_rmsnorm(o, z, w, eps: float) -> np.ndarray:
     o = _f64(o); z = _f64(z); w = _f32(w); y = np.zeros_like(o)
     lib().dno_gated_rmsnorm(o.size, _p(o), _p(z), _p(w), eps, _p(y))
@@ -168,8 +183,9 @@ def _weights(layers):
     for i, lay in enumerate(layers):
         ws = [np.ascontiguousarray(lay.w_in), _f32(lay.s_in), _f32(lay.conv_w), _f32(lay.norm_w),
               np.ascontiguousarray(lay.w_out), _f32(lay.s_out)]
-        keep += ws
-        arr[i] = _LayerW(*[a.ctypes.data for a in ws])
+        gs = [None if getattr(lay, n, None) is None else _f32(getattr(lay, n)) for n in ("a_log", "a_bias")]
+        keep += ws + [g for g in gs if g is not None]
+        arr[i] = _LayerW(*[a.ctypes.data for a in ws], *[None if g is None else g.ctypes.data for g in gs])
     return arr, keep
 
 

@@ -29,6 +29,7 @@
 
 #define DNO_X_RMSNORM 1u
 #define DNO_ALPHA_PER_KEY 2u
+#define DNO_GATES_ON_DEVICE 4u
 
 typedef struct {
   int d_model, n_k_heads, d_k, n_v_heads, d_v;
@@ -44,6 +45,8 @@ typedef struct {
   const float *norm_w;   /* [dv] */
   const void *w_out;     /* int8 [D][V] or packed 4-bit [D][V/2] */
   const float *s_out;    /* [D] */
+  const float *a_log;    /* [Hv] (DNO_GATES_ON_DEVICE) */
+  const float *a_bias;   /* [Hv] (DNO_GATES_ON_DEVICE) */
 } dno_layer_weights;
 
 /* SiLU(a) = a * sigmoid(a) = a / (1 + e^-a). */
@@ -166,6 +169,20 @@ void dno_delta_head_vec(int dk, int dv, double *S, const double *k, const double
   free(d);
 }
 
+/* softplus(y) = log(1 + e^y), written as max(y, 0) + log1p(e^-|y|) so that it neither overflows
+ * nor loses the small values. */
+double dno_softplus(double y) { return (y > 0.0 ? y : 0.0) + log1p(exp(-fabs(y))); }
+
+/* The two gates of a value head from its two gate rows a, b of the in_proj output.
+ * [DN-GPU] names the gates (a/b, one output per value head each) but leaves them to the engine
+ * and gives no formula. Reading, stated: the decay form of gated-delta-rule layers,
+ *   alpha = exp(-exp(a_log) * softplus(a + a_bias)),   beta = 1 / (1 + e^-b),
+ * with a_log and a_bias per value head. alpha is in (0, 1], beta in (0, 1). */
+void dno_gates(double a, double b, double a_log, double a_bias, double *alpha, double *beta) {
+  *alpha = exp(-exp(a_log) * dno_softplus(a + a_bias));
+  *beta = 1.0 / (1.0 + exp(-b));
+}
+
 /* Gated RMSNorm with silu(z) [DN-GPU], per value head over dv:
  *   y[j] = w[j] * o[j] / sqrt(mean(o^2) + eps) * silu(z[j]). */
 void dno_gated_rmsnorm(int n, const double *o, const double *z, const float *w, double eps, double *y) {
@@ -180,6 +197,8 @@ void dno_gated_rmsnorm(int n, const double *o, const double *z, const float *w, 
  * write-back, readout, gated RMSNorm, out_proj GEMV.
  * in_proj rows: q (Hk*dk) | k (Hk*dk) | v (Hv*dv) | z (Hv*dv) [TRUNK]; q, k, v are
  * convolved, z is not. Value head h reads key head h / (Hv/Hk).
+ * With DNO_GATES_ON_DEVICE the in_proj has two more blocks, a (Hv) | b (Hv), not convolved, and
+ * head h's gates come from a[h], b[h] through dno_gates; alpha and beta are then not read.
  *   S    [B][Hv][dk][dv]  (in/out)     hist [B][K-1][C] (in/out)
  *   x    [B][D]  alpha, beta [B][Hv]   out  [B][D]
  *   (with DNO_ALPHA_PER_KEY, alpha is [B][Hv][dk])                               */
@@ -188,7 +207,9 @@ int dno_layer_step(const dno_dims *d, const dno_layer_weights *W, double *S, dou
   const int D = d->d_model, Hk = d->n_k_heads, dk = d->d_k, Hv = d->n_v_heads, dv = d->d_v;
   const int K = d->conv_k, B = d->batch;
   if (D <= 0 || Hk <= 0 || dk <= 0 || Hv <= 0 || dv <= 0 || K <= 0 || B <= 0 || Hv % Hk) return -1;
-  const int QK = Hk * dk, V = Hv * dv, C = 2 * QK + V, R = C + V;
+  const int gates = (d->flags & DNO_GATES_ON_DEVICE) != 0;
+  if (gates && ((d->flags & DNO_ALPHA_PER_KEY) || !W->a_log || !W->a_bias)) return -1;
+  const int QK = Hk * dk, V = Hv * dv, C = 2 * QK + V, R = C + V + (gates ? 2 * Hv : 0);
   double *xin = (double *)malloc(sizeof(double) * D);
   double *u = (double *)malloc(sizeof(double) * R);
   double *c = (double *)malloc(sizeof(double) * C);
@@ -210,7 +231,11 @@ int dno_layer_step(const dno_dims *d, const dno_layer_weights *W, double *S, dou
       dno_l2norm(dk, c + QK + (long)g * dk, d->eps_l2, kh);
       const double *v = c + 2 * QK + (long)h * dv;
       double *Sh = S + ((long)b * Hv + h) * dk * dv;
-      if (d->flags & DNO_ALPHA_PER_KEY) {
+      if (gates) {
+        double ga, gb;
+        dno_gates(u[C + V + h], u[C + V + Hv + h], (double)W->a_log[h], (double)W->a_bias[h], &ga, &gb);
+        dno_delta_head(dk, dv, Sh, kh, v, qh, ga, gb, d->q_scale, o);
+      } else if (d->flags & DNO_ALPHA_PER_KEY) {
         double *av = (double *)malloc(sizeof(double) * dk);
         for (int i = 0; i < dk; ++i) av[i] = (double)alpha[((long)b * Hv + h) * dk + i];
         dno_delta_head_vec(dk, dv, Sh, kh, v, qh, av, (double)beta[(long)b * Hv + h], d->q_scale, o);

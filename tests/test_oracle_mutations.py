@@ -40,6 +40,14 @@ MUTATIONS = [
      "av[i] = (double)alpha[((long)h * B + b) * dk + i];", 0),
     ("per_key_alpha_layer_stride", "const long aa = (d->flags & DNO_ALPHA_PER_KEY) ? ab * d->d_k : ab;",
      "const long aa = ab;", 0),
+    ("gate_rows_swapped", "dno_gates(u[C + V + h], u[C + V + Hv + h],", "dno_gates(u[C + V + Hv + h], u[C + V + h],", 0),
+    ("gate_head_shifted", "dno_gates(u[C + V + h], u[C + V + Hv + h],", "dno_gates(u[C + V + (h + 1) % Hv], u[C + V + Hv + (h + 1) % Hv],", 0),
+    ("gate_param_head", "(double)W->a_log[h], (double)W->a_bias[h]", "(double)W->a_log[0], (double)W->a_bias[h]", 0),
+    ("softplus_dropped", "*alpha = exp(-exp(a_log) * dno_softplus(a + a_bias));", "*alpha = exp(-exp(a_log) * (a + a_bias));", 0),
+    ("a_log_not_exponentiated", "*alpha = exp(-exp(a_log) * dno_softplus(a + a_bias));", "*alpha = exp(-a_log * dno_softplus(a + a_bias));", 0),
+    ("a_bias_sign", "*alpha = exp(-exp(a_log) * dno_softplus(a + a_bias));", "*alpha = exp(-exp(a_log) * dno_softplus(a - a_bias));", 0),
+    ("beta_gate_sign", "*beta = 1.0 / (1.0 + exp(-b));", "*beta = 1.0 / (1.0 + exp(b));", 0),
+    ("softplus_negative_branch", "log1p(exp(-fabs(y)))", "log1p(exp(-y))", 0),
 ]
 
 

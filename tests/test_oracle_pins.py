@@ -388,3 +388,119 @@ def test_per_key_run_decay_only_closed_form():
     _, S, _ = orc.run(cfg, layers, gi.Stream(stream.x, a, zero), S=S0, hist=H0)
     want = S0 * np.prod(a.astype(np.float64), axis=0)[..., None]
     np.testing.assert_allclose(S, want, rtol=1e-14, atol=0)
+
+
+# --------------------------------------------------------------------------- gates on the card
+# The pages name the two gates (a/b, one output per value head each) and leave their formula to
+# the engine; the oracle states the decay form alpha = exp(-exp(a_log) softplus(a + a_bias)),
+# beta = sigmoid(b). These pins tie it to values that follow from that statement alone.
+
+def test_softplus_special_values_and_identity():
+    assert orc.softplus(0.0) == pytest.approx(np.log(2.0), rel=1e-15)
+    assert orc.softplus(np.log(np.e - 1.0)) == pytest.approx(1.0, rel=1e-15)
+    assert orc.softplus(40.0) == pytest.approx(40.0 + np.exp(-40.0), rel=1e-15)
+    assert orc.softplus(-40.0) == pytest.approx(np.exp(-40.0), rel=1e-12)
+    for y in (-30.0, -3.5, -0.25, 0.7, 5.0, 31.0):
+        # log(1 + e^y) - log(1 + e^-y) = y
+        assert orc.softplus(y) - orc.softplus(-y) == pytest.approx(y, rel=1e-14, abs=1e-14)
+
+
+def test_gates_special_values():
+    # a + a_bias = 0: softplus = ln 2, so alpha = 2^(-e^a_log)
+    assert orc.gates(0.0, 0.0, 0.0, 0.0) == pytest.approx((0.5, 0.5), rel=1e-15)
+    assert orc.gates(1.5, 0.0, np.log(2.0), -1.5)[0] == pytest.approx(0.25, rel=1e-14)
+    assert orc.gates(-2.0, 0.0, np.log(3.0), 2.0)[0] == pytest.approx(0.125, rel=1e-14)
+    # softplus = 1: alpha = exp(-e^a_log)
+    assert orc.gates(np.log(np.e - 1.0), 0.0, 0.0, 0.0)[0] == pytest.approx(np.exp(-1.0), rel=1e-14)
+    # beta = sigmoid(b)
+    assert orc.gates(0.0, np.log(3.0), 0.0, 0.0)[1] == pytest.approx(0.75, rel=1e-15)
+    assert orc.gates(0.0, -np.log(3.0), 0.0, 0.0)[1] == pytest.approx(0.25, rel=1e-15)
+    # a strongly negative gate input keeps the state (alpha -> 1), a strongly positive one clears it
+    assert orc.gates(-60.0, 0.0, 1.0, 0.0)[0] == pytest.approx(1.0, abs=1e-20)
+    assert orc.gates(60.0, 0.0, 0.0, 0.0)[0] == pytest.approx(np.exp(-60.0), rel=1e-12)
+    # alpha depends on a + a_bias only; beta on b only
+    for a, c, d in ((0.3, -4.0, 1.7), (-2.0, -6.5, -0.4)):
+        assert orc.gates(a, 0.2, 1.1, c) == pytest.approx(orc.gates(a + d, 0.2, 1.1, c - d), rel=1e-14)
+
+
+def _gates_layer(weight_bits=8):
+    cfg = gi.custom("gates_pin", d_model=64, n_k_heads=2, d_k=16, n_v_heads=4, d_v=16, n_tokens=3,
+                    flags=gi.DN_GATES_ON_DEVICE, weight_bits=weight_bits, ring_std=1.0)
+    layers, stream = gi.generate(cfg)
+    return cfg, layers[0], stream
+
+
+def _with_gate_rows(cfg, lay, a_rows, b_rows, a_bias=None):
+    """The layer with its gate rows' integer values replaced (0 keeps, None zeroes the block)."""
+    import copy
+    lay = copy.copy(lay)
+    vals = lay.w_in_vals.copy()
+    R0, Hv = cfg.conv_channels + cfg.v_dim, cfg.n_v_heads
+    if a_rows is None:
+        vals[R0:R0 + Hv] = 0
+    if b_rows is None:
+        vals[R0 + Hv:R0 + 2 * Hv] = 0
+    lay.w_in_vals = vals
+    lay.w_in = vals if cfg.weight_bits == 8 else gi.pack_int4(vals)
+    if a_bias is not None:
+        lay.a_bias = np.asarray(a_bias, np.float32)
+    return lay
+
+
+def _explicit_step(cfg, lay, S, hist, x, alpha, beta):
+    """The same layer without the gate flag, gates given: the oracle's pinned explicit-gate path."""
+    import copy
+    plain = cfg.replace(flags=cfg.flags & ~gi.DN_GATES_ON_DEVICE)
+    lay2 = copy.copy(lay)
+    R = plain.in_rows
+    lay2.w_in = np.ascontiguousarray(lay.w_in[:R]); lay2.s_in = np.ascontiguousarray(lay.s_in[:R])
+    return orc.layer_step(plain, lay2, S, hist, x, np.asarray(alpha, np.float32)[None],
+                          np.asarray(beta, np.float32)[None])
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_gates_zero_rows_give_closed_form_gates(bits):
+    """a = b = 0 and a_bias = 0: every head decays by 2^(-e^a_log[h]) with beta = 1/2."""
+    cfg, lay, stream = _gates_layer(bits)
+    lay = _with_gate_rows(cfg, lay, None, None, a_bias=np.zeros(cfg.n_v_heads))
+    Hv = cfg.n_v_heads
+    S1 = RNG.standard_normal((1, Hv, cfg.d_k, cfg.d_v)); S2 = S1.copy()
+    h1 = RNG.standard_normal((1, cfg.conv_k - 1, cfg.conv_channels)); h2 = h1.copy()
+    x = stream.x[0].astype(np.float64)
+    out = orc.layer_step(cfg, lay, S1, h1, x, np.zeros((1, Hv), np.float32), np.zeros((1, Hv), np.float32))
+    alpha = 2.0 ** (-np.exp(lay.a_log.astype(np.float64)))
+    ref = _explicit_step(cfg, lay, S2, h2, x, alpha, np.full(Hv, 0.5))
+    np.testing.assert_allclose(out, ref, rtol=1e-5, atol=1e-6 * np.max(np.abs(ref)))
+    np.testing.assert_allclose(S1, S2, rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("which", ["a", "b"])
+def test_gates_read_their_own_rows_and_head(which):
+    """Only one gate block nonzero: the other gate keeps its closed form, and the nonzero one
+    follows from that block's rows for each head (a swapped block or a shifted head shows)."""
+    cfg, lay, stream = _gates_layer()
+    Hv, R0 = cfg.n_v_heads, cfg.conv_channels + cfg.v_dim
+    lay = _with_gate_rows(cfg, lay, 0 if which == "a" else None, 0 if which == "b" else None)
+    x = stream.x[0].astype(np.float64)
+    rows = lay.s_in[R0:].astype(np.float64) * (lay.w_in_vals[R0:].astype(np.float64) @ x[0])
+    a, b = rows[:Hv], rows[Hv:]
+    assert np.all(a == 0) != (which == "a") and np.all(b == 0) != (which == "b")
+    y = a + lay.a_bias.astype(np.float64)
+    alpha = np.exp(-np.exp(lay.a_log.astype(np.float64)) * (np.maximum(y, 0) + np.log1p(np.exp(-np.abs(y)))))
+    beta = 1.0 / (1.0 + np.exp(-b))
+    S1 = RNG.standard_normal((1, Hv, cfg.d_k, cfg.d_v)); S2 = S1.copy()
+    h1 = RNG.standard_normal((1, cfg.conv_k - 1, cfg.conv_channels)); h2 = h1.copy()
+    out = orc.layer_step(cfg, lay, S1, h1, x, np.zeros((1, Hv), np.float32), np.zeros((1, Hv), np.float32))
+    ref = _explicit_step(cfg, lay, S2, h2, x, alpha, beta)
+    np.testing.assert_allclose(out, ref, rtol=1e-5, atol=1e-6 * np.max(np.abs(ref)))
+    np.testing.assert_allclose(S1, S2, rtol=1e-5, atol=1e-7)
+
+
+def test_gates_ignore_the_gate_arrays():
+    cfg, lay, stream = _gates_layer()
+    cfg3 = cfg.replace(n_tokens=3)
+    out1, S1, H1 = orc.run(cfg3, [lay], stream)
+    noise = gi.Stream(stream.x, RNG.uniform(0, 1, stream.alpha.shape).astype(np.float32),
+                      RNG.uniform(0, 1, stream.beta.shape).astype(np.float32))
+    out2, S2, H2 = orc.run(cfg3, [lay], noise)
+    assert np.array_equal(out1, out2) and np.array_equal(S1, S2)
