@@ -88,7 +88,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="stack",
-                    choices=["stack", "stack_int4", "stack_perkey", "layer", "batched", "prefill"])
+                    choices=["stack", "stack_int4", "stack_perkey", "stack_gates", "layer", "batched", "prefill"])
     ap.add_argument("--prompt", type=int, default=2048, help="prompt length of --config prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -122,6 +122,8 @@ def main():
         return bench_prefill(args, gi, dn)
     if args.config == "stack_perkey":  # the stack workload with one decay per key channel
         cfg = gi.CONFIGS["stack"].replace(name="stack_perkey", flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
+    elif args.config == "stack_gates":  # the stack workload with the gates computed on the card
+        cfg = gi.CONFIGS["stack"].replace(name="stack_gates", flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE)
     else:
         cfg = gi.CONFIGS[args.config]
     dev = torch.device("cuda:0")

@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("DN_LIB") or os.path.join(_PKG, "libdn.so")
 DN_OK, DN_E_INVAL, DN_E_NOMEM, DN_E_DEVICE, DN_E_DISABLED, DN_E_FAULT = 0, -1, -2, -3, -4, -5
 DN_X_RMSNORM = 1
 DN_ALPHA_PER_KEY = 2  # alpha [L][B][Hv][dk]: one decay per key channel
+DN_GATES_ON_DEVICE = 4  # gates from two more in_proj rows per value head; alpha/beta not read
 EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy", "dn_prefill")
 
 _ERR = {DN_OK: "ok", DN_E_INVAL: "invalid argument", DN_E_NOMEM: "out of device memory",
@@ -42,7 +43,8 @@ class dn_config(ctypes.Structure):
 
 class dn_weights(ctypes.Structure):
     _fields_ = [("w_in", ctypes.c_void_p), ("s_in", ctypes.c_void_p), ("conv_w", ctypes.c_void_p),
-                ("norm_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("s_out", ctypes.c_void_p)]
+                ("norm_w", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("s_out", ctypes.c_void_p),
+                ("a_log", ctypes.c_void_p), ("a_bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -128,7 +130,8 @@ def _dev(a, dtype, device):
 
 class DeltaNetStack:
     """A handle over n_layers layers. ``layers`` are objects with attributes w_in, s_in, conv_w,
-    norm_w, w_out, s_out (numpy arrays or tensors, in the layouts of include/dn.h)."""
+    norm_w, w_out, s_out (numpy arrays or tensors, in the layouts of include/dn.h), and a_log,
+    a_bias with DN_GATES_ON_DEVICE."""
 
     def __init__(self, *, d_model, n_k_heads, d_k, n_v_heads, d_v, layers, conv_k=4, batch=1,
                  weight_bits=8, flags=0, eps_l2=1e-6, eps_rms=1e-6, q_scale=1.0, device="cuda:0"):
@@ -142,8 +145,10 @@ class DeltaNetStack:
             t = [_dev(lay.w_in, wdt, self.device), _dev(lay.s_in, torch.float32, self.device),
                  _dev(lay.conv_w, torch.float32, self.device), _dev(lay.norm_w, torch.float32, self.device),
                  _dev(lay.w_out, wdt, self.device), _dev(lay.s_out, torch.float32, self.device)]
-            self._keep.append(t)
-            ws.append(dn_weights(*[x.data_ptr() for x in t]))
+            g = [None if getattr(lay, n, None) is None else _dev(getattr(lay, n), torch.float32, self.device)
+                 for n in ("a_log", "a_bias")]
+            self._keep.append(t + [x for x in g if x is not None])
+            ws.append(dn_weights(*[x.data_ptr() for x in t], *[None if x is None else x.data_ptr() for x in g]))
         with torch.cuda.device(self.device):
             self.h = dn_create(self.cfg, ws)
         self.L, self.B, self.D = len(layers), batch, d_model
@@ -175,7 +180,7 @@ class DeltaNetStack:
     def new_out(self):
         return torch.empty((self.L, self.B, self.D), dtype=torch.float32, device=self.device)
 
-    def step(self, x, alpha, beta, out=None, stream=None, check=True):
+    def step(self, x, alpha=None, beta=None, out=None, stream=None, check=True):
         if out is None:
             out = self.new_out()
         rc = dn_step(self.h, x, alpha, beta, out, stream)
@@ -183,8 +188,9 @@ class DeltaNetStack:
             _check(rc, "dn_step")
         return out if check else rc
 
-    def prefill(self, x, alpha, beta, out=None, stream=None, check=True):
-        """Run a prompt through every layer: x [T][D], alpha/beta [T][L][Hv]; returns out [L][T][D]."""
+    def prefill(self, x, alpha=None, beta=None, out=None, stream=None, check=True):
+        """Run a prompt through every layer: x [T][D], alpha/beta [T][L][Hv] (None with
+        DN_GATES_ON_DEVICE); returns out [L][T][D]."""
         T = x.shape[0]
         if out is None:
             out = torch.empty((self.L, T, self.D), dtype=torch.float32, device=self.device)

@@ -23,7 +23,10 @@ struct dn_layer {
   dn_config cfg;
   std::vector<dn_weights> w;
   int device = 0;
-  int R = 0, C = 0, V = 0;
+  int R = 0, C = 0, V = 0;  // R: in_proj rows q|k|v|z (gate rows, if any, follow them)
+  bool gates = false;       // DN_GATES_ON_DEVICE: 2 Hv gate rows after the R rows
+  float* gal = nullptr;     // [B][Hv] scratch: gates computed on the card (per-layer and batched paths)
+  float* gbe = nullptr;
   size_t s_elems = 0;     // per layer: B*Hv*dk*dv
   size_t ring_elems = 0;  // per layer: B*(K-1)*C
   float* S = nullptr;     // [L][B][Hv][dk][dv]
@@ -62,6 +65,8 @@ struct dn_layer {
   float* pf_cw = nullptr;                  // chunk terms of the recurrence
   float* pf_o = nullptr;                   // [T][V] readout, then gated output
   float* pf_ring = nullptr;                // the new conv history of a layer
+  float* pf_al = nullptr;                  // [T][Hv] gates computed on the card
+  float* pf_be = nullptr;
   bool disabled = false;
   long steps = 0;
   long fault_step = 0;    // 1-based step to fail (0 = never)
@@ -85,7 +90,8 @@ int validate(const dn_config* c) {
   if (c->conv_k < 1 || c->conv_k > 4) return DN_E_INVAL;
   if (c->batch < 1 || c->batch > 1024) return DN_E_INVAL;
   if (c->n_layers < 1 || c->n_layers > 256) return DN_E_INVAL;
-  if (c->flags & ~(DN_X_RMSNORM | DN_ALPHA_PER_KEY)) return DN_E_INVAL;
+  if (c->flags & ~(DN_X_RMSNORM | DN_ALPHA_PER_KEY | DN_GATES_ON_DEVICE)) return DN_E_INVAL;
+  if ((c->flags & DN_ALPHA_PER_KEY) && (c->flags & DN_GATES_ON_DEVICE)) return DN_E_INVAL;
   if (!(c->eps_l2 >= 0.f) || !(c->eps_rms >= 0.f)) return DN_E_INVAL;
   return DN_OK;
 }
@@ -101,6 +107,8 @@ void free_all(dn_layer* h) {
   dfree(h->ring);
   dfree(h->u);
   dfree(h->y);
+  dfree(h->gal);
+  dfree(h->gbe);
   dfree(h->d_layers);
   dfree(h->X);
   dfree(h->U);
@@ -122,6 +130,8 @@ void free_all(dn_layer* h) {
   dfree(h->pf_cw);
   dfree(h->pf_o);
   dfree(h->pf_ring);
+  dfree(h->pf_al);
+  dfree(h->pf_be);
   h->pf_cap = 0;
 }
 
@@ -177,7 +187,7 @@ int setup_persist(dn_layer* h) {
   dn::PersistShape& ps = h->ps;
   ps.batch = c.batch; ps.D = c.d_model; ps.V = h->V; ps.R = h->R; ps.dk = c.d_k; ps.dv = c.d_v;
   ps.Hv = c.n_v_heads; ps.K = c.conv_k; ps.bits = c.weight_bits;
-  ps.L = c.n_layers; ps.alpha_per_key = (c.flags & DN_ALPHA_PER_KEY) ? 1 : 0;
+  ps.L = c.n_layers; ps.alpha_per_key = (c.flags & DN_ALPHA_PER_KEY) ? 1 : 0; ps.gates = h->gates ? 1 : 0;
   const char* force = std::getenv("DN_LAYER_KERNELS");
   if ((force && std::atoi(force) != 0) || !dn::persist_supported(ps, h->nwg)) return DN_OK;
   int per_cu = 0;
@@ -185,7 +195,8 @@ int setup_persist(dn_layer* h) {
   const size_t L = c.n_layers;
   bool ok = hipMalloc(&h->d_layers, sizeof(dn::LayerW) * L) == hipSuccess;
   ok = ok && hipMalloc(&h->X, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
-  ok = ok && hipMalloc(&h->U, sizeof(uint64_t) * h->R) == hipSuccess;
+  const size_t u_words = h->R + (h->gates ? 2 * c.n_v_heads : 0);
+  ok = ok && hipMalloc(&h->U, sizeof(uint64_t) * u_words) == hipSuccess;
   ok = ok && hipMalloc(&h->G, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
   ok = ok && hipMalloc(&h->ctl, sizeof(dn::Ctl)) == hipSuccess;
   ok = ok && hipMalloc(&h->stage, sizeof(float) * L * h->s_elems) == hipSuccess;
@@ -198,11 +209,12 @@ int setup_persist(dn_layer* h) {
   if (!ok) return DN_E_NOMEM;
   std::vector<dn::LayerW> lw(L);
   for (size_t l = 0; l < L; ++l)
-    lw[l] = dn::LayerW{h->w[l].w_in, h->w[l].s_in, h->w[l].conv_w, h->w[l].norm_w, h->w[l].w_out, h->w[l].s_out};
+    lw[l] = dn::LayerW{h->w[l].w_in,  h->w[l].s_in,  h->w[l].conv_w, h->w[l].norm_w,
+                       h->w[l].w_out, h->w[l].s_out, h->w[l].a_log,  h->w[l].a_bias};
   const dn::Ctl ctl0{1u, 0u, 0u, 0u};
   ok = hipMemcpy(h->d_layers, lw.data(), sizeof(dn::LayerW) * L, hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemset(h->X, 0, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
-  ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * h->R) == hipSuccess;
+  ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * u_words) == hipSuccess;
   ok = ok && hipMemset(h->G, 0, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
   ok = ok && hipMemcpy(h->ctl, &ctl0, sizeof(ctl0), hipMemcpyHostToDevice) == hipSuccess;
   if (!ok) return DN_E_DEVICE;
@@ -231,6 +243,7 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
     if (!x.w_in || !x.s_in || !x.conv_w || !x.norm_w || !x.w_out || !x.s_out) return DN_E_INVAL;
     if (!aligned16(x.w_in) || !aligned16(x.w_out)) return DN_E_INVAL;
     if (!aligned16(x.s_in) || !aligned16(x.s_out)) return DN_E_INVAL;
+    if ((cfg->flags & DN_GATES_ON_DEVICE) && (!x.a_log || !x.a_bias)) return DN_E_INVAL;
   }
   dn_layer* h = new (std::nothrow) dn_layer();
   if (!h) return DN_E_NOMEM;
@@ -244,6 +257,7 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   h->V = cfg->n_v_heads * cfg->d_v;
   h->C = 2 * QK + h->V;
   h->R = h->C + h->V;
+  h->gates = (cfg->flags & DN_GATES_ON_DEVICE) != 0;
   const size_t L = cfg->n_layers, B = cfg->batch;
   h->s_elems = B * cfg->n_v_heads * (size_t)cfg->d_k * cfg->d_v;
   h->ring_elems = B * (size_t)(cfg->conv_k - 1) * h->C;
@@ -251,6 +265,10 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   ok = ok && hipMalloc(&h->ring, sizeof(float) * (L * h->ring_elems + 1)) == hipSuccess;
   ok = ok && hipMalloc(&h->u, sizeof(float) * B * h->R) == hipSuccess;
   ok = ok && hipMalloc(&h->y, sizeof(float) * B * h->V) == hipSuccess;
+  if (h->gates) {
+    ok = ok && hipMalloc(&h->gal, sizeof(float) * B * cfg->n_v_heads) == hipSuccess;
+    ok = ok && hipMalloc(&h->gbe, sizeof(float) * B * cfg->n_v_heads) == hipSuccess;
+  }
   if (!ok) {
     (void)hipGetLastError();
     free_all(h);
@@ -358,8 +376,26 @@ int batched_proj(dn_layer* h, const void* W, const float* s, const float* act, i
 }
 }  // namespace
 
+namespace {
+// Gates of N input rows of layer l (DN_GATES_ON_DEVICE) into alpha_out/beta_out [N][Hv].
+hipError_t launch_layer_gates(const dn_layer* h, size_t l, const float* xl, int N, float* alpha_out, float* beta_out,
+                              hipStream_t st) {
+  const dn_config& c = h->cfg;
+  const dn_weights& w = h->w[l];
+  const size_t rowbytes = c.weight_bits == 8 ? (size_t)c.d_model : (size_t)c.d_model / 2;
+  dn::GateArgs g{};
+  g.x = xl; g.x_stride = c.d_model; g.N = N; g.D = c.d_model;
+  g.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; g.eps = c.eps_rms;
+  g.W = static_cast<const uint8_t*>(w.w_in) + (size_t)h->R * rowbytes; g.s = w.s_in + h->R;
+  g.a_log = w.a_log; g.a_bias = w.a_bias; g.Hv = c.n_v_heads;
+  g.alpha = alpha_out; g.beta = beta_out;
+  return dn::launch_gates(g, c.weight_bits, st);
+}
+}  // namespace
+
 DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float* beta, float* out, void* hip_stream) {
-  if (!h || !x || !alpha || !beta || !out) return DN_E_INVAL;
+  if (!h || !x || !out) return DN_E_INVAL;
+  if (!h->gates && (!alpha || !beta)) return DN_E_INVAL;
   if (h->disabled) return DN_E_DISABLED;
   const dn_config& c = h->cfg;
   const size_t L = c.n_layers, B = c.batch, D = c.d_model;
@@ -379,6 +415,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     a.Hk = c.n_k_heads; a.Hv = c.n_v_heads; a.flags = c.flags;
     a.eps_l2 = c.eps_l2; a.eps_rms = c.eps_rms; a.q_scale = c.q_scale;
     a.alpha_per_key = (c.flags & DN_ALPHA_PER_KEY) ? 1 : 0;
+    a.gates = h->gates ? 1 : 0;
     if (dn::launch_persist(a, h->ps, h->nwg, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
     return DN_OK;
@@ -395,7 +432,14 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
         return fail(h, rc);
       dn::BStateArgs bs{};
       bs.u = h->u; bs.S = h->S + l * h->s_elems;
-      bs.alpha = alpha + l * a_layer; bs.beta = beta + l * B * c.n_v_heads; bs.alpha_per_key = pk;
+      if (h->gates) {
+        if (launch_layer_gates(h, l, l == 0 ? x : out + (l - 1) * B * D, (int)B, h->gal, h->gbe, st) != hipSuccess)
+          return fail(h, DN_E_DEVICE);
+        bs.alpha = h->gal; bs.beta = h->gbe;
+      } else {
+        bs.alpha = alpha + l * a_layer; bs.beta = beta + l * B * c.n_v_heads;
+      }
+      bs.alpha_per_key = pk;
       bs.norm_w = w.norm_w; bs.xs = h->xs; bs.sc = h->sc;
       bs.B = (int)B; bs.Hk = c.n_k_heads; bs.Hv = c.n_v_heads; bs.R = h->R; bs.C = h->C; bs.QK = QK; bs.V = h->V;
       bs.eps_l2 = c.eps_l2; bs.eps_rms = c.eps_rms; bs.q_scale = c.q_scale;
@@ -423,7 +467,13 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
 
     dn::HeadArgs ha{};
     ha.u = h->u; ha.S = h->S + l * h->s_elems;
-    ha.alpha = alpha + l * a_layer; ha.beta = beta + l * B * c.n_v_heads; ha.alpha_per_key = pk;
+    if (h->gates) {
+      if (launch_layer_gates(h, l, xl, (int)B, h->gal, h->gbe, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      ha.alpha = h->gal; ha.beta = h->gbe;
+    } else {
+      ha.alpha = alpha + l * a_layer; ha.beta = beta + l * B * c.n_v_heads;
+    }
+    ha.alpha_per_key = pk;
     ha.norm_w = w.norm_w; ha.y = h->y;
     ha.Hk = c.n_k_heads; ha.Hv = c.n_v_heads; ha.dk = c.d_k; ha.dv = c.d_v;
     ha.R = h->R; ha.C = h->C; ha.batch = (int)B;
@@ -459,7 +509,8 @@ int pf_reserve(dn_layer* h, int T) {
   for (void** p : {&h->pf_xs, reinterpret_cast<void**>(&h->pf_sc), reinterpret_cast<void**>(&h->pf_ssq),
                    reinterpret_cast<void**>(&h->pf_part), reinterpret_cast<void**>(&h->pf_u),
                    reinterpret_cast<void**>(&h->pf_cw), reinterpret_cast<void**>(&h->pf_o),
-                   reinterpret_cast<void**>(&h->pf_ring)})
+                   reinterpret_cast<void**>(&h->pf_ring), reinterpret_cast<void**>(&h->pf_al),
+                   reinterpret_cast<void**>(&h->pf_be)})
     if (*p) {
       (void)hipFree(*p);
       *p = nullptr;
@@ -473,6 +524,10 @@ int pf_reserve(dn_layer* h, int T) {
   ok = ok && hipMalloc(&h->pf_cw, sizeof(float) * c.n_v_heads * nch * dn::PF_CHUNK_FLOATS) == hipSuccess;
   ok = ok && hipMalloc(&h->pf_o, sizeof(float) * T * V) == hipSuccess;
   ok = ok && hipMalloc(&h->pf_ring, sizeof(float) * ring) == hipSuccess;
+  if (h->gates) {
+    ok = ok && hipMalloc(&h->pf_al, sizeof(float) * T * c.n_v_heads) == hipSuccess;
+    ok = ok && hipMalloc(&h->pf_be, sizeof(float) * T * c.n_v_heads) == hipSuccess;
+  }
   if (!ok) return DN_E_NOMEM;
   h->pf_cap = T;
   return DN_OK;
@@ -481,7 +536,8 @@ int pf_reserve(dn_layer* h, int T) {
 
 DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* alpha, const float* beta, float* out,
                       void* hip_stream) {
-  if (!h || !x || !alpha || !beta || !out || n_tokens < 1) return DN_E_INVAL;
+  if (!h || !x || !out || n_tokens < 1) return DN_E_INVAL;
+  if (!h->gates && (!alpha || !beta)) return DN_E_INVAL;
   if (h->disabled) return DN_E_DISABLED;
   const dn_config& c = h->cfg;
   const size_t L = c.n_layers, D = c.d_model, T = n_tokens;
@@ -520,7 +576,12 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
     // recurrence in chunks, then the gated RMSNorm
     dn::PIntraArgs pi{};
     pi.u = h->pf_u; pi.T = n_tokens; pi.R = R; pi.QK = QK; pi.Hv = c.n_v_heads; pi.Hk = c.n_k_heads;
-    pi.alpha = alpha + l * c.n_v_heads; pi.beta = beta + l * c.n_v_heads; pi.gstride = (int)L * c.n_v_heads;
+    if (h->gates) {
+      if (launch_layer_gates(h, l, xl, n_tokens, h->pf_al, h->pf_be, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      pi.alpha = h->pf_al; pi.beta = h->pf_be; pi.gstride = c.n_v_heads;
+    } else {
+      pi.alpha = alpha + l * c.n_v_heads; pi.beta = beta + l * c.n_v_heads; pi.gstride = (int)L * c.n_v_heads;
+    }
     pi.eps_l2 = c.eps_l2; pi.q_scale = c.q_scale; pi.NCH = nch; pi.cw = h->pf_cw;
     if (dn::launch_pintra(pi, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     dn::PScanArgs ps{};

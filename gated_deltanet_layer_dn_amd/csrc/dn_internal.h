@@ -41,6 +41,31 @@ struct HeadArgs {
 hipError_t launch_gemv(const GemvArgs& a, int bits, hipStream_t st);
 hipError_t launch_head(const HeadArgs& a, hipStream_t st);
 
+// The two gates of each value head from the in_proj's gate rows a | b (DN_GATES_ON_DEVICE):
+// alpha = exp(-exp(a_log) * softplus(a + a_bias)), beta = 1 / (1 + exp(-b)).
+__device__ __forceinline__ float dn_softplus(float y) { return fmaxf(y, 0.f) + log1pf(expf(-fabsf(y))); }
+__device__ __forceinline__ float dn_gate_alpha(float a, float a_log, float a_bias) {
+  return expf(-expf(a_log) * dn_softplus(a + a_bias));
+}
+__device__ __forceinline__ float dn_gate_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
+
+// Gates for N input rows (tokens or sequences): u = s[r] * prenorm(x) . W[r] for the 2 Hv gate
+// rows, then alpha[n][h] from row h and beta[n][h] from row Hv + h.
+struct GateArgs {
+  const float* x;        // [N][x_stride], D columns used
+  int x_stride, N, D;
+  int prenorm;           // RMS-normalise x first
+  float eps;
+  const void* W;         // the gate rows: [2 Hv][D] int8 or [2 Hv][D/2] packed int4
+  const float* s;        // [2 Hv]
+  const float* a_log;    // [Hv]
+  const float* a_bias;   // [Hv]
+  int Hv;
+  float* alpha;          // [N][Hv]
+  float* beta;           // [N][Hv]
+};
+hipError_t launch_gates(const GateArgs& a, int bits, hipStream_t st);
+
 // ---- batched path (B >= 2): int8-MFMA projections and a streaming state kernel ----
 // act[b][k] split into three int8 terms per (sequence, 128-column chunk), in the GEMM's fragment order.
 struct BSplitArgs {
@@ -152,6 +177,8 @@ struct LayerW {
   const float* norm_w;
   const void* w_out;
   const float* s_out;
+  const float* a_log;    // [Hv] (gates on the device)
+  const float* a_bias;   // [Hv]
 };
 
 // Control words of one handle in device memory: the tag base of the next launch, the count of
@@ -172,7 +199,7 @@ struct PersistArgs {
   const float* beta;     // [L][Hv]
   float* out;            // [L][D]
   unsigned* X;           // [8][D]  layer output, self-tagged 32-bit words, one copy per XCD
-  uint64_t* U;           // [R]  tagged in_proj output (post-conv q|k|v, raw z)
+  uint64_t* U;           // [R (+ 2 Hv)]  tagged in_proj output (post-conv q|k|v, raw z, raw gate rows)
   unsigned* G;           // [8][V + 256] gated readout and partial sums of squares of the readout,
                          // self-tagged 32-bit words, in four segments [V/4 columns | partials of
                          // those heads], one copy per XCD
@@ -183,12 +210,13 @@ struct PersistArgs {
   unsigned flags;
   float eps_l2, eps_rms, q_scale;
   int alpha_per_key;     // 1: key row i of head h decays by alpha[l][h][i] (at most PK_MAXL layers)
+  int gates;             // 1: gates from the in_proj rows R .. R + 2 Hv (U holds them after the R rows)
 };
 constexpr int PK_MAXL = 32;  // layers of a whole-stack launch with one decay per key channel
 
 struct PersistShape {
   int batch, D, V, R, dk, dv, Hv, K, bits;
-  int L, alpha_per_key;
+  int L, alpha_per_key, gates;
 };
 
 bool persist_supported(const PersistShape& s, int nwg);

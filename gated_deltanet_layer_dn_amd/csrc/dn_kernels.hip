@@ -354,4 +354,63 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Gates on the card (DN_GATES_ON_DEVICE): one workgroup per input row n. The row is staged in LDS
+// (RMS-normalised when asked), each wave takes gate rows w, w+4, ... and reduces its fp32 dot
+// product; row h < Hv gives alpha[n][h], row Hv + h gives beta[n][h].
+// ---------------------------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void k_gates(const GateArgs a) {
+  extern __shared__ float xr[];  // [D]
+  __shared__ float redf[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = blockIdx.x, D = a.D;
+  const float* xb = a.x + (size_t)n * a.x_stride;
+  float ss = 0.f;
+  for (int c = tid; c < D; c += 256) {
+    const float v = xb[c];
+    xr[c] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum(ss, redf);  // its barriers also publish xr
+  const float inv = a.prenorm ? rsqrtf(ss / (float)D + a.eps) : 1.0f;
+  constexpr int COLS = BITS == 8 ? 16 : 32;  // columns per 16-byte chunk
+  const size_t rowbytes = BITS == 8 ? (size_t)D : (size_t)D / 2;
+  for (int r = wave; r < 2 * a.Hv; r += 4) {
+    const uint8_t* wr = static_cast<const uint8_t*>(a.W) + (size_t)r * rowbytes;
+    float acc = 0.f;
+    for (int c0 = COLS * lane; c0 < D; c0 += 64 * COLS) {
+      const v4i w = *reinterpret_cast<const v4i*>(wr + (BITS == 8 ? c0 : c0 / 2));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned p = (unsigned)w[e];
+        if (BITS == 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc = fmaf((float)(int8_t)(p >> (8 * q)), xr[c0 + 4 * e + q], acc);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int nib = (int)((p >> (4 * q)) & 15u);
+            acc = fmaf((float)((nib ^ 8) - 8), xr[c0 + 8 * e + q], acc);
+          }
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const float u = a.s[r] * inv * acc;
+      if (r < a.Hv) a.alpha[(size_t)n * a.Hv + r] = dn_gate_alpha(u, a.a_log[r], a.a_bias[r]);
+      else a.beta[(size_t)n * a.Hv + (r - a.Hv)] = dn_gate_beta(u);
+    }
+  }
+}
+
+hipError_t launch_gates(const GateArgs& a, int bits, hipStream_t st) {
+  if (a.N < 1 || a.D < 1 || a.D > 16384 || a.D % (bits == 8 ? 16 : 32)) return hipErrorInvalidValue;
+  const size_t lds = sizeof(float) * a.D;
+  if (bits == 8) hipLaunchKernelGGL(k_gates<8>, dim3(a.N), dim3(256), lds, st, a);
+  else hipLaunchKernelGGL(k_gates<4>, dim3(a.N), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace dn

@@ -30,6 +30,10 @@
 //
 // GEMV arithmetic as in the layer kernels: activations split into three int8 terms, exact int32
 // dot products with v_dot4_i32_i8, combined in double.
+//
+// Gates on the card (GT): in workgroups wg < 2 Hv the second communication wave computes in_proj
+// row R + wg (gate a of head wg, or gate b of head wg - Hv) during phase A and publishes it with
+// the other in_proj rows; phase B gathers its head's two gate values with q, k, v, z.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -386,10 +390,10 @@ __device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid)
   if (tid == 0) sm.stat[8] = s1;
 }
 
-// Compute waves: phase A and phase C, weights prefetched one layer ahead in registers. (PK does
-// not change this role; it keeps one specialisation per kernel instantiation, which the host
-// compiler pass needs when both instantiations of the kernel are referenced.)
-template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK>
+// Compute waves: phase A and phase C, weights prefetched one layer ahead in registers. (PK and GT
+// do not change this role; they keep one specialisation per kernel instantiation, which the host
+// compiler pass needs when several instantiations of the kernel are referenced.)
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT>
 __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
                                              int tid, int lane) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
@@ -592,7 +596,8 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 // Each poll starts only once this workgroup's own share of the data it waits for is done, so
 // that the rounds that are bound to miss are not issued.
 // PK: one decay per key channel; apk [L][128] holds this head's decays (LDS).
-template <int BITS, int NCHA, int NCHC, bool PK>
+// GT: gates from the in_proj's gate rows; sm.gate holds this head's a_log, a_bias per layer.
+template <int BITS, int NCHA, int NCHC, bool PK, bool GT>
 __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const PersistArgs& a, const Geo& g,
                                           unsigned base_tag, int tid, int lane, int cw, int wg) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
@@ -625,14 +630,33 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
   if (runs_b) {
     // the per-layer gates and norm weights this workgroup needs, fetched once per launch
     for (int l = lane; l < a.L; l += 64) {
-      sm.gate[l][0] = PK ? 0.f : a.alpha[(size_t)l * Hv + g.bh];
-      sm.gate[l][1] = a.beta[(size_t)l * Hv + g.bh];
+      if constexpr (GT) {
+        sm.gate[l][0] = a.layers[l].a_log[g.bh];
+        sm.gate[l][1] = a.layers[l].a_bias[g.bh];
+      } else {
+        sm.gate[l][0] = PK ? 0.f : a.alpha[(size_t)l * Hv + g.bh];
+        sm.gate[l][1] = a.beta[(size_t)l * Hv + g.bh];
+      }
     }
     if constexpr (PK)
       for (int e = lane; e < a.L * DK; e += 64)
         apk[e / DK][e % DK] = a.alpha[((size_t)(e / DK) * Hv + g.bh) * DK + e % DK];
     for (int e = lane; e < a.L * CB; e += 64) sm.nw[e / CB][e % CB] = a.layers[e / CB].norm_w[g.bcb * CB + e % CB];
   }
+
+  // GT: the gate row this wave computes (workgroups wg < 2 Hv, second communication wave), its
+  // weights held one layer ahead like the compute waves' rows
+  constexpr int rowbytes_in = BITS == 8 ? D : D / 2;
+  const bool runs_gate = GT && cw == 1 && wg < 2 * Hv;
+  v4i gw[1][NCHA];
+  float gsc = 0.f;
+  auto load_g = [&](int l) {
+    const int8_t* wr = reinterpret_cast<const int8_t*>(a.layers[l].w_in) + (size_t)(a.R + wg) * rowbytes_in;
+#pragma unroll
+    for (int k = 0; k < NCHA; ++k) gw[0][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wr) + lane + 64 * k);
+    gsc = a.layers[l].s_in[a.R + wg];
+  };
+  if (runs_gate) load_g(0);
 
   for (int l = 0; l < a.L; ++l) {
     const unsigned tag = base_tag + (unsigned)l;
@@ -686,18 +710,37 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
     split_x<BITS, D>(sm, a, tid);
     __syncthreads();  // (2)
 
+    if (runs_gate) {
+      // gate row R + wg on the staged x, published as in_proj output; then the next layer's row
+      int acc[1][3];
+      dot_rows<BITS, 1, NCHA>(gw, sm.xs, D, lane, acc);
+      const float dot = reduce_rows<BITS, 1>(acc, sm.stat[8], lane);
+      if (lane == 0) ll_store(Ub + a.R + wg, gsc * dot, tag);
+      if (l + 1 < a.L) load_g(l + 1);
+    }
+
     bool ok = true;
     if (runs_b) {
       // phase B: recurrence on the 128 x 16 state slice
       const int vcol = g.bh * DV + g.bcb * CB;
       // raw q and k rows lane and lane+64 of key head bg; v and z of this lane's column
+      // with GT also this head's gate values a and b (in_proj rows R + bh and R + Hv + bh)
+      constexpr int NU = GT ? 8 : 6;
       const int qo = g.bg * DK + lane;
-      const int off[6] = {qo, qo + 64, QK + qo, QK + qo + 64, 2 * QK + vcol + jc, C + vcol + jc};
-      float val[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int off[NU];
+      off[0] = qo; off[1] = qo + 64; off[2] = QK + qo; off[3] = QK + qo + 64;
+      off[4] = 2 * QK + vcol + jc; off[5] = C + vcol + jc;
+      if constexpr (GT) {
+        off[6] = a.R + g.bh;
+        off[7] = a.R + Hv + g.bh;
+      }
+      float val[NU];
+#pragma unroll
+      for (int i = 0; i < NU; ++i) val[i] = 0.f;
       wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
       DN_MARK(a, l, 10);
       unsigned rounds = 0;
-      ok = poll_words_at<6>(Ub, off, tag, val, 6u, err, &rounds, DN_TS(a, l, 20));
+      ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, &rounds, DN_TS(a, l, 20));
       if (lane == 0) bump_counter(&sm.u_done);
       DN_MARK(a, l, 4);
       if (__all(ok)) {
@@ -712,7 +755,11 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
         const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
         DN_MARK(a, l, 11);
-        const float alpha = sm.gate[l][0], beta = sm.gate[l][1];
+        float alpha = sm.gate[l][0], beta = sm.gate[l][1];
+        if constexpr (GT) {
+          alpha = dn_gate_alpha(val[6], sm.gate[l][0], sm.gate[l][1]);
+          beta = dn_gate_beta(val[7]);
+        }
         const v4f* Q4 = reinterpret_cast<const v4f*>(sm.qk + 32 * pr);
         const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DK + 32 * pr);
         const v4f* A4 = reinterpret_cast<const v4f*>(&apk[PK ? l : 0][32 * pr]);
@@ -824,7 +871,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
   }
 }
 
-template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK>
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT>
 __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
   constexpr int D = COLS_PER_CHUNK * NCHA;
@@ -857,8 +904,8 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   __syncthreads();
   // The two roles run separate loops with the same sequence of three workgroup barriers per
   // layer, so each role's registers are its own.
-  if (wave < NCW) compute_role<BITS, NCHA, NCHC, RA, RC, PK>(sm, a, g, base_tag, tid, lane);
-  else comm_role<BITS, NCHA, NCHC, PK>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
+  if (wave < NCW) compute_role<BITS, NCHA, NCHC, RA, RC, PK, GT>(sm, a, g, base_tag, tid, lane);
+  else comm_role<BITS, NCHA, NCHC, PK, GT>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
 
   // the last workgroup to finish advances the tag base for the next launch
   __syncthreads();
@@ -876,16 +923,19 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
 template <int BITS, int NCHA, int NCHC>
 hipError_t go(const PersistArgs& a, int nwg, hipStream_t st) {
   if (a.alpha_per_key)
-    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, true>), dim3(nwg), dim3(NTHR), 0, st, a);
+    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, true, false>), dim3(nwg), dim3(NTHR), 0, st, a);
+  else if (a.gates)
+    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, false, true>), dim3(nwg), dim3(NTHR), 0, st, a);
   else
-    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, false>), dim3(nwg), dim3(NTHR), 0, st, a);
+    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, false, false>), dim3(nwg), dim3(NTHR), 0, st, a);
   return hipGetLastError();
 }
 
 template <int BITS, int NCHA, int NCHC>
-hipError_t occ(int* blocks, bool pk) {
-  return pk ? hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, true>, NTHR, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false>, NTHR, 0);
+hipError_t occ(int* blocks, bool pk, bool gt) {
+  if (pk) return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, true, false>, NTHR, 0);
+  if (gt) return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false, true>, NTHR, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false, false>, NTHR, 0);
 }
 
 }  // namespace
@@ -900,6 +950,8 @@ static int chunks(int cols, int bits) {
 bool persist_supported(const PersistShape& s, int nwg) {
   if (s.batch != 1 || s.dk != DK || s.dv != 128 || s.K < 1 || s.K > 4) return false;
   if (s.alpha_per_key && s.L > PK_MAXL) return false;
+  if (s.alpha_per_key && s.gates) return false;
+  if (s.gates && 2 * s.Hv > nwg) return false;
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
   const bool inst = s.bits == 8 ? ((na == 2 && nc == 4) || (na == 1 && nc == 1))
                                 : ((na == 1 && nc == 2) || (na == 1 && nc == 1));
@@ -913,9 +965,9 @@ bool persist_supported(const PersistShape& s, int nwg) {
 
 hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu) {
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
-  const bool pk = s.alpha_per_key != 0;
-  if (s.bits == 8) return na == 2 ? occ<8, 2, 4>(blocks_per_cu, pk) : occ<8, 1, 1>(blocks_per_cu, pk);
-  return nc == 2 ? occ<4, 1, 2>(blocks_per_cu, pk) : occ<4, 1, 1>(blocks_per_cu, pk);
+  const bool pk = s.alpha_per_key != 0, gt = s.gates != 0;
+  if (s.bits == 8) return na == 2 ? occ<8, 2, 4>(blocks_per_cu, pk, gt) : occ<8, 1, 1>(blocks_per_cu, pk, gt);
+  return nc == 2 ? occ<4, 1, 2>(blocks_per_cu, pk, gt) : occ<4, 1, 1>(blocks_per_cu, pk, gt);
 }
 
 hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, hipStream_t st) {

@@ -54,6 +54,17 @@ extern "C" {
  * alpha becomes [L][B][Hv][dk]. Single-sequence handles then run the per-layer kernels instead
  * of the whole-stack kernel. */
 #define DN_ALPHA_PER_KEY 2u
+/* Gates computed on the card. The page keeps the two gates (a/b, one output per value head each)
+ * in the engine and passes them in (page "qwen36: run the DeltaNet layer end to end on the card",
+ * section "What the PR does", Backend paragraph); in a stack run by one launch per token each
+ * layer's gates depend on that layer's input, which exists only on the device. With this flag
+ * the in_proj has two more row blocks after z, a (Hv rows) | b (Hv rows), per-row scaled like the
+ * others and not convolved, and value head h of every sequence takes
+ *   alpha = exp(-exp(a_log[h]) * softplus(a[h] + a_bias[h])),   beta = 1 / (1 + exp(-b[h]))
+ * (softplus(y) = log(1 + e^y)). The page gives no formula; this is the decay form of
+ * gated-delta-rule layers, stated as this library's reading. dn_step and dn_prefill then ignore
+ * their alpha and beta arguments, which may be NULL. Not combinable with DN_ALPHA_PER_KEY. */
+#define DN_GATES_ON_DEVICE 4u
 
 typedef struct dn_layer dn_layer; /* opaque */
 
@@ -67,7 +78,7 @@ typedef struct {
   int batch;        /* B: independent sequences stepped together, 1..1024 */
   int n_layers;     /* L: layers in the stack, 1..256 */
   int weight_bits;  /* 8 (int8) or 4 (packed signed int4) */
-  unsigned flags;   /* DN_X_RMSNORM | DN_ALPHA_PER_KEY, or 0 */
+  unsigned flags;   /* DN_X_RMSNORM, DN_ALPHA_PER_KEY, DN_GATES_ON_DEVICE (not with DN_ALPHA_PER_KEY), or 0 */
   float eps_l2;     /* eps inside the sqrt of the q/k L2 norms (1e-6) */
   float eps_rms;    /* eps of the gated RMSNorm and of the input pre-norm (1e-6) */
   float q_scale;    /* multiplies the readout q^T S (1.0) */
@@ -76,7 +87,8 @@ typedef struct {
 /* One layer's weights: DEVICE pointers, BORROWED (the caller keeps them alive and
  * unchanged until dn_destroy), 16-byte aligned.
  *   R = 2*Hk*dk + 2*Hv*dv in_proj rows, ordered q (Hk*dk) | k (Hk*dk) | v (Hv*dv) | z (Hv*dv)
- *   ("qkv ++ z", page "feat(qwen36): the dense trunk places itself", section "What this adds");
+ *   ("qkv ++ z", page "feat(qwen36): the dense trunk places itself", section "What this adds"),
+ *   and with DN_GATES_ON_DEVICE 2*Hv more rows a (Hv) | b (Hv);
  *   C = 2*Hk*dk + Hv*dv convolved channels (q, k, v); z is not convolved.
  * 8-bit weights are signed bytes; 4-bit weights are two per byte, element 2m in the
  * low nibble and 2m+1 in the high nibble, 4-bit two's complement. */
@@ -87,6 +99,8 @@ typedef struct {
   const float *norm_w;  /* [dv] gated RMSNorm weight, shared by all value heads */
   const void  *w_out;   /* [D][Hv*dv] int8, or [D][Hv*dv/2] packed int4 */
   const float *s_out;   /* [D] per-row scale */
+  const float *a_log;   /* [Hv] decay gate parameters with DN_GATES_ON_DEVICE, else ignored (may be NULL) */
+  const float *a_bias;  /* [Hv] */
 } dn_weights;
 
 /* Create a handle for cfg->n_layers layers; w points to n_layers dn_weights (host
@@ -115,7 +129,8 @@ int dn_get_state(dn_layer *h, float *S, float *ring);
  * DEVICE pointers:
  *   x            [B][D]        input of layer 0
  *   alpha, beta  [L][B][Hv]    per-head decay (multiplies S) and delta-rule step size;
- *                              alpha is [L][B][Hv][dk] with DN_ALPHA_PER_KEY
+ *                              alpha is [L][B][Hv][dk] with DN_ALPHA_PER_KEY; not read (may
+ *                              be NULL) with DN_GATES_ON_DEVICE
  *   out          [L][B][D]     out[l] is layer l's output and layer l+1's input;
  *                              out[L-1] is the stack's output. Must not overlap x.
  * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only: returns
@@ -138,7 +153,8 @@ int dn_step(dn_layer *h, const float *x, const float *alpha, const float *beta, 
  * d_model and n_v_heads * d_v multiples of 256.
  * DEVICE pointers:
  *   x            [T][D]        the prompt's inputs of layer 0
- *   alpha, beta  [T][L][Hv]    per token, the gates of dn_step
+ *   alpha, beta  [T][L][Hv]    per token, the gates of dn_step (not read, may be NULL, with
+ *                              DN_GATES_ON_DEVICE)
  *   out          [L][T][D]     out[l] is layer l's output for every token and layer
  *                              l+1's input. Must not overlap x.
  * T = n_tokens >= 1. The handle keeps scratch memory sized for the longest prompt

@@ -36,7 +36,7 @@ def _weights_for(cfg, layers):
     dict(conv_k=0),
     dict(weight_bits=6),
     dict(batch=0),
-    dict(flags=4),                              # an undefined flag bit
+    dict(flags=8),                              # an undefined flag bit
 ])
 def test_invalid_configs_are_rejected(bad):
     base = dict(d_model=128, n_k_heads=2, d_k=32, n_v_heads=4, d_v=32, conv_k=4, batch=1, n_layers=1,
