@@ -34,6 +34,9 @@ BATCHED = {
     # one decay per key channel, alpha [B][Hv][128]
     "b_perkey": gi.custom("b_perkey", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=5,
                           n_tokens=5, flags=gi.DN_ALPHA_PER_KEY, ring_std=1.0),
+    # 48 value heads of 128 over 16 key heads: in_proj 16384 rows, out_proj K = 6144
+    "b_heads48": gi.custom("b_heads48", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=48, d_v=128, batch=4,
+                           n_tokens=3, ring_std=1.0),
 }
 
 

@@ -49,6 +49,10 @@ SMALL = {
     "perkey_stack": gi.custom("perkey_stack", d_model=512, n_k_heads=2, d_k=128, n_v_heads=4, d_v=128,
                               n_layers=3, n_tokens=6, flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY,
                               ring_std=1.0),
+    # 48 value heads of 128 over 16 key heads (the other engine's layer the page names): more
+    # value heads than the whole-stack kernel takes, so the per-layer kernels run it
+    "heads48": gi.custom("heads48", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=48, d_v=128, n_tokens=4,
+                         ring_std=1.0),
 }
 
 
