@@ -61,6 +61,10 @@ constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
 #define DN_PREFETCH_INFLIGHT 2
 #endif
 static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
+// The last DN_PREFETCH_TAIL in_proj row-chunk loads of a layer are issued without the throttle.
+#ifndef DN_PREFETCH_TAIL
+#define DN_PREFETCH_TAIL 2
+#endif
 
 // s_waitcnt with vmcnt <= n and the other counters unconstrained
 #define DN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
@@ -414,7 +418,8 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       const int r = g.a_row0 + i;
 #pragma unroll
       for (int k = 0; k < NCHA; ++k) {
-        if ((i * NCHA + k) >= DN_PREFETCH_INFLIGHT) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
+        if ((i * NCHA + k) >= DN_PREFETCH_INFLIGHT && (i * NCHA + k) < RA * NCHA - DN_PREFETCH_TAIL)
+          DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
         if (r < g.a_row_end)
           wa[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_in) + lane + 64 * k);
         else
