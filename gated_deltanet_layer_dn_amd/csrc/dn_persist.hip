@@ -754,11 +754,6 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         sm.qk[lane + 64] = val[1];
         sm.qk[DK + lane] = val[2];
         sm.qk[DK + lane + 64] = val[3];
-        // L2 norms in double, eps inside the sqrt
-        const double sq = wave_total_d((double)val[0] * val[0] + (double)val[1] * val[1]);
-        const double sk = wave_total_d((double)val[2] * val[2] + (double)val[3] * val[3]);
-        const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
-        const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
         DN_MARK(a, l, 11);
         float alpha = sm.gate[l][0], beta = sm.gate[l][1];
         if constexpr (GT) {
@@ -771,6 +766,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         float sv[32];
         float kvp = 0.f;
         wait_counter(&sm.s_ready, NCW * (l + 1), &sm.abort_flag);  // the slice has landed in LDS
+        // the sums run over the raw q and k; the 1/norm factors multiply the finished sums (and the
+        // delta), so the fp64 norm reductions below can overlap the state arithmetic
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const v4f kk = K4[q], st = sm.sbuf[64 * q + lane];
@@ -779,11 +776,16 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             sv[4 * q + e] = av[e] * st[e];  // decay
-            kvp = fmaf(sv[4 * q + e], kk[e] * kn, kvp);
+            kvp = fmaf(sv[4 * q + e], kk[e], kvp);
           }
         }
-        const float kv = quad_sum(kvp);  // (decayed S)^T k of column jc
-        const float dl = beta * (val[4] - kv);
+        // L2 norms in double, eps inside the sqrt (independent of the loop above, so the two overlap)
+        const double sq = wave_total_d((double)val[0] * val[0] + (double)val[1] * val[1]);
+        const double sk = wave_total_d((double)val[2] * val[2] + (double)val[3] * val[3]);
+        const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
+        const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
+        const float kv = kn * quad_sum(kvp);  // (decayed S)^T k^ of column jc
+        const float dk = beta * (val[4] - kv) * kn;  // delta times 1/|k|
         DN_MARK(a, l, 13);
         float op = 0.f;
 #pragma unroll
@@ -791,11 +793,11 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
           const v4f qq = Q4[q], kk = K4[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sv[4 * q + e] = fmaf(kk[e] * kn, dl, sv[4 * q + e]);  // delta rule write
-            op = fmaf(sv[4 * q + e], qq[e] * qn, op);             // readout of the updated state
+            sv[4 * q + e] = fmaf(kk[e], dk, sv[4 * q + e]);  // delta rule write
+            op = fmaf(sv[4 * q + e], qq[e], op);             // readout of the updated state
           }
         }
-        const float o = quad_sum(op);
+        const float o = qn * quad_sum(op);
         // park the updated slice in LDS; it is written back while phase C runs
 #pragma unroll
         for (int q = 0; q < 8; ++q) sm.sbuf[q * 64 + lane] = v4f{sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]};
