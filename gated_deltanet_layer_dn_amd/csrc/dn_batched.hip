@@ -351,17 +351,19 @@ __global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
 
 // Finish the rows: add the K-range partial sums in order, row scale, input pre-norm factor, and for
 // rows r < C the causal conv over the history (oldest first) plus SiLU, advancing the history.
+template <int NB>
 __global__ __launch_bounds__(256) void k_bepi(const BEpiArgs a) {
   const int r = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   if (r >= a.M) return;
-  // partials are requested sixteen at a time before they are added (in a fixed order)
+  // partials are requested NB at a time (NB >= the count when it is at most 16) before they are
+  // added, in a fixed order
   float sum = 0.f;
-  for (int k0 = 0; k0 < a.KS; k0 += 16) {
-    float pv[16];
+  for (int k0 = 0; k0 < a.KS; k0 += NB) {
+    float pv[NB];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) pv[k] = k0 + k < a.KS ? a.part[((size_t)(k0 + k) * a.B + b) * a.M + r] : 0.f;
+    for (int k = 0; k < NB; ++k) pv[k] = k0 + k < a.KS ? a.part[((size_t)(k0 + k) * a.B + b) * a.M + r] : 0.f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < NB; ++k)
       if (k0 + k < a.KS) sum += pv[k];
   }
   float scale = a.s[r];
@@ -600,7 +602,10 @@ hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st) 
 }
 
 hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_bepi, dim3((a.M + 255) / 256, a.B), dim3(256), 0, st, a);
+  const dim3 grid((a.M + 255) / 256, a.B);
+  if (a.KS <= 4) hipLaunchKernelGGL(k_bepi<4>, grid, dim3(256), 0, st, a);
+  else if (a.KS <= 8) hipLaunchKernelGGL(k_bepi<8>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_bepi<16>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
