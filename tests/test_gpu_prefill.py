@@ -160,3 +160,34 @@ def test_prefill_rejects_unsupported_shapes():
             run_gpu(st, stream, T=1)
         finally:
             st.close()
+
+
+def test_prefill_arguments_are_checked():
+    """An empty prompt, a NULL input or gate array, and an output overlapping the input are refused
+    before anything is launched; the handle then still prefills and matches the oracle."""
+    import gated_deltanet_layer_dn_amd as dn
+    cfg = gi.custom("pf_args", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, n_layers=2, n_tokens=4,
+                    flags=gi.DN_X_RMSNORM, ring_std=1.0)
+    layers, stream = gi.generate(cfg)
+    st = make_stack(cfg, layers)
+    try:
+        T, D, L = 4, cfg.d_model, cfg.n_layers
+        x, a, b = _prompt(stream, T)
+        out = torch.empty((L, T, D), device="cuda:0")
+        for n in (0, -3):
+            assert dn.dn_prefill(st.h, x, n, a, b, out) == dn.DN_E_INVAL
+        assert dn.dn_prefill(st.h, None, T, a, b, out) == dn.DN_E_INVAL
+        assert dn.dn_prefill(st.h, x, T, None, b, out) == dn.DN_E_INVAL
+        assert dn.dn_prefill(st.h, x, T, a, None, out) == dn.DN_E_INVAL
+        assert dn.dn_prefill(st.h, x, T, a, b, None) == dn.DN_E_INVAL
+        buf = torch.zeros((L + 1) * T * D, device="cuda:0")
+        assert dn.dn_prefill(st.h, buf[:T * D], T, a, b, buf[T * D // 2:]) == dn.DN_E_INVAL
+        assert dn.dn_prefill(st.h, x, T, a, b, out) == dn.DN_OK
+        torch.cuda.synchronize()
+        gS, _ = st.get_state()
+    finally:
+        st.close()
+    ref_out, ref_S, _ = orc.run(cfg, layers, stream)
+    gpre = out.cpu().numpy().transpose(1, 0, 2)[:, :, None, :]
+    assert max(out_err(gpre[:, l], ref_out[:, l]) for l in range(L)) <= OUT_TOL
+    assert state_err(gS.cpu().numpy(), ref_S) <= STATE_TOL
