@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the decode token runs in the HIP kernels of
 ``libdn.so``. PyTorch provides device memory and streams. The functions carry the C ABI's
-names (``dn_create``, ``dn_set_state``, ``dn_get_state``, ``dn_step``, ``dn_destroy``);
+names (``dn_create``, ``dn_set_state``, ``dn_get_state``, ``dn_step``, ``dn_destroy``,
+``dn_prefill``);
 ``DeltaNetStack`` wraps them. Loading fails loudly when the library is not built.
 """
 from __future__ import annotations
@@ -83,7 +84,7 @@ def _check(rc: int, what: str):
         raise DNError(rc, what)
 
 
-# --- the five calls ------------------------------------------------------------------------
+# --- the six calls -------------------------------------------------------------------------
 
 def dn_create(cfg: dn_config, weights: list[dn_weights]) -> int:
     arr = (dn_weights * len(weights))(*weights)
