@@ -63,7 +63,7 @@ constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
 static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
 // The last DN_PREFETCH_TAIL in_proj row-chunk loads of a layer are issued without the throttle.
 #ifndef DN_PREFETCH_TAIL
-#define DN_PREFETCH_TAIL 2
+#define DN_PREFETCH_TAIL 4
 #endif
 
 // s_waitcnt with vmcnt <= n and the other counters unconstrained
@@ -225,6 +225,19 @@ struct Smem {
   int s_ready;                 // compute waves whose chunk of the layer's state slice is in LDS
   int abort_flag;
 };
+
+// Workgroup barrier for the per-layer hand-over of LDS data between the two wave roles. Unlike
+// __syncthreads(), whose fence waits for every outstanding global access of the wave (loads
+// included), it waits only for this wave's LDS accesses: the compute waves' weight prefetches stay
+// in flight across it. No global data passes between the waves of a workgroup through these
+// barriers (the hand-offs carry their own tags, and the state slice's copy into LDS is waited for
+// explicitly).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Wait (within the workgroup) until an LDS progress counter reaches `target` or the workgroup
 // aborts. The waves that advance the counter never wait on the waiting wave, so this ends.
@@ -470,10 +483,10 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
   load_c(0);
   for (int l = 0; l < a.L; ++l) {
     const unsigned tag = base_tag + (unsigned)l;
-    __syncthreads();  // (1) raw x staged
+    lds_barrier();  // (1) raw x staged
     if (sm.abort_flag) break;
     split_x<BITS, D>(sm, a, tid);
-    __syncthreads();  // (2) x split staged
+    lds_barrier();  // (2) x split staged
     if (tid == 0) DN_MARK(a, l, 2);
     {
       // phase A: in_proj + conv + SiLU
@@ -513,7 +526,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       if (l + 1 < a.L) load_a(l + 1);
       if (tid == 0) DN_MARK(a, l, 28);
     }
-    __syncthreads();  // (3) gated readout staged
+    lds_barrier();  // (3) gated readout staged
     if (sm.abort_flag) break;
     if (tid == 0) DN_MARK(a, l, 7);
     {
@@ -709,11 +722,11 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       if (!__all(ok)) fail();
       if (cw == 0) DN_MARK(a, l, 1);
     }
-    __syncthreads();  // (1)
+    lds_barrier();  // (1)
     if (cw == 0) DN_MARK(a, l, 9);
     if (sm.abort_flag) break;
     split_x<BITS, D>(sm, a, tid);
-    __syncthreads();  // (2)
+    lds_barrier();  // (2)
 
     if (runs_gate) {
       // gate row R + wg on the staged x, published as in_proj output; then the next layer's row
@@ -873,7 +886,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       if (lane == 0) sm.stat[9 + cw] = sy;
     }
     if (!__all(ok)) fail();
-    __syncthreads();  // (3)
+    lds_barrier();  // (3)
     if (sm.abort_flag) break;
   }
 }
