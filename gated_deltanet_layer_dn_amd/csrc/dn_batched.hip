@@ -53,6 +53,17 @@ __device__ __forceinline__ int nib4(unsigned h16) {
   return (int)(((y << 4) & 0x00F000F0u) | ((y & 0x00F000F0u) << 8));
 }
 
+// Workgroup barrier over LDS data only. __syncthreads() carries a fence that waits for every
+// outstanding global access of the wave (vmcnt counts loads too), which would make the next chunk's
+// copies and weight loads complete before the current chunk's MFMAs start; this waits only for the
+// wave's LDS accesses, and each wave waits for its own direct-to-LDS copies with an explicit vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Split v (|v| <= 127 s1) into three int8 terms.
 __device__ __forceinline__ void split3(float v, float inv1, float s1, float inv2, float s2, float inv3, int& h,
                                        int& m, int& l) {
@@ -136,8 +147,10 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
   constexpr int FRAGS = 3 * KSC * 4 * 64;  // v4i per chunk block (24 KB)
   constexpr int PER_WAVE = FRAGS / 64 / 4;  // 1 KB direct-to-LDS loads per wave per chunk
   static_assert(NCHUNK % 2 == 0, "chunks run in pairs");
-  __shared__ v4i xs[2][FRAGS];
-  __shared__ float scl[2][NT];
+  // two separate buffers, so that the compiler can tell the copies into one from the reads of the
+  // other and keeps the next chunk's copies in flight while the current chunk is read
+  __shared__ v4i xs0[FRAGS], xs1[FRAGS];
+  __shared__ float scl0[NT], scl1[NT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rb = blockIdx.x, ks = blockIdx.y, nb = blockIdx.z;
   const int M = a.M, K = a.K, B = a.B;
@@ -165,16 +178,16 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
         }
       }
   };
-  // copy chunk c's fragments and scales into LDS buffer c % 2
-  auto stage = [&](int c) {
+  // copy chunk c's fragments and scales into LDS buffer X, S
+  auto stage = [&](int c, v4i* X, float* S) {
     const size_t blk = (size_t)nb * NC + c0 + c;
     const v4i* src = static_cast<const v4i*>(a.xs) + blk * FRAGS;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;  // 1 KB piece
-      __builtin_amdgcn_global_load_lds(src + q * 64 + lane, &xs[c & 1][q * 64], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + q * 64 + lane, X + q * 64, 16, 0, 0);
     }
-    if (wave == 0) __builtin_amdgcn_global_load_lds(a.sc + blk * NT + lane, &scl[c & 1][0], 4, 0, 0);
+    if (wave == 0) __builtin_amdgcn_global_load_lds(a.sc + blk * NT + lane, S, 4, 0, 0);
   };
 
   float facc[MF][4][4];
@@ -186,12 +199,12 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
       for (int v = 0; v < 4; ++v) facc[mf][f][v] = 0.f;
 
   Frag A0, A1;
-  stage(0);
+  stage(0, xs0, scl0);
   load_a(0, A0);
-  // one chunk: request the next chunk, wait for this one, run its MFMAs
-  auto chunk = [&](int c, const Frag& A, Frag& Anext) {
+  // one chunk: request the next chunk into the other buffer, wait for this one, run its MFMAs
+  auto chunk = [&](int c, const Frag& A, Frag& Anext, const v4i* X, const float* S, v4i* Xn, float* Sn) {
     if (c + 1 < NCHUNK) {
-      stage(c + 1);
+      stage(c + 1, Xn, Sn);
       load_a(c + 1, Anext);
       // loads issued after this chunk's: the next chunk's pieces (+ its scales on wave 0) and weights
       if (wave == 0) DN_VMCNT_WAIT(PER_WAVE + 1 + KSC * MF);
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
     } else {
       DN_VMCNT_WAIT(0);
     }
-    __syncthreads();  // every wave's pieces of chunk c are in LDS
+    lds_barrier();  // every wave's pieces of chunk c are in LDS
     v4i acc[3][MF][4];
 #pragma unroll
     for (int t = 0; t < 3; ++t)
@@ -207,7 +220,6 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
       for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[t][mf][f] = v4i{0, 0, 0, 0};
-    const v4i* X = xs[c & 1];
 #pragma unroll
     for (int s = 0; s < KSC; ++s)
 #pragma unroll
@@ -219,26 +231,28 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
           for (int mf = 0; mf < MF; ++mf)
             acc[t][mf][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s][mf], bf, acc[t][mf][f], 0, 0, 0);
         }
-    // fold the chunk into the float sums with each sequence's scale (column lane % 16 of fragment f)
+    // fold the chunk into the float sums with each sequence's scale (column lane % 16 of fragment f);
+    // a chunk's sums are below 2^22 in magnitude: exact in fp32, combined in fp32
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const double s1b = (double)scl[c & 1][16 * f + (lane & 15)] * (BITS == 4 ? 1.0 / 16.0 : 1.0);
+      const float s1b = S[16 * f + (lane & 15)] * (BITS == 4 ? 1.0f / 16.0f : 1.0f);
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const double d = (double)acc[0][mf][f][v] +
-                           ((double)acc[1][mf][f][v] + (double)acc[2][mf][f][v] * (1.0 / 254.0)) * (1.0 / 254.0);
-          facc[mf][f][v] += (float)(s1b * d);
+          const float d = (float)acc[0][mf][f][v] +
+                          fmaf((float)acc[2][mf][f][v], 1.0f / 254.0f, (float)acc[1][mf][f][v]) * (1.0f / 254.0f);
+          facc[mf][f][v] = fmaf(s1b, d, facc[mf][f][v]);
         }
     }
-    __syncthreads();  // buffer c % 2 is refilled two chunks later
+    lds_barrier();  // buffer c % 2 is refilled two chunks later
   };
-  // rolled loop over chunk pairs (ping-pong weight buffers), so only two chunks of weights are live
+  // rolled loop over chunk pairs (ping-pong weight and LDS buffers), so only two chunks of weights
+  // are live
 #pragma clang loop unroll(disable)
   for (int c = 0; c < NCHUNK; c += 2) {
-    chunk(c, A0, A1);
-    chunk(c + 1, A1, A0);
+    chunk(c, A0, A1, xs0, scl0, xs1, scl1);
+    chunk(c + 1, A1, A0, xs1, scl1, xs0, scl0);
   }
 
   // partial sums: lane holds rows r0 + 16 mf + 4 (lane/16) .. +3 of sequence nb*64 + 16 f + lane%16
