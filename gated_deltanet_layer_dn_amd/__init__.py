@@ -101,19 +101,23 @@ def dn_get_state(h: int, S, ring=None) -> None:
     _check(lib().dn_get_state(h, _ptr(S), _ptr(ring)), "dn_get_state")
 
 
+def _stream(stream, ref):
+    """The stream handle to pass: the given one, else the current stream of ref's device."""
+    if stream is None:
+        dev = ref.device if isinstance(ref, torch.Tensor) and ref.is_cuda else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
 def dn_step(h: int, x, alpha, beta, out, stream=None) -> int:
     """Enqueue one token; returns the C return code (no exception, so callers can test errors)."""
-    s = torch.cuda.current_stream().cuda_stream if stream is None else (
-        stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
-    return lib().dn_step(h, _ptr(x), _ptr(alpha), _ptr(beta), _ptr(out), s)
+    return lib().dn_step(h, _ptr(x), _ptr(alpha), _ptr(beta), _ptr(out), _stream(stream, out))
 
 
 def dn_prefill(h: int, x, n_tokens: int, alpha, beta, out, stream=None) -> int:
     """Enqueue a prompt of n_tokens tokens (x [T][D], alpha/beta [T][L][Hv], out [L][T][D]);
     returns the C return code."""
-    s = torch.cuda.current_stream().cuda_stream if stream is None else (
-        stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
-    return lib().dn_prefill(h, _ptr(x), int(n_tokens), _ptr(alpha), _ptr(beta), _ptr(out), s)
+    return lib().dn_prefill(h, _ptr(x), int(n_tokens), _ptr(alpha), _ptr(beta), _ptr(out), _stream(stream, out))
 
 
 def dn_destroy(h: int) -> None:

@@ -77,6 +77,31 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Makes the handle's device current for the duration of a call and restores the caller's current
+// device on every return path, so that no entry point changes the calling thread's device.
+class DeviceScope {
+ public:
+  explicit DeviceScope(int dev) {
+    if (hipGetDevice(&prev_) != hipSuccess) {
+      prev_ = -1;
+      ok_ = false;
+      return;
+    }
+    ok_ = prev_ == dev || hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceScope() {
+    int cur = -1;
+    if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_) (void)hipSetDevice(prev_);
+  }
+  bool ok() const { return ok_; }
+  DeviceScope(const DeviceScope&) = delete;
+  DeviceScope& operator=(const DeviceScope&) = delete;
+
+ private:
+  int prev_ = -1;
+  bool ok_ = false;
+};
+
 int validate(const dn_config* c) {
   if (!c) return DN_E_INVAL;
   if (c->weight_bits != 8 && c->weight_bits != 4) return DN_E_INVAL;
@@ -284,11 +309,13 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
     return DN_E_DEVICE;
   }
   if (int rc = setup_persist(h); rc != DN_OK) {
+    (void)hipGetLastError();
     free_all(h);
     delete h;
     return rc;
   }
   if (int rc = setup_batched(h); rc != DN_OK) {
+    (void)hipGetLastError();
     free_all(h);
     delete h;
     return rc;
@@ -309,7 +336,8 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
 
 DN_API int dn_set_state(dn_layer* h, const float* S, const float* ring) {
   if (!h || !S) return DN_E_INVAL;
-  if (hipSetDevice(h->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return DN_E_DEVICE;
+  DeviceScope dev(h->device);
+  if (!dev.ok() || hipDeviceSynchronize() != hipSuccess) return DN_E_DEVICE;
   const size_t L = h->cfg.n_layers;
   if (h->persist) {
     if (hipMemcpy(h->stage, S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) return DN_E_DEVICE;
@@ -332,7 +360,8 @@ DN_API int dn_set_state(dn_layer* h, const float* S, const float* ring) {
 
 DN_API int dn_get_state(dn_layer* h, float* S, float* ring) {
   if (!h || !S) return DN_E_INVAL;
-  if (hipSetDevice(h->device) != hipSuccess) return DN_E_DEVICE;
+  DeviceScope dev(h->device);
+  if (!dev.ok()) return DN_E_DEVICE;
   (void)hipDeviceSynchronize();  // a failed step may have left an error; copy what the device holds
   (void)hipGetLastError();
   const size_t L = h->cfg.n_layers;
@@ -405,6 +434,8 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
   if (ob < xb + sizeof(float) * B * D && xb < ob + sizeof(float) * L * B * D) return DN_E_INVAL;
   ++h->steps;
   if (h->fault_step > 0 && h->steps == h->fault_step) return fail(h, DN_E_FAULT);
+  DeviceScope dev(h->device);
+  if (!dev.ok()) return fail(h, DN_E_DEVICE);
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   if (h->persist) {
     if (host_err(h)) return fail(h, DN_E_DEVICE);  // a completed launch reported a stalled hand-off
@@ -546,9 +577,13 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
   const char* xb = reinterpret_cast<const char*>(x);
   const char* ob = reinterpret_cast<const char*>(out);
   if (ob < xb + sizeof(float) * T * D && xb < ob + sizeof(float) * L * T * D) return DN_E_INVAL;
-  if (hipSetDevice(h->device) != hipSuccess) return fail(h, DN_E_DEVICE);
+  DeviceScope dev(h->device);
+  if (!dev.ok()) return fail(h, DN_E_DEVICE);
   if (h->persist && host_err(h)) return fail(h, DN_E_DEVICE);
-  if (int rc = pf_reserve(h, n_tokens); rc != DN_OK) return rc;
+  if (int rc = pf_reserve(h, n_tokens); rc != DN_OK) {
+    (void)hipGetLastError();  // the failed allocation's error; the handle stays usable
+    return rc;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   const int QK = c.n_k_heads * c.d_k, V = h->V, R = h->R, K = c.conv_k;
   const int nch = (n_tokens + dn::PF_CT - 1) / dn::PF_CT;
@@ -607,7 +642,7 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
 
 DN_API void dn_destroy(dn_layer* h) {
   if (!h) return;
-  (void)hipSetDevice(h->device);
+  DeviceScope dev(h->device);
   (void)hipDeviceSynchronize();
 #ifdef DN_PHASE_TIMERS
   if (const char* path = std::getenv("DN_PHASE_TIMERS"); path && h->timers) {

@@ -18,6 +18,10 @@
  *
  * All sizes are element counts. All matrices are row-major and C-contiguous.
  * The library never synchronises the device inside dn_step.
+ *
+ * Devices. A handle lives on the HIP device that was current at dn_create. Every other call
+ * makes that device current for its own duration and restores the caller's current device
+ * before it returns; a stream passed in must belong to the handle's device.
  */
 #ifndef DN_H
 #define DN_H

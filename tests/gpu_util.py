@@ -11,8 +11,8 @@ OUT_TOL = 2e-3
 STATE_TOL = 1e-3
 
 
-def make_stack(cfg, layers, S0=None, ring0=None):
-    st = dn.DeltaNetStack.from_config(cfg, layers)
+def make_stack(cfg, layers, S0=None, ring0=None, dev="cuda:0"):
+    st = dn.DeltaNetStack.from_config(cfg, layers, device=dev)
     S = np.stack([l.S0 for l in layers]) if S0 is None else S0
     R = np.stack([l.ring0 for l in layers]) if ring0 is None else ring0
     st.set_state(np.ascontiguousarray(S, np.float32), np.ascontiguousarray(R, np.float32))

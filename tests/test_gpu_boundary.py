@@ -155,3 +155,26 @@ def test_destroy_returns_device_memory():
         dn.dn_destroy(h)
         assert torch.cuda.mem_get_info()[0] >= free0 - 4 * 2**20
     wts.close()
+
+
+@pytest.mark.skipif(torch.cuda.device_count() < 2, reason="needs a second device to tell the devices apart")
+def test_calls_keep_the_callers_current_device():
+    """A handle created on device 1 is stepped, read and written while device 0 is current; every
+    call runs on the handle's device and leaves device 0 current."""
+    layers, stream = gi.generate(CFG)
+    prev = torch.cuda.current_device()
+    try:
+        torch.cuda.set_device(1)
+        st = make_stack(CFG, layers, dev="cuda:1")
+        x, a, b = upload_stream(stream, dev="cuda:1")
+        out = st.new_out()
+        torch.cuda.set_device(0)
+        s1 = torch.cuda.current_stream(1)
+        st.step(x[0], a[0], b[0], out, stream=s1)
+        assert torch.cuda.current_device() == 0
+        gS, _ = st.get_state()
+        assert torch.cuda.current_device() == 0 and np.all(np.isfinite(gS.cpu().numpy()))
+        st.close()
+        assert torch.cuda.current_device() == 0
+    finally:
+        torch.cuda.set_device(prev)
