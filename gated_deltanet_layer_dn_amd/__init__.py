@@ -21,6 +21,7 @@ DN_OK, DN_E_INVAL, DN_E_NOMEM, DN_E_DEVICE, DN_E_DISABLED, DN_E_FAULT = 0, -1, -
 DN_X_RMSNORM = 1
 DN_ALPHA_PER_KEY = 2  # alpha [L][B][Hv][dk]: one decay per key channel
 DN_GATES_ON_DEVICE = 4  # gates from two more in_proj rows per value head; alpha/beta not read
+DN_PREFILL_MAX_TOKENS = 65535  # prompt tokens per dn_prefill call
 EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy", "dn_prefill")
 
 _ERR = {DN_OK: "ok", DN_E_INVAL: "invalid argument", DN_E_NOMEM: "out of device memory",

@@ -567,7 +567,7 @@ int pf_reserve(dn_layer* h, int T) {
 
 DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* alpha, const float* beta, float* out,
                       void* hip_stream) {
-  if (!h || !x || !out || n_tokens < 1) return DN_E_INVAL;
+  if (!h || !x || !out || n_tokens < 1 || n_tokens > DN_PREFILL_MAX_TOKENS) return DN_E_INVAL;
   if (!h->gates && (!alpha || !beta)) return DN_E_INVAL;
   if (h->disabled) return DN_E_DISABLED;
   const dn_config& c = h->cfg;

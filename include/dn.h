@@ -161,11 +161,13 @@ int dn_step(dn_layer *h, const float *x, const float *alpha, const float *beta, 
  *                              DN_GATES_ON_DEVICE)
  *   out          [L][T][D]     out[l] is layer l's output for every token and layer
  *                              l+1's input. Must not overlap x.
- * T = n_tokens >= 1. The handle keeps scratch memory sized for the longest prompt
- * seen so far (allocated here, freed by dn_destroy).
+ * T = n_tokens, 1..DN_PREFILL_MAX_TOKENS per call; a longer prompt goes in several calls, each
+ * continuing from the state the previous one left. The handle keeps scratch memory sized for the
+ * longest prompt seen so far (allocated here, freed by dn_destroy).
  * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only. Returns DN_OK,
  * DN_E_INVAL (shape or arguments not supported; the handle stays usable), DN_E_NOMEM,
  * DN_E_DISABLED or DN_E_DEVICE (latches the handle off, as a failed dn_step does). */
+#define DN_PREFILL_MAX_TOKENS 65535
 int dn_prefill(dn_layer *h, const float *x, int n_tokens, const float *alpha, const float *beta, float *out,
                void *hip_stream);
 

@@ -48,3 +48,13 @@ def test_binding_names_match():
     assert set(dn.EXPORTED) == _declared()
     for n in dn.EXPORTED:
         assert callable(getattr(dn, n))
+
+
+def test_binding_constants_match_the_header():
+    """Every #define of include/dn.h has the same value in the binding."""
+    import gated_deltanet_layer_dn_amd as dn
+    src = re.sub(r"/\*.*?\*/", "", open(HDR).read(), flags=re.S)
+    defs = dict(re.findall(r"^#define\s+(DN_\w+)\s+(-?\d+)u?\s*$", src, flags=re.M))
+    assert {"DN_OK", "DN_E_INVAL", "DN_X_RMSNORM", "DN_GATES_ON_DEVICE", "DN_PREFILL_MAX_TOKENS"} <= set(defs)
+    for name, val in defs.items():
+        assert getattr(dn, name) == int(val), name

@@ -163,7 +163,7 @@ def test_prefill_rejects_unsupported_shapes():
 
 
 def test_prefill_arguments_are_checked():
-    """An empty prompt, a NULL input or gate array, and an output overlapping the input are refused
+    """An empty or over-long prompt, a NULL input or gate array, and an output overlapping the input are refused
     before anything is launched; the handle then still prefills and matches the oracle."""
     import gated_deltanet_layer_dn_amd as dn
     cfg = gi.custom("pf_args", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, n_layers=2, n_tokens=4,
@@ -174,7 +174,7 @@ def test_prefill_arguments_are_checked():
         T, D, L = 4, cfg.d_model, cfg.n_layers
         x, a, b = _prompt(stream, T)
         out = torch.empty((L, T, D), device="cuda:0")
-        for n in (0, -3):
+        for n in (0, -3, dn.DN_PREFILL_MAX_TOKENS + 1):
             assert dn.dn_prefill(st.h, x, n, a, b, out) == dn.DN_E_INVAL
         assert dn.dn_prefill(st.h, None, T, a, b, out) == dn.DN_E_INVAL
         assert dn.dn_prefill(st.h, x, T, None, b, out) == dn.DN_E_INVAL
