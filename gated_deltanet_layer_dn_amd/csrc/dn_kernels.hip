@@ -408,6 +408,11 @@ __global__ __launch_bounds__(256) void k_gates(const GateArgs a) {
 hipError_t launch_gates(const GateArgs& a, int bits, hipStream_t st) {
   if (a.N < 1 || a.D < 1 || a.D > 16384 || a.D % (bits == 8 ? 16 : 32)) return hipErrorInvalidValue;
   const size_t lds = sizeof(float) * a.D;
+  // the widest rows (64 KiB of x) with the kernel's static LDS exceed the default per-launch limit
+  const void* fn = bits == 8 ? reinterpret_cast<const void*>(&k_gates<8>) : reinterpret_cast<const void*>(&k_gates<4>);
+  if (lds > 48 * 1024)
+    if (hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); e != hipSuccess)
+      return e;
   if (bits == 8) hipLaunchKernelGGL(k_gates<8>, dim3(a.N), dim3(256), lds, st, a);
   else hipLaunchKernelGGL(k_gates<4>, dim3(a.N), dim3(256), lds, st, a);
   return hipGetLastError();

@@ -92,3 +92,27 @@ def test_batch_at_the_sequence_limit(env, path, capfd, monkeypatch):
     eh = state_err(gH.cpu().numpy(), ref_H)
     print(f"[limits] {cfg.name} ({path}): out {e:.2e} state {es:.2e} ring {eh:.2e}", flush=True)
     assert e <= OUT_TOL and es <= STATE_TOL and eh <= STATE_TOL
+
+
+@pytest.mark.parametrize("name,kw", [
+    # the widest model (16384 columns): in_proj rows and gate rows of 16 KiB, out_proj of 16384 rows
+    ("lim_D", dict(d_model=16384, n_k_heads=1, d_k=16, n_v_heads=1, d_v=16)),
+    # the widest readout: 64 value heads of 256 columns (out_proj rows of 16384 columns)
+    ("lim_V", dict(d_model=256, n_k_heads=1, d_k=16, n_v_heads=64, d_v=256)),
+])
+def test_widths_at_the_limit(name, kw):
+    """The per-layer kernels at the largest widths a handle takes, with the pre-norm and the gates
+    computed on the card, two sequences, against the oracle."""
+    cfg = gi.custom(name, batch=2, n_tokens=3, flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE, ring_std=1.0, **kw)
+    layers, stream = gi.generate(cfg)
+    print(f"[limits] {name}: D={cfg.d_model} V={cfg.n_v_heads * cfg.d_v}", flush=True)
+    ref_out, ref_S, ref_H = orc.run(cfg, layers, stream)
+    st = make_stack(cfg, layers)
+    try:
+        gout = run_gpu(st, stream)
+        gS, gH = st.get_state()
+    finally:
+        st.close()
+    e, es, eh = out_err(gout, ref_out), state_err(gS.cpu().numpy(), ref_S), state_err(gH.cpu().numpy(), ref_H)
+    print(f"[limits] {name}: out {e:.2e} state {es:.2e} ring {eh:.2e}", flush=True)
+    assert e <= OUT_TOL and es <= STATE_TOL and eh <= STATE_TOL
