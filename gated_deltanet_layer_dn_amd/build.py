@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dn_kernels.hip", "dn_persist.hip", "dn_batched.hip", "dn_prefill.hip", "dn_api.cpp"]
+SOURCES = ["dn_kernels.hip", "dn_persist.hip", "dn_batched.hip", "dn_prefill.hip", "dn_lt.cpp", "dn_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
@@ -19,6 +19,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
+# the prefill projections with 8-bit weights call the library's int8 GEMMs
+LIBS = ["-lhipblaslt"]
 
 
 def sources():
@@ -30,7 +32,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     instrumented build written to `out`)."""
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                                                          "-o", tmp] + sources()
+                                                          "-o", tmp] + sources() + LIBS
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -67,6 +67,10 @@ struct dn_layer {
   float* pf_ring = nullptr;                // the new conv history of a layer
   float* pf_al = nullptr;                  // [T][Hv] gates computed on the card
   float* pf_be = nullptr;
+  // 8-bit prefill projections as library int8 GEMMs (created at the first prefill)
+  dn::LtCtx* lt = nullptr;
+  bool lt_tried = false;
+  bool pf_own_gemm = false;                // DN_PREFILL_OWN_GEMM=1: always the hand-written GEMM
   bool disabled = false;
   long steps = 0;
   long fault_step = 0;    // 1-based step to fail (0 = never)
@@ -158,6 +162,8 @@ void free_all(dn_layer* h) {
   dfree(h->pf_al);
   dfree(h->pf_be);
   h->pf_cap = 0;
+  dn::lt_destroy(h->lt);
+  h->lt = nullptr;
 }
 
 // GEMM shape for an M x K projection: the all-loads-up-front kernel with 256-column K ranges and
@@ -327,6 +333,7 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   }
   if (const char* e = std::getenv("DN_FAULT_STEP")) h->fault_step = std::atol(e);
   if (const char* e = std::getenv("DN_SYNC_DEBUG")) h->sync_debug = std::atoi(e) != 0;
+  if (const char* e = std::getenv("DN_PREFILL_OWN_GEMM")) h->pf_own_gemm = std::atoi(e) != 0;
   if (const char* e = std::getenv("DN_VERBOSE"); e && std::atoi(e) != 0)
     std::fprintf(stderr, "[dn] handle: %d layer(s), batch %d: %s\n", cfg->n_layers, cfg->batch,
                  h->persist ? "whole-stack kernel" : h->batched ? "batched kernels" : "per-layer kernels");
@@ -535,7 +542,11 @@ int pf_reserve(dn_layer* h, int T) {
   const size_t D = c.d_model, V = h->V, R = h->R;
   const size_t nb = ((size_t)T + 63) / 64, nch = ((size_t)T + dn::PF_CT - 1) / dn::PF_CT;
   const size_t ncmax = std::max(D, V) / 128;
-  const size_t part = (size_t)T * std::max((D / pf_kr((int)D)) * R, (V / pf_kr((int)V)) * D);
+  // scratch of both GEMM paths: K-range partial sums (hand-written GEMM) or the three terms' int32
+  // sums (library GEMM); split activations in fragment blocks or as [3][T][K]
+  const size_t part = (size_t)T * std::max(std::max((D / pf_kr((int)D)) * R, (V / pf_kr((int)V)) * D),
+                                           3 * std::max(R, D));
+  const size_t xs_bytes = std::max(nb * ncmax * 24576, 3 * (size_t)T * std::max(D, V));
   const size_t ring = std::max<size_t>(1, (size_t)(c.conv_k - 1) * h->C);
   for (void** p : {&h->pf_xs, reinterpret_cast<void**>(&h->pf_sc), reinterpret_cast<void**>(&h->pf_ssq),
                    reinterpret_cast<void**>(&h->pf_part), reinterpret_cast<void**>(&h->pf_u),
@@ -547,8 +558,8 @@ int pf_reserve(dn_layer* h, int T) {
       *p = nullptr;
     }
   h->pf_cap = 0;
-  bool ok = hipMalloc(&h->pf_xs, nb * ncmax * 24576) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_sc, sizeof(float) * nb * ncmax * 64) == hipSuccess;
+  bool ok = hipMalloc(&h->pf_xs, xs_bytes) == hipSuccess;
+  ok = ok && hipMalloc(&h->pf_sc, sizeof(float) * std::max(nb * ncmax * 64, (size_t)T)) == hipSuccess;
   ok = ok && hipMalloc(&h->pf_ssq, sizeof(float) * T * ncmax) == hipSuccess;
   ok = ok && hipMalloc(&h->pf_part, sizeof(float) * part) == hipSuccess;
   ok = ok && hipMalloc(&h->pf_u, sizeof(float) * T * R) == hipSuccess;
@@ -589,17 +600,35 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
   const int nch = (n_tokens + dn::PF_CT - 1) / dn::PF_CT;
   const int kr_in = pf_kr((int)D), kr_out = pf_kr(V);
   auto check = [&]() { return !h->sync_debug || hipStreamSynchronize(st) == hipSuccess; };
+  // 8-bit weights: the projections as library int8 GEMMs over the three terms of every token
+  // (3T columns), where the library has an algorithm for the shape; else the hand-written GEMM
+  if (c.weight_bits == 8 && !h->pf_own_gemm && !h->lt_tried) {
+    h->lt_tried = true;
+    h->lt = dn::lt_create();
+  }
+  const bool lt_in = h->lt && !h->pf_own_gemm && dn::lt_prepare(h->lt, 0, R, 3 * n_tokens, (int)D);
+  const bool lt_out = h->lt && !h->pf_own_gemm && dn::lt_prepare(h->lt, 1, (int)D, 3 * n_tokens, V);
+  int8_t* const tx = static_cast<int8_t*>(h->pf_xs);
+  int32_t* const td = reinterpret_cast<int32_t*>(h->pf_part);
   for (size_t l = 0; l < L; ++l) {
     const dn_weights& w = h->w[l];
     const float* xl = l == 0 ? x : out + (l - 1) * T * D;
     // in_proj: split the prompt's inputs, int8 GEMM over the tokens, conv along the tokens
-    dn::BSplitArgs sp{xl, (int)D, (int)D, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
-    if (dn::launch_bsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    dn::BGemmArgs gi{w.w_in, h->pf_xs, h->pf_sc, h->pf_part, R, (int)D, n_tokens, kr_in};
-    if (dn::launch_bgemm(gi, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     dn::PConvArgs pc{};
-    pc.part = h->pf_part; pc.KS = (int)D / kr_in; pc.T = n_tokens; pc.M = R;
-    pc.s = w.s_in; pc.ssq = h->pf_ssq; pc.NC = (int)D / 128; pc.K = (int)D;
+    if (lt_in) {
+      dn::TSplitArgs sp{xl, (int)D, (int)D, n_tokens, tx, h->pf_sc, h->pf_ssq};
+      if (dn::launch_tsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      if (dn::lt_gemm_i8(h->lt, 0, w.w_in, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      pc.terms = td; pc.s1 = h->pf_sc; pc.KS = 0; pc.NC = 1;
+    } else {
+      dn::BSplitArgs sp{xl, (int)D, (int)D, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
+      if (dn::launch_bsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      dn::BGemmArgs gi{w.w_in, h->pf_xs, h->pf_sc, h->pf_part, R, (int)D, n_tokens, kr_in};
+      if (dn::launch_bgemm(gi, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      pc.part = h->pf_part; pc.KS = (int)D / kr_in; pc.NC = (int)D / 128;
+    }
+    pc.T = n_tokens; pc.M = R;
+    pc.s = w.s_in; pc.ssq = h->pf_ssq; pc.K = (int)D;
     pc.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; pc.eps = c.eps_rms;
     pc.conv_w = w.conv_w; pc.ring_in = h->ring + l * h->ring_elems; pc.ring_out = h->pf_ring;
     pc.C = h->C; pc.Kc = K; pc.out = h->pf_u;
@@ -627,12 +656,20 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
     if (dn::launch_pnorm(pn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (!check()) return fail(h, DN_E_DEVICE);
     // out_proj
-    dn::BSplitArgs so{h->pf_o, V, V, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
-    if (dn::launch_bsplit(so, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    dn::BGemmArgs go{w.w_out, h->pf_xs, h->pf_sc, h->pf_part, (int)D, V, n_tokens, kr_out};
-    if (dn::launch_bgemm(go, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     dn::BEpiArgs e{};
-    e.part = h->pf_part; e.KS = V / kr_out; e.M = (int)D; e.B = n_tokens; e.s = w.s_out;
+    if (lt_out) {
+      dn::TSplitArgs so{h->pf_o, V, V, n_tokens, tx, h->pf_sc, h->pf_ssq};
+      if (dn::launch_tsplit(so, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      if (dn::lt_gemm_i8(h->lt, 1, w.w_out, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      e.terms = td; e.s1 = h->pf_sc; e.KS = 0;
+    } else {
+      dn::BSplitArgs so{h->pf_o, V, V, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
+      if (dn::launch_bsplit(so, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      dn::BGemmArgs go{w.w_out, h->pf_xs, h->pf_sc, h->pf_part, (int)D, V, n_tokens, kr_out};
+      if (dn::launch_bgemm(go, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      e.part = h->pf_part; e.KS = V / kr_out;
+    }
+    e.M = (int)D; e.B = n_tokens; e.s = w.s_out;
     e.out = out + l * T * D; e.out_stride = (int)D;
     if (dn::launch_bepi(e, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (!check()) return fail(h, DN_E_DEVICE);

@@ -137,6 +137,58 @@ __global__ __launch_bounds__(256) void k_bsplit(const BSplitArgs a) {
   }
 }
 
+// Whole-row three-term split (library GEMM input): one workgroup per row t. The row's maximum and
+// sum of squares are reduced in a fixed order; the terms go to xs[i][t][k], four columns per thread
+// per pass, rows read twice (the second pass hits the cache).
+__global__ __launch_bounds__(256) void k_tsplit(const TSplitArgs a) {
+  __shared__ float rmx[4], rss[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, t = blockIdx.x;
+  const int K = a.K;
+  const float* row = a.act + (size_t)t * a.act_stride;
+  float mx = 0.f, ss = 0.f;
+  for (int c = 4 * tid; c < K; c += 1024) {
+    const v4f v = *reinterpret_cast<const v4f*>(row + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mx = fmaxf(mx, fabsf(v[e]));
+      ss = fmaf(v[e], v[e], ss);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    ss += __shfl_xor(ss, o);
+  }
+  if (lane == 0) {
+    rmx[wave] = mx;
+    rss[wave] = ss;
+  }
+  __syncthreads();
+  mx = fmaxf(fmaxf(rmx[0], rmx[1]), fmaxf(rmx[2], rmx[3]));
+  ss = (rss[0] + rss[1]) + (rss[2] + rss[3]);
+  float s1 = mx * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+  if (tid == 0) {
+    a.s1[t] = s1;
+    a.ssq[t] = ss;
+  }
+  const size_t plane = (size_t)a.T * K;
+  int8_t* xh = a.xs + (size_t)t * K;
+  for (int c = 4 * tid; c < K; c += 1024) {
+    const v4f v = *reinterpret_cast<const v4f*>(row + c);
+    int h[4], m[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split3(v[e], inv1, s1, inv2, s2, inv3, h[e], m[e], l[e]);
+    auto pack = [](const int (&q)[4]) {
+      return (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((q[3] & 0xFF) << 24);
+    };
+    *reinterpret_cast<int*>(xh + c) = pack(h);
+    *reinterpret_cast<int*>(xh + plane + c) = pack(m);
+    *reinterpret_cast<int*>(xh + 2 * plane + c) = pack(l);
+  }
+}
+
 // Split-K GEMM on the pre-split activations: partial sums of one K range for 64 MF rows and 64
 // sequences. Each 128-column chunk (24 KB of fragments + 64 scales) is copied straight into LDS
 // with direct-to-LDS loads, double-buffered, while the next chunk's weight fragments stream into
@@ -372,13 +424,20 @@ __global__ __launch_bounds__(256) void k_bepi(const BEpiArgs a) {
   // partials are requested NB at a time (NB >= the count when it is at most 16) before they are
   // added, in a fixed order
   float sum = 0.f;
-  for (int k0 = 0; k0 < a.KS; k0 += NB) {
-    float pv[NB];
+  if (a.terms) {
+    // exact sums of the three terms, folded in double with the row's split scale
+    const size_t plane = (size_t)a.B * a.M, at = (size_t)b * a.M + r;
+    const int d0 = a.terms[at], d1 = a.terms[plane + at], d2 = a.terms[2 * plane + at];
+    sum = (float)((double)a.s1[b] * ((double)d0 + ((double)d1 + (double)d2 * (1.0 / 254.0)) * (1.0 / 254.0)));
+  } else {
+    for (int k0 = 0; k0 < a.KS; k0 += NB) {
+      float pv[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) pv[k] = k0 + k < a.KS ? a.part[((size_t)(k0 + k) * a.B + b) * a.M + r] : 0.f;
+      for (int k = 0; k < NB; ++k) pv[k] = k0 + k < a.KS ? a.part[((size_t)(k0 + k) * a.B + b) * a.M + r] : 0.f;
 #pragma unroll
-    for (int k = 0; k < NB; ++k)
-      if (k0 + k < a.KS) sum += pv[k];
+      for (int k = 0; k < NB; ++k)
+        if (k0 + k < a.KS) sum += pv[k];
+    }
   }
   float scale = a.s[r];
   if (a.prenorm) {
@@ -613,6 +672,12 @@ bool bgemm2_shape_ok(int M, int K, int nrb, int kr) {
 hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st) {
   if (!bgemm2_shape_ok(a.M, a.K, nrb, a.KR)) return hipErrorInvalidValue;
   return bits == 8 ? bgemm2_bits<8>(a, nrb, st) : bgemm2_bits<4>(a, nrb, st);
+}
+
+hipError_t launch_tsplit(const TSplitArgs& a, hipStream_t st) {
+  if (a.T < 1 || a.K < 4 || a.K % 4 || a.act_stride % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tsplit, dim3(a.T), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st) {

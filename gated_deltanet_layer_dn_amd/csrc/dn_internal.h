@@ -88,6 +88,8 @@ struct BGemmArgs {
 struct BEpiArgs {
   const float* part;
   int KS, M, B;
+  const int32_t* terms;  // instead of part when set: [3][B][M] exact sums of the three int8 terms
+  const float* s1;       // [B] their per-row split scales (with terms)
   const float* s;        // [M]
   const float* ssq;      // [B][NC] (pre-norm only)
   int NC, K, prenorm;    // the pre-norm factor is 1/sqrt(sum ssq / K + eps)
@@ -119,12 +121,35 @@ hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st);
 hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st);
 hipError_t launch_bstate(const BStateArgs& a, hipStream_t st);
 
+// Whole-row three-term split for the library GEMMs: row t of act becomes
+// act[t][k] ~= s1[t] (h + (m + l/254)/254) with s1[t] = max_k |act[t][k]| / 127, the terms stored
+// term-major as xs[i][t][k] (i = 0, 1, 2 for h, m, l), and ssq[t] = sum_k act[t][k]^2.
+struct TSplitArgs {
+  const float* act;      // [T][act_stride], K columns used
+  int act_stride, K, T;  // K a multiple of 1024
+  int8_t* xs;            // [3][T][K]
+  float* s1;             // [T]
+  float* ssq;            // [T]
+};
+hipError_t launch_tsplit(const TSplitArgs& a, hipStream_t st);
+
+// int8 x int8 -> int32 library GEMMs (dn_lt.cpp): D [N][M] = W [M][K] (row-major int8) times
+// X [N][K] (row-major int8), exact. Two shape slots per context (in_proj, out_proj); lt_prepare
+// returns false when the library has no algorithm for the shape.
+struct LtCtx;
+LtCtx* lt_create();
+void lt_destroy(LtCtx* c);
+bool lt_prepare(LtCtx* c, int slot, int M, int N, int K);
+hipError_t lt_gemm_i8(LtCtx* c, int slot, const void* W, const int8_t* X, int32_t* D, hipStream_t st);
+
 // ---- prefill: T tokens of one sequence through a layer, chunkwise (128 x 128 state tiles) ----
 // in_proj epilogue along the tokens: u[t][r] = s[r] * prenorm(t) * sum_ks part[ks][t][r], then for
 // rows r < C the causal conv over the history (ring_in, oldest first) and the previous tokens, SiLU.
 struct PConvArgs {
   const float* part;     // [KS][T][M]
   int KS, T, M;
+  const int32_t* terms;  // instead of part when set: [3][T][M] exact sums of the three int8 terms
+  const float* s1;       // [T] their per-token split scales (with terms)
   const float* s;        // [M]
   const float* ssq;      // [T][NC] sums of squares of the layer input per 128-column chunk
   int NC, K, prenorm;    // pre-norm factor 1/sqrt(sum ssq / K + eps)

@@ -62,6 +62,12 @@ __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
   const float* __restrict__ part = a.part;
   float* __restrict__ out = a.out;
   auto pre = [&](int t, float f) {
+    if (a.terms) {
+      // exact sums of the three terms, folded in double with the token's split scale
+      const size_t plane = (size_t)a.T * a.M, at = (size_t)t * a.M + r;
+      const int d0 = a.terms[at], d1 = a.terms[plane + at], d2 = a.terms[2 * plane + at];
+      return sr * f * (float)((double)a.s1[t] * ((double)d0 + ((double)d1 + (double)d2 * (1.0 / 254.0)) * (1.0 / 254.0)));
+    }
     float pv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) pv[k] = k < a.KS ? part[((size_t)k * a.T + t) * a.M + r] : 0.f;

@@ -191,3 +191,12 @@ def test_prefill_arguments_are_checked():
     gpre = out.cpu().numpy().transpose(1, 0, 2)[:, :, None, :]
     assert max(out_err(gpre[:, l], ref_out[:, l]) for l in range(L)) <= OUT_TOL
     assert state_err(gS.cpu().numpy(), ref_S) <= STATE_TOL
+
+
+@pytest.mark.parametrize("name", ["stack3_prenorm", "ragged_chunks"])
+def test_prefill_hand_written_gemm(name, monkeypatch):
+    """8-bit weights with the hand-written split-K GEMM instead of the library GEMM (the path a
+    shape takes when the library has no algorithm for it)."""
+    monkeypatch.setenv("DN_PREFILL_OWN_GEMM", "1")
+    cfg, T = PF[name]
+    _check_prefill(cfg, T)
