@@ -169,10 +169,16 @@ void free_all(dn_layer* h) {
 // GEMM shape for an M x K projection: the all-loads-up-front kernel with 256-column K ranges and
 // NRB blocks of 64 rows (3 for in_proj, 2 for out_proj when the row count allows), else the chunked
 // kernel. Measured on MI355X at 64 sequences: in_proj 14.7 us (chunked 18.9), out_proj 6.9 us (9.1).
+#ifndef DN_BGEMM_KR_IN
+// K range of the in_proj GEMM's workgroups (256 or 512). 512 halves the split-K partial sums but
+// leaves one workgroup per compute unit: 107 against 97 us per step at 64 sequences on MI355X.
+#define DN_BGEMM_KR_IN 256
+#endif
 void pick_gemm(int M, int K, int* mf, int* kr, bool* up, int which) {
   *kr = 0;
+  const int kr2 = which == 1 ? DN_BGEMM_KR_IN : 256;
   for (int n : {which == 1 ? 3 : 2, 2, 1})
-    if (!*kr && dn::bgemm2_shape_ok(M, K, n, 256)) { *mf = n; *kr = 256; *up = true; }
+    if (!*kr && dn::bgemm2_shape_ok(M, K, n, kr2)) { *mf = n; *kr = kr2; *up = true; }
   if (*kr) return;
   *mf = 1;
   for (int c : {1024, 512, 256})
