@@ -399,13 +399,19 @@ namespace {
 int batched_proj(dn_layer* h, const void* W, const float* s, const float* act, int K, int M, int mf, int kr, bool up,
                  bool prenorm, const float* conv_w, float* ring, float* outp, int out_stride, hipStream_t st) {
   const dn_config& c = h->cfg;
-  if (act) {
+  // the up-front GEMM splits its own K range of the activations (8-bit weights, 256-column ranges,
+  // at least two row blocks); otherwise a separate split kernel runs first
+  const bool fuse = act && up && c.weight_bits == 8 && kr == 256 && mf >= 2;
+  if (act && !fuse) {
     dn::BSplitArgs sp{};
     sp.act = act; sp.act_stride = K; sp.K = K; sp.B = c.batch; sp.xs = h->xs; sp.sc = h->sc; sp.ssq = h->ssq;
     if (dn::launch_bsplit(sp, st) != hipSuccess) return DN_E_DEVICE;
   }
   dn::BGemmArgs g{};
   g.W = W; g.xs = h->xs; g.sc = h->sc; g.part = h->part; g.M = M; g.K = K; g.B = c.batch; g.KR = kr;
+  if (fuse) {
+    g.act = act; g.act_stride = K; g.ssq = h->ssq;
+  }
   if ((up ? dn::launch_bgemm2(g, c.weight_bits, mf, st) : dn::launch_bgemm(g, c.weight_bits, mf, st)) != hipSuccess)
     return DN_E_DEVICE;
   dn::BEpiArgs e{};

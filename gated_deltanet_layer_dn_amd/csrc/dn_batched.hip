@@ -325,7 +325,11 @@ __global__ __launch_bounds__(256) void k_bgemm(const BGemmArgs a) {
 // them alone (the compiler orders every later LDS read after all loads that precede it, so no
 // weight load may be in flight at that point); then each wave requests its whole K range of
 // weight fragments at once and runs the MFMAs as they arrive.
-template <int BITS, int NRB, int KR>
+//
+// SPLIT: the workgroup splits its K range of the fp32 activations itself (as k_bsplit does, into the
+// same LDS fragment order): eight waves load the slice with plain loads, every wave then requests
+// its weights, and the split waits only for the activation loads, so the two latencies overlap.
+template <int BITS, int NRB, int KR, bool SPLIT>
 __global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
   constexpr int NW = 4 * NRB;              // waves
   constexpr int NKS = KR / 64;             // k-steps
@@ -342,7 +346,22 @@ __global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
   const int k0 = ks * KR, c0 = k0 / KC;
   const int row0 = (rg * NRB + wave / 4) * 64 + 16 * (wave & 3);
 
-  {
+  static_assert(!SPLIT || (BITS == 8 && NCHUNK * 64 * 4 <= 256 * NRB), "split: 4 threads per (sequence, chunk)");
+  // SPLIT: thread (chunk sc, sequence sb, quarter sq4) holds columns 32 sq4 .. +31 of the chunk
+  const bool splitter = SPLIT && tid < NCHUNK * 64 * 4;
+  const int sc_ = tid >> 8, sb = (tid >> 2) & 63, sq4 = tid & 3;
+  const int bs = nb * NT + sb;
+  const bool bvalid = bs < B;
+  v4f xv[8];
+  if constexpr (SPLIT) {
+    if (splitter) {
+      // rows past the batch load row 0 (unconditional loads, no branches between them) and are
+      // zeroed once they arrive
+      const float* arow = a.act + (size_t)(bvalid ? bs : 0) * a.act_stride + k0 + sc_ * KC + 32 * sq4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] = reinterpret_cast<const v4f*>(arow)[i];
+    }
+  } else {
     const v4i* src = static_cast<const v4i*>(a.xs) + ((size_t)nb * NC + c0) * FRAGS;
     v4i* dst = &xs[0][0];
 #pragma unroll
@@ -354,9 +373,9 @@ __global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
 #pragma unroll
       for (int c = 0; c < NCHUNK; ++c)
         __builtin_amdgcn_global_load_lds(a.sc + ((size_t)nb * NC + c0 + c) * NT + lane, &scl[c][0], 4, 0, 0);
+    DN_VMCNT_WAIT(0);
+    __syncthreads();
   }
-  DN_VMCNT_WAIT(0);
-  __syncthreads();
   v4i A[NKS];
 #pragma unroll
   for (int s = 0; s < NKS; ++s) {
@@ -369,6 +388,55 @@ __global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
           reinterpret_cast<const v2u*>(static_cast<const uint8_t*>(a.W) + row * (K / 2) + kk / 2));
       A[s] = v4i{nib4(p.x & 0xFFFFu), nib4(p.x >> 16), nib4(p.y & 0xFFFFu), nib4(p.y >> 16)};
     }
+  }
+  if constexpr (SPLIT) {
+    // the activation loads are older than the weight loads: waiting for xv leaves the weights in
+    // flight
+    if (splitter) {
+      if (!bvalid)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xv[i] = v4f{0.f, 0.f, 0.f, 0.f};
+      float mx = 0.f, ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx = fmaxf(mx, fabsf(xv[i][e]));
+          ss = fmaf(xv[i][e], xv[i][e], ss);
+        }
+      mx = fmaxf(mx, dpp_f<0xB1>(mx));
+      mx = fmaxf(mx, dpp_f<0x4E>(mx));
+      ss += dpp_f<0xB1>(ss);
+      ss += dpp_f<0x4E>(ss);
+      float s1 = mx * (1.0f / 127.0f);
+      if (!(s1 > 0.f)) s1 = 1.0f;
+      const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+      if (sq4 == 0) {
+        scl[sc_][sb] = s1;
+        if (rg == 0 && bvalid) a.ssq[(size_t)bs * NC + c0 + sc_] = ss;
+      }
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        int hw[4], mw[4], lw[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          int h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+          const v4f v = xv[4 * gg + d];
+          split3(v[0], inv1, s1, inv2, s2, inv3, h0, m0, l0);
+          split3(v[1], inv1, s1, inv2, s2, inv3, h1, m1, l1);
+          split3(v[2], inv1, s1, inv2, s2, inv3, h2, m2, l2);
+          split3(v[3], inv1, s1, inv2, s2, inv3, h3, m3, l3);
+          hw[d] = (h0 & 0xFF) | ((h1 & 0xFF) << 8) | ((h2 & 0xFF) << 16) | ((h3 & 0xFF) << 24);
+          mw[d] = (m0 & 0xFF) | ((m1 & 0xFF) << 8) | ((m2 & 0xFF) << 16) | ((m3 & 0xFF) << 24);
+          lw[d] = (l0 & 0xFF) | ((l1 & 0xFF) << 8) | ((l2 & 0xFF) << 16) | ((l3 & 0xFF) << 24);
+        }
+        const int f = sb >> 4, ln = (sb & 15) + 16 * (2 * (sq4 & 1) + gg), ks2 = sq4 >> 1;
+        xs[sc_][((0 * KSC + ks2) * 4 + f) * 64 + ln] = v4i{hw[0], hw[1], hw[2], hw[3]};
+        xs[sc_][((1 * KSC + ks2) * 4 + f) * 64 + ln] = v4i{mw[0], mw[1], mw[2], mw[3]};
+        xs[sc_][((2 * KSC + ks2) * 4 + f) * 64 + ln] = v4i{lw[0], lw[1], lw[2], lw[3]};
+      }
+    }
+    lds_barrier();  // the staged terms and scales; the weight loads stay in flight
   }
 
   float facc[4][4];
@@ -646,7 +714,14 @@ hipError_t launch_bgemm(const BGemmArgs& a, int bits, int mf, hipStream_t st) {
 template <int BITS, int NRB, int KR>
 hipError_t go_bgemm2(const BGemmArgs& a, hipStream_t st) {
   const dim3 grid(a.M / (64 * NRB), a.K / KR, (a.B + NT - 1) / NT);
-  hipLaunchKernelGGL((k_bgemm2<BITS, NRB, KR>), grid, dim3(256 * NRB), 0, st, a);
+  if (a.act) {
+    if constexpr (BITS == 8 && KR == 256 && NRB >= 2)
+      hipLaunchKernelGGL((k_bgemm2<BITS, NRB, KR, true>), grid, dim3(256 * NRB), 0, st, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((k_bgemm2<BITS, NRB, KR, false>), grid, dim3(256 * NRB), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -83,6 +83,12 @@ struct BGemmArgs {
   const float* sc;       // their scales (BSplitArgs::sc)
   float* part;           // [K/KR][B][M]
   int M, K, B, KR;
+  // When act is set (8-bit weights, 256-column K ranges, two or three row blocks) the GEMM splits
+  // its own K range of act [B][act_stride] instead of reading xs / sc, and the workgroups of the
+  // first row block write the chunk sums of squares to ssq [B][K/128].
+  const float* act;
+  int act_stride;
+  float* ssq;
 };
 // out[b][r] = epilogue(s[r] * sum_ks part[ks][b][r]).
 struct BEpiArgs {
