@@ -224,10 +224,11 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
     float tc[CT];
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
-      float v = j == col ? 1.0f : 0.0f;
+      // four interleaved partial sums, so each row's dependent chain is a quarter as long
+      float v[4] = {j == col ? 1.0f : 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int m = 0; m < j; ++m) v = fmaf(-sA[j][m], tc[m], v);
-      tc[j] = v;
+      for (int m = 0; m < j; ++m) v[m & 3] = fmaf(-sA[j][m], tc[m], v[m & 3]);
+      tc[j] = (v[0] + v[1]) + (v[2] + v[3]);
     }
 #pragma unroll
     for (int j = 0; j < CT; ++j) sA[j][col] = tc[j];
