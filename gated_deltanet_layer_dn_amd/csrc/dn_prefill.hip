@@ -41,6 +41,16 @@ constexpr int LD = DK + 4;  // padded LDS row of 128 floats (keeps 16-byte align
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
+// Workgroup barrier that waits only for this wave's LDS accesses. A __syncthreads() also waits for
+// every outstanding global access, here the readout's stores of the chunk; the scan's barriers
+// order LDS data between waves and no global data.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float prenorm_of(const PConvArgs& a, int t) {
   if (!a.prenorm) return 1.0f;
   float ss = 0.f;
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
     for (int st = 0; st < 32; ++st) dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aW[st], bS[st], dacc, 0, 0, 0);
 #pragma unroll
     for (int v = 0; v < 4; ++v) sD[16 * w + 4 * lk + v][li] = dacc[v];
-    __syncthreads();
+    lds_barrier();
     float bD[16];
 #pragma unroll
     for (int st = 0; st < 16; ++st) bD[st] = sD[16 * lk + st][li];
@@ -364,12 +374,12 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
       for (int st = 0; st < 16; ++st)
         sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(aK[tau][st], bD[st], sacc[tau], 0, 0, 0);
     }
-    __syncthreads();  // every read of the old state block and of D is done
+    lds_barrier();  // every read of the old state block and of D is done
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int v = 0; v < 4; ++v) sS[32 * w + 16 * tau + 4 * lk + v][li] = sacc[tau][v];
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int st = 0; st < 32; ++st) bS[st] = sS[32 * lk + st][li];
   }
