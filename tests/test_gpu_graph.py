@@ -79,3 +79,52 @@ def test_graph_replays_match_eager(name, capfd, monkeypatch):
     finally:
         st.close()
     print(f"[graph] {name}: {T} replays identical to the eager steps", flush=True)
+
+
+def test_prefill_graph_replays_match_eager():
+    """dn_prefill captured after one eager call of the same length (which sizes the handle's
+    scratch), replayed for two prompts from the same starting state: outputs and states bit for
+    bit those of eager calls. 8-bit weights, so the capture holds the library GEMMs."""
+    cfg = gi.custom("gr_pf", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, n_layers=2, n_tokens=100,
+                    flags=gi.DN_X_RMSNORM, ring_std=1.0)
+    layers, stream = gi.generate(cfg)
+    T = 100
+    print(f"[graph] prefill: L={cfg.n_layers} T={T}", flush=True)
+    st = make_stack(cfg, layers)
+    try:
+        x = torch.from_numpy(np.ascontiguousarray(stream.x[:T, 0])).cuda()
+        a = torch.from_numpy(np.ascontiguousarray(stream.alpha[:T, :, 0])).cuda()
+        b = torch.from_numpy(np.ascontiguousarray(stream.beta[:T, :, 0])).cuda()
+        S0, H0 = st.get_state()
+        prompts = [(x, a, b), (x.flip(0).contiguous(), a.flip(0).contiguous(), b.flip(0).contiguous())]
+        eager = []
+        for px, pa, pb in prompts:
+            st.set_state(S0, H0)
+            out = st.prefill(px, pa, pb)
+            torch.cuda.synchronize()
+            eager.append((out.cpu().numpy(), st.get_state()[0].cpu().numpy()))
+        xs, as_, bs = x.clone(), a.clone(), b.clone()
+        out_s = torch.empty((cfg.n_layers, T, cfg.d_model), device="cuda:0")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            st.prefill(xs, as_, bs, out_s)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.prefill(xs, as_, bs, out_s)
+        torch.cuda.synchronize()
+        for i, (px, pa, pb) in enumerate(prompts):
+            st.set_state(S0, H0)
+            xs.copy_(px)
+            as_.copy_(pa)
+            bs.copy_(pb)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out_s.cpu().numpy(), eager[i][0]), i
+            assert np.array_equal(st.get_state()[0].cpu().numpy(), eager[i][1]), i
+        del g
+    finally:
+        st.close()
+    print("[graph] prefill: 2 replays identical to the eager calls", flush=True)
