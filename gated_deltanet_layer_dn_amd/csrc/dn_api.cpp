@@ -74,6 +74,7 @@ struct dn_layer {
   bool disabled = false;
   long steps = 0;
   long fault_step = 0;    // 1-based step to fail (0 = never)
+  long fault_stall = 0;   // 1-based step whose whole-stack launch may not wait in any hand-off (0 = never)
   bool sync_debug = false;
 };
 
@@ -260,6 +261,24 @@ int setup_persist(dn_layer* h) {
   return DN_OK;
 }
 
+// The hand-off state of the whole-stack kernel as dn_create leaves it: buffers zeroed, tag base 1,
+// no error. The x and gated-readout words carry only their tag mod 4, and after an aborted launch
+// words of any of its layers may remain; some of those would match the tags the next launch's
+// first polls wait for, so re-arming the handle starts the exchange state afresh.
+int reset_handoff(dn_layer* h) {
+  const dn_config& c = h->cfg;
+  const size_t u_words = h->R + (h->gates ? 2 * c.n_v_heads : 0);
+  const dn::Ctl ctl0{1u, 0u, 0u, 0u};
+  bool ok = hipMemset(h->X, 0, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
+  ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * u_words) == hipSuccess;
+  ok = ok && hipMemset(h->G, 0, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMemcpy(h->ctl, &ctl0, sizeof(ctl0), hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipDeviceSynchronize() == hipSuccess;
+  if (!ok) return DN_E_DEVICE;
+  *h->err_host = 0;
+  return DN_OK;
+}
+
 // The whole-stack kernel stores its error flag into host memory at the end of each launch; the
 // host reads it without synchronising, so a failure is seen at the first call after that launch.
 unsigned host_err(const dn_layer* h) { return *reinterpret_cast<volatile const unsigned*>(h->err_host); }
@@ -338,6 +357,7 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
     return DN_E_DEVICE;
   }
   if (const char* e = std::getenv("DN_FAULT_STEP")) h->fault_step = std::atol(e);
+  if (const char* e = std::getenv("DN_FAULT_STALL")) h->fault_stall = std::atol(e);
   if (const char* e = std::getenv("DN_SYNC_DEBUG")) h->sync_debug = std::atoi(e) != 0;
   if (const char* e = std::getenv("DN_PREFILL_OWN_GEMM")) h->pf_own_gemm = std::atoi(e) != 0;
   if (const char* e = std::getenv("DN_VERBOSE"); e && std::atoi(e) != 0)
@@ -357,9 +377,7 @@ DN_API int dn_set_state(dn_layer* h, const float* S, const float* ring) {
     if (dn::launch_state_tile(h->stage, h->S, (int)L, h->cfg.n_v_heads, h->cfg.d_k, h->cfg.d_v, true, nullptr) !=
         hipSuccess)
       return DN_E_DEVICE;
-    const unsigned zero = 0;
-    if (hipMemcpy(&h->ctl->error, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return DN_E_DEVICE;
-    *h->err_host = 0;
+    if (reset_handoff(h) != DN_OK) return DN_E_DEVICE;
   } else if (hipMemcpy(h->S, S, sizeof(float) * L * h->s_elems, hipMemcpyDefault) != hipSuccess) {
     return DN_E_DEVICE;
   }
@@ -466,6 +484,9 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     a.eps_l2 = c.eps_l2; a.eps_rms = c.eps_rms; a.q_scale = c.q_scale;
     a.alpha_per_key = (c.flags & DN_ALPHA_PER_KEY) ? 1 : 0;
     a.gates = h->gates ? 1 : 0;
+    // an injected stall: every hand-off gets a single poll round, so the launch aborts through its
+    // own error path (reported by the next call) as soon as one exchange is not already complete
+    a.spin_cap = (h->fault_stall > 0 && h->steps == h->fault_stall) ? 0u : dn::PERSIST_SPIN_CAP;
     if (dn::launch_persist(a, h->ps, h->nwg, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
     return DN_OK;

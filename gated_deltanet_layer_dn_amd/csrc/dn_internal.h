@@ -242,8 +242,10 @@ struct PersistArgs {
   float eps_l2, eps_rms, q_scale;
   int alpha_per_key;     // 1: key row i of head h decays by alpha[l][h][i] (at most PK_MAXL layers)
   int gates;             // 1: gates from the in_proj rows R .. R + 2 Hv (U holds them after the R rows)
+  unsigned spin_cap;     // poll rounds a hand-off may take before the launch aborts (PERSIST_SPIN_CAP)
 };
-constexpr int PK_MAXL = 32;  // layers of a whole-stack launch with one decay per key channel
+constexpr int PK_MAXL = 32;
+constexpr unsigned PERSIST_SPIN_CAP = 1u << 22;  // layers of a whole-stack launch with one decay per key channel
 
 struct PersistShape {
   int batch, D, V, R, dk, dv, Hv, K, bits;

@@ -52,7 +52,6 @@ constexpr int NCM = 4;                 // communication waves per workgroup
 constexpr int NTHR = (NCW + NCM) * 64;
 constexpr int DK = 128;                // key rows of a state tile
 constexpr int CB = 16;                 // value columns per phase-B workgroup
-constexpr unsigned SPIN_CAP = 1u << 22;
 constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
 // Weight prefetch throttle: a compute wave keeps at most this many 1 KiB row-chunk loads in
 // flight, so that the compute unit's memory pipeline is never full and the communication
@@ -321,14 +320,14 @@ __device__ __forceinline__ float reduce_rows(int (&acc)[RB][3], float s1, int la
 }
 
 // Poll N 64-bit tagged words per lane, word i at base + off[i] (element offsets), until every one
-// carries `want`; values go to v[]. Returns false if the spin cap is hit or another workgroup
+// carries `want`; values go to v[]. Returns false after `cap` rounds, or if another workgroup
 // reported an error. The base pointer is laundered through an empty asm statement each round so
 // that the compiler rebuilds the addresses from one register pair with immediate offsets instead
 // of keeping N 64-bit addresses alive across the loop.
 template <int N>
 __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&off)[N], unsigned want, float (&v)[N],
-                                              unsigned nvalid, const unsigned* err, unsigned* rounds = nullptr,
-                                              unsigned long long* round_ts = nullptr) {
+                                              unsigned nvalid, const unsigned* err, unsigned cap,
+                                              unsigned* rounds = nullptr, unsigned long long* round_ts = nullptr) {
   unsigned pend = (1u << N) - 1u;
   pend &= (1u << nvalid) - 1u;
   unsigned it = 0;
@@ -348,7 +347,7 @@ __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&
 #ifdef DN_PHASE_TIMERS
     if (round_ts && it < 4 && (threadIdx.x & 63) == 0) round_ts[it] = wall_clock64();
 #endif
-    if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
+    if (++it > cap || ((it & 255) == 0 && coherent_load_u32(err))) return false;
   }
   if (rounds) *rounds = it;
   return true;
@@ -357,10 +356,10 @@ __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&
 // Poll NQ 16-byte quads of self-tagged words per lane, quad i at byte offset boff + i * QSTRIDE of
 // the buffer, with device-coherent loads until every word carries `want` mod 4; quads i >= nvalid
 // are not polled. When ONE is set, the single word at byte offset boff1 is polled as well. Returns
-// false if the spin cap is hit or another workgroup reported an error.
+// false after `cap` rounds, or if another workgroup reported an error.
 template <int NQ, int QSTRIDE, bool ONE>
 __device__ __forceinline__ bool poll_quads(__amdgpu_buffer_rsrc_t rs, int boff, int boff1, unsigned want, v4u (&q)[NQ],
-                                           unsigned& w1, const unsigned* err) {
+                                           unsigned& w1, const unsigned* err, unsigned cap) {
   const unsigned t = want & 3u;
   unsigned pend = (1u << NQ) - 1u;
   bool pend1 = ONE;
@@ -375,7 +374,7 @@ __device__ __forceinline__ bool poll_quads(__amdgpu_buffer_rsrc_t rs, int boff, 
     for (int i = 0; i < NQ; ++i)
       if (((pend >> i) & 1) && st_tagged(q[i], t)) pend &= ~(1u << i);
     if (ONE && pend1 && (w1 & 3u) == t) pend1 = false;
-    if (++it > SPIN_CAP || ((it & 255) == 0 && coherent_load_u32(err))) return false;
+    if (++it > cap || ((it & 255) == 0 && coherent_load_u32(err))) return false;
   }
   return true;
 }
@@ -698,7 +697,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         wait_counter(&sm.c_done, NCW * l, &sm.abort_flag);
         v4u q[XQ];
         unsigned w1 = 0;
-        ok = poll_quads<XQ, 1024, false>(xrs, 4 * col0, 0, tag - 1, q, w1, err);
+        ok = poll_quads<XQ, 1024, false>(xrs, 4 * col0, 0, tag - 1, q, w1, err, a.spin_cap);
 #pragma unroll
         for (int h = 0; h < XQ; ++h)
 #pragma unroll
@@ -758,7 +757,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
       DN_MARK(a, l, 10);
       unsigned rounds = 0;
-      ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, &rounds, DN_TS(a, l, 20));
+      ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, a.spin_cap, &rounds, DN_TS(a, l, 20));
       if (lane == 0) bump_counter(&sm.u_done);
       DN_MARK(a, l, 4);
       if (__all(ok)) {
@@ -854,9 +853,9 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         unsigned w1 = 0;
         const int w0 = cw * GSEG + 4 * lane;
         if (lane < pn)
-          ok = poll_quads<GQ, 1024, true>(grs, 4 * w0, 4 * (cw * GSEG + V / NCM + lane), tag, q, w1, err);
+          ok = poll_quads<GQ, 1024, true>(grs, 4 * w0, 4 * (cw * GSEG + V / NCM + lane), tag, q, w1, err, a.spin_cap);
         else
-          ok = poll_quads<GQ, 1024, false>(grs, 4 * w0, 0, tag, q, w1, err);
+          ok = poll_quads<GQ, 1024, false>(grs, 4 * w0, 0, tag, q, w1, err, a.spin_cap);
 #pragma unroll
         for (int h = 0; h < GQ; ++h)
 #pragma unroll

@@ -40,6 +40,9 @@ extern "C" {
 
 /* Environment read by dn_create:
  *   DN_FAULT_STEP=n     fail the n-th dn_step of the handle before it launches anything
+ *   DN_FAULT_STALL=n    whole-stack handles: the n-th dn_step's launch gives every hand-off between
+ *                       workgroups a single poll round, so it aborts through the kernel's own error
+ *                       path unless every exchange is already complete; the next call reports it
  *   DN_SYNC_DEBUG=1     synchronise after every launch and check for errors
  *   DN_LAYER_KERNELS=1  use the per-layer kernels even where the whole-stack kernel applies
  *   DN_VERBOSE=1        print which path the handle uses to stderr
@@ -116,7 +119,8 @@ int dn_create(const dn_config *cfg, const dn_weights *w, dn_layer **out);
 
 /* Copy the state in. S: [L][B][Hv][dk][dv] fp32; ring: [L][B][K-1][C] fp32, oldest
  * token first (NULL leaves the history unchanged). Host or device pointers.
- * Synchronous: waits for all work on the device first. Re-arms a latched handle.
+ * Synchronous: waits for all work on the device first. Re-arms a latched handle, and restarts the
+ * whole-stack kernel's exchange state between workgroups as dn_create leaves it.
  * Returns DN_OK, DN_E_INVAL (NULL handle or S) or DN_E_DEVICE. */
 int dn_set_state(dn_layer *h, const float *S, const float *ring);
 

@@ -178,3 +178,43 @@ def test_calls_keep_the_callers_current_device():
         assert torch.cuda.current_device() == 0
     finally:
         torch.cuda.set_device(prev)
+
+
+def test_stalled_hand_off_aborts_and_the_handle_recovers(capfd, monkeypatch):
+    """A whole-stack launch whose exchanges between workgroups get a single poll round
+    (DN_FAULT_STALL=2) ends through the kernel's own abort path: the next call returns DN_E_DEVICE
+    and latches the handle, dn_get_state still returns what the card holds, and once dn_set_state
+    has re-armed the handle a run from the initial state matches the oracle (no word left by the
+    aborted launch is taken for a fresh one)."""
+    cfg = gi.custom("stall", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, n_layers=6, n_tokens=5,
+                    flags=gi.DN_X_RMSNORM, ring_std=1.0)
+    layers, stream = gi.generate(cfg)
+    monkeypatch.setenv("DN_FAULT_STALL", "2")
+    monkeypatch.setenv("DN_VERBOSE", "1")
+    st = make_stack(cfg, layers)
+    monkeypatch.delenv("DN_FAULT_STALL")
+    monkeypatch.delenv("DN_VERBOSE")
+    assert "whole-stack kernel" in capfd.readouterr().err
+    try:
+        x, a, b = upload_stream(stream)
+        out = st.new_out()
+        print("[stall] step 1, then the stalled step 2", flush=True)
+        assert st.step(x[0], a[0], b[0], out, check=False) == dn.DN_OK
+        assert st.step(x[1], a[1], b[1], out, check=False) == dn.DN_OK  # enqueued; aborts on the card
+        torch.cuda.synchronize()
+        assert st.step(x[2], a[2], b[2], out, check=False) == dn.DN_E_DEVICE
+        assert st.step(x[2], a[2], b[2], out, check=False) == dn.DN_E_DISABLED
+        gS, _ = st.get_state()
+        assert np.all(np.isfinite(gS.cpu().numpy()))
+        print("[stall] abort reported; re-arming from the initial state", flush=True)
+        S0 = np.ascontiguousarray(np.stack([l.S0 for l in layers]), np.float32)
+        R0 = np.ascontiguousarray(np.stack([l.ring0 for l in layers]), np.float32)
+        st.set_state(S0, R0)
+        gout = run_gpu(st, stream)
+        gS, _ = st.get_state()
+    finally:
+        st.close()
+    ref_out, ref_S, _ = orc.run(cfg, layers, stream)
+    e, es = out_err(gout, ref_out), state_err(gS.cpu().numpy(), ref_S)
+    print(f"[stall] after recovery: out {e:.2e} state {es:.2e}", flush=True)
+    assert e <= OUT_TOL and es <= STATE_TOL
