@@ -195,11 +195,13 @@ class DeltaNetStack:
         return out if check else rc
 
     def prefill(self, x, alpha=None, beta=None, out=None, stream=None, check=True):
-        """Run a prompt through every layer: x [T][D], alpha/beta [T][L][Hv] (None with
-        DN_GATES_ON_DEVICE); returns out [L][T][D]."""
-        T = x.shape[0]
+        """Run a prompt through every layer: x [T][D] (or [B][T][D], one prompt per sequence),
+        alpha/beta [T][L][Hv] (or [T][L][B][Hv]; None with DN_GATES_ON_DEVICE); returns out
+        [L][T][D] (or [L][B][T][D])."""
+        T = x.shape[-2]
         if out is None:
-            out = torch.empty((self.L, T, self.D), dtype=torch.float32, device=self.device)
+            shape = (self.L, T, self.D) if self.B == 1 else (self.L, self.B, T, self.D)
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
         rc = dn_prefill(self.h, x, T, alpha, beta, out, stream)
         if check:
             _check(rc, "dn_prefill")

@@ -615,12 +615,11 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
   if (!h->gates && (!alpha || !beta)) return DN_E_INVAL;
   if (h->disabled) return DN_E_DISABLED;
   const dn_config& c = h->cfg;
-  const size_t L = c.n_layers, D = c.d_model, T = n_tokens;
-  if (c.batch != 1 || c.d_k != 128 || c.d_v != 128 || (c.flags & DN_ALPHA_PER_KEY) || D % 256 || h->V % 256)
-    return DN_E_INVAL;
+  const size_t L = c.n_layers, D = c.d_model, T = n_tokens, B = c.batch;
+  if (c.d_k != 128 || c.d_v != 128 || (c.flags & DN_ALPHA_PER_KEY) || D % 256 || h->V % 256) return DN_E_INVAL;
   const char* xb = reinterpret_cast<const char*>(x);
   const char* ob = reinterpret_cast<const char*>(out);
-  if (ob < xb + sizeof(float) * T * D && xb < ob + sizeof(float) * L * T * D) return DN_E_INVAL;
+  if (ob < xb + sizeof(float) * B * T * D && xb < ob + sizeof(float) * L * B * T * D) return DN_E_INVAL;
   DeviceScope dev(h->device);
   if (!dev.ok()) return fail(h, DN_E_DEVICE);
   if (h->persist && host_err(h)) return fail(h, DN_E_DEVICE);
@@ -643,9 +642,14 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
   const bool lt_out = h->lt && !h->pf_own_gemm && dn::lt_prepare(h->lt, 1, (int)D, 3 * n_tokens, V);
   int8_t* const tx = static_cast<int8_t*>(h->pf_xs);
   int32_t* const td = reinterpret_cast<int32_t*>(h->pf_part);
+  const size_t ring_seq = (size_t)(K - 1) * h->C, s_seq = (size_t)c.n_v_heads * c.d_k * c.d_v;
+  // the sequences of a batch one after the other, each through every layer; out[l][b] is layer l's
+  // output for sequence b and layer l+1's input
+  for (size_t sb = 0; sb < B; ++sb)
   for (size_t l = 0; l < L; ++l) {
     const dn_weights& w = h->w[l];
-    const float* xl = l == 0 ? x : out + (l - 1) * T * D;
+    const float* xl = l == 0 ? x + sb * T * D : out + ((l - 1) * B + sb) * T * D;
+    float* const ring_l = h->ring + l * h->ring_elems + sb * ring_seq;
     // in_proj: split the prompt's inputs, int8 GEMM over the tokens, conv along the tokens
     dn::PConvArgs pc{};
     if (lt_in) {
@@ -663,11 +667,11 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
     pc.T = n_tokens; pc.M = R;
     pc.s = w.s_in; pc.ssq = h->pf_ssq; pc.K = (int)D;
     pc.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; pc.eps = c.eps_rms;
-    pc.conv_w = w.conv_w; pc.ring_in = h->ring + l * h->ring_elems; pc.ring_out = h->pf_ring;
+    pc.conv_w = w.conv_w; pc.ring_in = ring_l; pc.ring_out = h->pf_ring;
     pc.C = h->C; pc.Kc = K; pc.out = h->pf_u;
     if (dn::launch_pconv(pc, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    if (K > 1 && hipMemcpyAsync(h->ring + l * h->ring_elems, h->pf_ring, sizeof(float) * h->ring_elems,
-                                hipMemcpyDeviceToDevice, st) != hipSuccess)
+    if (K > 1 && hipMemcpyAsync(ring_l, h->pf_ring, sizeof(float) * ring_seq, hipMemcpyDeviceToDevice, st) !=
+                     hipSuccess)
       return fail(h, DN_E_DEVICE);
     if (!check()) return fail(h, DN_E_DEVICE);
     // recurrence in chunks, then the gated RMSNorm
@@ -677,12 +681,13 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
       if (launch_layer_gates(h, l, xl, n_tokens, h->pf_al, h->pf_be, st) != hipSuccess) return fail(h, DN_E_DEVICE);
       pi.alpha = h->pf_al; pi.beta = h->pf_be; pi.gstride = c.n_v_heads;
     } else {
-      pi.alpha = alpha + l * c.n_v_heads; pi.beta = beta + l * c.n_v_heads; pi.gstride = (int)L * c.n_v_heads;
+      pi.alpha = alpha + (l * B + sb) * c.n_v_heads; pi.beta = beta + (l * B + sb) * c.n_v_heads;
+      pi.gstride = (int)(L * B) * c.n_v_heads;
     }
     pi.eps_l2 = c.eps_l2; pi.q_scale = c.q_scale; pi.NCH = nch; pi.cw = h->pf_cw;
     if (dn::launch_pintra(pi, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     dn::PScanArgs ps{};
-    ps.cw = h->pf_cw; ps.S = h->S + l * h->s_elems; ps.transposed = h->persist ? 1 : 0;
+    ps.cw = h->pf_cw; ps.S = h->S + l * h->s_elems + sb * s_seq; ps.transposed = h->persist ? 1 : 0;
     ps.T = n_tokens; ps.Hv = c.n_v_heads; ps.NCH = nch; ps.V = V; ps.o = h->pf_o;
     if (dn::launch_pscan(ps, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     dn::PNormArgs pn{h->pf_o, h->pf_u, w.norm_w, n_tokens, R, h->C, V, c.eps_rms};
@@ -703,7 +708,7 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
       e.part = h->pf_part; e.KS = V / kr_out;
     }
     e.M = (int)D; e.B = n_tokens; e.s = w.s_out;
-    e.out = out + l * T * D; e.out_stride = (int)D;
+    e.out = out + (l * B + sb) * T * D; e.out_stride = (int)D;
     if (dn::launch_bepi(e, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (!check()) return fail(h, DN_E_DEVICE);
   }

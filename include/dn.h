@@ -157,13 +157,13 @@ int dn_step(dn_layer *h, const float *x, const float *alpha, const float *beta, 
  * keeps prompts on the CPU, this is the same computation on the card): the recurrence
  * is evaluated in chunks of 64 tokens, which is the per-token step rewritten and
  * agrees with it up to rounding.
- * Requires batch == 1, d_k == d_v == 128, a scalar decay (no DN_ALPHA_PER_KEY),
- * d_model and n_v_heads * d_v multiples of 256.
+ * Requires d_k == d_v == 128, a scalar decay (no DN_ALPHA_PER_KEY), d_model and n_v_heads * d_v
+ * multiples of 256. With batch B > 1 every sequence gets a prompt of the same T tokens.
  * DEVICE pointers:
- *   x            [T][D]        the prompt's inputs of layer 0
- *   alpha, beta  [T][L][Hv]    per token, the gates of dn_step (not read, may be NULL, with
+ *   x            [B][T][D]     the prompts' inputs of layer 0, one sequence after the other
+ *   alpha, beta  [T][L][B][Hv] per token, the gates of dn_step (not read, may be NULL, with
  *                              DN_GATES_ON_DEVICE)
- *   out          [L][T][D]     out[l] is layer l's output for every token and layer
+ *   out          [L][B][T][D]  out[l][b] is layer l's output for sequence b's tokens and layer
  *                              l+1's input. Must not overlap x.
  * T = n_tokens, 1..DN_PREFILL_MAX_TOKENS per call; a longer prompt goes in several calls, each
  * continuing from the state the previous one left. The handle keeps scratch memory sized for the

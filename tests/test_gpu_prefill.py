@@ -37,6 +37,9 @@ PF = {
     # 768-wide model: not a whole-stack shape, so the handle keeps the canonical state layout
     "layer_kernels_handle": (gi.custom("pf_lk", d_model=768, n_k_heads=2, d_k=128, n_v_heads=4, d_v=128,
                                        n_tokens=70, ring_std=1.0), 66),
+    # three sequences, each with its own 70-token prompt, then decode on the batched kernels
+    "batch3": (gi.custom("pf_b3", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=3, n_layers=2,
+                         n_tokens=74, flags=gi.DN_X_RMSNORM, ring_std=1.0), 70),
 }
 
 
@@ -46,10 +49,16 @@ def _sub(stream, t0, t1):
 
 
 def _prompt(stream, T, dev="cuda:0"):
-    x = torch.from_numpy(np.ascontiguousarray(stream.x[:T, 0])).to(dev)
-    a = torch.from_numpy(np.ascontiguousarray(stream.alpha[:T, :, 0])).to(dev)
-    b = torch.from_numpy(np.ascontiguousarray(stream.beta[:T, :, 0])).to(dev)
-    return x, a, b
+    """x [B][T][D] (one sequence after the other), alpha / beta [T][L][B][Hv]; for one sequence x is
+    [T][D] and the gates [T][L][Hv]."""
+    B = stream.x.shape[1]
+    if B == 1:
+        x = np.ascontiguousarray(stream.x[:T, 0])
+        a, b = np.ascontiguousarray(stream.alpha[:T, :, 0]), np.ascontiguousarray(stream.beta[:T, :, 0])
+    else:
+        x = np.ascontiguousarray(stream.x[:T].transpose(1, 0, 2))
+        a, b = np.ascontiguousarray(stream.alpha[:T]), np.ascontiguousarray(stream.beta[:T])
+    return tuple(torch.from_numpy(v).to(dev) for v in (x, a, b))
 
 
 def _check_prefill(cfg, T):
@@ -61,7 +70,8 @@ def _check_prefill(cfg, T):
     st = make_stack(cfg, layers)
     try:
         x, a, b = _prompt(stream, T)
-        out = st.prefill(x, a, b)  # [L][T][D]
+        out = torch.empty((cfg.n_layers, cfg.batch, T, cfg.d_model), device="cuda:0")
+        st.prefill(x, a, b, out)  # [L][B][T][D]
         torch.cuda.synchronize()
         gS, gH = st.get_state()
         gS_pre, gH_pre = gS.cpu().numpy(), gH.cpu().numpy()
@@ -69,7 +79,7 @@ def _check_prefill(cfg, T):
         gS, gH = st.get_state()
     finally:
         st.close()
-    gpre = out.cpu().numpy().transpose(1, 0, 2)[:, :, None, :]  # [T][L][1][D]
+    gpre = out.cpu().numpy().transpose(2, 0, 1, 3)  # [T][L][B][D]
     assert np.all(np.isfinite(gpre))
     e_pre = max(out_err(gpre[:, l], ref_pre[:, l]) for l in range(cfg.n_layers))
     es = state_err(gS_pre, ref_S_pre)
@@ -143,9 +153,8 @@ def test_prefill_rerun_is_bitwise_identical():
 
 def test_prefill_rejects_unsupported_shapes():
     import gated_deltanet_layer_dn_amd as dn
-    # a batch of two sequences, a 64-wide head and the per-key decay are not prefill shapes
-    for cfg in (gi.custom("pf_b2", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=2),
-                gi.custom("pf_d64", d_model=1024, n_k_heads=4, d_k=64, n_v_heads=8, d_v=64),
+    # a 64-wide head and the per-key decay are not prefill shapes
+    for cfg in (gi.custom("pf_d64", d_model=1024, n_k_heads=4, d_k=64, n_v_heads=8, d_v=64),
                 gi.custom("pf_pk", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128,
                           flags=gi.DN_ALPHA_PER_KEY)):
         layers, stream = gi.generate(cfg)
