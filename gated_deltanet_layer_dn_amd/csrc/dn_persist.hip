@@ -776,19 +776,23 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DK + 32 * pr);
         const v4f* A4 = reinterpret_cast<const v4f*>(&apk[PK ? l : 0][32 * pr]);
         float sv[32];
-        float kvp = 0.f;
+        float kvp = 0.f, qvp = 0.f, kqp = 0.f;
         wait_counter(&sm.s_ready, NCW * (l + 1), &sm.abort_flag);  // the slice has landed in LDS
         // the sums run over the raw q and k; the 1/norm factors multiply the finished sums (and the
-        // delta), so the fp64 norm reductions below can overlap the state arithmetic
+        // delta), so the fp64 norm reductions below can overlap the state arithmetic. The readout
+        // over the updated state, (S' )^T q = (decayed S)^T q + delta (k . q), takes its sums in the
+        // same pass, so it is published before the update of the slice.
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const v4f kk = K4[q], st = sm.sbuf[64 * q + lane];
+          const v4f kk = K4[q], qq = Q4[q], st = sm.sbuf[64 * q + lane];
           v4f av = {alpha, alpha, alpha, alpha};  // decay of rows 32 pr + 4 q ..
           if constexpr (PK) av = A4[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             sv[4 * q + e] = av[e] * st[e];  // decay
             kvp = fmaf(sv[4 * q + e], kk[e], kvp);
+            qvp = fmaf(sv[4 * q + e], qq[e], qvp);
+            kqp = fmaf(kk[e], qq[e], kqp);
           }
         }
         // L2 norms in double, eps inside the sqrt (independent of the loop above, so the two overlap)
@@ -799,21 +803,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         const float kv = kn * quad_sum(kvp);  // (decayed S)^T k^ of column jc
         const float dk = beta * (val[4] - kv) * kn;  // delta times 1/|k|
         DN_MARK(a, l, 13);
-        float op = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const v4f qq = Q4[q], kk = K4[q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[4 * q + e] = fmaf(kk[e], dk, sv[4 * q + e]);  // delta rule write
-            op = fmaf(sv[4 * q + e], qq[e], op);             // readout of the updated state
-          }
-        }
-        const float o = qn * quad_sum(op);
-        // park the updated slice in LDS; it is written back while phase C runs
-#pragma unroll
-        for (int q = 0; q < 8; ++q) sm.sbuf[q * 64 + lane] = v4f{sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]};
-        DN_MARK(a, l, 14);
+        const float o = qn * fmaf(dk, quad_sum(kqp), quad_sum(qvp));
         const float gt = sm.nw[l][jc] * o * silu(val[5]);
         const float osq = wave_total_f(pr == 0 ? o * o : 0.f);
         DN_MARK(a, l, 15);
@@ -830,6 +820,16 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
           if (lane < NREP)
             st_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
         }
+        // the delta rule write, after the readout is out; the slice is parked in LDS and written
+        // back while phase C runs
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const v4f kk = K4[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[4 * q + e] = fmaf(kk[e], dk, sv[4 * q + e]);
+          sm.sbuf[q * 64 + lane] = v4f{sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]};
+        }
+        DN_MARK(a, l, 14);
         DN_MARK(a, l, 5);
       }
       if (lane == 0) bump_counter(&sm.b_done);
