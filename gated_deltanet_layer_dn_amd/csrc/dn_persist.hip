@@ -502,14 +502,17 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 #pragma unroll
           for (int j = 0; j < 3; ++j)
             if (j < K - 1) accv = fmaf(ra_cw[j], ra_ring[j], accv);
+          outv = silu(accv);
+        }
+        // the hand-off word first: stores leave in order, and the history's can wait
+        ll_store(a.U + r, outv, tag);
+        if (r < C) {
           float* rg = a.ring + (size_t)l * (K - 1) * C + r;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             if (j + 1 < K - 1) rg[(size_t)j * C] = ra_ring[j + 1];
           if (K > 1) rg[(size_t)(K - 2) * C] = u;
-          outv = silu(accv);
         }
-        ll_store(a.U + r, outv, tag);
       }
       if (lane == 0) bump_counter(&sm.a_done);
       if (tid == 0) DN_MARK(a, l, 3);
@@ -582,9 +585,9 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       }
       const int r = g.c_row0 + lane;
       const float o = rc_s * mine;
-      if (lane < RC && r < g.c_row_end) a.out[(size_t)l * D + r] = o;
       if (l + 1 < a.L) {
-        // lanes 0..NREP-1 write the replicas of each row, row i's value taken from lane i
+        // lanes 0..NREP-1 write the replicas of each row, row i's value taken from lane i; these
+        // hand-off words go out before the layer's output store
 #pragma unroll
         for (int i = 0; i < RC; ++i) {
           const float oi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o), i));
@@ -592,6 +595,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
           if (lane < NREP && ri < g.c_row_end) st_store(a.X + (size_t)lane * D + ri, oi, tag);
         }
       }
+      if (lane < RC && r < g.c_row_end) a.out[(size_t)l * D + r] = o;
       if (lane == 0) bump_counter(&sm.c_done);
       if (tid == 0) DN_MARK(a, l, 8);
       if (g.has_b) {
@@ -610,8 +614,9 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 }
 
 // Communication waves: poll and stage x and the gated readout; the first one also runs phase B.
-// Each poll starts only once this workgroup's own share of the data it waits for is done, so
-// that the rounds that are bound to miss are not issued.
+// The polls of the layer input and of the gated readout start only once this workgroup's own
+// share of that data is done, so that the rounds that are bound to miss are not issued (starting
+// them at once measured slower); the in_proj poll of the recurrence starts at once.
 // PK: one decay per key channel; apk [L][128] holds this head's decays (LDS).
 // GT: gates from the in_proj's gate rows; sm.gate holds this head's a_log, a_bias per layer.
 template <int BITS, int NCHA, int NCHC, bool PK, bool GT>
@@ -754,7 +759,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       float val[NU];
 #pragma unroll
       for (int i = 0; i < NU; ++i) val[i] = 0.f;
-      wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
+      // the poll starts at once: waiting for this workgroup's own phase A first measured slower
       DN_MARK(a, l, 10);
       unsigned rounds = 0;
       ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, a.spin_cap, &rounds, DN_TS(a, l, 20));
