@@ -479,6 +479,16 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       int acc[RA][3];
       dot_rows<BITS, RA, NCHA>(wa, sm.xs, D, lane, acc);
       const float dot = reduce_rows<BITS, RA>(acc, s1, lane);
+      if (g.has_b) {
+        // this wave's chunk of the state slice has landed in LDS, before this phase's stores go
+        // out (vector memory operations complete in order, stores included): the only operations
+        // issued after its copy are the out_proj prefetch loads of this layer, RC * NCHC weight
+        // loads and one scale load when the wave owns a row, none otherwise
+        static_assert(RC * NCHC <= 15, "");
+        if (g.c_row0 + RC <= g.c_row_end) DN_WAIT_VMCNT(RC * NCHC);
+        else DN_WAIT_VMCNT(0);
+        if (lane == 0) bump_counter(&sm.s_ready);
+      }
       const int r = g.a_row0 + lane;
       if (lane < RA && r < g.a_row_end) {
         const float u = ra_s * dot;
@@ -502,12 +512,6 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       }
       if (lane == 0) bump_counter(&sm.a_done);
       if (tid == 0) DN_MARK(a, l, 3);
-      if (g.has_b) {
-        // this wave's chunk of the slice (prefetched a layer ago, older than its last weight
-        // loads) has landed; the wait also covers the write-back stores
-        DN_WAIT_VMCNT(0);
-        if (lane == 0) bump_counter(&sm.s_ready);
-      }
       // the next layer's in_proj rows stream in once this workgroup's phase-B inputs have
       // arrived, so that the u hand-off is not queued behind them
       wait_counter(&sm.u_done, l + 1, &sm.abort_flag);
