@@ -57,7 +57,7 @@ constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
 // flight, so that the compute unit's memory pipeline is never full and the communication
 // waves' hand-off loads and stores are not queued behind a whole layer of weights.
 #ifndef DN_PREFETCH_INFLIGHT
-#define DN_PREFETCH_INFLIGHT 2
+#define DN_PREFETCH_INFLIGHT 3
 #endif
 static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
 // The last DN_PREFETCH_TAIL in_proj row-chunk loads of a layer are issued without the throttle.
