@@ -14,8 +14,10 @@
 //    activations.
 //  * Phase B (recurrence): workgroup b owns value head b / (dv/16) and 16 of its value columns; its
 //    first communication wave keeps that 128x16 slice of the state in registers (lane 4j+p: column
-//    j, key rows 32p..32p+31), prefetched one layer ahead, and performs decay, delta rule, readout
-//    and the gate for those columns; sums over the key rows are in-lane plus two DPP steps.
+//    j, key rows 32p..32p+31), prefetched one layer ahead. It decays the slice, takes the sums
+//    for the delta and for the readout over the updated state in one pass, publishes the gated
+//    readout of its columns and only then writes the delta rule into the slice; sums over the key
+//    rows are in-lane plus two DPP steps.
 //  * Phase C (gated RMSNorm finish + out_proj): each workgroup owns D/NWG out_proj rows.
 // Hand-offs between workgroups carry no fences: every cross-workgroup value travels in a tagged
 // word stored and loaded with device-coherent (sc1) accesses, and a reader spins until each word
@@ -23,13 +25,13 @@
 // only in part, uses 64-bit words (fp32 value, 32-bit tag); the layer output and the gated readout,
 // which every workgroup reads whole, use 32-bit words whose two low mantissa bits hold the tag mod
 // 4, read four at a time. Tags grow by one per layer and never repeat within 2^32 layer steps, so
-// buffers need no reset.
+// buffers need no reset between launches (dn_set_state restarts them after an aborted launch).
 // Compute waves never poll, so their outstanding weight prefetches never delay a hand-off (a
 // wave's loads complete in order); the communication waves poll, stage activations into LDS, and
 // run phase B. The next layer's in_proj rows are requested only after phase B's inputs arrived.
 //
-// GEMV arithmetic as in the layer kernels: activations split into three int8 terms, exact int32
-// dot products with v_dot4_i32_i8, combined in double.
+// GEMV arithmetic: activations split into three int8 terms, exact int32 dot products with
+// v_dot4_i32_i8 per lane, folded into one fp32 partial per lane and summed over the wave in fp32.
 //
 // Gates on the card (GT): in workgroups wg < 2 Hv the second communication wave computes in_proj
 // row R + wg (gate a of head wg, or gate b of head wg - Hv) during phase A and publishes it with
