@@ -214,6 +214,7 @@ struct Smem {
   int8_t xs[3 * 4096];     // three-term split of x for phase A
   float inv[64];           // per value head 1/rms of the readout
   float qk[2 * DK];        // raw q and k of phase B's key head
+  v4i gwl[2][64];          // GT: the next layer's gate row (lane's 16-byte chunks), copied straight to LDS
   v4f sbuf[8 * 64];        // phase B's updated state slice until its write-back
   float stat[16];          // partial statistics from the communication waves, split scale
   float gate[MAXL][2];     // alpha, beta of this workgroup's value head, per layer
@@ -662,12 +663,15 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
   // weights held one layer ahead like the compute waves' rows
   constexpr int rowbytes_in = BITS == 8 ? D : D / 2;
   const bool runs_gate = GT && cw == 1 && wg < 2 * Hv;
-  v4i gw[1][NCHA];
+  // the row's weights wait in LDS rather than in registers, which this wave's other work needs
+  static_assert(NCHA <= 2, "");
   float gsc = 0.f;
   auto load_g = [&](int l) {
     const int8_t* wr = reinterpret_cast<const int8_t*>(a.layers[l].w_in) + (size_t)(a.R + wg) * rowbytes_in;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the previous row's LDS reads are done
 #pragma unroll
-    for (int k = 0; k < NCHA; ++k) gw[0][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wr) + lane + 64 * k);
+    for (int k = 0; k < NCHA; ++k)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const v4i*>(wr) + lane + 64 * k, &sm.gwl[k][0], 16, 0, 0);
     gsc = a.layers[l].s_in[a.R + wg];
   };
   if (runs_gate) load_g(0);
@@ -727,6 +731,9 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
     if (runs_gate) {
       // gate row R + wg on the staged x, published as in_proj output; then the next layer's row
       int acc[1][3];
+      v4i gw[1][NCHA];
+#pragma unroll
+      for (int k = 0; k < NCHA; ++k) gw[0][k] = sm.gwl[k][lane];
       dot_rows<BITS, 1, NCHA>(gw, sm.xs, D, lane, acc);
       const float dot = reduce_rows<BITS, 1>(acc, sm.stat[8], lane);
       if (lane == 0) ll_store(Ub + a.R + wg, gsc * dot, tag);
