@@ -16,6 +16,7 @@
 
 #include "dn.h"
 #include "dn_internal.h"
+#include "dn_tsplit_norm.h"
 
 #define DN_API extern "C" __attribute__((visibility("default")))
 
@@ -690,14 +691,24 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
     ps.cw = h->pf_cw; ps.S = h->S + l * h->s_elems + sb * s_seq; ps.transposed = h->persist ? 1 : 0;
     ps.T = n_tokens; ps.Hv = c.n_v_heads; ps.NCH = nch; ps.V = V; ps.o = h->pf_o;
     if (dn::launch_pscan(ps, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    dn::PNormArgs pn{h->pf_o, h->pf_u, w.norm_w, n_tokens, R, h->C, V, c.eps_rms};
-    if (dn::launch_pnorm(pn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    // the gated RMSNorm: its own pass, or fused into the split for the library GEMM (the readout
+    // rows and z are aligned: V, R and C are multiples of 128)
+    const bool norm_in_split = lt_out && V <= 8192;
+    if (!norm_in_split) {
+      dn::PNormArgs pn{h->pf_o, h->pf_u, w.norm_w, n_tokens, R, h->C, V, c.eps_rms};
+      if (dn::launch_pnorm(pn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    }
     if (!check()) return fail(h, DN_E_DEVICE);
     // out_proj
     dn::BEpiArgs e{};
     if (lt_out) {
       dn::TSplitArgs so{h->pf_o, V, V, n_tokens, tx, h->pf_sc, h->pf_ssq};
-      if (dn::launch_tsplit(so, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      if (norm_in_split) {
+        const dn::TSplitNormArgs sn{so, h->pf_u + h->C, R, w.norm_w, c.eps_rms};
+        if (dn::launch_tsplit_norm(sn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      } else if (dn::launch_tsplit(so, st) != hipSuccess) {
+        return fail(h, DN_E_DEVICE);
+      }
       if (dn::lt_gemm_i8(h->lt, 1, w.w_out, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
       e.terms = td; e.s1 = h->pf_sc; e.KS = 0;
     } else {

@@ -24,6 +24,7 @@
 #include <cstdint>
 
 #include "dn_internal.h"
+#include "dn_tsplit_norm.h"
 
 namespace dn {
 namespace {
@@ -186,6 +187,66 @@ __global__ __launch_bounds__(256) void k_tsplit(const TSplitArgs a) {
     *reinterpret_cast<int*>(xh + c) = pack(h);
     *reinterpret_cast<int*>(xh + plane + c) = pack(m);
     *reinterpret_cast<int*>(xh + 2 * plane + c) = pack(l);
+  }
+}
+
+// k_tsplit of the readout rows with the gated RMSNorm fused in front: thread i holds columns
+// 1024 p + 4 i .. +3 of pass p, so a head's 128 columns are 32 consecutive lanes of one pass; the
+// normalised, gated row stays in registers for the split.
+__global__ __launch_bounds__(256) void k_tsplit_norm(const TSplitNormArgs a) {
+  constexpr int NP = 8;  // passes of 1024 columns (K <= 8192)
+  __shared__ float rmx[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, t = blockIdx.x;
+  const int K = a.sp.K;
+  const float* row = a.sp.act + (size_t)t * a.sp.act_stride;
+  const float* zr = a.z + (size_t)t * a.z_stride;
+  v4f y[NP];
+  float mx = 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c = 1024 * p + 4 * tid;
+    y[p] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (c < K) {  // K is a multiple of 128, so a head's 32 lanes are all in or all out
+      const v4f o = *reinterpret_cast<const v4f*>(row + c);
+      const v4f z = *reinterpret_cast<const v4f*>(zr + c);
+      const v4f w = *reinterpret_cast<const v4f*>(a.norm_w + (c & 127));
+      float ss = (o[0] * o[0] + o[1] * o[1]) + (o[2] * o[2] + o[3] * o[3]);
+#pragma unroll
+      for (int m = 1; m < 32; m <<= 1) ss += __shfl_xor(ss, m);
+      const float inv = rsqrtf(ss / 128.0f + a.eps);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float g = z[e] / (1.0f + __expf(-z[e]));  // silu(z)
+        y[p][e] = w[e] * o[e] * inv * g;
+        mx = fmaxf(mx, fabsf(y[p][e]));
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+  if (lane == 0) rmx[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(rmx[0], rmx[1]), fmaxf(rmx[2], rmx[3]));
+  float s1 = mx * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+  if (tid == 0) a.sp.s1[t] = s1;
+  const size_t plane = (size_t)a.sp.T * K;
+  int8_t* xh = a.sp.xs + (size_t)t * K;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c = 1024 * p + 4 * tid;
+    if (c < K) {
+      int h[4], m[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split3(y[p][e], inv1, s1, inv2, s2, inv3, h[e], m[e], l[e]);
+      auto pack = [](const int (&q)[4]) {
+        return (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((q[3] & 0xFF) << 24);
+      };
+      *reinterpret_cast<int*>(xh + c) = pack(h);
+      *reinterpret_cast<int*>(xh + plane + c) = pack(m);
+      *reinterpret_cast<int*>(xh + 2 * plane + c) = pack(l);
+    }
   }
 }
 
@@ -752,6 +813,14 @@ hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st) 
 hipError_t launch_tsplit(const TSplitArgs& a, hipStream_t st) {
   if (a.T < 1 || a.K < 4 || a.K % 4 || a.act_stride % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tsplit, dim3(a.T), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tsplit_norm(const TSplitNormArgs& a, hipStream_t st) {
+  if (a.sp.T < 1 || a.sp.K < 128 || a.sp.K % 128 || a.sp.K > 8192 || a.sp.act_stride % 4 || a.z_stride % 4 ||
+      reinterpret_cast<uintptr_t>(a.z) % 16 || reinterpret_cast<uintptr_t>(a.sp.act) % 16)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tsplit_norm, dim3(a.sp.T), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
