@@ -692,9 +692,8 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
     ps.T = n_tokens; ps.Hv = c.n_v_heads; ps.NCH = nch; ps.V = V; ps.o = h->pf_o;
     if (dn::launch_pscan(ps, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     // the gated RMSNorm: its own pass, or fused into the split for the library GEMM (the readout
-    // rows and z are aligned: V, R and C are multiples of 128)
-    const bool norm_in_split = lt_out && V <= 8192;
-    if (!norm_in_split) {
+    // rows and z are aligned, V, R and C being multiples of 128; V <= 64 heads x 128 = 8192 columns)
+    if (!lt_out) {
       dn::PNormArgs pn{h->pf_o, h->pf_u, w.norm_w, n_tokens, R, h->C, V, c.eps_rms};
       if (dn::launch_pnorm(pn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     }
@@ -703,12 +702,8 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
     dn::BEpiArgs e{};
     if (lt_out) {
       dn::TSplitArgs so{h->pf_o, V, V, n_tokens, tx, h->pf_sc, h->pf_ssq};
-      if (norm_in_split) {
-        const dn::TSplitNormArgs sn{so, h->pf_u + h->C, R, w.norm_w, c.eps_rms};
-        if (dn::launch_tsplit_norm(sn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      } else if (dn::launch_tsplit(so, st) != hipSuccess) {
-        return fail(h, DN_E_DEVICE);
-      }
+      const dn::TSplitNormArgs sn{so, h->pf_u + h->C, R, w.norm_w, c.eps_rms};
+      if (dn::launch_tsplit_norm(sn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
       if (dn::lt_gemm_i8(h->lt, 1, w.w_out, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
       e.terms = td; e.s1 = h->pf_sc; e.KS = 0;
     } else {

@@ -37,6 +37,9 @@ PF = {
     # 768-wide model: not a whole-stack shape, so the handle keeps the canonical state layout
     "layer_kernels_handle": (gi.custom("pf_lk", d_model=768, n_k_heads=2, d_k=128, n_v_heads=4, d_v=128,
                                        n_tokens=70, ring_std=1.0), 66),
+    # the widest readout (64 value heads x 128 = 8192 columns), normalised and split in one pass
+    "widest_values": (gi.custom("pf_wv", d_model=256, n_k_heads=8, d_k=128, n_v_heads=64, d_v=128, n_tokens=70,
+                                ring_std=1.0), 66),
     # three sequences, each with its own 70-token prompt, then decode on the batched kernels
     "batch3": (gi.custom("pf_b3", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, batch=3, n_layers=2,
                          n_tokens=74, flags=gi.DN_X_RMSNORM, ring_std=1.0), 70),
