@@ -128,6 +128,90 @@ __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
       if (j < K - 1) a.ring_out[(size_t)j * a.C + r] = hist[j];
 }
 
+typedef int pc_v4i __attribute__((ext_vector_type(4)));
+
+// k_pconv on the library GEMM's exact term sums, four adjacent rows per thread: 16-byte loads and
+// stores, and every load unconditional (a token past the prompt reads the last token's row and is
+// not stored), so the loads of a run of tokens are all in flight together.
+constexpr int TR4 = 16;
+__global__ __launch_bounds__(256) void k_pconv4(const PConvArgs a) {
+  __shared__ float pn[TR4 + 3];  // pre-norm factors of tokens t0 - 3 .. t0 + TR4 - 1
+  const int r = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int t0 = blockIdx.y * TR4, nt = min(TR4, a.T - t0);
+  if ((int)threadIdx.x < TR4 + 3) {
+    const int tok = t0 - 3 + (int)threadIdx.x;
+    pn[threadIdx.x] = tok >= 0 && tok < a.T ? prenorm_of(a, tok) : 0.f;
+  }
+  __syncthreads();
+  if (r >= a.M) return;
+  float sr[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sr[e] = a.s[r + e];
+  const size_t plane = (size_t)a.T * a.M;
+  auto pre4 = [&](int t, float f, float (&o)[4]) {
+    const size_t at = (size_t)t * a.M + r;
+    const pc_v4i d0 = *reinterpret_cast<const pc_v4i*>(a.terms + at);
+    const pc_v4i d1 = *reinterpret_cast<const pc_v4i*>(a.terms + plane + at);
+    const pc_v4i d2 = *reinterpret_cast<const pc_v4i*>(a.terms + 2 * plane + at);
+    const double s1 = (double)a.s1[t];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = sr[e] * f * (float)(s1 * ((double)d0[e] + ((double)d1[e] + (double)d2[e] * (1.0 / 254.0)) * (1.0 / 254.0)));
+  };
+  float u[TR4][4];
+#pragma unroll
+  for (int i = 0; i < TR4; ++i) pre4(min(t0 + i, a.T - 1), pn[3 + i], u[i]);
+  if (r >= a.C) {  // z rows: no conv
+#pragma unroll
+    for (int i = 0; i < TR4; ++i)
+      if (i < nt) *reinterpret_cast<v4f*>(a.out + (size_t)(t0 + i) * a.M + r) = v4f{u[i][0], u[i][1], u[i][2], u[i][3]};
+    return;
+  }
+  const int K = a.Kc;
+  float w[4][4], hist[3][4] = {};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[e][j] = j < K ? a.conv_w[(size_t)(r + e) * K + j] : 0.f;
+  // hist[j]: pre-conv values of token t0 - (K-1) + j (oldest first); negative tokens from the history
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < K - 1) {
+      const int tok = t0 - (K - 1) + j;
+      if (tok >= 0) {
+        pre4(tok, pn[3 - (K - 1) + j], hist[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hist[j][e] = a.ring_in[(size_t)(tok + K - 1) * a.C + r + e];
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < TR4; ++i) {
+    if (i < nt) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float acc = w[e][K - 1] * u[i][e];
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          if (j < K - 1) acc = fmaf(w[e][j], hist[j][e], acc);
+        y[e] = silu(acc);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (j + 1 < K - 1) hist[j][e] = hist[j + 1][e];
+        if (K > 1) hist[K - 2][e] = u[i][e];
+      }
+      *reinterpret_cast<v4f*>(a.out + (size_t)(t0 + i) * a.M + r) = v4f{y[0], y[1], y[2], y[3]};
+    }
+  }
+  if (t0 + nt == a.T)
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < K - 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a.ring_out[(size_t)j * a.C + r + e] = hist[j][e];
+}
+
 // One workgroup per (value head, chunk): the chunk terms that do not depend on the incoming state.
 // The 64 x 64 and 64 x 128 products run on the fp32 matrix cores (lane layout and permuted sum
 // index as in k_pscan); the unit lower-triangular solve runs in the first wave (lane = column)
@@ -413,6 +497,11 @@ __global__ __launch_bounds__(128) void k_pnorm(const PNormArgs a) {
 }  // namespace
 
 hipError_t launch_pconv(const PConvArgs& a, hipStream_t st) {
+  if (a.terms && a.M % 4 == 0 && a.C % 4 == 0 && reinterpret_cast<uintptr_t>(a.terms) % 16 == 0 &&
+      reinterpret_cast<uintptr_t>(a.out) % 16 == 0) {
+    hipLaunchKernelGGL(k_pconv4, dim3((a.M / 4 + 255) / 256, (a.T + TR4 - 1) / TR4), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_pconv, dim3((a.M + 255) / 256, (a.T + TR - 1) / TR), dim3(256), 0, st, a);
   return hipGetLastError();
 }
