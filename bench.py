@@ -94,7 +94,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (reference for the HBM byte counters)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the read-stream ceiling of the device (libdn_probe) and print it")
+    ap.add_argument("--cpu-leg", type=int, default=0, metavar="THREADS",
+                    help=argparse.SUPPRESS)  # internal: the oracle sample, run in a child process
     args = ap.parse_args()
+
+    if args.cpu_leg:
+        return cpu_leg(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -102,8 +109,16 @@ def main():
                                    "is measured on a single MI355X (--gpus 1)"}))
         sys.exit(2)
 
+    # the CPU baseline first, in child processes that never touch the GPU (OpenMP settings are
+    # read when the oracle's library loads)
+    cpu = None if args.no_cpu_baseline or args.ceiling or args.copy_calibration else cpu_baseline(args)
+
     import numpy as np
     import torch
+
+    if args.ceiling:
+        print(json.dumps(read_ceiling()), flush=True)
+        return
 
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
@@ -119,7 +134,7 @@ def main():
     import gated_deltanet_layer_dn_amd as dn
 
     if args.config == "prefill":
-        return bench_prefill(args, gi, dn)
+        return bench_prefill(args, gi, dn, cpu)
     if args.config == "stack_perkey":  # the stack workload with one decay per key channel
         cfg = gi.CONFIGS["stack"].replace(name="stack_perkey", flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
     elif args.config == "stack_gates":  # the stack workload with the gates computed on the card
@@ -146,6 +161,13 @@ def main():
     outs = torch.empty((max(args.steps, 1), cfg.n_layers, cfg.batch, cfg.d_model), dtype=torch.float32, device=dev)
     scratch_out = st.new_out()
 
+    # an untimed run of the same steps from the initial state, kept for the bitwise comparison
+    # with the timed run (the decode step is deterministic run to run)
+    ref_outs = torch.empty_like(outs)
+    for i in range(args.steps):
+        t = i % T
+        st.step(x[t], al[t], be[t], ref_outs[i])
+    torch.cuda.synchronize()
     # warmup, then restart from the initial state so the timed run is the workload itself
     for i in range(args.warmup):
         t = i % T
@@ -172,6 +194,9 @@ def main():
     bytes_step = cfg.metric_bytes_per_step()
     gbs = bytes_step * args.steps / sec / 1e9
     assert torch.isfinite(outs).all().item(), "non-finite output"
+    assert st.status() == dn.DN_OK, "a step failed on the device"
+    same = bool(torch.equal(outs, ref_outs))
+    log(f"[bench] timed run bitwise equal to the untimed run: {same}")
     log(f"[bench] {args.steps} steps in {ms:.3f} ms: {ms * 1e3 / args.steps:.2f} us/step, "
         f"{tokens_per_s:.1f} tok/s, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
 
@@ -189,23 +214,11 @@ def main():
                 "launch_us_mean": round(kern_us, 2), "launch_us_min": round(float(launch_us.min()), 2),
                 "launch_us_max": round(float(launch_us.max()), 2), "bytes_per_launch": bytes_step}
     log(f"[bench] launch time mean {kern_us:.2f} us (min {launch_us.min():.2f}, max {launch_us.max():.2f})")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle as orc
-        orc.lib()
-        # calibrate on one token, then run a bounded sample of the same workload
-        c0 = time.time()
-        orc.run(cfg, layers, stream, n_tokens=1)
-        per_tok = max(time.time() - c0, 1e-3)
-        n = int(max(1, min(T, args.cpu_seconds / per_tok)))
-        c0 = time.time()
-        orc.run(cfg, layers, stream, n_tokens=n)
-        csec = time.time() - c0
-        cpu = {"value": round(n * cfg.batch / csec, 3), "unit": "tokens/s", "cores": orc.threads(),
-               "kind": "oracle",
-               "sample": f"first {n} of {T} tokens of the same workload (fp64 oracle, {csec:.1f} s)"}
-        log(f"[bench] oracle: {n} tokens in {csec:.1f}s on {orc.threads()} threads")
+    ceil = read_ceiling()
+    roofline["measured_ceiling"] = ceil["read_ceiling_gbs"]
+    roofline["frac_of_measured_ceiling"] = round(achieved / ceil["read_ceiling_gbs"], 4)
+    log(f"[bench] read-stream ceiling {ceil['read_ceiling_gbs']:.0f} GB/s: "
+        f"{100 * roofline['frac_of_measured_ceiling']:.1f}% of it")
 
     rec = {
         "metric": "DeltaNet decode tokens/s (30-layer stack) + achieved HBM GB/s % of peak",
@@ -229,13 +242,111 @@ def main():
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "timed_equals_untimed": same,
         "device": f"{props.name} {getattr(props, 'gcnArchName', '')}".strip(),
     }
     st.close()
     print(json.dumps(rec), flush=True)
 
 
-def bench_prefill(args, gi, dn):
+def read_ceiling(gib: int = 2, reps: int = 8):
+    """The read-stream ceiling of the device: a plain streaming read of `gib` GiB (beyond the
+    last-level cache) with every compute unit, timed with HIP events; the best of `reps` runs."""
+    import ctypes
+
+    import torch
+
+    import gated_deltanet_layer_dn_amd as dn
+    lib = ctypes.CDLL(dn.PROBE_LIB_PATH)
+    lib.dn_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.dn_probe_read_stream.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = cus * 8
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    best = 0.0
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        rc = lib.dn_probe_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        assert rc == 0, rc
+        if r:  # the first run warms up
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    return {"read_ceiling_gbs": round(best, 1), "bytes": nbytes, "blocks": blocks, "reps": reps,
+            "frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_leg(args):
+    """Child process: the oracle over a bounded sample of the workload, with the OpenMP settings
+    of its environment; prints one JSON line."""
+    import dn_inputs as gi
+    import oracle as orc
+    if args.config == "prefill":
+        cfg = gi.CONFIGS["stack"].replace(name="prefill", n_tokens=args.prompt)
+    elif args.config == "stack_perkey":
+        cfg = gi.CONFIGS["stack"].replace(name="stack_perkey", flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
+    elif args.config == "stack_gates":
+        cfg = gi.CONFIGS["stack"].replace(name="stack_gates", flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE)
+    else:
+        cfg = gi.CONFIGS[args.config]
+    layers, stream = gi.generate(cfg)
+    orc.lib()
+    # calibrate on one token, then run a bounded sample of the same workload
+    c0 = time.time()
+    orc.run(cfg, layers, stream, n_tokens=1)
+    per_tok = max(time.time() - c0, 1e-3)
+    n = int(max(1, min(cfg.n_tokens, args.cpu_seconds / per_tok)))
+    c0 = time.time()
+    orc.run(cfg, layers, stream, n_tokens=n)
+    csec = time.time() - c0
+    print(json.dumps({"tokens": n, "seconds": csec, "threads": orc.threads(), "batch": cfg.batch,
+                      "of_tokens": cfg.n_tokens}), flush=True)
+
+
+def cpu_baseline(args):
+    """The oracle timed on the host's cores: all of them (OMP_PLACES=cores, OMP_PROC_BIND=close),
+    then one thread, each on a bounded sample of the same workload, in child processes."""
+    import subprocess
+    allc = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    res = {}
+    for n, secs in ((allc, args.cpu_seconds), (1, max(2.0, args.cpu_seconds / 3))):
+        env = dict(os.environ, OMP_NUM_THREADS=str(n), OMP_PLACES="cores", OMP_PROC_BIND="close")
+        cmd = [sys.executable, os.path.abspath(__file__), "--cpu-leg", str(n), "--config", args.config,
+               "--prompt", str(args.prompt), "--cpu-seconds", str(secs)]
+        r = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            log(f"[bench] oracle leg with {n} thread(s) failed: {r.stderr[-500:]}")
+            return None
+        res[n] = json.loads(r.stdout.strip().splitlines()[-1])
+        log(f"[bench] oracle: {res[n]['tokens']} tokens in {res[n]['seconds']:.1f}s on {res[n]['threads']} thread(s)")
+    a, o = res[allc], res[1]
+    return {"value": round(a["tokens"] * a["batch"] / a["seconds"], 3), "unit": "tokens/s", "cores": a["threads"],
+            "kind": "oracle",
+            "sample": f"first {a['tokens']} of {a['of_tokens']} tokens of the same workload (fp64 oracle, "
+                      f"{a['seconds']:.1f} s, OMP_PLACES=cores OMP_PROC_BIND=close)",
+            "one_thread_value": round(o["tokens"] * o["batch"] / o["seconds"], 3),
+            "one_thread_sample": f"first {o['tokens']} tokens ({o['seconds']:.1f} s)",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def bench_prefill(args, gi, dn, cpu):
     """Prompt throughput: one step is a prompt of --prompt tokens through the 30-layer stack
     (dn_prefill), starting from the seeded initial states each time (the reset is outside the
     timed region). Synthetic inputs of the stack workload's distributions."""
@@ -280,20 +391,6 @@ def bench_prefill(args, gi, dn):
     proj_flops = 2.0 * w_per_layer * T * cfg.n_layers
     log(f"[bench] prefill of {T} tokens x {cfg.n_layers} layers: {per:.3f} ms ({tok_s:.0f} prompt tokens/s); "
         f"projections {proj_flops / (per * 1e-3) / 1e12:.1f} TFLOP/s algorithmic")
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle as orc
-        orc.lib()
-        c0 = time.time()
-        orc.run(cfg, layers, stream, n_tokens=1)
-        per_tok = max(time.time() - c0, 1e-3)
-        n = int(max(1, min(T, args.cpu_seconds / per_tok)))
-        c0 = time.time()
-        orc.run(cfg, layers, stream, n_tokens=n)
-        csec = time.time() - c0
-        cpu = {"value": round(n / csec, 3), "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
-               "sample": f"first {n} of {T} prompt tokens of the same workload, token by token (fp64 oracle, "
-                         f"{csec:.1f} s)"}
     rec = {
         "metric": "DeltaNet prefill prompt tokens/s (30-layer stack)",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -1,10 +1,10 @@
 """Thin Python binding of libdn (the gated-DeltaNet decode step on MI355X).
 
 Argument marshalling only: every step of the decode token runs in the HIP kernels of
-``libdn.so``. PyTorch provides device memory and streams. The functions carry the C ABI's
-names (``dn_create``, ``dn_set_state``, ``dn_get_state``, ``dn_step``, ``dn_destroy``,
-``dn_prefill``);
-``DeltaNetStack`` wraps them. Loading fails loudly when the library is not built.
+``libdn.so`` (``dn_create``, ``dn_set_state``, ``dn_get_state``, ``dn_step``, ``dn_destroy``),
+and of a prompt in those of ``libdn_prefill.so`` (``dn_prefill``). PyTorch provides device
+memory and streams. The functions carry the C ABI's names; ``DeltaNetStack`` wraps them.
+Loading fails loudly when a library is not built.
 """
 from __future__ import annotations
 
@@ -16,13 +16,16 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # DN_LIB selects another build of the library (an instrumented one, for instance)
 LIB_PATH = os.environ.get("DN_LIB") or os.path.join(_PKG, "libdn.so")
+PREFILL_LIB_PATH = os.environ.get("DN_PREFILL_LIB") or os.path.join(_PKG, "libdn_prefill.so")
+PROBE_LIB_PATH = os.path.join(_PKG, "libdn_probe.so")  # measurement only (bench.py)
 
 DN_OK, DN_E_INVAL, DN_E_NOMEM, DN_E_DEVICE, DN_E_DISABLED, DN_E_FAULT = 0, -1, -2, -3, -4, -5
 DN_X_RMSNORM = 1
 DN_ALPHA_PER_KEY = 2  # alpha [L][B][Hv][dk]: one decay per key channel
 DN_GATES_ON_DEVICE = 4  # gates from two more in_proj rows per value head; alpha/beta not read
 DN_PREFILL_MAX_TOKENS = 65535  # prompt tokens per dn_prefill call
-EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy", "dn_prefill")
+EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy")  # libdn.so
+PREFILL_EXPORTED = ("dn_prefill",)  # libdn_prefill.so
 
 _ERR = {DN_OK: "ok", DN_E_INVAL: "invalid argument", DN_E_NOMEM: "out of device memory",
         DN_E_DEVICE: "device error", DN_E_DISABLED: "layer disabled after a failed step",
@@ -66,9 +69,25 @@ def lib():
         L.dn_get_state.argtypes = [P, P, P]; L.dn_get_state.restype = ctypes.c_int
         L.dn_step.argtypes = [P, P, P, P, P, P]; L.dn_step.restype = ctypes.c_int
         L.dn_destroy.argtypes = [P]; L.dn_destroy.restype = None
-        L.dn_prefill.argtypes = [P, P, ctypes.c_int, P, P, P, P]; L.dn_prefill.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+_plib = None
+
+
+def prefill_lib():
+    """Load libdn_prefill.so (after libdn.so, whose handles it takes); raises if it is missing."""
+    global _plib
+    if _plib is None:
+        lib()
+        if not os.path.exists(PREFILL_LIB_PATH):
+            raise ImportError(f"libdn_prefill.so is not built ({PREFILL_LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(PREFILL_LIB_PATH)
+        P = ctypes.c_void_p
+        L.dn_prefill.argtypes = [P, P, ctypes.c_int, P, P, P, P]; L.dn_prefill.restype = ctypes.c_int
+        _plib = L
+    return _plib
 
 
 def _ptr(t) -> int | None:
@@ -85,7 +104,7 @@ def _check(rc: int, what: str):
         raise DNError(rc, what)
 
 
-# --- the six calls -------------------------------------------------------------------------
+# --- the calls -------------------------------------------------------------------------
 
 def dn_create(cfg: dn_config, weights: list[dn_weights]) -> int:
     arr = (dn_weights * len(weights))(*weights)
@@ -100,6 +119,12 @@ def dn_set_state(h: int, S, ring=None) -> None:
 
 def dn_get_state(h: int, S, ring=None) -> None:
     _check(lib().dn_get_state(h, _ptr(S), _ptr(ring)), "dn_get_state")
+
+
+def dn_status(h: int) -> int:
+    """dn_get_state with no buffers: wait for the device and return the C return code that
+    reports whether every step so far completed."""
+    return lib().dn_get_state(h, None, None)
 
 
 def _stream(stream, ref):
@@ -118,7 +143,8 @@ def dn_step(h: int, x, alpha, beta, out, stream=None) -> int:
 def dn_prefill(h: int, x, n_tokens: int, alpha, beta, out, stream=None) -> int:
     """Enqueue a prompt of n_tokens tokens (x [T][D], alpha/beta [T][L][Hv], out [L][T][D]);
     returns the C return code."""
-    return lib().dn_prefill(h, _ptr(x), int(n_tokens), _ptr(alpha), _ptr(beta), _ptr(out), _stream(stream, out))
+    return prefill_lib().dn_prefill(h, _ptr(x), int(n_tokens), _ptr(alpha), _ptr(beta), _ptr(out),
+                                    _stream(stream, out))
 
 
 def dn_destroy(h: int) -> None:
@@ -182,6 +208,10 @@ class DeltaNetStack:
         ring = torch.empty(rs, dtype=torch.float32, device=self.device)
         dn_get_state(self.h, S, ring)
         return S, ring
+
+    def status(self) -> int:
+        """Wait for the device; DN_OK if every step so far completed, else the error code."""
+        return dn_status(self.h)
 
     def new_out(self):
         return torch.empty((self.L, self.B, self.D), dtype=torch.float32, device=self.device)

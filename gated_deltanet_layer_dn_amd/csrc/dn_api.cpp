@@ -1,9 +1,5 @@
-// C-ABI host side of libdn: handle lifecycle, validation, state movement, launch sequence.
-//
-// The handle is the per-layer device object of page "qwen36: run the DeltaNet layer end to end
-// on the card" (section "What the PR does", Backend and Tier paragraphs): it owns the conv
-// history, the recurrent state and one token's scratch; the state moves only through
-// dn_set_state / dn_get_state, and dn_get_state still works after a failed step.
+// C-ABI host side of libdn: handle lifecycle, validation, state movement, launch sequence of
+// dn_step. The handle's layout is in dn_handle.h (shared with libdn_prefill).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -15,98 +11,18 @@
 #include <vector>
 
 #include "dn.h"
+#include "dn_handle.h"
 #include "dn_internal.h"
-#include "dn_tsplit_norm.h"
 
 #define DN_API extern "C" __attribute__((visibility("default")))
 
-struct dn_layer {
-  dn_config cfg;
-  std::vector<dn_weights> w;
-  int device = 0;
-  int R = 0, C = 0, V = 0;  // R: in_proj rows q|k|v|z (gate rows, if any, follow them)
-  bool gates = false;       // DN_GATES_ON_DEVICE: 2 Hv gate rows after the R rows
-  float* gal = nullptr;     // [B][Hv] scratch: gates computed on the card (per-layer and batched paths)
-  float* gbe = nullptr;
-  size_t s_elems = 0;     // per layer: B*Hv*dk*dv
-  size_t ring_elems = 0;  // per layer: B*(K-1)*C
-  float* S = nullptr;     // [L][B][Hv][dk][dv]
-  float* ring = nullptr;  // [L][B][K-1][C], oldest first
-  float* u = nullptr;     // [B][R] scratch: post-conv q|k|v, raw z
-  float* y = nullptr;     // [B][V] scratch: gated RMSNorm output
-  // whole-stack kernel (single sequence, 128 x 128 state tiles)
-  bool persist = false;
-  int nwg = 0;
-  dn::PersistShape ps{};
-  dn::LayerW* d_layers = nullptr;
-  unsigned* X = nullptr;    // hand-off buffers: layer output and gated readout in self-tagged
-                            // 32-bit words, in_proj output in 64-bit tagged words
-  uint64_t* U = nullptr;
-  unsigned* G = nullptr;
-  dn::Ctl* ctl = nullptr;
-  float* stage = nullptr;   // canonical-layout staging of the state for set/get
-  unsigned* err_host = nullptr;  // pinned host word the whole-stack kernel writes its error flag to
-  unsigned* err_dev = nullptr;   // the same word as the device addresses it
-  unsigned long long* timers = nullptr;  // instrumented builds: phase timestamps of the last step
-  // batched path (B >= 2, 128 x 128 state tiles): MFMA projections with split-K partial sums
-  bool batched = false;
-  int mf1 = 0, kr1 = 0, mf2 = 0, kr2 = 0;  // rows per workgroup / 64 and K range of in_proj, out_proj
-  bool up1 = false, up2 = false;           // the projection uses the all-loads-up-front GEMM (NRB = mf)
-  float* part = nullptr;                   // split-K partial sums
-  void* xs = nullptr;                      // activations split into int8 terms, fragment order
-  float* sc = nullptr;                     // their per-(sequence, 128-column chunk) scales
-  float* ssq = nullptr;                    // per-(sequence, chunk) sums of squares (input pre-norm)
-  // prefill scratch, sized for the longest prompt so far (pf_cap tokens)
-  int pf_cap = 0;
-  void* pf_xs = nullptr;                   // split activations of the prompt
-  float* pf_sc = nullptr;                  // their scales
-  float* pf_ssq = nullptr;                 // their per-chunk sums of squares
-  float* pf_part = nullptr;                // GEMM K-range partial sums [KS][T][M]
-  float* pf_u = nullptr;                   // [T][R] post-conv in_proj output
-  float* pf_cw = nullptr;                  // chunk terms of the recurrence
-  float* pf_o = nullptr;                   // [T][V] readout, then gated output
-  float* pf_ring = nullptr;                // the new conv history of a layer
-  float* pf_al = nullptr;                  // [T][Hv] gates computed on the card
-  float* pf_be = nullptr;
-  // 8-bit prefill projections as library int8 GEMMs (created at the first prefill)
-  dn::LtCtx* lt = nullptr;
-  bool lt_tried = false;
-  bool pf_own_gemm = false;                // DN_PREFILL_OWN_GEMM=1: always the hand-written GEMM
-  bool disabled = false;
-  long steps = 0;
-  long fault_step = 0;    // 1-based step to fail (0 = never)
-  long fault_stall = 0;   // 1-based step whose whole-stack launch may not wait in any hand-off (0 = never)
-  bool sync_debug = false;
-};
+using dn::DeviceScope;
+using dn::fail;
+using dn::host_err;
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Makes the handle's device current for the duration of a call and restores the caller's current
-// device on every return path, so that no entry point changes the calling thread's device.
-class DeviceScope {
- public:
-  explicit DeviceScope(int dev) {
-    if (hipGetDevice(&prev_) != hipSuccess) {
-      prev_ = -1;
-      ok_ = false;
-      return;
-    }
-    ok_ = prev_ == dev || hipSetDevice(dev) == hipSuccess;
-  }
-  ~DeviceScope() {
-    int cur = -1;
-    if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_) (void)hipSetDevice(prev_);
-  }
-  bool ok() const { return ok_; }
-  DeviceScope(const DeviceScope&) = delete;
-  DeviceScope& operator=(const DeviceScope&) = delete;
-
- private:
-  int prev_ = -1;
-  bool ok_ = false;
-};
 
 int validate(const dn_config* c) {
   if (!c) return DN_E_INVAL;
@@ -140,6 +56,8 @@ void free_all(dn_layer* h) {
   dfree(h->y);
   dfree(h->gal);
   dfree(h->gbe);
+  dfree(h->S_alt);
+  dfree(h->ring_alt);
   dfree(h->d_layers);
   dfree(h->X);
   dfree(h->U);
@@ -153,19 +71,9 @@ void free_all(dn_layer* h) {
   dfree(h->xs);
   dfree(h->sc);
   dfree(h->ssq);
-  dfree(h->pf_xs);
-  dfree(h->pf_sc);
-  dfree(h->pf_ssq);
-  dfree(h->pf_part);
-  dfree(h->pf_u);
-  dfree(h->pf_cw);
-  dfree(h->pf_o);
-  dfree(h->pf_ring);
-  dfree(h->pf_al);
-  dfree(h->pf_be);
-  h->pf_cap = 0;
-  dn::lt_destroy(h->lt);
-  h->lt = nullptr;
+  if (h->ext && h->ext_free) h->ext_free(h->ext);
+  h->ext = nullptr;
+  h->ext_free = nullptr;
 }
 
 // GEMM shape for an M x K projection: the all-loads-up-front kernel with 256-column K ranges and
@@ -233,6 +141,8 @@ int setup_persist(dn_layer* h) {
   if (dn::persist_occupancy(ps, &per_cu) != hipSuccess || per_cu < 1) return DN_OK;
   const size_t L = c.n_layers;
   bool ok = hipMalloc(&h->d_layers, sizeof(dn::LayerW) * L) == hipSuccess;
+  ok = ok && hipMalloc(&h->S_alt, sizeof(float) * L * h->s_elems) == hipSuccess;
+  ok = ok && hipMalloc(&h->ring_alt, sizeof(float) * (L * h->ring_elems + 1)) == hipSuccess;
   ok = ok && hipMalloc(&h->X, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
   const size_t u_words = h->R + (h->gates ? 2 * c.n_v_heads : 0);
   ok = ok && hipMalloc(&h->U, sizeof(uint64_t) * u_words) == hipSuccess;
@@ -246,6 +156,13 @@ int setup_persist(dn_layer* h) {
   ok = ok && hipMemset(h->timers, 0, sizeof(unsigned long long) * h->nwg * L * 32) == hipSuccess;
 #endif
   if (!ok) return DN_E_NOMEM;
+  // Cooperative launches make the runtime start the grid only when every workgroup can be resident
+  // at once, which the kernel's waits between workgroups need (DN_PERSIST_LAUNCH=plain: ordinary
+  // launches, which rely on the device being otherwise idle).
+  int coop = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device) != hipSuccess) coop = 0;
+  const char* lm = std::getenv("DN_PERSIST_LAUNCH");
+  h->coop = coop != 0 && !(lm && std::strcmp(lm, "plain") == 0);
   std::vector<dn::LayerW> lw(L);
   for (size_t l = 0; l < L; ++l)
     lw[l] = dn::LayerW{h->w[l].w_in,  h->w[l].s_in,  h->w[l].conv_w, h->w[l].norm_w,
@@ -278,15 +195,6 @@ int reset_handoff(dn_layer* h) {
   if (!ok) return DN_E_DEVICE;
   *h->err_host = 0;
   return DN_OK;
-}
-
-// The whole-stack kernel stores its error flag into host memory at the end of each launch; the
-// host reads it without synchronising, so a failure is seen at the first call after that launch.
-unsigned host_err(const dn_layer* h) { return *reinterpret_cast<volatile const unsigned*>(h->err_host); }
-
-int fail(dn_layer* h, int rc) {
-  h->disabled = true;
-  return rc;
 }
 
 }  // namespace
@@ -360,10 +268,10 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   if (const char* e = std::getenv("DN_FAULT_STEP")) h->fault_step = std::atol(e);
   if (const char* e = std::getenv("DN_FAULT_STALL")) h->fault_stall = std::atol(e);
   if (const char* e = std::getenv("DN_SYNC_DEBUG")) h->sync_debug = std::atoi(e) != 0;
-  if (const char* e = std::getenv("DN_PREFILL_OWN_GEMM")) h->pf_own_gemm = std::atoi(e) != 0;
   if (const char* e = std::getenv("DN_VERBOSE"); e && std::atoi(e) != 0)
-    std::fprintf(stderr, "[dn] handle: %d layer(s), batch %d: %s\n", cfg->n_layers, cfg->batch,
-                 h->persist ? "whole-stack kernel" : h->batched ? "batched kernels" : "per-layer kernels");
+    std::fprintf(stderr, "[dn] handle: %d layer(s), batch %d: %s%s\n", cfg->n_layers, cfg->batch,
+                 h->persist ? "whole-stack kernel" : h->batched ? "batched kernels" : "per-layer kernels",
+                 h->persist ? (h->coop ? ", cooperative launch" : ", ordinary launch") : "");
   *out = h;
   return DN_OK;
 }
@@ -391,14 +299,27 @@ DN_API int dn_set_state(dn_layer* h, const float* S, const float* ring) {
 }
 
 DN_API int dn_get_state(dn_layer* h, float* S, float* ring) {
-  if (!h || !S) return DN_E_INVAL;
+  if (!h || (!S && ring)) return DN_E_INVAL;
   DeviceScope dev(h->device);
   if (!dev.ok()) return DN_E_DEVICE;
+  if (!S) {
+    // status only: every launch so far has completed after the wait, so the whole-stack kernel's
+    // host-mapped error word is final
+    if (hipDeviceSynchronize() != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (h->persist && host_err(h)) return fail(h, DN_E_DEVICE);
+    return DN_OK;
+  }
   (void)hipDeviceSynchronize();  // a failed step may have left an error; copy what the device holds
   (void)hipGetLastError();
   const size_t L = h->cfg.n_layers;
+  const float* ring_cur = h->ring;
   if (h->persist) {
-    if (dn::launch_state_tile(h->S, h->stage, (int)L, h->cfg.n_v_heads, h->cfg.d_k, h->cfg.d_v, false, nullptr) !=
+    // the current one of the two buffers (a failed launch left it as before its token)
+    dn::Ctl ctl{};
+    if (hipMemcpy(&ctl, h->ctl, sizeof(ctl), hipMemcpyDeviceToHost) != hipSuccess) return DN_E_DEVICE;
+    const float* S_cur = (ctl.parity & 1u) ? h->S_alt : h->S;
+    ring_cur = (ctl.parity & 1u) ? h->ring_alt : h->ring;
+    if (dn::launch_state_tile(S_cur, h->stage, (int)L, h->cfg.n_v_heads, h->cfg.d_k, h->cfg.d_v, false, nullptr) !=
             hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
       return DN_E_DEVICE;
@@ -407,7 +328,7 @@ DN_API int dn_get_state(dn_layer* h, float* S, float* ring) {
     return DN_E_DEVICE;
   }
   if (ring && h->ring_elems &&
-      hipMemcpy(ring, h->ring, sizeof(float) * L * h->ring_elems, hipMemcpyDefault) != hipSuccess)
+      hipMemcpy(ring, ring_cur, sizeof(float) * L * h->ring_elems, hipMemcpyDefault) != hipSuccess)
     return DN_E_DEVICE;
   return hipDeviceSynchronize() == hipSuccess ? DN_OK : DN_E_DEVICE;
 }
@@ -443,22 +364,6 @@ int batched_proj(dn_layer* h, const void* W, const float* s, const float* act, i
 }
 }  // namespace
 
-namespace {
-// Gates of N input rows of layer l (DN_GATES_ON_DEVICE) into alpha_out/beta_out [N][Hv].
-hipError_t launch_layer_gates(const dn_layer* h, size_t l, const float* xl, int N, float* alpha_out, float* beta_out,
-                              hipStream_t st) {
-  const dn_config& c = h->cfg;
-  const dn_weights& w = h->w[l];
-  const size_t rowbytes = c.weight_bits == 8 ? (size_t)c.d_model : (size_t)c.d_model / 2;
-  dn::GateArgs g{};
-  g.x = xl; g.x_stride = c.d_model; g.N = N; g.D = c.d_model;
-  g.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; g.eps = c.eps_rms;
-  g.W = static_cast<const uint8_t*>(w.w_in) + (size_t)h->R * rowbytes; g.s = w.s_in + h->R;
-  g.a_log = w.a_log; g.a_bias = w.a_bias; g.Hv = c.n_v_heads;
-  g.alpha = alpha_out; g.beta = beta_out;
-  return dn::launch_gates(g, c.weight_bits, st);
-}
-}  // namespace
 
 DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float* beta, float* out, void* hip_stream) {
   if (!h || !x || !out) return DN_E_INVAL;
@@ -478,7 +383,8 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
   if (h->persist) {
     if (host_err(h)) return fail(h, DN_E_DEVICE);  // a completed launch reported a stalled hand-off
     dn::PersistArgs a{};
-    a.layers = h->d_layers; a.S = h->S; a.ring = h->ring; a.x = x; a.alpha = alpha; a.beta = beta; a.out = out;
+    a.layers = h->d_layers; a.x = x; a.alpha = alpha; a.beta = beta; a.out = out;
+    a.S[0] = h->S; a.S[1] = h->S_alt; a.ring[0] = h->ring; a.ring[1] = h->ring_alt;
     a.X = h->X; a.U = h->U; a.G = h->G; a.ctl = h->ctl; a.err_host = h->err_dev; a.timers = h->timers;
     a.L = (int)L; a.R = h->R; a.C = h->C; a.QK = c.n_k_heads * c.d_k; a.K = c.conv_k;
     a.Hk = c.n_k_heads; a.Hv = c.n_v_heads; a.flags = c.flags;
@@ -488,7 +394,12 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     // an injected stall: every hand-off gets a single poll round, so the launch aborts through its
     // own error path (reported by the next call) as soon as one exchange is not already complete
     a.spin_cap = (h->fault_stall > 0 && h->steps == h->fault_stall) ? 0u : dn::PERSIST_SPIN_CAP;
-    if (dn::launch_persist(a, h->ps, h->nwg, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    // a cooperative launch cannot be recorded into a graph here: under capture the launch is an
+    // ordinary one, and co-residency rests on the device being otherwise idle when it replays
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) return fail(h, DN_E_DEVICE);
+    const bool coop = h->coop && cap == hipStreamCaptureStatusNone;
+    if (dn::launch_persist(a, h->ps, h->nwg, coop, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
     return DN_OK;
   }
@@ -505,7 +416,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
       dn::BStateArgs bs{};
       bs.u = h->u; bs.S = h->S + l * h->s_elems;
       if (h->gates) {
-        if (launch_layer_gates(h, l, l == 0 ? x : out + (l - 1) * B * D, (int)B, h->gal, h->gbe, st) != hipSuccess)
+        if (dn::launch_layer_gates(h, l, l == 0 ? x : out + (l - 1) * B * D, (int)B, h->gal, h->gbe, st) != hipSuccess)
           return fail(h, DN_E_DEVICE);
         bs.alpha = h->gal; bs.beta = h->gbe;
       } else {
@@ -540,7 +451,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     dn::HeadArgs ha{};
     ha.u = h->u; ha.S = h->S + l * h->s_elems;
     if (h->gates) {
-      if (launch_layer_gates(h, l, xl, (int)B, h->gal, h->gbe, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+      if (dn::launch_layer_gates(h, l, xl, (int)B, h->gal, h->gbe, st) != hipSuccess) return fail(h, DN_E_DEVICE);
       ha.alpha = h->gal; ha.beta = h->gbe;
     } else {
       ha.alpha = alpha + l * a_layer; ha.beta = beta + l * B * c.n_v_heads;
@@ -561,162 +472,6 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     go.conv_w = nullptr; go.ring = nullptr; go.C = 0; go.K = 0;
     if (dn::launch_gemv(go, c.weight_bits, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
-  }
-  return DN_OK;
-}
-
-namespace {
-// K range of a prefill GEMM: the widest of 1024, 512, 256 columns that divides K.
-int pf_kr(int K) { return K % 1024 == 0 ? 1024 : K % 512 == 0 ? 512 : 256; }
-
-// Prefill scratch for prompts of up to T tokens (grown, never shrunk).
-int pf_reserve(dn_layer* h, int T) {
-  if (T <= h->pf_cap) return DN_OK;
-  const dn_config& c = h->cfg;
-  const size_t D = c.d_model, V = h->V, R = h->R;
-  const size_t nb = ((size_t)T + 63) / 64, nch = ((size_t)T + dn::PF_CT - 1) / dn::PF_CT;
-  const size_t ncmax = std::max(D, V) / 128;
-  // scratch of both GEMM paths: K-range partial sums (hand-written GEMM) or the three terms' int32
-  // sums (library GEMM); split activations in fragment blocks or as [3][T][K]
-  const size_t part = (size_t)T * std::max(std::max((D / pf_kr((int)D)) * R, (V / pf_kr((int)V)) * D),
-                                           3 * std::max(R, D));
-  const size_t xs_bytes = std::max(nb * ncmax * 24576, 3 * (size_t)T * std::max(D, V));
-  const size_t ring = std::max<size_t>(1, (size_t)(c.conv_k - 1) * h->C);
-  for (void** p : {&h->pf_xs, reinterpret_cast<void**>(&h->pf_sc), reinterpret_cast<void**>(&h->pf_ssq),
-                   reinterpret_cast<void**>(&h->pf_part), reinterpret_cast<void**>(&h->pf_u),
-                   reinterpret_cast<void**>(&h->pf_cw), reinterpret_cast<void**>(&h->pf_o),
-                   reinterpret_cast<void**>(&h->pf_ring), reinterpret_cast<void**>(&h->pf_al),
-                   reinterpret_cast<void**>(&h->pf_be)})
-    if (*p) {
-      (void)hipFree(*p);
-      *p = nullptr;
-    }
-  h->pf_cap = 0;
-  bool ok = hipMalloc(&h->pf_xs, xs_bytes) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_sc, sizeof(float) * std::max(nb * ncmax * 64, (size_t)T)) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_ssq, sizeof(float) * T * ncmax) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_part, sizeof(float) * part) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_u, sizeof(float) * T * R) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_cw, sizeof(float) * c.n_v_heads * nch * dn::PF_CHUNK_FLOATS) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_o, sizeof(float) * T * V) == hipSuccess;
-  ok = ok && hipMalloc(&h->pf_ring, sizeof(float) * ring) == hipSuccess;
-  if (h->gates) {
-    ok = ok && hipMalloc(&h->pf_al, sizeof(float) * T * c.n_v_heads) == hipSuccess;
-    ok = ok && hipMalloc(&h->pf_be, sizeof(float) * T * c.n_v_heads) == hipSuccess;
-  }
-  if (!ok) return DN_E_NOMEM;
-  h->pf_cap = T;
-  return DN_OK;
-}
-}  // namespace
-
-DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* alpha, const float* beta, float* out,
-                      void* hip_stream) {
-  if (!h || !x || !out || n_tokens < 1 || n_tokens > DN_PREFILL_MAX_TOKENS) return DN_E_INVAL;
-  if (!h->gates && (!alpha || !beta)) return DN_E_INVAL;
-  if (h->disabled) return DN_E_DISABLED;
-  const dn_config& c = h->cfg;
-  const size_t L = c.n_layers, D = c.d_model, T = n_tokens, B = c.batch;
-  if (c.d_k != 128 || c.d_v != 128 || (c.flags & DN_ALPHA_PER_KEY) || D % 256 || h->V % 256) return DN_E_INVAL;
-  const char* xb = reinterpret_cast<const char*>(x);
-  const char* ob = reinterpret_cast<const char*>(out);
-  if (ob < xb + sizeof(float) * B * T * D && xb < ob + sizeof(float) * L * B * T * D) return DN_E_INVAL;
-  DeviceScope dev(h->device);
-  if (!dev.ok()) return fail(h, DN_E_DEVICE);
-  if (h->persist && host_err(h)) return fail(h, DN_E_DEVICE);
-  if (int rc = pf_reserve(h, n_tokens); rc != DN_OK) {
-    (void)hipGetLastError();  // the failed allocation's error; the handle stays usable
-    return rc;
-  }
-  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-  const int QK = c.n_k_heads * c.d_k, V = h->V, R = h->R, K = c.conv_k;
-  const int nch = (n_tokens + dn::PF_CT - 1) / dn::PF_CT;
-  const int kr_in = pf_kr((int)D), kr_out = pf_kr(V);
-  auto check = [&]() { return !h->sync_debug || hipStreamSynchronize(st) == hipSuccess; };
-  // 8-bit weights: the projections as library int8 GEMMs over the three terms of every token
-  // (3T columns), where the library has an algorithm for the shape; else the hand-written GEMM
-  if (c.weight_bits == 8 && !h->pf_own_gemm && !h->lt_tried) {
-    h->lt_tried = true;
-    h->lt = dn::lt_create();
-  }
-  const bool lt_in = h->lt && !h->pf_own_gemm && dn::lt_prepare(h->lt, 0, R, 3 * n_tokens, (int)D);
-  const bool lt_out = h->lt && !h->pf_own_gemm && dn::lt_prepare(h->lt, 1, (int)D, 3 * n_tokens, V);
-  int8_t* const tx = static_cast<int8_t*>(h->pf_xs);
-  int32_t* const td = reinterpret_cast<int32_t*>(h->pf_part);
-  const size_t ring_seq = (size_t)(K - 1) * h->C, s_seq = (size_t)c.n_v_heads * c.d_k * c.d_v;
-  // the sequences of a batch one after the other, each through every layer; out[l][b] is layer l's
-  // output for sequence b and layer l+1's input
-  for (size_t sb = 0; sb < B; ++sb)
-  for (size_t l = 0; l < L; ++l) {
-    const dn_weights& w = h->w[l];
-    const float* xl = l == 0 ? x + sb * T * D : out + ((l - 1) * B + sb) * T * D;
-    float* const ring_l = h->ring + l * h->ring_elems + sb * ring_seq;
-    // in_proj: split the prompt's inputs, int8 GEMM over the tokens, conv along the tokens
-    dn::PConvArgs pc{};
-    if (lt_in) {
-      dn::TSplitArgs sp{xl, (int)D, (int)D, n_tokens, tx, h->pf_sc, h->pf_ssq};
-      if (dn::launch_tsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      if (dn::lt_gemm_i8(h->lt, 0, w.w_in, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      pc.terms = td; pc.s1 = h->pf_sc; pc.KS = 0; pc.NC = 1;
-    } else {
-      dn::BSplitArgs sp{xl, (int)D, (int)D, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
-      if (dn::launch_bsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      dn::BGemmArgs gi{w.w_in, h->pf_xs, h->pf_sc, h->pf_part, R, (int)D, n_tokens, kr_in};
-      if (dn::launch_bgemm(gi, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      pc.part = h->pf_part; pc.KS = (int)D / kr_in; pc.NC = (int)D / 128;
-    }
-    pc.T = n_tokens; pc.M = R;
-    pc.s = w.s_in; pc.ssq = h->pf_ssq; pc.K = (int)D;
-    pc.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; pc.eps = c.eps_rms;
-    pc.conv_w = w.conv_w; pc.ring_in = ring_l; pc.ring_out = h->pf_ring;
-    pc.C = h->C; pc.Kc = K; pc.out = h->pf_u;
-    if (dn::launch_pconv(pc, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    if (K > 1 && hipMemcpyAsync(ring_l, h->pf_ring, sizeof(float) * ring_seq, hipMemcpyDeviceToDevice, st) !=
-                     hipSuccess)
-      return fail(h, DN_E_DEVICE);
-    if (!check()) return fail(h, DN_E_DEVICE);
-    // recurrence in chunks, then the gated RMSNorm
-    dn::PIntraArgs pi{};
-    pi.u = h->pf_u; pi.T = n_tokens; pi.R = R; pi.QK = QK; pi.Hv = c.n_v_heads; pi.Hk = c.n_k_heads;
-    if (h->gates) {
-      if (launch_layer_gates(h, l, xl, n_tokens, h->pf_al, h->pf_be, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      pi.alpha = h->pf_al; pi.beta = h->pf_be; pi.gstride = c.n_v_heads;
-    } else {
-      pi.alpha = alpha + (l * B + sb) * c.n_v_heads; pi.beta = beta + (l * B + sb) * c.n_v_heads;
-      pi.gstride = (int)(L * B) * c.n_v_heads;
-    }
-    pi.eps_l2 = c.eps_l2; pi.q_scale = c.q_scale; pi.NCH = nch; pi.cw = h->pf_cw;
-    if (dn::launch_pintra(pi, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    dn::PScanArgs ps{};
-    ps.cw = h->pf_cw; ps.S = h->S + l * h->s_elems + sb * s_seq; ps.transposed = h->persist ? 1 : 0;
-    ps.T = n_tokens; ps.Hv = c.n_v_heads; ps.NCH = nch; ps.V = V; ps.o = h->pf_o;
-    if (dn::launch_pscan(ps, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    // the gated RMSNorm: its own pass, or fused into the split for the library GEMM (the readout
-    // rows and z are aligned, V, R and C being multiples of 128; V <= 64 heads x 128 = 8192 columns)
-    if (!lt_out) {
-      dn::PNormArgs pn{h->pf_o, h->pf_u, w.norm_w, n_tokens, R, h->C, V, c.eps_rms};
-      if (dn::launch_pnorm(pn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    }
-    if (!check()) return fail(h, DN_E_DEVICE);
-    // out_proj
-    dn::BEpiArgs e{};
-    if (lt_out) {
-      dn::TSplitArgs so{h->pf_o, V, V, n_tokens, tx, h->pf_sc, h->pf_ssq};
-      const dn::TSplitNormArgs sn{so, h->pf_u + h->C, R, w.norm_w, c.eps_rms};
-      if (dn::launch_tsplit_norm(sn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      if (dn::lt_gemm_i8(h->lt, 1, w.w_out, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      e.terms = td; e.s1 = h->pf_sc; e.KS = 0;
-    } else {
-      dn::BSplitArgs so{h->pf_o, V, V, n_tokens, h->pf_xs, h->pf_sc, h->pf_ssq};
-      if (dn::launch_bsplit(so, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      dn::BGemmArgs go{w.w_out, h->pf_xs, h->pf_sc, h->pf_part, (int)D, V, n_tokens, kr_out};
-      if (dn::launch_bgemm(go, c.weight_bits, 1, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      e.part = h->pf_part; e.KS = V / kr_out;
-    }
-    e.M = (int)D; e.B = n_tokens; e.s = w.s_out;
-    e.out = out + (l * B + sb) * T * D; e.out_stride = (int)D;
-    if (dn::launch_bepi(e, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-    if (!check()) return fail(h, DN_E_DEVICE);
   }
   return DN_OK;
 }

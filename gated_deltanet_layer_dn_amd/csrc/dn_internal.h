@@ -213,18 +213,20 @@ struct LayerW {
 };
 
 // Control words of one handle in device memory: the tag base of the next launch, the count of
-// workgroups that finished the current launch, and a sticky error flag.
+// workgroups that finished the current launch, a sticky error flag, and which of the two state and
+// history buffers holds the current ones (a launch reads that one, writes the other, and the last
+// workgroup to finish makes the written one current only if no workgroup failed).
 struct Ctl {
   unsigned epoch;
   unsigned done;
   unsigned error;
-  unsigned pad;
+  unsigned parity;
 };
 
 struct PersistArgs {
   const LayerW* layers;  // [L], device memory
-  float* S;              // [L][Hv][dv][dk]: each head's state stored transposed
-  float* ring;           // [L][K-1][C], oldest first
+  float* S[2];           // two buffers of [L][Hv][dv][dk] (each head's state stored transposed)
+  float* ring[2];        // two buffers of [L][K-1][C], oldest first
   const float* x;        // [D]
   const float* alpha;    // [L][Hv], or [L][Hv][128] with alpha_per_key
   const float* beta;     // [L][Hv]
@@ -244,8 +246,11 @@ struct PersistArgs {
   int gates;             // 1: gates from the in_proj rows R .. R + 2 Hv (U holds them after the R rows)
   unsigned spin_cap;     // poll rounds a hand-off may take before the launch aborts (PERSIST_SPIN_CAP)
 };
-constexpr int PK_MAXL = 32;
-constexpr unsigned PERSIST_SPIN_CAP = 1u << 22;  // layers of a whole-stack launch with one decay per key channel
+constexpr int PK_MAXL = 32;  // layers of a whole-stack launch with one decay per key channel
+// Poll rounds of one hand-off before the launch gives up (a round is about 1 us, so about a second):
+// far beyond any exchange of a launch whose workgroups are all resident, short enough that a grid
+// that cannot become resident fails in about a second.
+constexpr unsigned PERSIST_SPIN_CAP = 1u << 20;
 
 struct PersistShape {
   int batch, D, V, R, dk, dv, Hv, K, bits;
@@ -254,8 +259,14 @@ struct PersistShape {
 
 bool persist_supported(const PersistShape& s, int nwg);
 hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu);
-hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, hipStream_t st);
+// coop: launch cooperatively (every workgroup resident at once, or the launch fails)
+hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, bool coop, hipStream_t st);
 hipError_t launch_state_tile(const float* src, float* dst, int L, int Hv, int dk, int dv, bool to_tiled,
                              hipStream_t st);
+// Make buffer 0 the current one: copy buffer 1 of the state (n_s floats) and of the history (n_ring
+// floats) into buffer 0 if ctl->parity says buffer 1 is current, then set the parity to 0. For work
+// that updates the state in place (prompts) on a whole-stack handle.
+hipError_t launch_persist_settle(float* const S[2], float* const ring[2], size_t n_s, size_t n_ring, Ctl* ctl,
+                                 hipStream_t st);
 
 }  // namespace dn

@@ -418,4 +418,24 @@ hipError_t launch_gates(const GateArgs& a, int bits, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Buffer 0 made current (see launch_persist_settle): the copy runs only if buffer 1 is current.
+__global__ void k_settle_copy(const float* __restrict__ s1, float* __restrict__ s0, size_t n_s,
+                              const float* __restrict__ r1, float* __restrict__ r0, size_t n_ring, const Ctl* ctl) {
+  if (!(ctl->parity & 1u)) return;
+  const size_t step = (size_t)gridDim.x * blockDim.x;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n_s; e += step) s0[e] = s1[e];
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n_ring; e += step) r0[e] = r1[e];
+}
+__global__ void k_settle_flag(Ctl* ctl) {
+  if (threadIdx.x == 0) ctl->parity = 0u;
+}
+
+hipError_t launch_persist_settle(float* const S[2], float* const ring[2], size_t n_s, size_t n_ring, Ctl* ctl,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(k_settle_copy, dim3(1024), dim3(256), 0, st, S[1], S[0], n_s, ring[1], ring[0], n_ring, ctl);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(k_settle_flag, dim3(1), dim3(64), 0, st, ctl);
+  return hipGetLastError();
+}
+
 }  // namespace dn

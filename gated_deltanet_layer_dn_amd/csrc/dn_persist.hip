@@ -400,6 +400,7 @@ __device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid)
 // compiler pass needs when several instantiations of the kernel are referenced.)
 template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT>
 __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
+                                             const float* S_in, float* S_out, const float* ring_in, float* ring_out,
                                              int tid, int lane) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
   constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC;
@@ -432,7 +433,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       ra_s = W.s_in[r];
       if (r < C) {
         const float* cwp = W.conv_w + (size_t)r * K;
-        const float* rg = a.ring + (size_t)l * (K - 1) * C + r;
+        const float* rg = ring_in + (size_t)l * (K - 1) * C + r;
 #pragma unroll
         for (int j = 0; j < 4; ++j) ra_cw[j] = j < K ? cwp[j] : 0.f;
 #pragma unroll
@@ -461,12 +462,11 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 
   // Phase B's state slice: compute wave w moves chunk w (lane's 4 floats at rows 32p + 4w, column
   // j, for lane 4j + p) between HBM and LDS: prefetched into LDS one layer ahead by a direct-to-LDS
-  // load, written back from LDS after phase C.
+  // load from the current state buffer, written back from LDS after phase C into the other one.
   const int cwv = tid >> 6;
-  auto s_chunk = [&](int l) {
-    return a.S + (((size_t)l * a.Hv + g.bh) * DK + g.bcb * CB + (lane >> 2)) * DK + 32 * (lane & 3) + 4 * cwv;
-  };
-  if (g.has_b) __builtin_amdgcn_global_load_lds(s_chunk(0), &sm.sbuf[64 * cwv], 16, 0, 0);
+  const size_t s_off = ((size_t)g.bh * DK + g.bcb * CB + (lane >> 2)) * DK + 32 * (lane & 3) + 4 * cwv;
+  const size_t s_layer = (size_t)a.Hv * DK * DK;
+  if (g.has_b) __builtin_amdgcn_global_load_lds(S_in + s_off, &sm.sbuf[64 * cwv], 16, 0, 0);
   load_a(0);
   load_c(0);
   for (int l = 0; l < a.L; ++l) {
@@ -506,7 +506,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
         // the hand-off word first: stores leave in order, and the history's can wait
         ll_store(a.U + r, outv, tag);
         if (r < C) {
-          float* rg = a.ring + (size_t)l * (K - 1) * C + r;
+          float* rg = ring_out + (size_t)l * (K - 1) * C + r;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             if (j + 1 < K - 1) rg[(size_t)j * C] = ra_ring[j + 1];
@@ -595,10 +595,10 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
         // write back this wave's chunk of the updated slice (parked in LDS by phase B before
         // barrier 3), then prefetch the next layer's chunk into the same LDS slots
         const v4f v = sm.sbuf[64 * cwv + lane];
-        *reinterpret_cast<v4f*>(s_chunk(l)) = v;
+        *reinterpret_cast<v4f*>(S_out + (size_t)l * s_layer + s_off) = v;
         if (l + 1 < a.L) {
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS read is done before the slots refill
-          __builtin_amdgcn_global_load_lds(s_chunk(l + 1), &sm.sbuf[64 * cwv], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + s_off, &sm.sbuf[64 * cwv], 16, 0, 0);
         }
       }
       if (l + 1 < a.L) load_c(l + 1);
@@ -904,6 +904,10 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NWG = gridDim.x, wg = blockIdx.x;
   const unsigned base_tag = coherent_load_u32(&a.ctl->epoch);
+  // A launch after one that abandoned its token does nothing (the error flag is sticky until the
+  // host restarts the handle), so the current buffers keep the state before the abandoned token.
+  const bool skip = coherent_load_u32(&a.ctl->error) != 0;
+  const unsigned par = coherent_load_u32(&a.ctl->parity) & 1u;
 
   Geo g;
   const int a_per_wg = (a.R + NWG - 1) / NWG;
@@ -926,32 +930,49 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   }
   __syncthreads();
   // The two roles run separate loops with the same sequence of three workgroup barriers per
-  // layer, so each role's registers are its own.
-  if (wave < NCW) compute_role<BITS, NCHA, NCHC, RA, RC, PK, GT>(sm, a, g, base_tag, tid, lane);
-  else comm_role<BITS, NCHA, NCHC, PK, GT>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
+  // layer, so each role's registers are its own. Reads come from the current buffers (par), writes
+  // go to the other ones.
+  if (!skip) {
+    if (wave < NCW)
+      compute_role<BITS, NCHA, NCHC, RA, RC, PK, GT>(sm, a, g, base_tag, a.S[par], a.S[par ^ 1u], a.ring[par],
+                                                     a.ring[par ^ 1u], tid, lane);
+    else
+      comm_role<BITS, NCHA, NCHC, PK, GT>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
+  }
 
-  // the last workgroup to finish advances the tag base for the next launch
+  // The last workgroup to finish advances the tag base for the next launch and, if no workgroup
+  // failed, makes the written buffers current; every workgroup's stores have completed before its
+  // count (the barrier's fence waits for them).
   __syncthreads();
   if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == (unsigned)NWG - 1) {
+      const unsigned err = coherent_load_u32(&a.ctl->error);
       coherent_store_u32(&a.ctl->done, 0u);
       coherent_store_u32(&a.ctl->epoch, base_tag + (unsigned)a.L);
+      if (!err) coherent_store_u32(&a.ctl->parity, par ^ 1u);
       // publish this launch's error flag to the host without a copy on the stream
-      __hip_atomic_store(a.err_host, coherent_load_u32(&a.ctl->error), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(a.err_host, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }
 
-template <int BITS, int NCHA, int NCHC>
-hipError_t go(const PersistArgs& a, int nwg, hipStream_t st) {
-  if (a.alpha_per_key)
-    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, true, false>), dim3(nwg), dim3(NTHR), 0, st, a);
-  else if (a.gates)
-    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, false, true>), dim3(nwg), dim3(NTHR), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_persist<BITS, NCHA, NCHC, 6, 1, false, false>), dim3(nwg), dim3(NTHR), 0, st, a);
+template <typename F>
+hipError_t launch_one(F kern, const PersistArgs& a, int nwg, bool coop, hipStream_t st) {
+  if (coop) {
+    // the runtime starts the grid only when every workgroup can be resident at once
+    void* args[] = {const_cast<PersistArgs*>(&a)};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(nwg), dim3(NTHR), args, 0, st);
+  }
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(NTHR), 0, st, a);
   return hipGetLastError();
+}
+
+template <int BITS, int NCHA, int NCHC>
+hipError_t go(const PersistArgs& a, int nwg, bool coop, hipStream_t st) {
+  if (a.alpha_per_key) return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, true, false>, a, nwg, coop, st);
+  if (a.gates) return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, false, true>, a, nwg, coop, st);
+  return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, false, false>, a, nwg, coop, st);
 }
 
 template <int BITS, int NCHA, int NCHC>
@@ -993,11 +1014,12 @@ hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu) {
   return nc == 2 ? occ<4, 1, 2>(blocks_per_cu, pk, gt) : occ<4, 1, 1>(blocks_per_cu, pk, gt);
 }
 
-hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, hipStream_t st) {
+hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, bool coop, hipStream_t st) {
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
-  if (s.bits == 8) return na == 2 ? go<8, 2, 4>(a, nwg, st) : go<8, 1, 1>(a, nwg, st);
-  return nc == 2 ? go<4, 1, 2>(a, nwg, st) : go<4, 1, 1>(a, nwg, st);
+  if (s.bits == 8) return na == 2 ? go<8, 2, 4>(a, nwg, coop, st) : go<8, 1, 1>(a, nwg, coop, st);
+  return nc == 2 ? go<4, 1, 2>(a, nwg, coop, st) : go<4, 1, 1>(a, nwg, coop, st);
 }
+
 
 // Canonical state [L][Hv][dk][dv] <-> the whole-stack kernel's layout [L][Hv][dv][dk] (each head transposed).
 __global__ void k_state_tile(const float* __restrict__ src, float* __restrict__ dst, int L, int Hv, int dk, int dv,

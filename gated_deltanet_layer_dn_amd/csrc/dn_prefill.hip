@@ -219,7 +219,8 @@ __global__ __launch_bounds__(256) void k_pconv4(const PConvArgs a) {
 __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
   __shared__ __attribute__((aligned(16))) float sQ[CT][LD], sK[CT][LD], sV[CT][LD];
   __shared__ float sA[CT][CT + 1];  // A, then Tm = (I + A)^-1 in place
-  __shared__ float slg[CT], sb[CT], sbg[CT];
+  __shared__ double slg[CT];
+  __shared__ float sb[CT], sbg[CT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
   const int h = blockIdx.x, c = blockIdx.y;
@@ -262,34 +263,36 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
       *reinterpret_cast<v4f*>(&sV[j][col]) = vv[e];
     }
   }
-  // gates; slg = running sum of log decay within the chunk (a decay of 0 is clamped to e^-80)
+  // gates; slg = running sum of log decay within the chunk, in double so that the difference of
+  // two sums (the log of the decay between two tokens) keeps fp32 accuracy however strong the
+  // decays are; a decay of 0 is clamped to e^-80 (below 1e-34, so what it multiplies vanishes)
   if (wave == 0) {
     const bool live = lane < nj;
     const size_t gi = (size_t)(t0 + lane) * a.gstride + h;
     const float al = live ? a.alpha[gi] : 1.0f;
     const float be = live ? a.beta[gi] : 0.0f;
-    float lg = fmaxf(logf(al), -80.0f);
+    double lg = (double)fmaxf(logf(al), -80.0f);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const float v = __shfl_up(lg, o);
+      const double v = __shfl_up(lg, o);
       if (lane >= o) lg += v;
     }
     slg[lane] = lg;
     sb[lane] = be;
-    sbg[lane] = be * expf(lg);
+    sbg[lane] = be * expf((float)lg);
   }
   __syncthreads();
 
   // decayed q rows, k rows weighted by the decay to the chunk's end, the chunk's total decay
   {
-    const float lgl = slg[nj - 1];
+    const double lgl = slg[nj - 1];
     for (int e = tid; e < CT * (DK / 4); e += 256) {
       const int j = e / (DK / 4), i4 = (e % (DK / 4)) * 4;
       const v4f q = *reinterpret_cast<const v4f*>(&sQ[j][i4]), k = *reinterpret_cast<const v4f*>(&sK[j][i4]);
-      *reinterpret_cast<v4f*>(out + OFF_QG + j * DK + i4) = q * expf(slg[j]);
-      *reinterpret_cast<v4f*>(out + OFF_KT + j * DK + i4) = j < nj ? k * expf(lgl - slg[j]) : v4f{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<v4f*>(out + OFF_QG + j * DK + i4) = q * expf((float)slg[j]);
+      *reinterpret_cast<v4f*>(out + OFF_KT + j * DK + i4) = j < nj ? k * expf((float)(lgl - slg[j])) : v4f{0.f, 0.f, 0.f, 0.f};
     }
-    if (tid == 0) out[OFF_G] = expf(lgl);
+    if (tid == 0) out[OFF_G] = expf((float)lgl);
   }
 
   // 64 x 64 tile (rt, ct) of X K^T for X = sQ or sK (sum over 128 columns, permuted)
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int j = 16 * wave + 4 * lk + v, m = 16 * ct + li;
-      sA[j][m] = m < j ? sb[j] * expf(slg[j] - slg[m]) * gt[v] : 0.f;
+      sA[j][m] = m < j ? sb[j] * expf((float)(slg[j] - slg[m])) * gt[v] : 0.f;
     }
   }
   __syncthreads();
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = 16 * rt + 4 * lk + v, m = 16 * ct + li;
-        out[OFF_P + j * CT + m] = m <= j ? expf(slg[j] - slg[m]) * qt[v] : 0.f;
+        out[OFF_P + j * CT + m] = m <= j ? expf((float)(slg[j] - slg[m])) * qt[v] : 0.f;
       }
     }
   }

@@ -1,0 +1,56 @@
+// Measurement only (libdn_probe): the read-stream ceiling of this device's HBM, the figure the
+// decode step's achieved bandwidth is set against next to the vendor peak. Not part of the decode
+// path and not linked into libdn.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dn_probe.h"
+
+#define DN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+constexpr int PROBE_THREADS = 256;
+constexpr int PROBE_UNROLL = 8;  // 16-byte loads in flight per thread
+
+// Every thread streams 16-byte pieces with PROBE_UNROLL nontemporal loads in flight, grid-stride,
+// and folds them into one word, which the block writes so the loads are not dropped.
+__global__ __launch_bounds__(PROBE_THREADS) void k_read_stream(const v4u* __restrict__ p, size_t n16,
+                                                               unsigned* __restrict__ sink) {
+  const size_t step = (size_t)gridDim.x * PROBE_THREADS;
+  unsigned acc = 0;
+  size_t i = (size_t)blockIdx.x * PROBE_THREADS + threadIdx.x;
+  for (; i + (PROBE_UNROLL - 1) * step < n16; i += PROBE_UNROLL * step) {
+    v4u v[PROBE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) v[u] = __builtin_nontemporal_load(p + i + u * step);
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += step) {
+    const v4u v = __builtin_nontemporal_load(p + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  __shared__ unsigned red[PROBE_THREADS];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned a = 0;
+    for (int t = 0; t < PROBE_THREADS; ++t) a ^= red[t];
+    sink[blockIdx.x] = a;
+  }
+}
+
+}  // namespace
+
+DN_API int dn_probe_read_stream(const void* buf, size_t bytes, unsigned* sink, int blocks, void* hip_stream) {
+  if (!buf || !sink || blocks < 1 || blocks > DN_PROBE_MAX_BLOCKS || (bytes & 15u) ||
+      (reinterpret_cast<uintptr_t>(buf) & 15u))
+    return -1;
+  hipLaunchKernelGGL(k_read_stream, dim3(blocks), dim3(PROBE_THREADS), 0, reinterpret_cast<hipStream_t>(hip_stream),
+                     static_cast<const v4u*>(buf), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}

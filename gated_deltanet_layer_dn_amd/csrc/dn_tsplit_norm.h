@@ -1,5 +1,6 @@
-// The out_proj input split of the prefill path with the gated RMSNorm applied first (page "Gated
-// Delta Networks", section on the output gate: a per-head RMSNorm of the readout times silu(z)).
+// The out_proj input split of the prefill path with the gated RMSNorm applied first (page "qwen36:
+// run the DeltaNet layer end to end on the card", section "What the PR does", Backend paragraph:
+// the gated RMSNorm with silu(z), per value head over the readout).
 // Per head of 128 columns: y = w o / sqrt(mean o^2 + eps) silu(z), then the three-term int8 split
 // of each token's row y, as launch_tsplit does for an unnormalised row.
 #pragma once

@@ -12,9 +12,9 @@
  *
  * Five entry points mirror the page's five optional backend calls (the
  * "Verified" section counts them): create, set_state, get_state, step, destroy.
- * A sixth, dn_prefill, runs a whole prompt through the handle on the card (the page
- * leaves prompts to the CPU). dn_strerror is static inline, so the library exports
- * exactly these six.
+ * dn_strerror is static inline, so libdn exports exactly these five. Prompts go
+ * through a handle on the card with the separate library libdn_prefill
+ * (include/dn_prefill.h); the page leaves prompts to the CPU.
  *
  * All sizes are element counts. All matrices are row-major and C-contiguous.
  * The library never synchronises the device inside dn_step.
@@ -117,16 +117,24 @@ typedef struct {
  * *out = NULL. */
 int dn_create(const dn_config *cfg, const dn_weights *w, dn_layer **out);
 
-/* Copy the state in. S: [L][B][Hv][dk][dv] fp32; ring: [L][B][K-1][C] fp32, oldest
- * token first (NULL leaves the history unchanged). Host or device pointers.
+/* Copy the state in (page "qwen36: run the DeltaNet layer end to end on the card", section
+ * "What the PR does", Tier paragraph: the host copy of the state moves to and from the card with
+ * set/get_state). S: [L][B][Hv][dk][dv] fp32; ring: [L][B][K-1][C] fp32, oldest token first (NULL
+ * leaves the history unchanged). Host or device pointers, read during the call (not retained).
  * Synchronous: waits for all work on the device first. Re-arms a latched handle, and restarts the
  * whole-stack kernel's exchange state between workgroups as dn_create leaves it.
  * Returns DN_OK, DN_E_INVAL (NULL handle or S) or DN_E_DEVICE. */
 int dn_set_state(dn_layer *h, const float *S, const float *ring);
 
-/* Copy the state out, same layouts as dn_set_state (ring may be NULL). Host or
- * device pointers. Synchronous. Valid after a failed step: it returns what the
- * device holds. Returns DN_OK, DN_E_INVAL or DN_E_DEVICE. */
+/* Copy the state out, same layouts as dn_set_state (ring may be NULL). Host or device pointers,
+ * written during the call. Synchronous: waits for all work on the device first. Valid after a
+ * failed step: it returns what the device holds (page "qwen36: run the DeltaNet layer end to end
+ * on the card", section "What the PR does", Tier paragraph: get_state works after a failed step).
+ * With S and ring both NULL it copies nothing and only reports, after that wait, whether every
+ * dn_step launched so far completed: DN_E_DEVICE (and the handle latches off) if a whole-stack
+ * launch abandoned its token, else DN_OK. This is the synchronous form of the report the next
+ * dn_step would otherwise give.
+ * Returns DN_OK, DN_E_INVAL (NULL handle, or S NULL with ring not NULL) or DN_E_DEVICE. */
 int dn_get_state(dn_layer *h, float *S, float *ring);
 
 /* One decode token for every sequence, through every layer (page "qwen36: run the
@@ -149,33 +157,10 @@ int dn_get_state(dn_layer *h, float *S, float *ring);
  * launch has completed returns DN_E_DEVICE. */
 int dn_step(dn_layer *h, const float *x, const float *alpha, const float *beta, float *out, void *hip_stream);
 
-/* Prefill: run a prompt of T tokens of ONE sequence through every layer (all T tokens
- * through layer 0, then layer 1, ...), starting from the state and conv history the
- * handle holds and leaving them after the last prompt token, so that dn_step continues
- * the sequence. Each token gets exactly the decode step of dn_step (page "qwen36: run
- * the DeltaNet layer end to end on the card", section "What the PR does"; the page
- * keeps prompts on the CPU, this is the same computation on the card): the recurrence
- * is evaluated in chunks of 64 tokens, which is the per-token step rewritten and
- * agrees with it up to rounding.
- * Requires d_k == d_v == 128, a scalar decay (no DN_ALPHA_PER_KEY), d_model and n_v_heads * d_v
- * multiples of 256. With batch B > 1 every sequence gets a prompt of the same T tokens.
- * DEVICE pointers:
- *   x            [B][T][D]     the prompts' inputs of layer 0, one sequence after the other
- *   alpha, beta  [T][L][B][Hv] per token, the gates of dn_step (not read, may be NULL, with
- *                              DN_GATES_ON_DEVICE)
- *   out          [L][B][T][D]  out[l][b] is layer l's output for sequence b's tokens and layer
- *                              l+1's input. Must not overlap x.
- * T = n_tokens, 1..DN_PREFILL_MAX_TOKENS per call; a longer prompt goes in several calls, each
- * continuing from the state the previous one left. The handle keeps scratch memory sized for the
- * longest prompt seen so far (allocated here, freed by dn_destroy).
- * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only. Returns DN_OK,
- * DN_E_INVAL (shape or arguments not supported; the handle stays usable), DN_E_NOMEM,
- * DN_E_DISABLED or DN_E_DEVICE (latches the handle off, as a failed dn_step does). */
-#define DN_PREFILL_MAX_TOKENS 65535
-int dn_prefill(dn_layer *h, const float *x, int n_tokens, const float *alpha, const float *beta, float *out,
-               void *hip_stream);
-
-/* Free everything the handle owns (waits for the device first). NULL-safe. */
+/* Free everything the handle owns, including what libdn_prefill keeps in it (waits for the device
+ * first); the borrowed weights stay the caller's. The end of the page's per-layer object (page
+ * "qwen36: run the DeltaNet layer end to end on the card", section "What the PR does", Backend
+ * paragraph). NULL-safe. */
 void dn_destroy(dn_layer *h);
 
 static inline const char *dn_strerror(int rc) {

@@ -1,0 +1,49 @@
+/*
+ * dn_prefill.h -- C ABI of libdn_prefill: prompts through a gated-DeltaNet handle on the card.
+ *
+ * The page "qwen36: run the DeltaNet layer end to end on the card (Q36_DN_GPU=1): conv, recurrence
+ * and gated norm join the two projections" keeps a prompt (more than one token) on the CPU (section
+ * "What the PR does", Engine paragraph); this library runs the same per-token computation for a
+ * whole prompt on the card, through a handle made by libdn's dn_create (include/dn.h). It is a
+ * separate library so that libdn exports exactly the page's five calls. Load libdn first: the
+ * handle, its state and its history are libdn's, and dn_destroy releases what this library keeps
+ * in the handle.
+ */
+#ifndef DN_PREFILL_H
+#define DN_PREFILL_H
+
+#include "dn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Prefill: run a prompt of T tokens of ONE sequence through every layer (all T tokens
+ * through layer 0, then layer 1, ...), starting from the state and conv history the
+ * handle holds and leaving them after the last prompt token, so that dn_step continues
+ * the sequence. Each token gets exactly the decode step of dn_step (page "qwen36: run
+ * the DeltaNet layer end to end on the card", section "What the PR does", Backend paragraph);
+ * the recurrence is evaluated in chunks of 64 tokens, which is the per-token step rewritten
+ * and agrees with it up to rounding.
+ * Requires d_k == d_v == 128, a scalar decay (no DN_ALPHA_PER_KEY), d_model and n_v_heads * d_v
+ * multiples of 256. With batch B > 1 every sequence gets a prompt of the same T tokens.
+ * DEVICE pointers:
+ *   x            [B][T][D]     the prompts' inputs of layer 0, one sequence after the other
+ *   alpha, beta  [T][L][B][Hv] per token, the gates of dn_step (not read, may be NULL, with
+ *                              DN_GATES_ON_DEVICE)
+ *   out          [L][B][T][D]  out[l][b] is layer l's output for sequence b's tokens and layer
+ *                              l+1's input. Must not overlap x.
+ * T = n_tokens, 1..DN_PREFILL_MAX_TOKENS per call; a longer prompt goes in several calls, each
+ * continuing from the state the previous one left. The handle keeps scratch memory sized for the
+ * longest prompt seen so far (allocated here, freed by dn_destroy).
+ * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only. Returns DN_OK,
+ * DN_E_INVAL (shape or arguments not supported; the handle stays usable), DN_E_NOMEM,
+ * DN_E_DISABLED or DN_E_DEVICE (latches the handle off, as a failed dn_step does). */
+#define DN_PREFILL_MAX_TOKENS 65535
+int dn_prefill(dn_layer *h, const float *x, int n_tokens, const float *alpha, const float *beta, float *out,
+               void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DN_PREFILL_H */

@@ -1,0 +1,28 @@
+/*
+ * dn_probe.h -- measurement only (libdn_probe): the device's read-stream ceiling.
+ *
+ * The decode step is bound by HBM bandwidth; its achieved rate is reported against the vendor
+ * peak and against what a plain streaming read reaches on the same device. This library holds
+ * that streaming read. It is not part of the decode path.
+ */
+#ifndef DN_PROBE_H
+#define DN_PROBE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DN_PROBE_MAX_BLOCKS 65536
+
+/* Enqueue one streaming read of `bytes` bytes of device memory at buf (16-byte aligned, bytes a
+ * multiple of 16) with `blocks` workgroups of 256 threads; each workgroup writes one word of a
+ * fold of what it read to sink[block] (device memory of at least `blocks` words). hip_stream: a
+ * hipStream_t (NULL = the default stream). Returns 0, -1 (bad arguments) or -3 (launch error). */
+int dn_probe_read_stream(const void *buf, size_t bytes, unsigned *sink, int blocks, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DN_PROBE_H */

@@ -54,3 +54,27 @@ def state_err(gS, rS):
     num = np.linalg.norm(g - r, axis=2)
     den = np.linalg.norm(r, axis=2)
     return float(np.max(num / np.maximum(den, 1e-30)))
+
+
+def check_layers_fed_from_the_card(cfg, layers, stream, gout, gS, gH):
+    """Compare a stack run on the card layer by layer with the oracle's step of that layer fed the
+    card's own input to it (x for layer 0, the card's out[l-1] after), the oracle carrying each
+    layer's state and history over the tokens. gout [T][L][B][D], gS / gH the card's final state and
+    history. Returns the worst (output, state, history) errors over layers: output per token relative
+    to its rms, state and history relative Frobenius per layer. The chain's own amplification of
+    rounding does not enter: each layer sees exactly the input the card gave it."""
+    import oracle as orc
+    one = cfg.replace(n_layers=1)
+    worst = [0.0, 0.0, 0.0]
+    for l, lay in enumerate(layers):
+        S = lay.S0.astype(np.float64).copy()
+        H = lay.ring0.astype(np.float64).copy()
+        refs = np.empty((gout.shape[0],) + gout.shape[2:], np.float64)
+        for t in range(gout.shape[0]):
+            x = stream.x[t] if l == 0 else gout[t, l - 1]
+            refs[t] = orc.layer_step(one, lay, S, H, x.astype(np.float64), stream.alpha[t, l], stream.beta[t, l])
+        worst[0] = max(worst[0], out_err(gout[:, l], refs))
+        worst[1] = max(worst[1], state_err(gS[l:l + 1], S[None]))
+        if cfg.conv_k > 1:
+            worst[2] = max(worst[2], state_err(gH[l:l + 1], H[None]))
+    return worst

@@ -1,10 +1,16 @@
-/* A host-only stand-in for the dn.h calls that dn_residency.h uses (test infrastructure): the
- * "device" state lives in host memory, a step adds the step count to every element, and a step
- * can be told to fail after updating half of the state, as a failing device step can leave the
- * card partly advanced. */
+/* A host-only stand-in for the dn.h / dn_prefill.h calls that dn_residency.h uses (test
+ * infrastructure). The "device" state lives in host memory and a step adds the step's size to every
+ * element. A step can be told to fail in one of two ways, as a step of libdn can:
+ *   at once  the call returns DN_E_DEVICE and nothing of the token is done (an injected failure,
+ *            a launch error);
+ *   late     the call returns DN_OK, the token is abandoned on the "device" (the state keeps its
+ *            value from before the token, as libdn's whole-stack kernel keeps it), and the failure
+ *            is reported by the next call: dn_step, or dn_get_state(h, NULL, NULL).
+ * The handle latches off after a failure until dn_set_state re-arms it. */
 #include <string.h>
 
 #include "dn.h"
+#include "dn_prefill.h"
 
 #define FAKE_N 64
 #define FAKE_M 16
@@ -12,8 +18,9 @@
 struct dn_layer {
   float S[FAKE_N], ring[FAKE_M];
   int disabled;
-  long steps, fail_at;
-  long sets, gets;
+  int late_err;  /* a step was abandoned: reported by the next call, and later steps do nothing */
+  long steps, fail_at, fail_late_at;
+  long sets, gets, checks;
 };
 
 static struct dn_layer fake_handle;
@@ -25,20 +32,31 @@ dn_layer *fake_create(long fail_at) {
 }
 long fake_sets(void) { return fake_handle.sets; }
 long fake_gets(void) { return fake_handle.gets; }
+long fake_checks(void) { return fake_handle.checks; }
 const float *fake_device_S(void) { return fake_handle.S; }
 void fake_fail_at(long n) { fake_handle.fail_at = n; }
+void fake_fail_late_at(long n) { fake_handle.fail_late_at = n; }
 
 int dn_set_state(dn_layer *h, const float *S, const float *ring) {
   if (!h || !S) return DN_E_INVAL;
   memcpy(h->S, S, sizeof(h->S));
   if (ring) memcpy(h->ring, ring, sizeof(h->ring));
   h->disabled = 0;
+  h->late_err = 0;
   ++h->sets;
   return DN_OK;
 }
 
 int dn_get_state(dn_layer *h, float *S, float *ring) {
-  if (!h || !S) return DN_E_INVAL;
+  if (!h || (!S && ring)) return DN_E_INVAL;
+  if (!S) {
+    ++h->checks;
+    if (h->late_err) {
+      h->disabled = 1;
+      return DN_E_DEVICE;
+    }
+    return DN_OK;
+  }
   memcpy(S, h->S, sizeof(h->S));
   if (ring) memcpy(ring, h->ring, sizeof(h->ring));
   ++h->gets;
@@ -46,15 +64,22 @@ int dn_get_state(dn_layer *h, float *S, float *ring) {
 }
 
 static int advance(dn_layer *h, float by) {
-  if (h->disabled) return DN_E_DISABLED;
-  ++h->steps;
-  const int fail = h->fail_at > 0 && h->steps == h->fail_at;
-  for (int i = 0; i < (fail ? FAKE_N / 2 : FAKE_N); ++i) h->S[i] += by;
-  for (int i = 0; i < FAKE_M; ++i) h->ring[i] = by;
-  if (fail) {
+  if (h->late_err) {
     h->disabled = 1;
     return DN_E_DEVICE;
   }
+  if (h->disabled) return DN_E_DISABLED;
+  ++h->steps;
+  if (h->fail_at > 0 && h->steps == h->fail_at) {
+    h->disabled = 1;
+    return DN_E_DEVICE;
+  }
+  if (h->fail_late_at > 0 && h->steps == h->fail_late_at) {
+    h->late_err = 1;
+    return DN_OK;
+  }
+  for (int i = 0; i < FAKE_N; ++i) h->S[i] += by;
+  for (int i = 0; i < FAKE_M; ++i) h->ring[i] = by;
   return DN_OK;
 }
 

@@ -1,8 +1,8 @@
 """dn_step captured in a HIP graph (through torch.cuda.graph) and replayed token by token: every
 replay, with eager copies and synchronisations between the replays, gives bit for bit the output
 and state of the same tokens run eagerly. One case per execution path: the whole-stack kernel,
-the batched kernels and the per-layer kernels. (The page "qwen36: run the DeltaNet layer end to end
-on the card", section "What the PR does", runs the step as one graph per token.)"""
+the batched kernels and the per-layer kernels. Capture is this library's own concern (callers that
+replay a step without host work per token); the pages do not describe it."""
 import numpy as np
 import pytest
 import torch

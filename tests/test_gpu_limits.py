@@ -14,7 +14,7 @@ import torch
 import dn_inputs as gi
 import oracle as orc
 
-from gpu_util import OUT_TOL, STATE_TOL, make_stack, out_err, run_gpu, state_err
+from gpu_util import OUT_TOL, STATE_TOL, check_layers_fed_from_the_card, make_stack, out_err, run_gpu, state_err
 
 pytestmark = pytest.mark.gpu
 
@@ -42,17 +42,7 @@ def _check_layers_fed_from_the_card(cfg, capfd, monkeypatch, path):
     finally:
         st.close()
     assert np.all(np.isfinite(gout))
-    one = cfg.replace(n_layers=1)
-    worst = [0.0, 0.0, 0.0]
-    for l, lay in enumerate(layers):
-        S = lay.S0.astype(np.float64).copy()
-        H = lay.ring0.astype(np.float64).copy()
-        for t in range(cfg.n_tokens):
-            x = stream.x[t] if l == 0 else gout[t, l - 1]
-            ref = orc.layer_step(one, lay, S, H, x.astype(np.float64), stream.alpha[t, l], stream.beta[t, l])
-            worst[0] = max(worst[0], out_err(gout[t:t + 1, l], ref[None]))
-        worst[1] = max(worst[1], state_err(gS[l:l + 1], S[None]))
-        worst[2] = max(worst[2], state_err(gH[l:l + 1], H[None]))
+    worst = check_layers_fed_from_the_card(cfg, layers, stream, gout, gS, gH)
     print(f"[limits] {cfg.name} ({path}): worst layer out {worst[0]:.2e} state {worst[1]:.2e} ring {worst[2]:.2e}",
           flush=True)
     assert worst[0] <= OUT_TOL and worst[1] <= STATE_TOL and worst[2] <= STATE_TOL

@@ -98,16 +98,31 @@ def _check_prefill(cfg, T):
         assert e_dec <= OUT_TOL and es2 <= STATE_TOL
 
 
+LIB_PATH = "in_proj library int8 GEMM, out_proj library int8 GEMM after the fused norm-and-split"
+OWN_PATH = "in_proj hand-written int8 GEMM, out_proj hand-written int8 GEMM"
+
+
+def _check_path(capfd, want):
+    err = capfd.readouterr().err
+    assert want in err, err
+
+
 @pytest.mark.parametrize("name", list(PF))
-def test_prefill_parity(name):
+def test_prefill_parity(name, capfd, monkeypatch):
     cfg, T = PF[name]
+    monkeypatch.setenv("DN_VERBOSE", "1")
     _check_prefill(cfg, T)
+    if cfg.weight_bits == 8:
+        # 8-bit weights take the library GEMMs, with the gated RMSNorm fused into out_proj's split
+        _check_path(capfd, LIB_PATH)
 
 
-def test_prefill_full_layer():
+def test_prefill_full_layer(capfd, monkeypatch):
     """The hybrid-35B layer shape: a 320-token prompt (five chunks), then 16 decode tokens."""
     base = gi.CONFIGS["layer"]
+    monkeypatch.setenv("DN_VERBOSE", "1")
     _check_prefill(base.replace(name="pf_full", n_tokens=336), 320)
+    _check_path(capfd, LIB_PATH)
 
 
 def test_prefill_full_stack_teacher_forced():
@@ -206,9 +221,11 @@ def test_prefill_arguments_are_checked():
 
 
 @pytest.mark.parametrize("name", ["stack3_prenorm", "ragged_chunks"])
-def test_prefill_hand_written_gemm(name, monkeypatch):
+def test_prefill_hand_written_gemm(name, capfd, monkeypatch):
     """8-bit weights with the hand-written split-K GEMM instead of the library GEMM (the path a
     shape takes when the library has no algorithm for it)."""
     monkeypatch.setenv("DN_PREFILL_OWN_GEMM", "1")
+    monkeypatch.setenv("DN_VERBOSE", "1")
     cfg, T = PF[name]
     _check_prefill(cfg, T)
+    _check_path(capfd, OWN_PATH)
