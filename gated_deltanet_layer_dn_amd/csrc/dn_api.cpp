@@ -268,7 +268,8 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   if (const char* e = std::getenv("DN_FAULT_STEP")) h->fault_step = std::atol(e);
   if (const char* e = std::getenv("DN_FAULT_STALL")) h->fault_stall = std::atol(e);
   if (const char* e = std::getenv("DN_SYNC_DEBUG")) h->sync_debug = std::atoi(e) != 0;
-  if (const char* e = std::getenv("DN_VERBOSE"); e && std::atoi(e) != 0)
+  if (const char* e = std::getenv("DN_VERBOSE"); e && std::atoi(e) != 0) h->verbose = true;
+  if (h->verbose)
     std::fprintf(stderr, "[dn] handle: %d layer(s), batch %d: %s%s\n", cfg->n_layers, cfg->batch,
                  h->persist ? "whole-stack kernel" : h->batched ? "batched kernels" : "per-layer kernels",
                  h->persist ? (h->coop ? ", cooperative launch" : ", ordinary launch") : "");
@@ -381,7 +382,10 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
   if (!dev.ok()) return fail(h, DN_E_DEVICE);
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   if (h->persist) {
-    if (host_err(h)) return fail(h, DN_E_DEVICE);  // a completed launch reported a stalled hand-off
+    if (host_err(h)) {  // a completed launch reported a stalled hand-off
+      if (h->verbose) std::fprintf(stderr, "[dn] dn_step: an earlier whole-stack launch abandoned its token\n");
+      return fail(h, DN_E_DEVICE);
+    }
     dn::PersistArgs a{};
     a.layers = h->d_layers; a.x = x; a.alpha = alpha; a.beta = beta; a.out = out;
     a.S[0] = h->S; a.S[1] = h->S_alt; a.ring[0] = h->ring; a.ring[1] = h->ring_alt;
@@ -397,9 +401,28 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     // a cooperative launch cannot be recorded into a graph here: under capture the launch is an
     // ordinary one, and co-residency rests on the device being otherwise idle when it replays
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cap) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (hipError_t e = hipStreamIsCapturing(st, &cap); e != hipSuccess) {
+      if (h->verbose) std::fprintf(stderr, "[dn] dn_step: stream capture query failed: %s\n", hipGetErrorString(e));
+      return fail(h, DN_E_DEVICE);
+    }
     const bool coop = h->coop && cap == hipStreamCaptureStatusNone;
-    if (dn::launch_persist(a, h->ps, h->nwg, coop, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    hipError_t e = dn::launch_persist(a, h->ps, h->nwg, coop, st);
+    if (e != hipSuccess && coop) {
+      // The runtime may refuse a cooperative launch (for one, while another process on the device
+      // holds the global wave sync its cooperative launches use). Nothing was launched: the handle
+      // falls back to ordinary launches, whose co-residency rests on the device being otherwise idle
+      // and whose bounded waits end a launch that cannot be resident.
+      (void)hipGetLastError();
+      if (h->verbose)
+        std::fprintf(stderr, "[dn] dn_step: cooperative launch refused (%s); ordinary launches from now on\n",
+                     hipGetErrorString(e));
+      h->coop = false;
+      e = dn::launch_persist(a, h->ps, h->nwg, false, st);
+    }
+    if (e != hipSuccess) {
+      if (h->verbose) std::fprintf(stderr, "[dn] dn_step: launch failed: %s\n", hipGetErrorString(e));
+      return fail(h, DN_E_DEVICE);
+    }
     if (h->sync_debug && (hipStreamSynchronize(st) != hipSuccess || host_err(h))) return fail(h, DN_E_DEVICE);
     return DN_OK;
   }

@@ -63,6 +63,7 @@ struct dn_layer {
   long fault_step = 0;    // 1-based step to fail (0 = never)
   long fault_stall = 0;   // 1-based step whose whole-stack launch may not wait in any hand-off (0 = never)
   bool sync_debug = false;
+  bool verbose = false;   // DN_VERBOSE=1: the path at creation, and the HIP error of a failed launch
 };
 
 namespace dn {

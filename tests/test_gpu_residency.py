@@ -66,7 +66,7 @@ def test_engine_over_the_libraries(tmp_path):
     tmp = str(tmp_path)
     exe = _build(tmp)
     _write_inputs(tmp, cfg, layers, stream)
-    env = dict(os.environ, DN_FAULT_STEP="4", DN_FAULT_STALL="9")
+    env = dict(os.environ, DN_FAULT_STEP="4", DN_FAULT_STALL="9", DN_VERBOSE="1")
     print("[residency] engine: 12 tokens, 3 layers, faults at dn_step 4 (at once) and 9 (on the device)", flush=True)
     r = subprocess.run([exe, tmp], env=env, capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr, flush=True)
