@@ -156,13 +156,16 @@ int setup_persist(dn_layer* h) {
   ok = ok && hipMemset(h->timers, 0, sizeof(unsigned long long) * h->nwg * L * 32) == hipSuccess;
 #endif
   if (!ok) return DN_E_NOMEM;
-  // Cooperative launches make the runtime start the grid only when every workgroup can be resident
-  // at once, which the kernel's waits between workgroups need (DN_PERSIST_LAUNCH=plain: ordinary
-  // launches, which rely on the device being otherwise idle).
+  // The kernel's waits between workgroups need every workgroup resident at once. An ordinary launch
+  // gets that on a device with no other work (one workgroup per compute unit, occupancy checked
+  // above); where other work may share the device, a launch whose grid cannot become resident ends
+  // through the bounded waits, leaves the state of the last completed token and is reported.
+  // DN_PERSIST_LAUNCH=cooperative makes the runtime start the grid only when all of it fits, at
+  // about 20 us more per launch on MI355X.
   int coop = 0;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device) != hipSuccess) coop = 0;
   const char* lm = std::getenv("DN_PERSIST_LAUNCH");
-  h->coop = coop != 0 && !(lm && std::strcmp(lm, "plain") == 0);
+  h->coop = coop != 0 && lm && std::strcmp(lm, "cooperative") == 0;
   std::vector<dn::LayerW> lw(L);
   for (size_t l = 0; l < L; ++l)
     lw[l] = dn::LayerW{h->w[l].w_in,  h->w[l].s_in,  h->w[l].conv_w, h->w[l].norm_w,

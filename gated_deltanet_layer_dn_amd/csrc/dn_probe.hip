@@ -14,10 +14,10 @@ namespace {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int PROBE_THREADS = 256;
-constexpr int PROBE_UNROLL = 8;  // 16-byte loads in flight per thread
 
 // Every thread streams 16-byte pieces with PROBE_UNROLL nontemporal loads in flight, grid-stride,
 // and folds them into one word, which the block writes so the loads are not dropped.
+template <int PROBE_UNROLL>
 __global__ __launch_bounds__(PROBE_THREADS) void k_read_stream(const v4u* __restrict__ p, size_t n16,
                                                                unsigned* __restrict__ sink) {
   const size_t step = (size_t)gridDim.x * PROBE_THREADS;
@@ -46,11 +46,16 @@ __global__ __launch_bounds__(PROBE_THREADS) void k_read_stream(const v4u* __rest
 
 }  // namespace
 
-DN_API int dn_probe_read_stream(const void* buf, size_t bytes, unsigned* sink, int blocks, void* hip_stream) {
+DN_API int dn_probe_read_stream(const void* buf, size_t bytes, unsigned* sink, int blocks, int in_flight,
+                                void* hip_stream) {
   if (!buf || !sink || blocks < 1 || blocks > DN_PROBE_MAX_BLOCKS || (bytes & 15u) ||
       (reinterpret_cast<uintptr_t>(buf) & 15u))
     return -1;
-  hipLaunchKernelGGL(k_read_stream, dim3(blocks), dim3(PROBE_THREADS), 0, reinterpret_cast<hipStream_t>(hip_stream),
-                     static_cast<const v4u*>(buf), bytes / 16, sink);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const v4u* p = static_cast<const v4u*>(buf);
+  if (in_flight == 4) hipLaunchKernelGGL(k_read_stream<4>, dim3(blocks), dim3(PROBE_THREADS), 0, st, p, bytes / 16, sink);
+  else if (in_flight == 8) hipLaunchKernelGGL(k_read_stream<8>, dim3(blocks), dim3(PROBE_THREADS), 0, st, p, bytes / 16, sink);
+  else if (in_flight == 16) hipLaunchKernelGGL(k_read_stream<16>, dim3(blocks), dim3(PROBE_THREADS), 0, st, p, bytes / 16, sink);
+  else return -1;
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

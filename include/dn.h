@@ -45,11 +45,19 @@ extern "C" {
  *                       path unless every exchange is already complete; the next call reports it
  *   DN_SYNC_DEBUG=1     synchronise after every launch and check for errors
  *   DN_LAYER_KERNELS=1  use the per-layer kernels even where the whole-stack kernel applies
- *   DN_VERBOSE=1        print which path the handle uses to stderr
+ *   DN_VERBOSE=1        print which path the handle uses to stderr, and the HIP error of a failed launch
+ *   DN_PERSIST_LAUNCH=cooperative
+ *                       launch the whole-stack kernel cooperatively: the runtime starts it only when
+ *                       the whole grid can be resident (about 20 us more per launch on MI355X; not
+ *                       while the stream is being captured into a graph)
  *
  * Execution paths. A single-sequence handle (batch 1) with d_k = d_v = 128 and supported widths
- * runs each dn_step as one whole-stack kernel launch that occupies every compute unit of the
- * device; two such steps must not run concurrently on one device (issue them on one stream).
+ * runs each dn_step as one whole-stack kernel launch with one workgroup per compute unit, whose
+ * workgroups wait for one another; they must all be resident at once, which an otherwise idle
+ * device gives (two such steps must not run concurrently on one device: issue them on one stream).
+ * If other work keeps part of the grid from starting for about a second, the launch gives up: it
+ * leaves the state and history of the last completed token, later launches do nothing, and the
+ * failure is reported (DN_E_DEVICE) by the next dn_step or by dn_get_state(h, NULL, NULL).
  * Other shapes run three kernels per layer. */
 
 /* dn_config.flags */

@@ -17,10 +17,11 @@ extern "C" {
 #define DN_PROBE_MAX_BLOCKS 65536
 
 /* Enqueue one streaming read of `bytes` bytes of device memory at buf (16-byte aligned, bytes a
- * multiple of 16) with `blocks` workgroups of 256 threads; each workgroup writes one word of a
- * fold of what it read to sink[block] (device memory of at least `blocks` words). hip_stream: a
- * hipStream_t (NULL = the default stream). Returns 0, -1 (bad arguments) or -3 (launch error). */
-int dn_probe_read_stream(const void *buf, size_t bytes, unsigned *sink, int blocks, void *hip_stream);
+ * multiple of 16) with `blocks` workgroups of 256 threads, each thread keeping `in_flight` (4, 8 or
+ * 16) nontemporal 16-byte loads in flight; each workgroup writes one word of a fold of what it read
+ * to sink[block] (device memory of at least `blocks` words). hip_stream: a hipStream_t (NULL = the
+ * default stream). Returns 0, -1 (bad arguments) or -3 (launch error). */
+int dn_probe_read_stream(const void *buf, size_t bytes, unsigned *sink, int blocks, int in_flight, void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -228,19 +228,24 @@ def test_status_reports_every_completed_step():
         st.close()
 
 
-def test_whole_stack_step_shares_the_device_with_other_work(capfd, monkeypatch):
-    """The whole-stack kernel needs all of its workgroups resident at once. It is launched
-    cooperatively, so the runtime starts it only when the whole grid fits; launched while another
-    stream's kernels occupy the compute units, each step waits for room and gives bit for bit the
-    result of the same steps on an idle device."""
+@pytest.mark.parametrize("launch", ["ordinary", "cooperative"])
+def test_whole_stack_step_shares_the_device_with_other_work(launch, capfd, monkeypatch):
+    """The whole-stack kernel needs all of its workgroups resident at once. Launched while another
+    stream's kernels occupy the compute units, an ordinary launch's first workgroups wait (within
+    their bounded waits) for the rest to be placed as the other kernels drain, and a cooperative
+    launch is started by the runtime only when the whole grid fits. Either way each step gives bit
+    for bit the result of the same steps on an idle device."""
     cfg = gi.custom("shared", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, n_layers=2, n_tokens=4,
                     flags=gi.DN_X_RMSNORM, ring_std=1.0)
     layers, stream = gi.generate(cfg)
     monkeypatch.setenv("DN_VERBOSE", "1")
+    if launch == "cooperative":
+        monkeypatch.setenv("DN_PERSIST_LAUNCH", "cooperative")
     st = make_stack(cfg, layers)
     monkeypatch.delenv("DN_VERBOSE")
+    monkeypatch.delenv("DN_PERSIST_LAUNCH", raising=False)
     err = capfd.readouterr().err
-    assert "whole-stack kernel, cooperative launch" in err, err
+    assert f"whole-stack kernel, {launch} launch" in err, err
     try:
         idle = run_gpu(st, stream)
         S0 = np.ascontiguousarray(np.stack([l.S0 for l in layers]), np.float32)
