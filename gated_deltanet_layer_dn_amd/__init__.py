@@ -24,8 +24,9 @@ DN_X_RMSNORM = 1
 DN_ALPHA_PER_KEY = 2  # alpha [L][B][Hv][dk]: one decay per key channel
 DN_GATES_ON_DEVICE = 4  # gates from two more in_proj rows per value head; alpha/beta not read
 DN_PREFILL_MAX_TOKENS = 65535  # prompt tokens per dn_prefill call
+DN_PREFILL_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static scratch of dn_prefill_noalloc, per device
 EXPORTED = ("dn_create", "dn_set_state", "dn_get_state", "dn_step", "dn_destroy")  # libdn.so
-PREFILL_EXPORTED = ("dn_prefill",)  # libdn_prefill.so
+PREFILL_EXPORTED = ("dn_prefill", "dn_prefill_noalloc")  # libdn_prefill.so
 
 _ERR = {DN_OK: "ok", DN_E_INVAL: "invalid argument", DN_E_NOMEM: "out of device memory",
         DN_E_DEVICE: "device error", DN_E_DISABLED: "layer disabled after a failed step",
@@ -86,6 +87,7 @@ def prefill_lib():
         L = ctypes.CDLL(PREFILL_LIB_PATH)
         P = ctypes.c_void_p
         L.dn_prefill.argtypes = [P, P, ctypes.c_int, P, P, P, P]; L.dn_prefill.restype = ctypes.c_int
+        L.dn_prefill_noalloc.argtypes = [P, P, ctypes.c_int, P, P, P, P]; L.dn_prefill_noalloc.restype = ctypes.c_int
         _plib = L
     return _plib
 
@@ -145,6 +147,12 @@ def dn_prefill(h: int, x, n_tokens: int, alpha, beta, out, stream=None) -> int:
     returns the C return code."""
     return prefill_lib().dn_prefill(h, _ptr(x), int(n_tokens), _ptr(alpha), _ptr(beta), _ptr(out),
                                     _stream(stream, out))
+
+
+def dn_prefill_noalloc(h: int, x, n_tokens: int, alpha, beta, out, stream=None) -> int:
+    """dn_prefill on the library's static scratch, allocating nothing; returns the C return code."""
+    return prefill_lib().dn_prefill_noalloc(h, _ptr(x), int(n_tokens), _ptr(alpha), _ptr(beta), _ptr(out),
+                                            _stream(stream, out))
 
 
 def dn_destroy(h: int) -> None:

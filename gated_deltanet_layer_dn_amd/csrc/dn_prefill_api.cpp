@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 
 #include "dn.h"
@@ -259,4 +260,58 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
   pf_layout(h, n_tokens, static_cast<char*>(e->buf), &pb);
   return pf_run(h, pb, e->own_gemm ? nullptr : e->lt, e->verbose, x, n_tokens, alpha, beta, out,
                 reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+// ---- prompts without allocation (dn_prefill_noalloc) ----
+//
+// The scratch lives in a file-scope device array, one per device the library runs on, held until
+// the process ends. Host code reaches it only through the address hipGetSymbolAddress gives on that
+// device (the array's name is a host-side stand-in, not a device address).
+namespace {
+
+__device__ __align__(256) unsigned char scratch[DN_PREFILL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of this device's scratch array, looked up once per device with that device
+// current (the caller's DeviceScope); nullptr if the lookup fails.
+void* scratch_on(int device) {
+  if (device < 0 || device >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[device] = p;
+  }
+  return g_scratch_ptr[device];
+}
+
+}  // namespace
+
+DN_API int dn_prefill_noalloc(dn_layer* h, const float* x, int n_tokens, const float* alpha, const float* beta,
+                              float* out, void* hip_stream) {
+  if (int rc = pf_check(h, x, n_tokens, alpha, beta, out); rc != DN_OK) return rc;
+  const size_t need = pf_layout(h, n_tokens, nullptr, nullptr);
+  if (need > (size_t)DN_PREFILL_NOALLOC_SCRATCH_BYTES) {
+    if (h->verbose)
+      std::fprintf(stderr,
+                   "[dn] dn_prefill_noalloc: %d tokens need %zu bytes of scratch, more than the %d bytes it has;"
+                   " pass fewer tokens per call\n",
+                   n_tokens, need, DN_PREFILL_NOALLOC_SCRATCH_BYTES);
+    return DN_E_INVAL;
+  }
+  DeviceScope dev(h->device);
+  if (!dev.ok()) return fail(h, DN_E_DEVICE);
+  if (h->persist && host_err(h)) return fail(h, DN_E_DEVICE);
+  char* base = static_cast<char*>(scratch_on(h->device));
+  if (!base) return fail(h, DN_E_DEVICE);
+  PfBufs pb{};
+  pf_layout(h, n_tokens, base, &pb);
+  if (h->verbose) std::fprintf(stderr, "[dn] dn_prefill_noalloc: %zu bytes of the device's scratch array\n", need);
+  return pf_run(h, pb, nullptr, h->verbose, x, n_tokens, alpha, beta, out, reinterpret_cast<hipStream_t>(hip_stream));
 }

@@ -43,6 +43,25 @@ extern "C" {
 int dn_prefill(dn_layer *h, const float *x, int n_tokens, const float *alpha, const float *beta, float *out,
                void *hip_stream);
 
+/* dn_prefill without any allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it. Same arguments, layouts, state
+ * handling and return codes as dn_prefill, and the same computation; the projections always run in
+ * this library's own int8 GEMM kernels (no library GEMM, whose workspace and setup would allocate),
+ * so results agree with dn_prefill to rounding and equal those of dn_prefill under
+ * DN_PREFILL_OWN_GEMM=1 bit for bit.
+ * Its scratch is one static device array of DN_PREFILL_NOALLOC_SCRATCH_BYTES per device the library
+ * runs on, held until the process ends; the call calls no allocator (neither HIP's nor a library's).
+ * A call whose scratch would exceed the array returns DN_E_INVAL without launching anything (and,
+ * with DN_VERBOSE=1, says how many bytes it needed): pass the prompt in pieces of fewer tokens, each
+ * call continuing from the state the previous one left. For the 30-layer stack's layer shape (d_model
+ * 2048, 16 x 128 key and 32 x 128 value heads) a call takes up to about 200 tokens.
+ * Every call on one device shares that device's array, which keeps the last call's contents (nothing
+ * in it needs to start at zero): calls that overlap in time on one device race and must not be
+ * issued (use one stream per device, or order them). */
+#define DN_PREFILL_NOALLOC_SCRATCH_BYTES (64 << 20)
+int dn_prefill_noalloc(dn_layer *h, const float *x, int n_tokens, const float *alpha, const float *beta, float *out,
+                       void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

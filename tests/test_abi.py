@@ -41,8 +41,8 @@ def test_header_declares_the_five_calls():
     assert _declared(HDR) == FIVE
 
 
-def test_prefill_header_declares_the_prompt_call():
-    assert _declared(PHDR) == {"dn_prefill"}
+def test_prefill_header_declares_the_prompt_calls():
+    assert _declared(PHDR) == {"dn_prefill", "dn_prefill_noalloc"}
 
 
 def test_library_exports_exactly_the_five_calls(built):
