@@ -70,26 +70,26 @@ static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
 // s_waitcnt with vmcnt <= n and the other counters unconstrained
 #define DN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
-// Instrumented builds (-DDN_PHASE_TIMERS) record the 100 MHz wall clock at phase boundaries.
+// Instrumented builds (-DDN_PHASE_TIMERS) record the 100 MHz wall clock at phase boundaries of the
+// first TS_MAXL layers into LDS (so that the instrumentation holds no registers across the phases)
+// and copy them to PersistArgs::timers [NWG][L][32] when the launch ends.
 #ifdef DN_PHASE_TIMERS
-#define DN_MARK(a, l, k)                                                                       \
-  do {                                                                                         \
-    if ((threadIdx.x & 63) == 0)                                                               \
-      (a).timers[((size_t)blockIdx.x * (a).L + (l)) * 32 + (k)] = wall_clock64();              \
-  } while (0)
-#define DN_TS(a, l, k) ((a).timers + ((size_t)blockIdx.x * (a).L + (l)) * 32 + (k))
-#define DN_COUNT(a, l, k, v)                                                                   \
-  do {                                                                                         \
-    if ((threadIdx.x & 63) == 0) (a).timers[((size_t)blockIdx.x * (a).L + (l)) * 32 + (k)] = (v); \
+constexpr int TS_MAXL = 32;
+__shared__ unsigned long long g_ts[TS_MAXL][32];
+// the marks recorded (a bit per mark index); the others compile to nothing, which keeps the
+// instrumented kernel's registers as the uninstrumented one's
+#ifndef DN_TS_MARKS
+#define DN_TS_MARKS ((1u << 1) | (1u << 2) | (1u << 3) | (1u << 4) | (1u << 15) | (1u << 6) | (1u << 7) | (1u << 8))
+#endif
+#define DN_MARK(a, l, k)                                                                              \
+  do {                                                                                                \
+    if (((DN_TS_MARKS) >> (k)) & 1u)                                                                  \
+      if ((threadIdx.x & 63) == 0 && (l) < TS_MAXL) g_ts[(l)][(k)] = wall_clock64();                \
   } while (0)
 #else
 #define DN_MARK(a, l, k) \
   do {                   \
   } while (0)
-#define DN_COUNT(a, l, k, v) \
-  do {                       \
-  } while (0)
-#define DN_TS(a, l, k) nullptr
 #endif
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
@@ -130,17 +130,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, unsign
 }
 constexpr int CPOL_SC1 = 16;  // cache policy of a device-coherent load
 
-template <typename T>
-__device__ __forceinline__ T wsum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wmax(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
 
 // Staged activation position of column c (4-bit weights hold 8 columns per dword as nibbles;
 // the masked low and high nibbles are the even and odd columns).
@@ -225,6 +214,17 @@ struct Smem {
   int abort_flag;
 };
 
+// Position in Smem::yf of readout column c: phase C reads, for lane l and 16-byte weight chunk k,
+// the readout quads of the chunk's columns as one contiguous 16-byte word per lane, so that the
+// wave's LDS reads are consecutive rather than 64 bytes apart (8-bit weights: 16 columns per chunk,
+// 4-bit: 32).
+template <int BITS>
+__device__ __forceinline__ int ypos(int c) {
+  constexpr int CWC = BITS == 8 ? 16 : 32, NQ = CWC / 4;
+  const int l = (c / CWC) & 63, k = c / (64 * CWC), q = (c % CWC) >> 2;
+  return ((k * NQ + q) * 64 + l) * 4 + (c & 3);
+}
+
 // Workgroup barrier for the per-layer hand-over of LDS data between the two wave roles. Unlike
 // __syncthreads(), whose fence waits for every outstanding global access of the wave (loads
 // included), it waits only for this wave's LDS accesses: the compute waves' weight prefetches stay
@@ -291,6 +291,24 @@ __device__ __forceinline__ float quad_sum(float x) {
   x += __int_as_float(dpp_i<0x4E>(__float_as_int(x)));
   return x;
 }
+// Sum over each group of eight consecutive lanes (quads, then the mirrored half row).
+__device__ __forceinline__ float oct_sum(float x) {
+  x = quad_sum(x);
+  x += __int_as_float(dpp_i<0x141>(__float_as_int(x)));
+  return x;
+}
+// Maximum over the 64 lanes of a wave (of non-negative values) with DPP lane permutations,
+// returned uniformly.
+__device__ __forceinline__ float wave_max_f(float x) {
+  int v = __float_as_int(x);
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0xB1>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x4E>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x141>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x140>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x142, 0xA>(v))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(dpp_i<0x143, 0xC>(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
 
 // Reduce the lane partials of RB rows; lane i (< RB) receives row i's dot product. Each lane's three
 // term sums are exact integers below 2^24 (so exact in fp32); they are folded into one fp32 partial
@@ -316,7 +334,7 @@ __device__ __forceinline__ float reduce_rows(int (&acc)[RB][3], float s1, int la
 template <int N>
 __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&off)[N], unsigned want, float (&v)[N],
                                               unsigned nvalid, const unsigned* err, unsigned cap,
-                                              unsigned* rounds = nullptr, unsigned long long* round_ts = nullptr) {
+                                              unsigned* rounds = nullptr) {
   unsigned pend = (1u << N) - 1u;
   pend &= (1u << nvalid) - 1u;
   unsigned it = 0;
@@ -333,9 +351,6 @@ __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&
         v[i] = __uint_as_float((unsigned)w[i]);
         pend &= ~(1u << i);
       }
-#ifdef DN_PHASE_TIMERS
-    if (round_ts && it < 4 && (threadIdx.x & 63) == 0) round_ts[it] = wall_clock64();
-#endif
     if (++it > cap || ((it & 255) == 0 && coherent_load_u32(err))) return false;
   }
   if (rounds) *rounds = it;
@@ -532,13 +547,12 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       float acc[RC];
 #pragma unroll
       for (int i = 0; i < RC; ++i) acc[i] = 0.f;
+      const v4f* Y4 = reinterpret_cast<const v4f*>(sm.yf);
 #pragma unroll
       for (int k = 0; k < NCHC; ++k) {
-        const int c = lane + 64 * k;
         if (BITS == 8) {
-          const v4f* Y = reinterpret_cast<const v4f*>(sm.yf + 16 * c);
-          const v4f y0 = Y[0], y1 = Y[1], y2 = Y[2], y3 = Y[3];
-          const v4f yq[4] = {y0, y1, y2, y3};
+          const v4f yq[4] = {Y4[(k * 4 + 0) * 64 + lane], Y4[(k * 4 + 1) * 64 + lane], Y4[(k * 4 + 2) * 64 + lane],
+                             Y4[(k * 4 + 3) * 64 + lane]};
 #pragma unroll
           for (int i = 0; i < RC; ++i)
 #pragma unroll
@@ -550,10 +564,10 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
               acc[i] = fmaf((float)(u >> 24), yq[e][3], acc[i]);
             }
         } else {
-          const v4f* Y = reinterpret_cast<const v4f*>(sm.yf + 32 * c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const v4f ya = Y[2 * e], yb = Y[2 * e + 1];  // columns 32c + 8e .. +7
+            // columns 32c + 8e .. +7 of the lane's chunk c = lane + 64 k
+            const v4f ya = Y4[(k * 8 + 2 * e) * 64 + lane], yb = Y4[(k * 8 + 2 * e + 1) * 64 + lane];
 #pragma unroll
             for (int i = 0; i < RC; ++i) {
               const unsigned p = (unsigned)wc[i][k][e] ^ 0x88888888u;
@@ -713,8 +727,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         ss = fmaf(xv[i], xv[i], ss);
         mx = fmaxf(mx, fabsf(xv[i]));
       }
-      ss = wsum(ss);
-      mx = wmax(mx);
+      ss = wave_total_f(ss);
+      mx = wave_max_f(mx);
       if (lane == 0) {
         sm.stat[cw] = ss;
         sm.stat[4 + cw] = mx;
@@ -761,7 +775,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       // the poll starts at once: waiting for this workgroup's own phase A first measured slower
       DN_MARK(a, l, 10);
       unsigned rounds = 0;
-      ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, a.spin_cap, &rounds, DN_TS(a, l, 20));
+      ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, a.spin_cap, &rounds);
       if (lane == 0) bump_counter(&sm.u_done);
       DN_MARK(a, l, 4);
       if (__all(ok)) {
@@ -869,9 +883,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       if (cw == 0) DN_MARK(a, l, 6);
       // per-head sums of the partials: head h's nblk partials sit in nblk consecutive lanes
       {
-        float sp = gv[GW];
-#pragma unroll
-        for (int o = 1; o < nblk; o <<= 1) sp += __shfl_xor(sp, o);
+        static_assert(nblk == 8, "");
+        const float sp = oct_sum(gv[GW]);
         if ((lane % nblk) == 0 && lane < pn) sm.inv[(pbase + lane) / nblk] = rsqrtf(sp / (float)DV + a.eps_rms);
       }
       // y = g / rms(head), staged for phase C, and the sum of this quarter of y
@@ -882,13 +895,14 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         const int c = gcol0 + 256 * h;  // the four columns of a quad belong to one head
         const float iv = sm.inv[c / DV];
         const v4f y = v4f{gv[4 * h], gv[4 * h + 1], gv[4 * h + 2], gv[4 * h + 3]} * iv;
-        *reinterpret_cast<v4f*>(sm.yf + c) = y;
+        *reinterpret_cast<v4f*>(sm.yf + ypos<BITS>(c)) = y;
         sy += (y[0] + y[1]) + (y[2] + y[3]);
       }
       sy = wave_total_f(sy);
       if (lane == 0) sm.stat[9 + cw] = sy;
     }
     if (!__all(ok)) fail();
+    if (cw == 0) DN_MARK(a, l, 29);
     lds_barrier();  // (3)
     if (sm.abort_flag) break;
   }
@@ -928,6 +942,9 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
     sm.abort_flag = 0;
     sm.a_done = sm.b_done = sm.c_done = sm.u_done = sm.s_ready = 0;
   }
+#ifdef DN_PHASE_TIMERS
+  for (int e = tid; e < TS_MAXL * 32; e += NTHR) g_ts[e / 32][e % 32] = 0;
+#endif
   __syncthreads();
   // The two roles run separate loops with the same sequence of three workgroup barriers per
   // layer, so each role's registers are its own. Reads come from the current buffers (par), writes
@@ -940,6 +957,11 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
       comm_role<BITS, NCHA, NCHC, PK, GT>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
   }
 
+#ifdef DN_PHASE_TIMERS
+  __syncthreads();
+  for (int e = tid; e < min(a.L, TS_MAXL) * 32; e += NTHR)
+    a.timers[((size_t)blockIdx.x * a.L + e / 32) * 32 + e % 32] = g_ts[e / 32][e % 32];
+#endif
   // The last workgroup to finish advances the tag base for the next launch and, if no workgroup
   // failed, makes the written buffers current; every workgroup's stores have completed before its
   // count (the barrier's fence waits for them).
