@@ -62,9 +62,16 @@ constexpr int MAXL = 256;              // layers per handle (the C ABI's limit)
 #define DN_PREFETCH_INFLIGHT 3
 #endif
 static_assert(DN_PREFETCH_INFLIGHT >= 1 && DN_PREFETCH_INFLIGHT < 16, "");
-// The last DN_PREFETCH_TAIL in_proj row-chunk loads of a layer are issued without the throttle.
+// The last DN_PREFETCH_TAIL row-chunk loads of each part of a layer's in_proj prefetch are issued
+// without the throttle.
 #ifndef DN_PREFETCH_TAIL
-#define DN_PREFETCH_TAIL 4
+#define DN_PREFETCH_TAIL 2
+#endif
+// A compute wave prefetches the first DN_PREFETCH_EARLY_ROWS of its in_proj rows of the next layer
+// while phase B and the gated-readout exchange run, and the others after phase C (issuing them all
+// before phase C kept the compute waves from phase C well after the readout had arrived).
+#ifndef DN_PREFETCH_EARLY_ROWS
+#define DN_PREFETCH_EARLY_ROWS 4
 #endif
 
 // s_waitcnt with vmcnt <= n and the other counters unconstrained
@@ -427,22 +434,28 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
   float ra_s = 0.f, ra_cw[4] = {0.f, 0.f, 0.f, 0.f}, ra_ring[3] = {0.f, 0.f, 0.f};
   float rc_s = 0.f;
 
-  auto load_a = [&](int l) {
+  // in_proj rows of layer l into registers: part 0 the first DN_PREFETCH_EARLY_ROWS rows (and the
+  // rows' scales, conv taps and history), part 1 the others; each part throttled to
+  // DN_PREFETCH_INFLIGHT loads in flight but for its last DN_PREFETCH_TAIL
+  constexpr int EARLY = DN_PREFETCH_EARLY_ROWS < RA ? DN_PREFETCH_EARLY_ROWS : RA;
+  auto load_a = [&](int l, int part) {
     const LayerW& W = a.layers[l];
     const int8_t* wbase = reinterpret_cast<const int8_t*>(W.w_in);
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
+      if ((part == 0) != (i < EARLY)) continue;
       const int r = g.a_row0 + i;
 #pragma unroll
       for (int k = 0; k < NCHA; ++k) {
-        if ((i * NCHA + k) >= DN_PREFETCH_INFLIGHT && (i * NCHA + k) < RA * NCHA - DN_PREFETCH_TAIL)
-          DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
+        const int n = (part == 0 ? i : i - EARLY) * NCHA + k, ntot = (part == 0 ? EARLY : RA - EARLY) * NCHA;
+        if (n >= DN_PREFETCH_INFLIGHT && n < ntot - DN_PREFETCH_TAIL) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
         if (r < g.a_row_end)
           wa[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_in) + lane + 64 * k);
         else
           wa[i][k] = v4i{0, 0, 0, 0};
       }
     }
+    if (part != 0) return;
     const int r = g.a_row0 + lane;
     if (lane < RA && r < g.a_row_end) {
       ra_s = W.s_in[r];
@@ -482,7 +495,8 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
   const size_t s_off = ((size_t)g.bh * DK + g.bcb * CB + (lane >> 2)) * DK + 32 * (lane & 3) + 4 * cwv;
   const size_t s_layer = (size_t)a.Hv * DK * DK;
   if (g.has_b) __builtin_amdgcn_global_load_lds(S_in + s_off, &sm.sbuf[64 * cwv], 16, 0, 0);
-  load_a(0);
+  load_a(0, 0);
+  load_a(0, 1);
   load_c(0);
   for (int l = 0; l < a.L; ++l) {
     const unsigned tag = base_tag + (unsigned)l;
@@ -533,7 +547,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       // the next layer's in_proj rows stream in once this workgroup's phase-B inputs have
       // arrived, so that the u hand-off is not queued behind them
       wait_counter(&sm.u_done, l + 1, &sm.abort_flag);
-      if (l + 1 < a.L) load_a(l + 1);
+      if (l + 1 < a.L) load_a(l + 1, 0);
       if (tid == 0) DN_MARK(a, l, 28);
     }
     lds_barrier();  // (3) gated readout staged
@@ -615,7 +629,10 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
           __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + s_off, &sm.sbuf[64 * cwv], 16, 0, 0);
         }
       }
-      if (l + 1 < a.L) load_c(l + 1);
+      if (l + 1 < a.L) {
+        load_c(l + 1);
+        load_a(l + 1, 1);
+      }
     }
   }
 }
