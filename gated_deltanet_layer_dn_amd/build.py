@@ -56,7 +56,9 @@ def _compile(src: str, obj: str, defines, verbose: bool):
 
 def _link(objs, out: str, libs, verbose: bool):
     tmp = out + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + libs, verbose)
+    # -z defs: a symbol left undefined (a kernel the host pass did not emit, say) fails the link
+    # here rather than the library's load
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs + libs, verbose)
     os.replace(tmp, out)
 
 

@@ -120,6 +120,13 @@ int setup_batched(dn_layer* h) {
   ok = ok && hipMalloc(&h->ssq, sizeof(float) * B * nc) == hipSuccess;
   if (!ok) return DN_E_NOMEM;
   h->mf1 = mf1; h->kr1 = kr1; h->mf2 = mf2; h->kr2 = kr2; h->up1 = up1; h->up2 = up2;
+  // in_proj, with enough rows for every compute unit, as one whole-K kernel with its epilogue.
+  // DN_BPROJ=0 keeps the split-K GEMM and the separate epilogue; DN_BPROJ=1 takes the whole-K
+  // kernel for every shape it supports (fewer rows too).
+  int rt = 0;
+  const char* bp = std::getenv("DN_BPROJ");
+  const int bpv = bp ? std::atoi(bp) : -1;
+  if (bpv != 0 && c.weight_bits == 8 && dn::bproj_shape_ok(R, D, &rt) && (rt == 3 || bpv == 1)) h->rt1 = rt;
   h->batched = true;
   return DN_OK;
 }
@@ -275,7 +282,9 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   if (h->verbose)
     std::fprintf(stderr, "[dn] handle: %d layer(s), batch %d: %s%s\n", cfg->n_layers, cfg->batch,
                  h->persist ? "whole-stack kernel" : h->batched ? "batched kernels" : "per-layer kernels",
-                 h->persist ? (h->coop ? ", cooperative launch" : ", ordinary launch") : "");
+                 h->persist   ? (h->coop ? ", cooperative launch" : ", ordinary launch")
+                 : h->batched ? (h->rt1 ? ", in_proj whole-K" : ", in_proj split-K")
+                              : "");
   *out = h;
   return DN_OK;
 }
@@ -338,11 +347,29 @@ DN_API int dn_get_state(dn_layer* h, float* S, float* ring) {
 }
 
 namespace {
-// One batched projection: split the activations, split-K MFMA GEMM, epilogue.
+// One batched projection: split the activations, split-K MFMA GEMM, epilogue; or, with rt > 0,
+// split the activations and run the whole-K kernel that ends in the epilogue.
 // act == nullptr: the activations are already split (the state kernel splits the gated readout).
 int batched_proj(dn_layer* h, const void* W, const float* s, const float* act, int K, int M, int mf, int kr, bool up,
-                 bool prenorm, const float* conv_w, float* ring, float* outp, int out_stride, hipStream_t st) {
+                 bool prenorm, const float* conv_w, float* ring, float* outp, int out_stride, hipStream_t st,
+                 int rt = 0) {
   const dn_config& c = h->cfg;
+  if (rt > 0) {
+    if (act) {
+      dn::BSplitArgs sp{};
+      sp.act = act; sp.act_stride = K; sp.K = K; sp.B = c.batch; sp.xs = h->xs; sp.sc = h->sc; sp.ssq = h->ssq;
+      if (dn::launch_bsplit_row(sp, st) != hipSuccess) return DN_E_DEVICE;
+    }
+    dn::BGemmArgs g{};
+    g.W = W; g.xs = h->xs; g.sc = h->sc; g.M = M; g.K = K; g.B = c.batch;
+    dn::BEpiArgs e{};
+    e.M = M; e.B = c.batch; e.s = s; e.ssq = h->ssq; e.NC = K / 128; e.K = K; e.prenorm = prenorm ? 1 : 0;
+    e.eps = c.eps_rms; e.conv_w = conv_w; e.ring = ring; e.C = h->C; e.Kc = c.conv_k; e.out = outp;
+    e.out_stride = out_stride;
+    if (dn::launch_bproj(g, e, c.weight_bits, rt, st) != hipSuccess) return DN_E_DEVICE;
+    if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return DN_E_DEVICE;
+    return DN_OK;
+  }
   // the up-front GEMM splits its own K range of the activations (8-bit weights, 256-column ranges,
   // at least two row blocks); otherwise a separate split kernel runs first
   const bool fuse = act && up && c.weight_bits == 8 && kr == 256 && mf >= 2;
@@ -436,7 +463,8 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     for (size_t l = 0; l < L; ++l) {
       const dn_weights& w = h->w[l];
       if (int rc = batched_proj(h, w.w_in, w.s_in, l == 0 ? x : out + (l - 1) * B * D, (int)D, h->R, h->mf1, h->kr1,
-                                h->up1, (c.flags & DN_X_RMSNORM) != 0, w.conv_w, h->ring + l * h->ring_elems, h->u, h->R, st);
+                                h->up1, (c.flags & DN_X_RMSNORM) != 0, w.conv_w, h->ring + l * h->ring_elems, h->u, h->R, st,
+                                h->rt1);
           rc != DN_OK)
         return fail(h, rc);
       dn::BStateArgs bs{};

@@ -82,10 +82,12 @@ __device__ __forceinline__ void split3(float v, float inv1, float s1, float inv2
 // the order the GEMM's LDS fragments take: for column block nb and chunk c a 24 KB block
 // [term][k-step][column fragment][lane][16 bytes] (lane = sequence % 16 + 16 * (16-column group of
 // the k-step)), the chunk's scale per sequence, and its sum of squares (for the input pre-norm).
-__global__ __launch_bounds__(256) void k_bsplit(const BSplitArgs a) {
-  const int tid = threadIdx.x, c = blockIdx.x, nb = blockIdx.y;
+__global__ __launch_bounds__(64) void k_bsplit(const BSplitArgs a) {
+  // one wave per 16 sequences of a chunk: blockIdx.y = 4 * (block of 64 sequences) + group of 16
+  const int tid = threadIdx.x, c = blockIdx.x, nb = blockIdx.y >> 2;
   const int NC = gridDim.x;
-  const int sb = tid >> 2, sq4 = tid & 3;  // sequence nb*64 + sb, columns 32 sq4 .. +31 of the chunk
+  // sequence nb*64 + sb, columns 32 sq4 .. +31 of the chunk
+  const int sb = 16 * (blockIdx.y & 3) + (tid >> 2), sq4 = tid & 3;
   const int b = nb * NT + sb;
   const bool valid = b < a.B;
   const float* arow = a.act + (size_t)(valid ? b : 0) * a.act_stride + c * KC + 32 * sq4;
@@ -544,6 +546,230 @@ __global__ __launch_bounds__(256 * NRB) void k_bgemm2(const BGemmArgs a) {
   }
 }
 
+// Three-term split of whole activation rows for the whole-K projection: one workgroup per sequence,
+// one scale per row (s1 = max|v| / 127 over all K columns, as the single-sequence path splits its
+// input), written in the fragment order of k_bsplit; the row's scale goes to sc [block][64] and its
+// sum of squares (for the input pre-norm) to ssq [B].
+__global__ __launch_bounds__(256) void k_bsplit_row(const BSplitArgs a) {
+  constexpr int NP = 8;  // passes of 1024 columns (K <= 8192)
+  __shared__ float rmx[4], rss[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+  const int K = a.K, NC = K / KC, nb = b / NT, sb = b % NT;
+  const float* row = a.act + (size_t)b * a.act_stride;
+  v4f v[NP];
+  float mx = 0.f, ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c = 4 * tid + 1024 * p;
+    v[p] = c < K ? *reinterpret_cast<const v4f*>(row + c) : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mx = fmaxf(mx, fabsf(v[p][e]));
+      ss = fmaf(v[p][e], v[p][e], ss);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+    ss += __shfl_xor(ss, o);
+  }
+  if (lane == 0) {
+    rmx[wave] = mx;
+    rss[wave] = ss;
+  }
+  __syncthreads();
+  mx = fmaxf(fmaxf(rmx[0], rmx[1]), fmaxf(rmx[2], rmx[3]));
+  ss = (rss[0] + rss[1]) + (rss[2] + rss[3]);
+  float s1 = mx * (1.0f / 127.0f);
+  if (!(s1 > 0.f)) s1 = 1.0f;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
+  if (tid == 0) {
+    a.sc[(size_t)nb * NT + sb] = s1;
+    a.ssq[b] = ss;
+  }
+  int8_t* xs = static_cast<int8_t*>(a.xs);
+  const int f = sb >> 4;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int k0 = 4 * tid + 1024 * p;
+    if (k0 >= K) break;
+    int h[4], m[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split3(v[p][e], inv1, s1, inv2, s2, inv3, h[e], m[e], l[e]);
+    // column k0 .. k0+3: chunk c, k-step ks, 16-column group g, bytes (k0 % 16) .. +3 of lane
+    // (sb % 16) + 16 g of column fragment f
+    const int c = k0 / KC, kk = k0 % KC, ks = kk / 64, gq = (kk % 64) / 16;
+    const size_t frag0 = ((size_t)(nb * NC + c) * (3 * KSC * 4 * 64)) * 16 + (kk % 16);
+    const int ln = (sb & 15) + 16 * gq;
+    auto pack = [](const int (&q)[4]) {
+      return (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | ((q[3] & 0xFF) << 24);
+    };
+    *reinterpret_cast<int*>(xs + frag0 + (size_t)(((0 * KSC + ks) * 4 + f) * 64 + ln) * 16) = pack(h);
+    *reinterpret_cast<int*>(xs + frag0 + (size_t)(((1 * KSC + ks) * 4 + f) * 64 + ln) * 16) = pack(m);
+    *reinterpret_cast<int*>(xs + frag0 + (size_t)(((2 * KSC + ks) * 4 + f) * 64 + ln) * 16) = pack(l);
+  }
+}
+
+// Whole-K projection with the epilogue fused (no partial sums), 8-bit weights: a workgroup of eight
+// waves owns 16*RT weight rows and 64 sequences; wave w takes the K quarter w % 4 (chunks of 128
+// columns (w % 4)*CPW .. +CPW-1) for the 32 sequences of half w / 4. The activations are split with
+// one scale per row (k_bsplit_row), so each wave keeps exact int32 sums of the three terms over its
+// whole K quarter (at most 127 * 127 * 1024 < 2^24 in magnitude: exact in fp32 too) and folds them
+// once.
+//  * Weights and split activations stream into registers, two chunks in flight; the two sequence
+//    halves read the same weight rows (the second from cache), and every workgroup reads the same
+//    few hundred KB of activations (L2-resident).
+//  * Epilogue inputs (row scales, conv taps, conv history, sums of squares) go to LDS by direct
+//    loads issued first, so their latency hides behind the stream.
+// The four K quarters' sums meet in LDS and are added in quarter order; then each (row, sequence)
+// gets k_bepi's epilogue. (Staging the weights in LDS instead, shared by the two halves, measured
+// slower: 19.7 against 17.2 us for the 12288 x 2048 in_proj at 64 sequences on MI355X.)
+template <int RT, int CPW>
+__global__ __launch_bounds__(512) void k_bproj(const BGemmArgs g, const BEpiArgs e) {
+  constexpr int ROWS = 16 * RT, NF = 2;  // sequence tiles of 16 per wave
+  // dynamic LDS (bproj_lds_bytes): [quarter sums 4*NT*ROWS | history 3*NT*ROWS | taps 4*ROWS |
+  // scales 64 | sums of squares NT] floats. The direct-to-LDS copies write it behind the compiler's
+  // back, which it must not assume to be unwritten.
+  extern __shared__ float bproj_lds[];
+  float(*red)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds);                     // [4]
+  float(*ring_l)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds + 4 * NT * ROWS);  // [3]
+  float* cw_l = bproj_lds + 7 * NT * ROWS;
+  float* s_l = cw_l + 4 * ROWS;
+  float* ssq_l = s_l + 64;
+  // wave index uniform (scalar): the direct-to-LDS destinations derive from it
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = wave & 3, f0 = NF * (wave >> 2);
+  const int rb = blockIdx.x, nb = blockIdx.y;
+  const int M = g.M, K = g.K, B = g.B, NC = K / KC;
+  const int row0 = rb * ROWS;
+  const bool conv = e.conv_w != nullptr;
+  const int Kc = e.Kc, C = e.C;
+
+  // epilogue inputs into LDS, slot 64 i + lane of instruction i (addresses clamped into range)
+  {
+    const int nring = (conv && row0 < C) ? (Kc - 1) * NT * ROWS / 64 : 0;
+    for (int i = wave; i < nring; i += 8) {
+      const int idx = 64 * i + lane, j = idx / (NT * ROWS), rem = idx % (NT * ROWS);
+      const int bl = rem / ROWS, rl = rem % ROWS;
+      const int b = min(nb * NT + bl, B - 1), r = min(row0 + rl, C - 1);
+      __builtin_amdgcn_global_load_lds(e.ring + ((size_t)b * (Kc - 1) + j) * C + r, &ring_l[0][0][0] + 64 * i, 4, 0, 0);
+    }
+    if (wave == 0) __builtin_amdgcn_global_load_lds(e.s + min(row0 + lane, M - 1), s_l, 4, 0, 0);
+    if (wave == 1) __builtin_amdgcn_global_load_lds(e.ssq + min(nb * NT + lane, B - 1), ssq_l, 4, 0, 0);
+    for (int i = wave; conv && row0 < C && i < ROWS * 4 / 64; i += 8) {
+      const int idx = 64 * i + lane, rl = idx / 4, q = idx % 4;
+      __builtin_amdgcn_global_load_lds(e.conv_w + (size_t)min(row0 + rl, C - 1) * Kc + min(q, Kc - 1), cw_l + 64 * i, 4, 0, 0);
+    }
+  }
+
+  // buffer loads: one VGPR offset per weight row tile and one for the activations, the chunk and
+  // k-step offsets in scalars, so that the chunks in flight hold no per-load addresses
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(g.W), (short)0, (int)((size_t)M * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(g.xs), (short)0, (int)((size_t)(nb + 1) * NC * 24576), 0x00020000);
+  // the lane's weight row in each row tile (rows past M read row M-1; their sums are discarded)
+  int wofs[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) wofs[rt] = min(row0 + 16 * rt + (lane & 15), M - 1) * K + 16 * (lane >> 4);
+  const int xofs = 16 * lane + f0 * 1024;
+  const int xblk = nb * NC * 24576;
+  float s1[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) s1[f] = g.sc[(size_t)nb * NT + 16 * (f0 + f) + (lane & 15)];
+
+  v4i A[2][KSC][RT];
+  v4i X[2][KSC][3][NF];
+  auto load_chunk = [&](int i, int buf) {
+    const int c = kq * CPW + i;
+#pragma unroll
+    for (int s = 0; s < KSC; ++s) {
+      const int kb = c * KC + 64 * s;  // byte offset of the k-step in a weight row
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        A[buf][s][rt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wofs[rt], kb, 0));
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          X[buf][s][t][f] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, xofs + ((t * KSC + s) * 4 + f) * 1024, xblk + c * 24576, 0));
+    }
+  };
+
+  v4i acc[RT][3][NF];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[rt][t][f] = v4i{0, 0, 0, 0};
+  // Two chunks in flight, one per buffer. The scheduler would sink each load next to its first use;
+  // the barriers keep the lead, so the wait before a chunk's MFMAs leaves the other buffer's loads in
+  // flight.
+  load_chunk(0, 0);
+  if (CPW > 1) load_chunk(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int buf = i & 1;
+#pragma unroll
+    for (int s = 0; s < KSC; ++s)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+            acc[rt][t][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[buf][s][rt], X[buf][s][t][f], acc[rt][t][f], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < CPW) load_chunk(i + 2, buf);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // fold the three exact term sums with the row scale; the MFMA output layout: lane holds sequence
+  // 16 f + lane % 16, rows 16 rt + 4 (lane / 16) + v
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float d = (float)acc[rt][0][f][v] +
+                        fmaf((float)acc[rt][2][f][v], 1.0f / 254.0f, (float)acc[rt][1][f][v]) * (1.0f / 254.0f);
+        red[kq][16 * (f0 + f) + (lane & 15)][16 * rt + 4 * (lane >> 4) + v] = s1[f] * d;
+      }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS copies have landed (they were issued first)
+  __syncthreads();
+
+  // epilogue, rows fastest (coalesced history and output)
+  constexpr int EPI = NT * ROWS / 512;
+  static_assert(NT * ROWS % 512 == 0, "");
+#pragma unroll
+  for (int j = 0; j < EPI; ++j) {
+    const int idx = j * 512 + tid, rl = idx % ROWS, bl = idx / ROWS;
+    const int r = row0 + rl, b = nb * NT + bl;
+    if (r >= M || b >= B) continue;
+    const float sum = ((red[0][bl][rl] + red[1][bl][rl]) + red[2][bl][rl]) + red[3][bl][rl];
+    const float pf = e.prenorm ? rsqrtf(ssq_l[bl] / (float)K + e.eps) : 1.0f;
+    const float u = s_l[rl] * pf * sum;
+    float o = u;
+    if (conv && r < C) {
+      float acc2 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (q < Kc - 1) acc2 = fmaf(cw_l[4 * rl + q], ring_l[q][bl][rl], acc2);
+      acc2 = fmaf(cw_l[4 * rl + min(3, Kc - 1)], u, acc2);
+      float* rg = e.ring + (size_t)b * (Kc - 1) * C + r;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (q + 1 < Kc - 1) rg[(size_t)q * C] = ring_l[q + 1][bl][rl];
+      if (Kc > 1) rg[(size_t)(Kc - 2) * C] = u;
+      o = silu(acc2);
+    }
+    e.out[(size_t)b * e.out_stride + r] = o;
+  }
+}
+
 // Finish the rows: add the K-range partial sums in order, row scale, input pre-norm factor, and for
 // rows r < C the causal conv over the history (oldest first) plus SiLU, advancing the history.
 template <int NB>
@@ -755,15 +981,44 @@ hipError_t bgemm_bits(const BGemmArgs& a, int mf, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+constexpr size_t bproj_lds_bytes(int rt) { return sizeof(float) * (7 * NT * 16 * rt + 4 * 16 * rt + 64 + NT); }
+
+template <int RT, int CPW>
+hipError_t go_bproj(const BGemmArgs& g, const BEpiArgs& e, hipStream_t st) {
+  constexpr size_t lds = bproj_lds_bytes(RT);
+  static_assert(lds <= 160 * 1024, "");
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bproj<RT, CPW>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((g.M + 16 * RT - 1) / (16 * RT), (g.B + NT - 1) / NT);
+  hipLaunchKernelGGL((k_bproj<RT, CPW>), grid, dim3(512), lds, st, g, e);
+  return hipGetLastError();
+}
+
+template <int RT>
+hipError_t bproj_rt(const BGemmArgs& g, const BEpiArgs& e, hipStream_t st) {
+  switch (g.K / (4 * KC)) {
+    case 2: return go_bproj<RT, 2>(g, e, st);
+    case 4: return go_bproj<RT, 4>(g, e, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 bool bgemm_shape_ok(int M, int K, int mf, int kr) {
   return M > 0 && K > 0 && mf == 1 && M % (64 * mf) == 0 && (kr == 256 || kr == 512 || kr == 1024) && K % kr == 0;
 }
 
+hipError_t launch_bsplit_row(const BSplitArgs& a, hipStream_t st) {
+  if (a.K % 1024 || a.K > 8192 || a.act_stride % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bsplit_row, dim3(a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bsplit(const BSplitArgs& a, hipStream_t st) {
   if (a.K % KC) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bsplit, dim3(a.K / KC, (a.B + NT - 1) / NT), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_bsplit, dim3(a.K / KC, 4 * ((a.B + NT - 1) / NT)), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -838,6 +1093,21 @@ hipError_t launch_bstate(const BStateArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL(k_bstate<false>, dim3(a.Hv, a.B), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// The whole-K projection (8-bit weights) takes K = 4 * CPW * 128 with CPW 2 or 4 (every wave two or
+// four chunks) and row tiles of 48 rows when M leaves at least one workgroup per compute unit's worth
+// of them, else of 32.
+bool bproj_shape_ok(int M, int K, int* rt) {
+  if (M <= 0 || K <= 0 || K % (4 * KC) || (K / (4 * KC) != 2 && K / (4 * KC) != 4)) return false;
+  *rt = M >= 48 * 256 ? 3 : 2;
+  return true;
+}
+
+hipError_t launch_bproj(const BGemmArgs& g, const BEpiArgs& e, int bits, int rt, hipStream_t st) {
+  int want = 0;
+  if (bits != 8 || !bproj_shape_ok(g.M, g.K, &want) || (rt != 2 && rt != 3)) return hipErrorInvalidValue;
+  return rt == 2 ? bproj_rt<2>(g, e, st) : bproj_rt<3>(g, e, st);
 }
 
 }  // namespace dn

@@ -51,6 +51,7 @@ struct dn_layer {
   bool batched = false;
   int mf1 = 0, kr1 = 0, mf2 = 0, kr2 = 0;  // rows per workgroup / 64 and K range of in_proj, out_proj
   bool up1 = false, up2 = false;           // the projection uses the all-loads-up-front GEMM (NRB = mf)
+  int rt1 = 0;                             // in_proj as one whole-K kernel with 16*rt1-row tiles (0: split-K GEMM)
   float* part = nullptr;                   // split-K partial sums
   void* xs = nullptr;                      // activations split into int8 terms, fragment order
   float* sc = nullptr;                     // their per-(sequence, 128-column chunk) scales

@@ -125,6 +125,15 @@ hipError_t launch_bgemm(const BGemmArgs& a, int bits, int mf, hipStream_t st);
 bool bgemm2_shape_ok(int M, int K, int nrb, int kr);
 hipError_t launch_bgemm2(const BGemmArgs& a, int bits, int nrb, hipStream_t st);
 hipError_t launch_bepi(const BEpiArgs& a, hipStream_t st);
+// The three-term split of whole rows (one scale per row) for the whole-K projection: xs as for
+// launch_bsplit, sc [ceil(B/64)][64] row scales, ssq [B] row sums of squares; K a multiple of 1024.
+hipError_t launch_bsplit_row(const BSplitArgs& a, hipStream_t st);
+// out[b][r] = epilogue(s[r] * sum_k W[r][k] act[b][k]) over the whole K in one kernel: a
+// workgroup takes 16*RT rows and 64 sequences, its eight waves a quarter of K and half of the
+// sequences each (act split by launch_bsplit_row). g supplies W, xs, sc, M, K, B; e the epilogue
+// (part and KS unused; ssq the row sums of launch_bsplit_row).
+bool bproj_shape_ok(int M, int K, int* rt);
+hipError_t launch_bproj(const BGemmArgs& g, const BEpiArgs& e, int bits, int rt, hipStream_t st);
 hipError_t launch_bstate(const BStateArgs& a, hipStream_t st);
 
 // Whole-row three-term split for the library GEMMs: row t of act becomes

@@ -1,7 +1,9 @@
-"""The batched path (B >= 2 sequences with 128 x 128 state tiles: int8-MFMA projections with
-split-K partial sums, streaming state kernel): parity with the oracle per sequence, ragged
-batches (a partial block of 64 sequences), int4 weights, conv widths, a pre-normed stack, K ranges
-of 1024 / 512 / 256 columns, agreement with the per-layer kernels and bitwise reruns."""
+"""The batched path (B >= 2 sequences with 128 x 128 state tiles: int8-MFMA projections, streaming
+state kernel): parity with the oracle per sequence, ragged batches (a partial block of 64
+sequences), int4 weights, conv widths, a pre-normed stack, K ranges of 1024 / 512 / 256 columns,
+agreement with the per-layer kernels and bitwise reruns. The in_proj runs as the split-K GEMM with a
+separate epilogue, or (shapes with at least 48 x 256 rows, or every supported shape under
+DN_BPROJ=1) as one whole-K kernel that ends in the epilogue; both are checked."""
 import numpy as np
 import pytest
 
@@ -37,7 +39,18 @@ BATCHED = {
     # 48 value heads of 128 over 16 key heads: in_proj 16384 rows, out_proj K = 6144
     "b_heads48": gi.custom("b_heads48", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=48, d_v=128, batch=4,
                            n_tokens=3, ring_std=1.0),
+    # the stack's layer shape (in_proj 12288 rows: the whole-K kernel by default), pre-normed, 70
+    # sequences (a full block of 64 and a ragged block of 6)
+    "b_wide": gi.custom("b_wide", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=32, d_v=128, batch=70,
+                        n_tokens=2, flags=gi.DN_X_RMSNORM, ring_std=1.0),
 }
+# shapes whose in_proj also runs through the whole-K kernel when forced (8-bit weights, K of 1024 or
+# 2048); b_int4 stays on the split-K GEMM
+WHOLE_K = ["b_small", "b_int4", "b_conv1", "b_conv2", "b_stack", "b_perkey"]
+
+
+def _in_rows(cfg):
+    return 2 * cfg.n_k_heads * cfg.d_k + 2 * cfg.n_v_heads * cfg.d_v
 
 
 def _path_of(cfg, layers, capfd, monkeypatch):
@@ -53,14 +66,23 @@ def _per_seq_out_err(gout, ref):
     return max(out_err(gout[:, l, b], ref[:, l, b]) for l in range(L) for b in range(B))
 
 
-@pytest.mark.parametrize("name", list(BATCHED))
-def test_batched_parity(name, capfd, monkeypatch):
+CASES = [(n, None) for n in BATCHED] + [(n, "1") for n in WHOLE_K]
+
+
+@pytest.mark.parametrize("name,bproj", CASES)
+def test_batched_parity(name, bproj, capfd, monkeypatch):
     cfg = BATCHED[name]
     layers, stream = gi.generate(cfg)
-    print(f"[batched] {name}", flush=True)
+    print(f"[batched] {name} (DN_BPROJ={bproj})", flush=True)
+    if bproj:
+        monkeypatch.setenv("DN_BPROJ", bproj)
     st, err = _path_of(cfg, layers, capfd, monkeypatch)
+    if bproj:
+        monkeypatch.delenv("DN_BPROJ")
     try:
         assert "batched kernels" in err, err
+        whole_k = cfg.weight_bits == 8 and (bproj or (_in_rows(cfg) >= 48 * 256 and cfg.d_model in (1024, 2048)))
+        assert ("in_proj whole-K" if whole_k else "in_proj split-K") in err, err
         gout = run_gpu(st, stream)
         gS, gH = st.get_state()
     finally:
@@ -69,7 +91,7 @@ def test_batched_parity(name, capfd, monkeypatch):
     e = _per_seq_out_err(gout, ref_out)
     es = state_err(gS.cpu().numpy(), ref_S)
     eh = state_err(gH.cpu().numpy(), ref_H) if cfg.conv_k > 1 else 0.0
-    print(f"[batched] {name}: out {e:.2e} state {es:.2e} ring {eh:.2e}", flush=True)
+    print(f"[batched] {name} (DN_BPROJ={bproj}): out {e:.2e} state {es:.2e} ring {eh:.2e}", flush=True)
     assert e <= OUT_TOL and es <= STATE_TOL and eh <= STATE_TOL
 
 
