@@ -847,13 +847,15 @@ __global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
   // Every barrier below hands over LDS data only (lds_barrier): the state tile's stores are not
   // waited for, so the workgroup goes on with the readout while they drain.
   // The tile through a buffer resource: one offset register per lane, the row steps in scalars (the
-  // addresses of sixteen loads and stores held in registers would cost a workgroup per CU). Plain
-  // cache policy: non-temporal loads and stores of the tile measured 45 against 34 us on MI355X.
+  // addresses of sixteen loads and stores held in registers would cost a workgroup per CU).
+  // Non-temporal: with the plain policy a single layer's states stay in the last-level cache from
+  // one step to the next (39 us), but states that do not fit it, as in a stack of layers, take
+  // 61 us against 50 for the non-temporal form on MI355X.
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(Sb, (short)0, DK * DV * 4, 0x00020000);
   const int soff = (16 * rg * DV + 4 * cg) * 4;
   v4f s[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(srs, soff, r * DV * 4, 0));
+  for (int r = 0; r < 16; ++r) s[r] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(srs, soff, r * DV * 4, 2));
 
   const float* ub = a.u + (size_t)b * a.R;
   const int g = h / (a.Hv / a.Hk);
@@ -923,7 +925,7 @@ __global__ __launch_bounds__(256) void k_bstate(const BStateArgs a) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, s[r]), srs, soff, r * DV * 4, 0);
+  for (int r = 0; r < 16; ++r) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, s[r]), srs, soff, r * DV * 4, 2);
 #pragma unroll
   for (int j = 0; j < 4; ++j) red[rg][4 * cg + j] = op[j];
   lds_barrier();
