@@ -404,6 +404,13 @@ def bench_prefill(args, gi, dn, cpu):
                                f"{cfg.n_k_heads}x{cfg.d_k} key / {cfg.n_v_heads}x{cfg.d_v} value heads, 8-bit weights",
                    "layers": cfg.n_layers, "prompt_tokens": T},
         "projection_tflops_algorithmic": round(proj_flops / (per * 1e-3) / 1e12, 2),
+        # the prompt's dominant work is the two projections on the int8 matrix cores: their
+        # algorithmic ops (2 per weight per token) over the whole step's time, against the int8
+        # dense peak; the three-term split executes three times those ops
+        "roofline": {"bound": "mfma", "achieved": round(proj_flops / (per * 1e-3) / 1e12, 1), "peak": 5000.0,
+                     "unit": "TOP/s (int8)", "frac": round(proj_flops / (per * 1e-3) / 1e12 / 5000.0, 4),
+                     "traffic": None, "kernel": "dn_prefill step (every kernel of the prompt)",
+                     "executed_int8_tops": round(3 * proj_flops / (per * 1e-3) / 1e12, 1)},
         "cpu_baseline": cpu,
         "device": f"{props.name} {getattr(props, 'gcnArchName', '')}".strip(),
     }
