@@ -208,6 +208,20 @@ hipError_t launch_pconv(const PConvArgs& a, hipStream_t st);
 hipError_t launch_pintra(const PIntraArgs& a, hipStream_t st);
 hipError_t launch_pscan(const PScanArgs& a, hipStream_t st);
 hipError_t launch_pnorm(const PNormArgs& a, hipStream_t st);
+// The prompt projections with 8-bit weights as one int8 matrix-core GEMM with the fold of the three
+// terms in its epilogue: out[t][m] = s1[t] * (D0 + (D1 + D2 / 254) / 254), Dτ = sum_k W[m][k] X[τ][t][k]
+// exact in int32, folded in double. X is k_tsplit's [3][T][K]; out has the layout of a single
+// K-range partial sum ([1][T][M]) for k_pconv / k_bepi. K a multiple of 128, M of 4, M K and 3 T K
+// below 2^31 (32-bit byte offsets); out 16-byte aligned.
+struct PGemmArgs {
+  const int8_t* W;  // [M][K]
+  const int8_t* X;  // [3][T][K]
+  const float* s1;  // [T]
+  float* out;       // [T][M]
+  int M, K, T;
+};
+bool pgemm_shape_ok(int M, int K, int T);
+hipError_t launch_pgemm(const PGemmArgs& a, hipStream_t st);
 
 // ---- whole-stack kernel (single sequence, 128 x 128 state tiles) ----
 struct LayerW {

@@ -130,9 +130,10 @@ __global__ __launch_bounds__(256) void k_pconv(const PConvArgs a) {
 
 typedef int pc_v4i __attribute__((ext_vector_type(4)));
 
-// k_pconv on the library GEMM's exact term sums, four adjacent rows per thread: 16-byte loads and
-// stores, and every load unconditional (a token past the prompt reads the last token's row and is
-// not stored), so the loads of a run of tokens are all in flight together.
+// k_pconv on the exact term sums of the three-term GEMM (folded here in double with the token's
+// scale), or on sums the GEMM already folded the same way (one K range), four adjacent rows per
+// thread: 16-byte loads and stores, and every load unconditional (a token past the prompt reads the
+// last token's row and is not stored), so the loads of a run of tokens are all in flight together.
 constexpr int TR4 = 16;
 __global__ __launch_bounds__(256) void k_pconv4(const PConvArgs a) {
   __shared__ float pn[TR4 + 3];  // pre-norm factors of tokens t0 - 3 .. t0 + TR4 - 1
@@ -150,6 +151,12 @@ __global__ __launch_bounds__(256) void k_pconv4(const PConvArgs a) {
   const size_t plane = (size_t)a.T * a.M;
   auto pre4 = [&](int t, float f, float (&o)[4]) {
     const size_t at = (size_t)t * a.M + r;
+    if (!a.terms) {  // the sums already folded (one K range)
+      const v4f p = *reinterpret_cast<const v4f*>(a.part + at);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = sr[e] * f * p[e];
+      return;
+    }
     const pc_v4i d0 = *reinterpret_cast<const pc_v4i*>(a.terms + at);
     const pc_v4i d1 = *reinterpret_cast<const pc_v4i*>(a.terms + plane + at);
     const pc_v4i d2 = *reinterpret_cast<const pc_v4i*>(a.terms + 2 * plane + at);
@@ -497,10 +504,141 @@ __global__ __launch_bounds__(128) void k_pnorm(const PNormArgs a) {
   *op = a.norm_w[j] * o * inv * silu(z);
 }
 
+typedef int pg_v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void pg_lds_t;
+
+// k_pgemm: a workgroup of eight waves owns 256 weight rows and 64 tokens (x 3 terms); wave w the rows
+// 64 (w % 4) .. +63 (four 16-row tiles) against the 32 tokens of half w / 4 and their three terms:
+// 4 x 2 x 3 MFMA tiles (v_mfma_i32_16x16x64_i8), 96 accumulators. K advances in stages of 128
+// columns, two LDS buffers: while a stage's products run, the next stage goes from memory straight
+// into the other buffer (buffer loads with the LDS bit, no registers between). A stage holds 28 tiles
+// of 16 rows (or tokens) x 128 columns, 2 KB each: 16 weight tiles, then 3 terms x 4 token tiles.
+// Each load instruction covers 8 whole rows of 128 bytes (lane l: row l / 8, 16-byte chunk
+// (l % 8) ^ PG_SWZ(row)), so every cache line fetched is used whole; the xor permutation of the
+// chunks makes the operand reads (lane l: row l % 16, chunk 4 k + l / 16 of k-step k) hit every LDS
+// bank once per group of 16 lanes. One barrier per stage.
+constexpr int PG_ROWS = 256, PG_TOK = 64, PG_KC = 128, PG_WAVES = 8;
+constexpr int PG_AT = PG_ROWS / 16, PG_XT = 3 * (PG_TOK / 16);  // weight and token tiles per stage
+constexpr int PG_TILE = 2048, PG_STAGE = (PG_AT + PG_XT) * PG_TILE;
+constexpr int PG_NI = (PG_AT + PG_XT) * 2 / PG_WAVES;  // load instructions per wave per stage: 7
+
+__device__ __forceinline__ int pg_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ void pg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(512) void k_pgemm(const PGemmArgs a) {
+  __shared__ pg_v4i sq[2][PG_STAGE / 16];
+  // wave index uniform (scalar): which tile each of its loads fills derives from it
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = wave & 3, th = wave >> 2;  // row group of 64, token half of 32
+  const int row0 = blockIdx.x * PG_ROWS, t0 = blockIdx.y * PG_TOK;
+  const int NS = a.K / PG_KC;
+  const __amdgpu_buffer_rsrc_t rsW =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.W), (short)0, (int)((size_t)a.M * a.K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsX =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.X), (short)0, (int)((size_t)3 * a.T * a.K), 0x00020000);
+  // load instruction g = 7 w + i of a stage fills rows 8 (g % 2) .. +7 of tile g / 2; rows and tokens
+  // past the end are clamped (their sums are never stored); per-lane byte offsets at the stage's
+  // first column
+  int off[PG_NI];
+#pragma unroll
+  for (int i = 0; i < PG_NI; ++i) {
+    const int g = PG_NI * wave + i, r = 8 * (g & 1) + (lane >> 3), c = (lane & 7) ^ pg_swz(r);
+    if (g < 2 * PG_AT) {
+      off[i] = min(row0 + 16 * (g >> 1) + r, a.M - 1) * a.K + 16 * c;
+    } else {
+      const int xt = (g - 2 * PG_AT) >> 1, term = xt >> 2, tt = xt & 3;
+      off[i] = (term * a.T + min(t0 + 16 * tt + r, a.T - 1)) * a.K + 16 * c;
+    }
+  }
+  auto issue = [&](int stage) {
+    char* const base = reinterpret_cast<char*>(sq[stage & 1]);
+#pragma unroll
+    for (int i = 0; i < PG_NI; ++i) {
+      const int g = PG_NI * wave + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < 2 * PG_AT ? rsW : rsX, (pg_lds_t*)(base + 1024 * g), 16, off[i],
+                                               stage * PG_KC, 0, 0);
+    }
+  };
+  // operand reads within a tile: byte offsets of lane l's chunk for k-steps 0 and 1
+  const int rr = lane & 15, rd0 = 16 * (64 * (rr >> 3) + 8 * (rr & 7) + ((lane >> 4) ^ pg_swz(rr)));
+  const int rd1 = rd0 ^ 64;
+  struct Ops { pg_v4i A[4], X[3][2]; };
+  auto read = [&](int stage, int rd, Ops& o) {
+    const char* const base = reinterpret_cast<const char*>(sq[stage & 1]) + rd;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o.A[r] = *reinterpret_cast<const pg_v4i*>(base + (4 * rg + r) * PG_TILE);
+#pragma unroll
+    for (int term = 0; term < 3; ++term)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        o.X[term][tt] = *reinterpret_cast<const pg_v4i*>(base + (PG_AT + 4 * term + 2 * th + tt) * PG_TILE);
+  };
+  pg_v4i acc[4][2][3];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int term = 0; term < 3; ++term) acc[r][tt][term] = pg_v4i{0, 0, 0, 0};
+  auto mfma = [&](const Ops& o) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int term = 0; term < 3; ++term)
+          acc[r][tt][term] = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.A[r], o.X[term][tt], acc[r][tt][term], 0, 0, 0);
+  };
+  issue(0);
+  for (int st = 0; st < NS; ++st) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage st have landed
+    pg_barrier();  // every wave's loads of stage st landed; every wave is done with stage st - 1's buffer
+    if (st + 1 < NS) issue(st + 1);
+    Ops o0, o1;
+    read(st, rd0, o0);
+    read(st, rd1, o1);
+    __builtin_amdgcn_sched_barrier(0);  // all reads first: the second k-step's arrive under the first's products
+    mfma(o0);
+    mfma(o1);
+  }
+  // epilogue: lane holds token t0 + 32 th + 16 tt + lane % 16, rows 16 r + 4 (lane / 16) + v of the
+  // wave's four row tiles; the three terms folded in double with the token's scale (as k_pconv
+  // folds the library GEMM's sums), four consecutive rows per 16-byte store
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = t0 + 32 * th + 16 * tt + (lane & 15);
+    const double s1 = (double)a.s1[min(t, a.T - 1)];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = row0 + 64 * rg + 16 * r + 4 * (lane >> 4);
+      v4f o;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        o[v] = (float)(s1 * ((double)acc[r][tt][0][v] +
+                             ((double)acc[r][tt][1][v] + (double)acc[r][tt][2][v] * (1.0 / 254.0)) * (1.0 / 254.0)));
+      if (t < a.T) {
+        if (m + 3 < a.M) {
+          *reinterpret_cast<v4f*>(a.out + (size_t)t * a.M + m) = o;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (m + v < a.M) a.out[(size_t)t * a.M + m + v] = o[v];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one tile's doubles live at a time
+    }
+  }
+}
 }  // namespace
 
 hipError_t launch_pconv(const PConvArgs& a, hipStream_t st) {
-  if (a.terms && a.M % 4 == 0 && a.C % 4 == 0 && reinterpret_cast<uintptr_t>(a.terms) % 16 == 0 &&
+  const void* in4 = a.terms ? static_cast<const void*>(a.terms) : a.KS == 1 ? static_cast<const void*>(a.part) : nullptr;
+  if (in4 && a.M % 4 == 0 && a.C % 4 == 0 && reinterpret_cast<uintptr_t>(in4) % 16 == 0 &&
       reinterpret_cast<uintptr_t>(a.out) % 16 == 0) {
     hipLaunchKernelGGL(k_pconv4, dim3((a.M / 4 + 255) / 256, (a.T + TR4 - 1) / TR4), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -521,6 +659,17 @@ hipError_t launch_pscan(const PScanArgs& a, hipStream_t st) {
 
 hipError_t launch_pnorm(const PNormArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_pnorm, dim3(a.T, a.V / DV), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+bool pgemm_shape_ok(int M, int K, int T) {
+  return M >= 1 && T >= 1 && K >= PG_KC && K % PG_KC == 0 && M % 4 == 0 &&
+         (size_t)M * K < (1u << 31) && (size_t)3 * T * K < (1u << 31);
+}
+
+hipError_t launch_pgemm(const PGemmArgs& a, hipStream_t st) {
+  if (!pgemm_shape_ok(a.M, a.K, a.T) || reinterpret_cast<uintptr_t>(a.out) % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_pgemm, dim3((a.M + PG_ROWS - 1) / PG_ROWS, (a.T + PG_TOK - 1) / PG_TOK), dim3(64 * PG_WAVES), 0, st, a);
   return hipGetLastError();
 }
 

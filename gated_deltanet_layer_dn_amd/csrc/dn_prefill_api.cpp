@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <mutex>
 #include <new>
+#include <string>
 
 #include "dn.h"
 #include "dn_handle.h"
@@ -78,6 +79,23 @@ size_t pf_layout(const dn_layer* h, int T, char* base, PfBufs* b) {
   return off;
 }
 
+// GEMM paths of the projections with 8-bit weights (4-bit weights always take the split-K one):
+//   PF_GEMM_AUTO    the fused hand-written GEMM where its shape constraints hold, else the library
+//                   GEMM where the library has an algorithm for the shape, else split-K
+//   PF_GEMM_FUSED   int8 MFMA GEMM over the three terms with their fold in its epilogue (k_pgemm),
+//                   where its shape constraints hold, else split-K
+//   PF_GEMM_LIBRARY the library's int8 GEMM over the three terms, folded by the next kernel, where
+//                   the library has an algorithm for the shape, else split-K
+//   PF_GEMM_SPLITK  the hand-written split-K GEMM on fragment blocks with a separate reduction
+enum { PF_GEMM_AUTO = 0, PF_GEMM_FUSED, PF_GEMM_LIBRARY, PF_GEMM_SPLITK };
+
+int gemm_from_env() {
+  const char* v = std::getenv("DN_PREFILL_GEMM");
+  if (!v) return PF_GEMM_AUTO;
+  const std::string m(v);
+  return m == "fused" ? PF_GEMM_FUSED : m == "library" ? PF_GEMM_LIBRARY : m == "splitk" ? PF_GEMM_SPLITK : PF_GEMM_AUTO;
+}
+
 // The prompt path's state kept in the handle: scratch sized for the longest prompt so far (grown,
 // never shrunk) and the library GEMMs of 8-bit projections (created at the first prefill).
 struct PrefillExt {
@@ -85,8 +103,8 @@ struct PrefillExt {
   void* buf = nullptr;
   dn::LtCtx* lt = nullptr;
   bool lt_tried = false;
-  bool own_gemm = false;  // DN_PREFILL_OWN_GEMM=1: always the hand-written GEMM
-  bool verbose = false;   // DN_VERBOSE=1: print the projection path of each call
+  int gemm = 0;          // DN_PREFILL_GEMM: the projections' GEMM path (PF_GEMM_*)
+  bool verbose = false;  // DN_VERBOSE=1: print the projection path of each call
 };
 
 void ext_free(void* p) {
@@ -101,7 +119,7 @@ PrefillExt* ext_of(dn_layer* h) {
   if (!h->ext) {
     PrefillExt* e = new (std::nothrow) PrefillExt();
     if (!e) return nullptr;
-    if (const char* v = std::getenv("DN_PREFILL_OWN_GEMM")) e->own_gemm = std::atoi(v) != 0;
+    e->gemm = gemm_from_env();
     if (const char* v = std::getenv("DN_VERBOSE")) e->verbose = std::atoi(v) != 0;
     h->ext = e;
     h->ext_free = ext_free;
@@ -133,9 +151,9 @@ int pf_check(dn_layer* h, const float* x, int n_tokens, const float* alpha, cons
   return DN_OK;
 }
 
-// The prompt through every layer on the given scratch. lt: the library GEMM context, or nullptr
-// for the hand-written GEMM path.
-int pf_run(dn_layer* h, const PfBufs& pb, dn::LtCtx* lt, bool verbose, const float* x, int n_tokens,
+// The prompt through every layer on the given scratch. gemm: PF_GEMM_*; lt: the library GEMM
+// context, or nullptr (no library GEMM).
+int pf_run(dn_layer* h, const PfBufs& pb, int gemm, dn::LtCtx* lt, bool verbose, const float* x, int n_tokens,
            const float* alpha, const float* beta, float* out, hipStream_t st) {
   const dn_config& c = h->cfg;
   const size_t L = c.n_layers, D = c.d_model, T = n_tokens, B = c.batch;
@@ -143,14 +161,20 @@ int pf_run(dn_layer* h, const PfBufs& pb, dn::LtCtx* lt, bool verbose, const flo
   const int nch = (n_tokens + dn::PF_CT - 1) / dn::PF_CT;
   const int kr_in = pf_kr((int)D), kr_out = pf_kr(V);
   auto check = [&]() { return !h->sync_debug || hipStreamSynchronize(st) == hipSuccess; };
-  // 8-bit weights: the projections as library int8 GEMMs over the three terms of every token
-  // (3T columns), where the library has an algorithm for the shape; else the hand-written GEMM
-  const bool lt_in = lt && dn::lt_prepare(lt, 0, R, 3 * n_tokens, (int)D);
-  const bool lt_out = lt && dn::lt_prepare(lt, 1, (int)D, 3 * n_tokens, V);
+  // 8-bit weights: the projections as int8 GEMMs over the three terms of every token (the fused
+  // hand-written one or the library's), each where its shape constraints hold; else split-K
+  const bool w8 = c.weight_bits == 8;
+  const bool fu_in = w8 && gemm != PF_GEMM_LIBRARY && gemm != PF_GEMM_SPLITK && dn::pgemm_shape_ok(R, (int)D, n_tokens);
+  const bool fu_out = w8 && gemm != PF_GEMM_LIBRARY && gemm != PF_GEMM_SPLITK && dn::pgemm_shape_ok((int)D, V, n_tokens);
+  const bool lib_ok = w8 && lt && (gemm == PF_GEMM_AUTO || gemm == PF_GEMM_LIBRARY);
+  const bool lt_in = !fu_in && lib_ok && dn::lt_prepare(lt, 0, R, 3 * n_tokens, (int)D);
+  const bool lt_out = !fu_out && lib_ok && dn::lt_prepare(lt, 1, (int)D, 3 * n_tokens, V);
+  const bool tri_in = fu_in || lt_in, tri_out = fu_out || lt_out;  // [3][T][K] split, sums folded
   if (verbose)
     std::fprintf(stderr, "[dn] prefill of %d token(s): in_proj %s, out_proj %s\n", n_tokens,
-                 lt_in ? "library int8 GEMM" : "hand-written int8 GEMM",
-                 lt_out ? "library int8 GEMM after the fused norm-and-split" : "hand-written int8 GEMM");
+                 fu_in ? "fused int8 GEMM" : lt_in ? "library int8 GEMM" : "split-K int8 GEMM",
+                 fu_out ? "fused int8 GEMM after the fused norm-and-split"
+                 : lt_out ? "library int8 GEMM after the fused norm-and-split" : "split-K int8 GEMM");
   if (h->persist) {
     // the prompt updates the state and history in place: make the first of the whole-stack
     // kernel's two buffers the current one
@@ -171,11 +195,18 @@ int pf_run(dn_layer* h, const PfBufs& pb, dn::LtCtx* lt, bool verbose, const flo
     float* const ring_l = h->ring + l * h->ring_elems + sb * ring_seq;
     // in_proj: split the prompt's inputs, int8 GEMM over the tokens, conv along the tokens
     dn::PConvArgs pc{};
-    if (lt_in) {
+    if (tri_in) {
       dn::TSplitArgs sp{xl, (int)D, (int)D, n_tokens, tx, pb.sc, pb.ssq};
       if (dn::launch_tsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      if (dn::lt_gemm_i8(lt, 0, w.w_in, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      pc.terms = td; pc.s1 = pb.sc; pc.KS = 0; pc.NC = 1;
+      if (fu_in) {
+        const dn::PGemmArgs g{static_cast<const int8_t*>(w.w_in), tx, pb.sc, pb.part, R, (int)D, n_tokens};
+        if (dn::launch_pgemm(g, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+        pc.part = pb.part; pc.KS = 1;
+      } else {
+        if (dn::lt_gemm_i8(lt, 0, w.w_in, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+        pc.terms = td; pc.s1 = pb.sc; pc.KS = 0;
+      }
+      pc.NC = 1;
     } else {
       dn::BSplitArgs sp{xl, (int)D, (int)D, n_tokens, pb.xs, pb.sc, pb.ssq};
       if (dn::launch_bsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
@@ -210,19 +241,25 @@ int pf_run(dn_layer* h, const PfBufs& pb, dn::LtCtx* lt, bool verbose, const flo
     if (dn::launch_pscan(ps, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     // the gated RMSNorm: its own pass, or fused into the split for the library GEMM (the readout
     // rows and z are aligned, V, R and C being multiples of 128; V <= 64 heads x 128 = 8192 columns)
-    if (!lt_out) {
+    if (!tri_out) {
       dn::PNormArgs pn{pb.o, pb.u, w.norm_w, n_tokens, R, h->C, V, c.eps_rms};
       if (dn::launch_pnorm(pn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     }
     if (!check()) return fail(h, DN_E_DEVICE);
     // out_proj
     dn::BEpiArgs e{};
-    if (lt_out) {
+    if (tri_out) {
       dn::TSplitArgs so{pb.o, V, V, n_tokens, tx, pb.sc, pb.ssq};
       const dn::TSplitNormArgs sn{so, pb.u + h->C, R, w.norm_w, c.eps_rms};
       if (dn::launch_tsplit_norm(sn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      if (dn::lt_gemm_i8(lt, 1, w.w_out, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-      e.terms = td; e.s1 = pb.sc; e.KS = 0;
+      if (fu_out) {
+        const dn::PGemmArgs g{static_cast<const int8_t*>(w.w_out), tx, pb.sc, pb.part, (int)D, V, n_tokens};
+        if (dn::launch_pgemm(g, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+        e.part = pb.part; e.KS = 1;
+      } else {
+        if (dn::lt_gemm_i8(lt, 1, w.w_out, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+        e.terms = td; e.s1 = pb.sc; e.KS = 0;
+      }
     } else {
       dn::BSplitArgs so{pb.o, V, V, n_tokens, pb.xs, pb.sc, pb.ssq};
       if (dn::launch_bsplit(so, st) != hipSuccess) return fail(h, DN_E_DEVICE);
@@ -252,13 +289,13 @@ DN_API int dn_prefill(dn_layer* h, const float* x, int n_tokens, const float* al
     (void)hipGetLastError();  // the failed allocation's error; the handle stays usable
     return rc;
   }
-  if (h->cfg.weight_bits == 8 && !e->own_gemm && !e->lt_tried) {
+  if (h->cfg.weight_bits == 8 && (e->gemm == PF_GEMM_AUTO || e->gemm == PF_GEMM_LIBRARY) && !e->lt_tried) {
     e->lt_tried = true;
     e->lt = dn::lt_create();
   }
   PfBufs pb{};
   pf_layout(h, n_tokens, static_cast<char*>(e->buf), &pb);
-  return pf_run(h, pb, e->own_gemm ? nullptr : e->lt, e->verbose, x, n_tokens, alpha, beta, out,
+  return pf_run(h, pb, e->gemm, e->lt, e->verbose, x, n_tokens, alpha, beta, out,
                 reinterpret_cast<hipStream_t>(hip_stream));
 }
 
@@ -313,5 +350,7 @@ DN_API int dn_prefill_noalloc(dn_layer* h, const float* x, int n_tokens, const f
   PfBufs pb{};
   pf_layout(h, n_tokens, base, &pb);
   if (h->verbose) std::fprintf(stderr, "[dn] dn_prefill_noalloc: %zu bytes of the device's scratch array\n", need);
-  return pf_run(h, pb, nullptr, h->verbose, x, n_tokens, alpha, beta, out, reinterpret_cast<hipStream_t>(hip_stream));
+  // no library GEMM here: its path gives the fused GEMM's results bit for bit, so that one stands in
+  const int gemm = gemm_from_env() == PF_GEMM_LIBRARY ? PF_GEMM_FUSED : gemm_from_env();
+  return pf_run(h, pb, gemm, nullptr, h->verbose, x, n_tokens, alpha, beta, out, reinterpret_cast<hipStream_t>(hip_stream));
 }

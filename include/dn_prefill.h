@@ -36,6 +36,11 @@ extern "C" {
  * T = n_tokens, 1..DN_PREFILL_MAX_TOKENS per call; a longer prompt goes in several calls, each
  * continuing from the state the previous one left. The handle keeps scratch memory sized for the
  * longest prompt seen so far (allocated here, freed by dn_destroy).
+ * Projections with 8-bit weights: this library's int8 matrix-core GEMM over the three int8 terms of
+ * each input row, the terms folded in its epilogue; the environment variable DN_PREFILL_GEMM, read at
+ * a handle's first prefill, selects another path for comparison: "library" (the GPU BLAS library's
+ * int8 GEMM over the same terms, folded by the next kernel the same way: results equal the default's
+ * bit for bit) or "splitk" (split-K GEMM on fragment blocks, as for 4-bit weights).
  * hip_stream: a hipStream_t (NULL = the default stream). Enqueue only. Returns DN_OK,
  * DN_E_INVAL (shape or arguments not supported; the handle stays usable), DN_E_NOMEM,
  * DN_E_DISABLED or DN_E_DEVICE (latches the handle off, as a failed dn_step does). */
@@ -45,10 +50,9 @@ int dn_prefill(dn_layer *h, const float *x, int n_tokens, const float *alpha, co
 
 /* dn_prefill without any allocation, for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid it. Same arguments, layouts, state
- * handling and return codes as dn_prefill, and the same computation; the projections always run in
- * this library's own int8 GEMM kernels (no library GEMM, whose workspace and setup would allocate),
- * so results agree with dn_prefill to rounding and equal those of dn_prefill under
- * DN_PREFILL_OWN_GEMM=1 bit for bit.
+ * handling and return codes as dn_prefill, and the same computation in the same kernels (never the
+ * library GEMM, whose workspace and setup would allocate): results equal those of dn_prefill bit for
+ * bit.
  * Its scratch is one static device array of DN_PREFILL_NOALLOC_SCRATCH_BYTES per device the library
  * runs on, held until the process ends; the call calls no allocator (neither HIP's nor a library's).
  * A call whose scratch would exceed the array returns DN_E_INVAL without launching anything (and,

@@ -140,8 +140,8 @@ def _pf_gates(cfg, case):
 
 
 @pytest.mark.parametrize("case", PF_CASES)
-@pytest.mark.parametrize("env", [None, "DN_PREFILL_OWN_GEMM"])
-def test_prefill_edge_cases(case, env, monkeypatch):
+@pytest.mark.parametrize("gemm", [None, "library", "splitk"])
+def test_prefill_edge_cases(case, gemm, monkeypatch):
     """A 100-token prompt (two chunks, the second ragged), then two decode tokens."""
     cfg = gi.custom("pfedge_" + case, **PF_BASE)
     layers, stream = gi.generate(cfg)
@@ -151,14 +151,12 @@ def test_prefill_edge_cases(case, env, monkeypatch):
         x[:] = 0.0
     stream = gi.Stream(x, a, b)
     T = 98
-    print(f"[edges] prefill ({env or 'default GEMM'}) / {case}", flush=True)
+    print(f"[edges] prefill ({gemm or 'default'} GEMM) / {case}", flush=True)
     ref_all, ref_S, ref_H = orc.run(cfg, layers, stream)
     _, ref_S_pre, ref_H_pre = orc.run(cfg, layers, stream, n_tokens=T)
-    if env:
-        monkeypatch.setenv(env, "1")
+    if gemm:
+        monkeypatch.setenv("DN_PREFILL_GEMM", gemm)
     st = make_stack(cfg, layers)
-    if env:
-        monkeypatch.delenv(env)
     try:
         xp = torch.from_numpy(np.ascontiguousarray(x[:T, 0])).cuda()
         ap = torch.from_numpy(np.ascontiguousarray(a[:T, :, 0])).cuda()

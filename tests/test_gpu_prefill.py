@@ -98,8 +98,9 @@ def _check_prefill(cfg, T):
         assert e_dec <= OUT_TOL and es2 <= STATE_TOL
 
 
+FUSED_PATH = "in_proj fused int8 GEMM, out_proj fused int8 GEMM after the fused norm-and-split"
 LIB_PATH = "in_proj library int8 GEMM, out_proj library int8 GEMM after the fused norm-and-split"
-OWN_PATH = "in_proj hand-written int8 GEMM, out_proj hand-written int8 GEMM"
+SPLITK_PATH = "in_proj split-K int8 GEMM, out_proj split-K int8 GEMM"
 
 
 def _check_path(capfd, want):
@@ -113,8 +114,8 @@ def test_prefill_parity(name, capfd, monkeypatch):
     monkeypatch.setenv("DN_VERBOSE", "1")
     _check_prefill(cfg, T)
     if cfg.weight_bits == 8:
-        # 8-bit weights take the library GEMMs, with the gated RMSNorm fused into out_proj's split
-        _check_path(capfd, LIB_PATH)
+        # 8-bit weights take the fused int8 GEMMs, with the gated RMSNorm fused into out_proj's split
+        _check_path(capfd, FUSED_PATH)
 
 
 def test_prefill_full_layer(capfd, monkeypatch):
@@ -122,7 +123,7 @@ def test_prefill_full_layer(capfd, monkeypatch):
     base = gi.CONFIGS["layer"]
     monkeypatch.setenv("DN_VERBOSE", "1")
     _check_prefill(base.replace(name="pf_full", n_tokens=336), 320)
-    _check_path(capfd, LIB_PATH)
+    _check_path(capfd, FUSED_PATH)
 
 
 def test_prefill_full_stack_teacher_forced():
@@ -221,11 +222,54 @@ def test_prefill_arguments_are_checked():
 
 
 @pytest.mark.parametrize("name", ["stack3_prenorm", "ragged_chunks"])
-def test_prefill_hand_written_gemm(name, capfd, monkeypatch):
-    """8-bit weights with the hand-written split-K GEMM instead of the library GEMM (the path a
-    shape takes when the library has no algorithm for it)."""
-    monkeypatch.setenv("DN_PREFILL_OWN_GEMM", "1")
+def test_prefill_split_k_gemm(name, capfd, monkeypatch):
+    """8-bit weights with the hand-written split-K GEMM (the path of a shape that neither the fused
+    GEMM nor the library takes)."""
+    monkeypatch.setenv("DN_PREFILL_GEMM", "splitk")
     monkeypatch.setenv("DN_VERBOSE", "1")
     cfg, T = PF[name]
     _check_prefill(cfg, T)
-    _check_path(capfd, OWN_PATH)
+    _check_path(capfd, SPLITK_PATH)
+
+
+@pytest.mark.parametrize("name", ["stack3_prenorm", "ragged_chunks"])
+def test_prefill_library_gemm(name, capfd, monkeypatch):
+    """8-bit weights with the library's int8 GEMM over the three terms, folded by the next kernel."""
+    monkeypatch.setenv("DN_PREFILL_GEMM", "library")
+    monkeypatch.setenv("DN_VERBOSE", "1")
+    cfg, T = PF[name]
+    _check_prefill(cfg, T)
+    _check_path(capfd, LIB_PATH)
+
+
+def _prefill_outputs(cfg, T, gemm, monkeypatch):
+    layers, stream = gi.generate(cfg)
+    monkeypatch.setenv("DN_PREFILL_GEMM", gemm)
+    st = make_stack(cfg, layers)
+    try:
+        x, a, b = _prompt(stream, T)
+        out = torch.empty((cfg.n_layers, cfg.batch, T, cfg.d_model), device="cuda:0")
+        st.prefill(x, a, b, out)
+        torch.cuda.synchronize()
+        S, H = (v.cpu().numpy() for v in st.get_state())
+    finally:
+        st.close()
+    monkeypatch.delenv("DN_PREFILL_GEMM")
+    return out.cpu().numpy(), S, H
+
+
+@pytest.mark.parametrize("name", ["ragged_chunks", "stack3_prenorm", "layer_kernels_handle", "widest_values",
+                                  "batch3", "one_token"])
+def test_fused_gemm_equals_library_gemm(name, capfd, monkeypatch):
+    """The fused int8 GEMM and the library's sum the same int8 products exactly (int32) and fold the
+    three terms with the same double expression, so every output, state and history agree bit for
+    bit; ragged token counts, a 768-row out_proj and the 8192-column readout included."""
+    cfg, T = PF[name]
+    monkeypatch.setenv("DN_VERBOSE", "1")
+    fo, fS, fH = _prefill_outputs(cfg, T, "fused", monkeypatch)
+    _check_path(capfd, FUSED_PATH)
+    lo, lS, lH = _prefill_outputs(cfg, T, "library", monkeypatch)
+    _check_path(capfd, LIB_PATH)
+    print(f"[prefill] {name}: fused vs library GEMM, max |diff| out {np.abs(fo - lo).max():.3e} "
+          f"state {np.abs(fS - lS).max():.3e}", flush=True)
+    assert np.array_equal(fo, lo) and np.array_equal(fS, lS) and np.array_equal(fH, lH)

@@ -1,9 +1,9 @@
 """dn_prefill_noalloc (include/dn_prefill.h), the prompt call that allocates nothing, through the C
 ABI on the card: two calls in a row, the second with fewer tokens, each compared with the existing
 entry point dn_prefill on a twin handle (same weights, same starting state): bit for bit against
-dn_prefill on this library's own GEMM kernels, and within the decode step's bars (output 2e-3 of
-each token's rms, state 1e-3 relative Frobenius) against dn_prefill on the library GEMMs. A call
-whose scratch would not fit the static array is refused before anything runs."""
+dn_prefill on its default kernels, and within the decode step's bars (output 2e-3 of each token's
+rms, state 1e-3 relative Frobenius) against dn_prefill on the library GEMMs. A call whose scratch
+would not fit the static array is refused before anything runs."""
 import numpy as np
 import pytest
 import torch
@@ -53,10 +53,10 @@ def test_noalloc_prefill_matches_dn_prefill(name, monkeypatch):
     layers, stream = gi.generate(cfg)
     print(f"[noalloc] {name}: calls of {sizes} tokens", flush=True)
     got = _run(cfg, layers, stream, sizes, dn.dn_prefill_noalloc)
-    lib_gemm = _run(cfg, layers, stream, sizes, dn.dn_prefill)
-    monkeypatch.setenv("DN_PREFILL_OWN_GEMM", "1")
     own_gemm = _run(cfg, layers, stream, sizes, dn.dn_prefill)
-    monkeypatch.delenv("DN_PREFILL_OWN_GEMM")
+    monkeypatch.setenv("DN_PREFILL_GEMM", "library")
+    lib_gemm = _run(cfg, layers, stream, sizes, dn.dn_prefill)
+    monkeypatch.delenv("DN_PREFILL_GEMM")
     for i, T in enumerate(sizes):
         g, r, o = got[0][i], lib_gemm[0][i], own_gemm[0][i]
         assert np.array_equal(g, o), f"call {i}: output differs from dn_prefill on the same kernels"
@@ -65,7 +65,7 @@ def test_noalloc_prefill_matches_dn_prefill(name, monkeypatch):
         es = state_err(got[1][i][0], lib_gemm[1][i][0].astype(np.float64))
         eh = state_err(got[1][i][1], lib_gemm[1][i][1].astype(np.float64))
         print(f"[noalloc] {name} call {i} ({T} tokens): against dn_prefill with the library GEMMs: out {e:.2e} "
-              f"state {es:.2e} ring {eh:.2e}; bit for bit against its own-GEMM path", flush=True)
+              f"state {es:.2e} ring {eh:.2e}; bit for bit against dn_prefill", flush=True)
         assert e <= OUT_TOL and es <= STATE_TOL and eh <= STATE_TOL
 
 
