@@ -36,6 +36,20 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int DK = 128, DV = 128, CT = PF_CT;
 constexpr int OFF_W = 0, OFF_UV = CT * DK, OFF_QG = 2 * CT * DK, OFF_KT = 3 * CT * DK, OFF_P = 4 * CT * DK,
               OFF_G = 4 * CT * DK + CT * CT;
+// The chunk terms are stored in the order k_pscan's lanes read them (every load instruction of the
+// scan then reads 1 KB in one piece): 16-byte units, unit u holding four consecutive values.
+//   W, Qg [64][128]: element (row, col) in unit ((row/16) 8 + (col%32)/4) 64 + row%16 + 16 (col/32)
+//   P [64][64]:      element (row, col) in unit ((row/16) 4 + (col%16)/4) 64 + row%16 + 16 (col/16)
+//   Kt (k weighted by the decay to the chunk's end, token tok, key column i): unit
+//                    ((i/32) 2 + (i/16)%2) 4 + (tok%16)/4) 64 + i%16 + 16 (tok/16), value tok % 4
+//   Uv [64][128]:    element (row, col) in unit ((col/16) 4 + row/16) 64 + col%16 + 16 ((row%16)/4),
+//                    value row % 4
+__device__ __forceinline__ int pf_wq_at(int row, int col) {
+  return 4 * ((((row >> 4) * 8 + ((col & 31) >> 2)) * 64) + (row & 15) + 16 * (col >> 5)) + (col & 3);
+}
+__device__ __forceinline__ int pf_p_at(int row, int col) {
+  return 4 * ((((row >> 4) * 4 + ((col & 15) >> 2)) * 64) + (row & 15) + 16 * (col >> 4)) + (col & 3);
+}
 constexpr int TR = 32;  // tokens per thread in k_pconv
 constexpr int LD = DK + 4;  // padded LDS row of 128 floats (keeps 16-byte alignment)
 
@@ -290,14 +304,26 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
   }
   __syncthreads();
 
-  // decayed q rows, k rows weighted by the decay to the chunk's end, the chunk's total decay
+  // decayed q rows, k rows weighted by the decay to the chunk's end (stored transposed, [dk][token],
+  // the layout k_pscan reads), the chunk's total decay
   {
     const double lgl = slg[nj - 1];
-    for (int e = tid; e < CT * (DK / 4); e += 256) {
-      const int j = e / (DK / 4), i4 = (e % (DK / 4)) * 4;
-      const v4f q = *reinterpret_cast<const v4f*>(&sQ[j][i4]), k = *reinterpret_cast<const v4f*>(&sK[j][i4]);
-      *reinterpret_cast<v4f*>(out + OFF_QG + j * DK + i4) = q * expf((float)slg[j]);
-      *reinterpret_cast<v4f*>(out + OFF_KT + j * DK + i4) = j < nj ? k * expf((float)(lgl - slg[j])) : v4f{0.f, 0.f, 0.f, 0.f};
+    // one 16-byte unit per thread and step, consecutive threads on consecutive units
+    for (int u = tid; u < CT * DK / 4; u += 256) {
+      const int ul = u & 63, j = 16 * (u >> 9) + (ul & 15), i4 = 32 * (ul >> 4) + 4 * ((u >> 6) & 7);
+      const v4f q = *reinterpret_cast<const v4f*>(&sQ[j][i4]);
+      *reinterpret_cast<v4f*>(out + OFF_QG + 4 * u) = q * expf((float)slg[j]);
+    }
+    for (int u = tid; u < CT * DK / 4; u += 256) {
+      const int ul = u & 63, i = 32 * (u >> 9) + 16 * ((u >> 8) & 1) + (ul & 15);
+      const int tok0 = 16 * (ul >> 4) + 4 * ((u >> 6) & 3);
+      v4f kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tk = tok0 + e;
+        kv[e] = tk < nj ? sK[tk][i] * expf((float)(lgl - slg[tk])) : 0.f;
+      }
+      *reinterpret_cast<v4f*>(out + OFF_KT + 4 * u) = kv;
     }
     if (tid == 0) out[OFF_G] = expf((float)lgl);
   }
@@ -345,7 +371,7 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = 16 * rt + 4 * lk + v, m = 16 * ct + li;
-        out[OFF_P + j * CT + m] = m <= j ? expf((float)(slg[j] - slg[m])) * qt[v] : 0.f;
+        out[OFF_P + pf_p_at(j, m)] = m <= j ? expf((float)(slg[j] - slg[m])) * qt[v] : 0.f;
       }
     }
   }
@@ -370,23 +396,34 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
         uacc = __builtin_amdgcn_mfma_f32_16x16x4f32(au[st], sV[m][16 * ct + li], uacc, 0, 0, 0);
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = 16 * wave + 4 * lk + v;
-        out[OFF_W + j * DK + 16 * ct + li] = wacc[v];
-        out[OFF_UV + j * DV + 16 * ct + li] = uacc[v];
-      }
+      for (int v = 0; v < 4; ++v) out[OFF_W + pf_wq_at(16 * wave + 4 * lk + v, 16 * ct + li)] = wacc[v];
+      // rows 16 wave + 4 lk + v, column 16 ct + li: one whole unit of the Uv order per lane
+      *reinterpret_cast<v4f*>(out + OFF_UV + 4 * ((ct * 4 + wave) * 64 + lane)) = uacc;
     }
   }
 }
 
 // One workgroup per (value head, block of 16 value columns): the state block is carried through
-// the chunks in order; each chunk gives D = Uv - W S, the readout Qg S + P D and the next state
-// g_last S + Kt^T D. The products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane l
+// the chunks in order; each chunk gives D = Uv - W S, the next state g_last S + Kt^T D and the
+// readout Qg S + P D. The products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32: lane l
 // holds A[l%16][k] and B[k][l%16] with k = l/16, and D[4(l/16)+v][l%16]). The sum index is
 // permuted so that every lane reads contiguous runs: at step s, lane group k = l/16 covers column
 // 32k + s of a 128-long sum and 16k + s of a 64-long one, on both operands. Wave w owns rows
 // 16w..16w+15 of D and of the readout, and rows 32w..32w+31 of the next state; the state block
 // also sits in every wave's registers as the B operand, refreshed through LDS after each chunk.
+// The chain from one state to the next is D, then the next state; the next chunk's chain operands
+// are loaded while a chunk computes, and the readout's products go after the state's (their
+// operands requested at the chunk's start), filling the matrix pipe while the new state block
+// passes through LDS.
+struct PScanOps {  // a chunk's operands on the chain from one state to the next
+  float aW[32], aK[2][16];  // rows 16w + li of W; columns 32w + 16tau + li of Kt^T
+  float uv[4];              // Uv rows 16w + 4lk + v, column 16b + li
+  float gl;                 // the chunk's total decay
+};
+struct PScanRead {  // a chunk's readout operands
+  float aQ[32], aP[16];  // rows 16w + li of Qg, P
+};
+
 __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
   __shared__ __attribute__((aligned(16))) float sS[DK][16], sD[CT][16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = blockIdx.x, b = blockIdx.y;
@@ -401,73 +438,90 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
       sS[i][cc] = Sh[(size_t)i * DV + 16 * b + cc];
     }
   }
+  // loads only (no arithmetic on the loaded values, which would wait for them at once)
+  auto load_ops = [&](int c, PScanOps& o) {
+    const float* cw = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
+    const float* wr = cw + OFF_W + 4 * (w * 8 * 64 + lane);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const v4f x = *reinterpret_cast<const v4f*>(wr + 256 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.aW[4 * q + e] = x[e];
+    }
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const float* kr = cw + OFF_KT + 4 * ((w * 2 + tau) * 4 * 64 + lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f x = *reinterpret_cast<const v4f*>(kr + 256 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.aK[tau][4 * q + e] = x[e];
+      }
+    }
+    const v4f x = *reinterpret_cast<const v4f*>(cw + OFF_UV + 4 * ((b * 4 + w) * 64 + lane));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o.uv[v] = x[v];
+    o.gl = cw[OFF_G];
+  };
+  auto load_read = [&](int c, PScanRead& o) {
+    const float* cw = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
+    const float* qr = cw + OFF_QG + 4 * (w * 8 * 64 + lane);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const v4f y = *reinterpret_cast<const v4f*>(qr + 256 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.aQ[4 * q + e] = y[e];
+    }
+    const float* pr = cw + OFF_P + 4 * (w * 4 * 64 + lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f x = *reinterpret_cast<const v4f*>(pr + 256 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.aP[4 * q + e] = x[e];
+    }
+  };
   __syncthreads();
   float bS[32];
 #pragma unroll
   for (int st = 0; st < 32; ++st) bS[st] = sS[32 * lk + st][li];
-  for (int c = 0; c < a.NCH; ++c) {
-    const float* cw = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
+  // one chunk; `last`: the prompt's last chunk, which may be ragged (the others are whole, so their
+  // loads and stores are unconditional and the waits for them exact)
+  auto chunk = [&](int c, const PScanOps& o, PScanOps& nx, bool last) {
+    // the readout operands of this chunk (needed after the chain's products) and the chain operands
+    // of the next chunk (needed a whole chunk later) are requested first
+    PScanRead rd;
+    load_read(c, rd);
+    load_ops(min(c + 1, a.NCH - 1), nx);
     const int t0 = c * CT, nj = min(CT, a.T - t0);
-    // A operands of this wave: rows 16w + li of W, Qg, P; columns 32w + 16tau + li of Kt^T
-    float aW[32], aQ[32], aP[16], aK[2][16];
-    {
-      const float* wr = cw + OFF_W + (16 * w + li) * DK + 32 * lk;
-      const float* qr = cw + OFF_QG + (16 * w + li) * DK + 32 * lk;
+    // D = Uv - W S for rows 16w..
+    v4f dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const v4f x = *reinterpret_cast<const v4f*>(wr + 4 * q), y = *reinterpret_cast<const v4f*>(qr + 4 * q);
+    for (int st = 0; st < 32; ++st) dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.aW[st], bS[st], dacc, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          aW[4 * q + e] = -x[e];
-          aQ[4 * q + e] = y[e];
-        }
-      }
-      const float* pr = cw + OFF_P + (16 * w + li) * CT + 16 * lk;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v4f x = *reinterpret_cast<const v4f*>(pr + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) aP[4 * q + e] = x[e];
-      }
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int st = 0; st < 16; ++st) aK[tau][st] = cw[OFF_KT + (16 * lk + st) * DK + 32 * w + 16 * tau + li];
-    }
-    const float gl = cw[OFF_G];
-    // D = Uv - W S for rows 16w.., started from Uv
-    v4f dacc;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) dacc[v] = cw[OFF_UV + (16 * w + 4 * lk + v) * DV + 16 * b + li];
-#pragma unroll
-    for (int st = 0; st < 32; ++st) dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aW[st], bS[st], dacc, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sD[16 * w + 4 * lk + v][li] = dacc[v];
+    for (int v = 0; v < 4; ++v) sD[16 * w + 4 * lk + v][li] = o.uv[v] - dacc[v];
     lds_barrier();
     float bD[16];
 #pragma unroll
     for (int st = 0; st < 16; ++st) bD[st] = sD[16 * lk + st][li];
-    // readout Qg S + P D
-    v4f oacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < 32; ++st) oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aQ[st], bS[st], oacc, 0, 0, 0);
-#pragma unroll
-    for (int st = 0; st < 16; ++st) oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aP[st], bD[st], oacc, 0, 0, 0);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = 16 * w + 4 * lk + v;
-      if (j < nj) a.o[(size_t)(t0 + j) * a.V + h * DV + 16 * b + li] = oacc[v];
-    }
-    // next state, rows 32w + 16tau + 4lk + v
+    // next state, rows 32w + 16tau + 4lk + v: on the chain, so first
     v4f sacc[2];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
+    for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sacc[tau][v] = gl * sS[32 * w + 16 * tau + 4 * lk + v][li];
+      for (int v = 0; v < 4; ++v) sacc[tau][v] = o.gl * sS[32 * w + 16 * tau + 4 * lk + v][li];
 #pragma unroll
-      for (int st = 0; st < 16; ++st)
-        sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(aK[tau][st], bD[st], sacc[tau], 0, 0, 0);
-    }
+    for (int st = 0; st < 16; ++st)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+        sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.aK[tau][st], bD[st], sacc[tau], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // readout Qg S + P D: off the chain
+    v4f oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 32; ++st) oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(rd.aQ[st], bS[st], oacc, 0, 0, 0);
+#pragma unroll
+    for (int st = 0; st < 16; ++st) oacc = __builtin_amdgcn_mfma_f32_16x16x4f32(rd.aP[st], bD[st], oacc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // every read of the old state block and of D is done
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
@@ -476,6 +530,24 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
     lds_barrier();
 #pragma unroll
     for (int st = 0; st < 32; ++st) bS[st] = sS[32 * lk + st][li];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * w + 4 * lk + v;
+      if (!last || j < nj) a.o[(size_t)(t0 + j) * a.V + h * DV + 16 * b + li] = oacc[v];
+    }
+  };
+  PScanOps o0, o1;
+  load_ops(0, o0);
+  int c = 0;
+  for (; c + 2 < a.NCH; c += 2) {
+    chunk(c, o0, o1, false);
+    chunk(c + 1, o1, o0, false);
+  }
+  if (c + 1 < a.NCH) {
+    chunk(c, o0, o1, false);
+    chunk(c + 1, o1, o0, true);
+  } else {
+    chunk(c, o0, o1, true);
   }
   for (int e = tid; e < DK * 16; e += 256) {
     if (a.transposed) {
