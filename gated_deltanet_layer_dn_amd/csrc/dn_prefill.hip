@@ -234,12 +234,14 @@ __global__ __launch_bounds__(256) void k_pconv4(const PConvArgs a) {
 }
 
 // One workgroup per (value head, chunk): the chunk terms that do not depend on the incoming state.
-// The 64 x 64 and 64 x 128 products run on the fp32 matrix cores (lane layout and permuted sum
-// index as in k_pscan); the unit lower-triangular solve runs in the first wave (lane = column)
-// while the other three form the masked q.k products.
+// The 64 x 64 and 64 x 128 products run on the fp32 matrix cores (lane layout as in k_pscan); the
+// unit lower-triangular inverse goes in 16 x 16 blocks: the four diagonal blocks by substitution in
+// the first wave (lane = column) while the other three form the masked q.k products, then the
+// blocks below the diagonal by matrix-core products.
 __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
   __shared__ __attribute__((aligned(16))) float sQ[CT][LD], sK[CT][LD], sV[CT][LD];
-  __shared__ float sA[CT][CT + 1];  // A, then Tm = (I + A)^-1 in place
+  __shared__ float sA[CT][CT + 1];  // A
+  __shared__ float sT[CT][CT + 1];  // Tm = (I + A)^-1 (lower triangular)
   __shared__ double slg[CT];
   __shared__ float sb[CT], sbg[CT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -348,20 +350,25 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
   }
   __syncthreads();
 
+  // Tm = (I + A)^-1 in 16 x 16 blocks: the diagonal blocks by forward substitution (wave 0, lane l
+  // column l % 16 of block l / 16) while the other waves form P; then the blocks below the diagonal,
+  // one diagonal of blocks after the other, on the matrix cores:
+  //   T_ij = -T_ii sum_{j <= k < i} A_ik T_kj
   if (wave == 0) {
-    // Tm = (I + A)^-1 by forward substitution; lane `col` solves column col, then Tm overwrites A
-    const int col = lane;
-    float tc[CT];
+    const int r0 = 16 * (lane >> 4), c = lane & 15;
+    float tc[16];
 #pragma unroll
-    for (int j = 0; j < CT; ++j) {
-      // four interleaved partial sums, so each row's dependent chain is a quarter as long
-      float v[4] = {j == col ? 1.0f : 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < 16; ++r) {
+      float v0 = r == c ? 1.0f : 0.0f, v1 = 0.0f;  // two interleaved partial sums
 #pragma unroll
-      for (int m = 0; m < j; ++m) v[m & 3] = fmaf(-sA[j][m], tc[m], v[m & 3]);
-      tc[j] = (v[0] + v[1]) + (v[2] + v[3]);
+      for (int m = 0; m < r; ++m) {
+        if (m & 1) v1 = fmaf(-sA[r0 + r][r0 + m], tc[m], v1);
+        else v0 = fmaf(-sA[r0 + r][r0 + m], tc[m], v0);
+      }
+      tc[r] = v0 + v1;
     }
 #pragma unroll
-    for (int j = 0; j < CT; ++j) sA[j][col] = tc[j];
+    for (int r = 0; r < 16; ++r) sT[r0 + r][r0 + c] = tc[r];
   } else {
     // P = lower part (with the diagonal) of (g_j/g_m) Q K^T; the 10 tiles with ct <= rt over the
     // three other waves, zeros above
@@ -376,29 +383,55 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
     }
   }
   __syncthreads();
-
-  // W = Tm diag(beta g) K and Uv = Tm diag(beta) V: wave w forms rows 16w..16w+15, all columns
-  {
-    float aw[16], au[16];
+  // 16 x 16 products with the sum index 4 s + k at step s (lane group k = l / 16)
+  for (int L = 1; L < 4; ++L) {
+    if (wave < 4 - L) {
+      const int i = wave + L, j = wave;
+      v4f x = {0.f, 0.f, 0.f, 0.f};
+      for (int k = j; k < i; ++k)
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {
-      const int m = 16 * lk + st;
-      const float tm = sA[16 * wave + li][m];
+        for (int st = 0; st < 4; ++st)
+          x = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * i + li][16 * k + 4 * st + lk],
+                                                   sT[16 * k + 4 * st + lk][16 * j + li], x, 0, 0, 0);
+      // T_ii x: x's rows 4 k + v sit in this lane's x[v], so the sum index here is 4 k + s
+      v4f y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[16 * i + li][16 * i + 4 * lk + st], x[st], y, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sT[16 * i + 4 * lk + v][16 * j + li] = -y[v];
+    }
+    __syncthreads();
+  }
+
+  // W = Tm diag(beta g) K and Uv = Tm diag(beta) V. Tm is lower triangular: row tile rt sums over
+  // the first 16 (rt + 1) rows of K and V only. Wave w forms column tiles 2w and 2w + 1 of every
+  // row tile (the same number of products on every wave).
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    constexpr int NS = 16;
+    float aw[NS], au[NS];
+#pragma unroll
+    for (int st = 0; st < 4 * (rt + 1); ++st) {
+      const int m = 4 * st + lk;
+      const float tm = sT[16 * rt + li][m];
       aw[st] = tm * sbg[m];
       au[st] = tm * sb[m];
     }
-    for (int ct = 0; ct < 8; ++ct) {
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+      const int ct = 2 * wave + cl;
       v4f wacc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        const int m = 16 * lk + st;
+      for (int st = 0; st < 4 * (rt + 1); ++st) {
+        const int m = 4 * st + lk;
         wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[st], sK[m][16 * ct + li], wacc, 0, 0, 0);
         uacc = __builtin_amdgcn_mfma_f32_16x16x4f32(au[st], sV[m][16 * ct + li], uacc, 0, 0, 0);
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) out[OFF_W + pf_wq_at(16 * wave + 4 * lk + v, 16 * ct + li)] = wacc[v];
-      // rows 16 wave + 4 lk + v, column 16 ct + li: one whole unit of the Uv order per lane
-      *reinterpret_cast<v4f*>(out + OFF_UV + 4 * ((ct * 4 + wave) * 64 + lane)) = uacc;
+      for (int v = 0; v < 4; ++v) out[OFF_W + pf_wq_at(16 * rt + 4 * lk + v, 16 * ct + li)] = wacc[v];
+      // rows 16 rt + 4 lk + v, column 16 ct + li: one whole unit of the Uv order per lane
+      *reinterpret_cast<v4f*>(out + OFF_UV + 4 * ((ct * 4 + rt) * 64 + lane)) = uacc;
     }
   }
 }
