@@ -219,9 +219,28 @@ struct PGemmArgs {
   const float* s1;  // [T]
   float* out;       // [T][M]
   int M, K, T;
+  // in_proj epilogue when conv != 0 (what k_pconv does after the library GEMM): pre-conv values
+  // s[m] f(t) sum (f the pre-norm factor 1/sqrt(ssq[t] / K + eps) if prenorm, else 1), then for rows
+  // m < C the causal conv over the previous Kc - 1 tokens and SiLU, into out, for every token whose
+  // history lies in its 64-token tile (local index >= 3); rows m >= C get the pre-conv value. The
+  // pre-conv values of each tile's first and last three tokens and of the prompt's last three go to
+  // edge ([T][M], other tokens' rows untouched) for k_pconv_edge, which finishes the first three.
+  int conv;
+  const float* s;       // [M] row scales; without conv, when set: out[t][m] = s[m] * the fold (the
+                        // out_proj rows finished, as k_bepi finishes them)
+  const float* ssq;     // [T] sums of squares of the layer input (one chunk: k_tsplit's)
+  int prenorm;
+  float eps;
+  const float* conv_w;  // [C][Kc]
+  int C, Kc;
+  float* edge;          // [T][M]
 };
 bool pgemm_shape_ok(int M, int K, int T);
 hipError_t launch_pgemm(const PGemmArgs& a, hipStream_t st);
+// After k_pgemm's conv epilogue: the first three tokens of every 64-token tile (rows < C) from the
+// edge values and, before the prompt, the history; and the new history (the last Kc - 1 pre-conv
+// values). part = the edge buffer, out = k_pgemm's out; s, terms, ssq unused.
+hipError_t launch_pconv_edge(const PConvArgs& a, hipStream_t st);
 
 // ---- whole-stack kernel (single sequence, 128 x 128 state tiles) ----
 struct LayerW {

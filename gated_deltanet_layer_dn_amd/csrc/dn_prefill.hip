@@ -53,7 +53,8 @@ __device__ __forceinline__ int pf_p_at(int row, int col) {
 constexpr int TR = 32;  // tokens per thread in k_pconv
 constexpr int LD = DK + 4;  // padded LDS row of 128 floats (keeps 16-byte alignment)
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+// SiLU with the hardware reciprocal (within an ulp of the quotient)
+__device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 // Workgroup barrier that waits only for this wave's LDS accesses. A __syncthreads() also waits for
 // every outstanding global access, here the readout's stores of the chunk; the scan's barriers
@@ -635,6 +636,9 @@ __device__ __forceinline__ void pg_barrier() {
   asm volatile("" ::: "memory");
 }
 
+constexpr int PG_PLD = PG_ROWS + 4;  // padded row of the conv epilogue's staging ([64 tokens][256 rows])
+
+template <bool CONV>
 __global__ __launch_bounds__(512) void k_pgemm(const PGemmArgs a) {
   __shared__ pg_v4i sq[2][PG_STAGE / 16];
   // wave index uniform (scalar): which tile each of its loads fills derives from it
@@ -714,30 +718,125 @@ __global__ __launch_bounds__(512) void k_pgemm(const PGemmArgs a) {
   // epilogue: lane holds token t0 + 32 th + 16 tt + lane % 16, rows 16 r + 4 (lane / 16) + v of the
   // wave's four row tiles; the three terms folded in double with the token's scale (as k_pconv
   // folds the library GEMM's sums), four consecutive rows per 16-byte store
+  if constexpr (!CONV) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = t0 + 32 * th + 16 * tt + (lane & 15);
-    const double s1 = (double)a.s1[min(t, a.T - 1)];
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = t0 + 32 * th + 16 * tt + (lane & 15);
+      const double s1 = (double)a.s1[min(t, a.T - 1)];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = row0 + 64 * rg + 16 * r + 4 * (lane >> 4);
-      v4f o;
+      for (int r = 0; r < 4; ++r) {
+        const int m = row0 + 64 * rg + 16 * r + 4 * (lane >> 4);
+        v4f o;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        o[v] = (float)(s1 * ((double)acc[r][tt][0][v] +
-                             ((double)acc[r][tt][1][v] + (double)acc[r][tt][2][v] * (1.0 / 254.0)) * (1.0 / 254.0)));
-      if (t < a.T) {
-        if (m + 3 < a.M) {
-          *reinterpret_cast<v4f*>(a.out + (size_t)t * a.M + m) = o;
-        } else {
+        for (int v = 0; v < 4; ++v) {
+          o[v] = (float)(s1 * ((double)acc[r][tt][0][v] +
+                               ((double)acc[r][tt][1][v] + (double)acc[r][tt][2][v] * (1.0 / 254.0)) * (1.0 / 254.0)));
+          if (a.s) o[v] = a.s[min(m + v, a.M - 1)] * o[v];  // out_proj: the row scale (k_bepi's last step)
+        }
+        if (t < a.T) {
+          if (m + 3 < a.M) {
+            *reinterpret_cast<v4f*>(a.out + (size_t)t * a.M + m) = o;
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (m + v < a.M) a.out[(size_t)t * a.M + m + v] = o[v];
+            for (int v = 0; v < 4; ++v)
+              if (m + v < a.M) a.out[(size_t)t * a.M + m + v] = o[v];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one tile's doubles live at a time
+      }
+    }
+  } else {
+    // in_proj: pre-conv values (the fold times the row scale and the token's pre-norm factor, as
+    // k_pconv computes them) staged in LDS as [64 tokens][256 rows] over the stage buffers, which every
+    // wave is done with; the edge tokens' values also to global memory
+    float(*sP)[PG_PLD] = reinterpret_cast<float(*)[PG_PLD]>(&sq[0][0]);
+    pg_barrier();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tl = 32 * th + 16 * tt + (lane & 15), t = t0 + tl, tc = min(t, a.T - 1);
+      const double s1 = (double)a.s1[tc];
+      const float f = a.prenorm ? rsqrtf(a.ssq[tc] / (float)a.K + a.eps) : 1.0f;
+      const bool edge_t = t < a.T && (tl < 3 || tl >= PG_TOK - 3 || t >= a.T - 3);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = 64 * rg + 16 * r + 4 * (lane >> 4), m = row0 + rl;
+        v4f o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float fold = (float)(s1 * ((double)acc[r][tt][0][v] +
+                                           ((double)acc[r][tt][1][v] + (double)acc[r][tt][2][v] * (1.0 / 254.0)) *
+                                               (1.0 / 254.0)));
+          o[v] = a.s[min(m + v, a.M - 1)] * f * fold;
+        }
+        *reinterpret_cast<v4f*>(&sP[tl][rl]) = o;
+        if (edge_t && m < a.M) *reinterpret_cast<v4f*>(a.edge + (size_t)t * a.M + m) = o;  // M % 4 == 0
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    pg_barrier();
+    // thread: row rl, tokens 32 h2 .. +31 of the tile; rows < C: conv over the previous Kc - 1
+    // tokens and SiLU, in k_pconv's order of operations, for tokens whose history is in the tile
+    const int rl = threadIdx.x & (PG_ROWS - 1), j0 = 32 * (threadIdx.x / PG_ROWS), m = row0 + rl;
+    if (m < a.M) {
+      if (m >= a.C) {
+        for (int i = 0; i < 32; ++i)
+          if (t0 + j0 + i < a.T) a.out[(size_t)(t0 + j0 + i) * a.M + m] = sP[j0 + i][rl];
+      } else {
+        const int Kc = a.Kc;
+        float w[4], hist[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = q < Kc ? a.conv_w[(size_t)m * Kc + q] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          if (q < Kc - 1 && j0 - (Kc - 1) + q >= 0) hist[q] = sP[j0 - (Kc - 1) + q][rl];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int j = j0 + i;
+          const float u = sP[j][rl];
+          float accv = w[Kc - 1] * u;
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            if (q < Kc - 1) accv = fmaf(w[q], hist[q], accv);
+          if (j >= 3 && t0 + j < a.T) a.out[(size_t)(t0 + j) * a.M + m] = silu(accv);
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            if (q + 1 < Kc - 1) hist[q] = hist[q + 1];
+          if (Kc > 1) hist[Kc - 2] = u;
         }
       }
-      __builtin_amdgcn_sched_barrier(0);  // one tile's doubles live at a time
     }
   }
+}
+
+// The first three tokens of each 64-token tile after k_pgemm's conv epilogue (rows < C): the conv
+// over the edge buffer's pre-conv values (tokens before the prompt from the history) and SiLU, in
+// k_pconv's order of operations; the last tile's workgroups also leave the new history.
+__global__ __launch_bounds__(256) void k_pconv_edge(const PConvArgs a) {
+  const int r = blockIdx.x * 256 + threadIdx.x, t0 = PG_TOK * blockIdx.y;
+  if (r >= a.C) return;
+  const int Kc = a.Kc;
+  float w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = q < Kc ? a.conv_w[(size_t)r * Kc + q] : 0.f;
+  auto pre = [&](int tok) {
+    return tok >= 0 ? a.part[(size_t)tok * a.M + r] : a.ring_in[(size_t)(tok + Kc - 1) * a.C + r];
+  };
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int t = t0 + i;
+    if (t < a.T) {
+      float acc = w[Kc - 1] * a.part[(size_t)t * a.M + r];
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (q < Kc - 1) acc = fmaf(w[q], pre(t - (Kc - 1) + q), acc);
+      a.out[(size_t)t * a.M + r] = silu(acc);
+    }
+  }
+  if (blockIdx.y == gridDim.y - 1)
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (q < Kc - 1) a.ring_out[(size_t)q * a.C + r] = pre(a.T - (Kc - 1) + q);
 }
 }  // namespace
 
@@ -774,7 +873,18 @@ bool pgemm_shape_ok(int M, int K, int T) {
 
 hipError_t launch_pgemm(const PGemmArgs& a, hipStream_t st) {
   if (!pgemm_shape_ok(a.M, a.K, a.T) || reinterpret_cast<uintptr_t>(a.out) % 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_pgemm, dim3((a.M + PG_ROWS - 1) / PG_ROWS, (a.T + PG_TOK - 1) / PG_TOK), dim3(64 * PG_WAVES), 0, st, a);
+  const dim3 grid((a.M + PG_ROWS - 1) / PG_ROWS, (a.T + PG_TOK - 1) / PG_TOK);
+  if (a.conv) {
+    if (a.Kc < 1 || a.Kc > 4 || a.C > a.M || reinterpret_cast<uintptr_t>(a.edge) % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_pgemm<true>, grid, dim3(64 * PG_WAVES), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_pgemm<false>, grid, dim3(64 * PG_WAVES), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pconv_edge(const PConvArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_pconv_edge, dim3((a.C + 255) / 256, (a.T + PG_TOK - 1) / PG_TOK), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

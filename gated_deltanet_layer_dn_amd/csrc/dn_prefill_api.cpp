@@ -193,13 +193,17 @@ int pf_run(dn_layer* h, const PfBufs& pb, int gemm, dn::LtCtx* lt, bool verbose,
     const dn_weights& w = h->w[l];
     const float* xl = l == 0 ? x + sb * T * D : out + ((l - 1) * B + sb) * T * D;
     float* const ring_l = h->ring + l * h->ring_elems + sb * ring_seq;
-    // in_proj: split the prompt's inputs, int8 GEMM over the tokens, conv along the tokens
+    // in_proj: split the prompt's inputs, int8 GEMM over the tokens, conv along the tokens (the
+    // fused GEMM's epilogue does the conv within each 64-token tile, k_pconv_edge the tiles' first
+    // three tokens; else k_pconv after the GEMM)
     dn::PConvArgs pc{};
     if (tri_in) {
       dn::TSplitArgs sp{xl, (int)D, (int)D, n_tokens, tx, pb.sc, pb.ssq};
       if (dn::launch_tsplit(sp, st) != hipSuccess) return fail(h, DN_E_DEVICE);
       if (fu_in) {
-        const dn::PGemmArgs g{static_cast<const int8_t*>(w.w_in), tx, pb.sc, pb.part, R, (int)D, n_tokens};
+        dn::PGemmArgs g{static_cast<const int8_t*>(w.w_in), tx, pb.sc, pb.u, R, (int)D, n_tokens};
+        g.conv = 1; g.s = w.s_in; g.ssq = pb.ssq; g.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; g.eps = c.eps_rms;
+        g.conv_w = w.conv_w; g.C = h->C; g.Kc = K; g.edge = pb.part;
         if (dn::launch_pgemm(g, st) != hipSuccess) return fail(h, DN_E_DEVICE);
         pc.part = pb.part; pc.KS = 1;
       } else {
@@ -219,7 +223,7 @@ int pf_run(dn_layer* h, const PfBufs& pb, int gemm, dn::LtCtx* lt, bool verbose,
     pc.prenorm = (c.flags & DN_X_RMSNORM) ? 1 : 0; pc.eps = c.eps_rms;
     pc.conv_w = w.conv_w; pc.ring_in = ring_l; pc.ring_out = pb.ring;
     pc.C = h->C; pc.Kc = K; pc.out = pb.u;
-    if (dn::launch_pconv(pc, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if ((fu_in ? dn::launch_pconv_edge(pc, st) : dn::launch_pconv(pc, st)) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (K > 1 && hipMemcpyAsync(ring_l, pb.ring, sizeof(float) * ring_seq, hipMemcpyDeviceToDevice, st) != hipSuccess)
       return fail(h, DN_E_DEVICE);
     if (!check()) return fail(h, DN_E_DEVICE);
@@ -253,9 +257,10 @@ int pf_run(dn_layer* h, const PfBufs& pb, int gemm, dn::LtCtx* lt, bool verbose,
       const dn::TSplitNormArgs sn{so, pb.u + h->C, R, w.norm_w, c.eps_rms};
       if (dn::launch_tsplit_norm(sn, st) != hipSuccess) return fail(h, DN_E_DEVICE);
       if (fu_out) {
-        const dn::PGemmArgs g{static_cast<const int8_t*>(w.w_out), tx, pb.sc, pb.part, (int)D, V, n_tokens};
+        // the GEMM's epilogue applies the row scale and writes the layer's output: no k_bepi
+        dn::PGemmArgs g{static_cast<const int8_t*>(w.w_out), tx, pb.sc, out + (l * B + sb) * T * D, (int)D, V, n_tokens};
+        g.s = w.s_out;
         if (dn::launch_pgemm(g, st) != hipSuccess) return fail(h, DN_E_DEVICE);
-        e.part = pb.part; e.KS = 1;
       } else {
         if (dn::lt_gemm_i8(lt, 1, w.w_out, tx, td, st) != hipSuccess) return fail(h, DN_E_DEVICE);
         e.terms = td; e.s1 = pb.sc; e.KS = 0;
@@ -269,7 +274,7 @@ int pf_run(dn_layer* h, const PfBufs& pb, int gemm, dn::LtCtx* lt, bool verbose,
     }
     e.M = (int)D; e.B = n_tokens; e.s = w.s_out;
     e.out = out + (l * B + sb) * T * D; e.out_stride = (int)D;
-    if (dn::launch_bepi(e, st) != hipSuccess) return fail(h, DN_E_DEVICE);
+    if (!fu_out && dn::launch_bepi(e, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (!check()) return fail(h, DN_E_DEVICE);
   }
   return DN_OK;
