@@ -718,11 +718,25 @@ __global__ __launch_bounds__(512) void k_pgemm(const PGemmArgs a) {
   // epilogue: lane holds token t0 + 32 th + 16 tt + lane % 16, rows 16 r + 4 (lane / 16) + v of the
   // wave's four row tiles; the three terms folded in double with the token's scale (as k_pconv
   // folds the library GEMM's sums), four consecutive rows per 16-byte store
+  // the epilogue's scalars first, all requested together: the token scales, the row scales of the
+  // lane's 16 rows (four runs of four), the pre-norm sums
+  float s1v[2], ssqv[2];
+  v4f srow[4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int tc = min(t0 + 32 * th + 16 * tt + (lane & 15), a.T - 1);
+    s1v[tt] = a.s1[tc];
+    ssqv[tt] = CONV ? a.ssq[tc] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    srow[r] = a.s ? *reinterpret_cast<const v4f*>(a.s + min(row0 + 64 * rg + 16 * r + 4 * (lane >> 4), a.M - 4))
+                  : v4f{1.f, 1.f, 1.f, 1.f};
   if constexpr (!CONV) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = t0 + 32 * th + 16 * tt + (lane & 15);
-      const double s1 = (double)a.s1[min(t, a.T - 1)];
+      const double s1 = (double)s1v[tt];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = row0 + 64 * rg + 16 * r + 4 * (lane >> 4);
@@ -731,7 +745,7 @@ __global__ __launch_bounds__(512) void k_pgemm(const PGemmArgs a) {
         for (int v = 0; v < 4; ++v) {
           o[v] = (float)(s1 * ((double)acc[r][tt][0][v] +
                                ((double)acc[r][tt][1][v] + (double)acc[r][tt][2][v] * (1.0 / 254.0)) * (1.0 / 254.0)));
-          if (a.s) o[v] = a.s[min(m + v, a.M - 1)] * o[v];  // out_proj: the row scale (k_bepi's last step)
+          if (a.s) o[v] = srow[r][v] * o[v];  // out_proj: the row scale (k_bepi's last step)
         }
         if (t < a.T) {
           if (m + 3 < a.M) {
@@ -753,9 +767,9 @@ __global__ __launch_bounds__(512) void k_pgemm(const PGemmArgs a) {
     pg_barrier();
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int tl = 32 * th + 16 * tt + (lane & 15), t = t0 + tl, tc = min(t, a.T - 1);
-      const double s1 = (double)a.s1[tc];
-      const float f = a.prenorm ? rsqrtf(a.ssq[tc] / (float)a.K + a.eps) : 1.0f;
+      const int tl = 32 * th + 16 * tt + (lane & 15), t = t0 + tl;
+      const double s1 = (double)s1v[tt];
+      const float f = a.prenorm ? rsqrtf(ssqv[tt] / (float)a.K + a.eps) : 1.0f;
       const bool edge_t = t < a.T && (tl < 3 || tl >= PG_TOK - 3 || t >= a.T - 3);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -766,7 +780,7 @@ __global__ __launch_bounds__(512) void k_pgemm(const PGemmArgs a) {
           const float fold = (float)(s1 * ((double)acc[r][tt][0][v] +
                                            ((double)acc[r][tt][1][v] + (double)acc[r][tt][2][v] * (1.0 / 254.0)) *
                                                (1.0 / 254.0)));
-          o[v] = a.s[min(m + v, a.M - 1)] * f * fold;
+          o[v] = srow[r][v] * f * fold;
         }
         *reinterpret_cast<v4f*>(&sP[tl][rl]) = o;
         if (edge_t && m < a.M) *reinterpret_cast<v4f*>(a.edge + (size_t)t * a.M + m) = o;  // M % 4 == 0
