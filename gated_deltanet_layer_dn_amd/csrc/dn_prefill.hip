@@ -472,9 +472,11 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
       sS[i][cc] = Sh[(size_t)i * DV + 16 * b + cc];
     }
   }
-  // loads only (no arithmetic on the loaded values, which would wait for them at once)
-  auto load_ops = [&](int c, PScanOps& o) {
+  // loads only (no arithmetic on the loaded values, which would wait for them at once); part: 1 W,
+  // 2 Kt, 4 Uv and the decay
+  auto load_ops = [&](int c, PScanOps& o, int part) {
     const float* cw = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
+    if (part & 1) {
     const float* wr = cw + OFF_W + 4 * (w * 8 * 64 + lane);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -482,6 +484,8 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) o.aW[4 * q + e] = x[e];
     }
+    }
+    if (part & 2) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const float* kr = cw + OFF_KT + 4 * ((w * 2 + tau) * 4 * 64 + lane);
@@ -492,10 +496,13 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
         for (int e = 0; e < 4; ++e) o.aK[tau][4 * q + e] = x[e];
       }
     }
+    }
+    if (part & 4) {
     const v4f x = *reinterpret_cast<const v4f*>(cw + OFF_UV + 4 * ((b * 4 + w) * 64 + lane));
 #pragma unroll
     for (int v = 0; v < 4; ++v) o.uv[v] = x[v];
     o.gl = cw[OFF_G];
+    }
   };
   auto load_read = [&](int c, PScanRead& o) {
     const float* cw = a.cw + ((size_t)h * a.NCH + c) * PF_CHUNK_FLOATS;
@@ -521,16 +528,22 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
   // one chunk; `last`: the prompt's last chunk, which may be ragged (the others are whole, so their
   // loads and stores are unconditional and the waits for them exact)
   auto chunk = [&](int c, const PScanOps& o, PScanOps& nx, bool last) {
-    // the readout operands of this chunk (needed after the chain's products) and the chain operands
-    // of the next chunk (needed a whole chunk later) are requested first
+    // the readout operands of this chunk (needed after the chain's products) are requested first,
+    // the next chunk's chain operands (needed a whole chunk later) in three parts between this chunk's
+    // products: all at once, the loads would hold the wave's issue while the memory pipe takes them
     PScanRead rd;
     load_read(c, rd);
-    load_ops(min(c + 1, a.NCH - 1), nx);
+    const int cn = min(c + 1, a.NCH - 1);
+    load_ops(cn, nx, 1);
+    __builtin_amdgcn_sched_barrier(0);
     const int t0 = c * CT, nj = min(CT, a.T - t0);
     // D = Uv - W S for rows 16w..
     v4f dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 32; ++st) dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(o.aW[st], bS[st], dacc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(cn, nx, 2);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int v = 0; v < 4; ++v) sD[16 * w + 4 * lk + v][li] = o.uv[v] - dacc[v];
     lds_barrier();
@@ -548,6 +561,8 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
         sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.aK[tau][st], bD[st], sacc[tau], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_ops(cn, nx, 4);
     __builtin_amdgcn_sched_barrier(0);
     // readout Qg S + P D: off the chain
     v4f oacc = {0.f, 0.f, 0.f, 0.f};
@@ -571,7 +586,7 @@ __global__ __launch_bounds__(256) void k_pscan(const PScanArgs a) {
     }
   };
   PScanOps o0, o1;
-  load_ops(0, o0);
+  load_ops(0, o0, 7);
   int c = 0;
   for (; c + 2 < a.NCH; c += 2) {
     chunk(c, o0, o1, false);
