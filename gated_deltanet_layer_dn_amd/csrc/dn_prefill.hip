@@ -44,12 +44,6 @@ constexpr int OFF_W = 0, OFF_UV = CT * DK, OFF_QG = 2 * CT * DK, OFF_KT = 3 * CT
 //                    ((i/32) 2 + (i/16)%2) 4 + (tok%16)/4) 64 + i%16 + 16 (tok/16), value tok % 4
 //   Uv [64][128]:    element (row, col) in unit ((col/16) 4 + row/16) 64 + col%16 + 16 ((row%16)/4),
 //                    value row % 4
-__device__ __forceinline__ int pf_wq_at(int row, int col) {
-  return 4 * ((((row >> 4) * 8 + ((col & 31) >> 2)) * 64) + (row & 15) + 16 * (col >> 5)) + (col & 3);
-}
-__device__ __forceinline__ int pf_p_at(int row, int col) {
-  return 4 * ((((row >> 4) * 4 + ((col & 15) >> 2)) * 64) + (row & 15) + 16 * (col >> 4)) + (col & 3);
-}
 constexpr int TR = 32;  // tokens per thread in k_pconv
 constexpr int LD = DK + 4;  // padded LDS row of 128 floats (keeps 16-byte alignment)
 
@@ -243,6 +237,7 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
   __shared__ __attribute__((aligned(16))) float sQ[CT][LD], sK[CT][LD], sV[CT][LD];
   __shared__ float sA[CT][CT + 1];  // A
   __shared__ float sT[CT][CT + 1];  // Tm = (I + A)^-1 (lower triangular)
+  __shared__ __attribute__((aligned(16))) float sPs[CT][CT + 4];  // P, staged for whole-unit stores
   __shared__ double slg[CT];
   __shared__ float sb[CT], sbg[CT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -379,11 +374,16 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = 16 * rt + 4 * lk + v, m = 16 * ct + li;
-        out[OFF_P + pf_p_at(j, m)] = m <= j ? expf((float)(slg[j] - slg[m])) * qt[v] : 0.f;
+        sPs[j][m] = m <= j ? expf((float)(slg[j] - slg[m])) * qt[v] : 0.f;
       }
     }
   }
   __syncthreads();
+  // P in the scan's order, one whole 16-byte unit per thread and step
+  for (int u = tid; u < CT * CT / 4; u += 256) {
+    const int ul = u & 63, j = 16 * (u >> 8) + (ul & 15), m4 = 16 * (ul >> 4) + 4 * ((u >> 6) & 3);
+    *reinterpret_cast<v4f*>(out + OFF_P + 4 * u) = *reinterpret_cast<const v4f*>(&sPs[j][m4]);
+  }
   // 16 x 16 products with the sum index 4 s + k at step s (lane group k = l / 16)
   for (int L = 1; L < 4; ++L) {
     if (wave < 4 - L) {
@@ -429,11 +429,17 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
         wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[st], sK[m][16 * ct + li], wacc, 0, 0, 0);
         uacc = __builtin_amdgcn_mfma_f32_16x16x4f32(au[st], sV[m][16 * ct + li], uacc, 0, 0, 0);
       }
+      // W staged in sQ (free since P), written in the scan's order below
 #pragma unroll
-      for (int v = 0; v < 4; ++v) out[OFF_W + pf_wq_at(16 * rt + 4 * lk + v, 16 * ct + li)] = wacc[v];
+      for (int v = 0; v < 4; ++v) sQ[16 * rt + 4 * lk + v][16 * ct + li] = wacc[v];
       // rows 16 rt + 4 lk + v, column 16 ct + li: one whole unit of the Uv order per lane
       *reinterpret_cast<v4f*>(out + OFF_UV + 4 * ((ct * 4 + rt) * 64 + lane)) = uacc;
     }
+  }
+  __syncthreads();
+  for (int u = tid; u < CT * DK / 4; u += 256) {
+    const int ul = u & 63, j = 16 * (u >> 9) + (ul & 15), c4 = 32 * (ul >> 4) + 4 * ((u >> 6) & 7);
+    *reinterpret_cast<v4f*>(out + OFF_W + 4 * u) = *reinterpret_cast<const v4f*>(&sQ[j][c4]);
   }
 }
 
