@@ -407,33 +407,43 @@ __global__ __launch_bounds__(256) void k_pintra(const PIntraArgs a) {
 
   // W = Tm diag(beta g) K and Uv = Tm diag(beta) V. Tm is lower triangular: row tile rt sums over
   // the first 16 (rt + 1) rows of K and V only. Wave w forms column tiles 2w and 2w + 1 of every
-  // row tile (the same number of products on every wave).
+  // row tile (the same number of products on every wave). Every operand is read into registers
+  // first (Tm's nonzero blocks scaled, 40 steps, and a column tile's K and V rows), so the products
+  // of a column tile issue back to back.
+  {
+    float aw[40], au[40];  // step st of row tile rt at index 2 rt (rt + 1) + st
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    constexpr int NS = 16;
-    float aw[NS], au[NS];
-#pragma unroll
-    for (int st = 0; st < 4 * (rt + 1); ++st) {
-      const int m = 4 * st + lk;
-      const float tm = sT[16 * rt + li][m];
-      aw[st] = tm * sbg[m];
-      au[st] = tm * sb[m];
-    }
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl) {
-      const int ct = 2 * wave + cl;
-      v4f wacc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int st = 0; st < 4 * (rt + 1); ++st) {
         const int m = 4 * st + lk;
-        wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[st], sK[m][16 * ct + li], wacc, 0, 0, 0);
-        uacc = __builtin_amdgcn_mfma_f32_16x16x4f32(au[st], sV[m][16 * ct + li], uacc, 0, 0, 0);
+        const float tm = sT[16 * rt + li][m];
+        aw[2 * rt * (rt + 1) + st] = tm * sbg[m];
+        au[2 * rt * (rt + 1) + st] = tm * sb[m];
       }
-      // W staged in sQ (free since P), written in the scan's order below
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sQ[16 * rt + 4 * lk + v][16 * ct + li] = wacc[v];
-      // rows 16 rt + 4 lk + v, column 16 ct + li: one whole unit of the Uv order per lane
-      *reinterpret_cast<v4f*>(out + OFF_UV + 4 * ((ct * 4 + rt) * 64 + lane)) = uacc;
+    for (int cl = 0; cl < 2; ++cl) {
+      const int ct = 2 * wave + cl;
+      float bk[16], bv[16];
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        bk[st] = sK[4 * st + lk][16 * ct + li];
+        bv[st] = sV[4 * st + lk][16 * ct + li];
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        v4f wacc = {0.f, 0.f, 0.f, 0.f}, uacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4 * (rt + 1); ++st) {
+          wacc = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[2 * rt * (rt + 1) + st], bk[st], wacc, 0, 0, 0);
+          uacc = __builtin_amdgcn_mfma_f32_16x16x4f32(au[2 * rt * (rt + 1) + st], bv[st], uacc, 0, 0, 0);
+        }
+        // W staged in sQ (free since P), written in the scan's order below
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sQ[16 * rt + 4 * lk + v][16 * ct + li] = wacc[v];
+        // rows 16 rt + 4 lk + v, column 16 ct + li: one whole unit of the Uv order per lane
+        *reinterpret_cast<v4f*>(out + OFF_UV + 4 * ((ct * 4 + rt) * 64 + lane)) = uacc;
+      }
     }
   }
   __syncthreads();
