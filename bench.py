@@ -95,7 +95,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (reference for the HBM byte counters)")
     ap.add_argument("--ceiling", action="store_true",
-                    help="only measure the read-stream ceiling of the device (libdn_probe) and print it")
+                    help="only measure the read-stream and read-modify-write ceilings of the device (libdn_probe) and print them")
     ap.add_argument("--cpu-leg", type=int, default=0, metavar="THREADS",
                     help=argparse.SUPPRESS)  # internal: the oracle sample, run in a child process
     args = ap.parse_args()
@@ -118,6 +118,7 @@ def main():
 
     if args.ceiling:
         print(json.dumps(read_ceiling()), flush=True)
+        print(json.dumps(rmw_ceiling()), flush=True)
         return
 
     if args.copy_calibration:
@@ -210,15 +211,25 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_persist (whole-stack decode, one launch per token)" if whole_stack
-                          else "per-layer kernels (whole step)",
+                          else f"{path} (whole step)",
                 "launch_us_mean": round(kern_us, 2), "launch_us_min": round(float(launch_us.min()), 2),
                 "launch_us_max": round(float(launch_us.max()), 2), "bytes_per_launch": bytes_step}
     log(f"[bench] launch time mean {kern_us:.2f} us (min {launch_us.min():.2f}, max {launch_us.max():.2f})")
+    # measured ceiling of this step's bytes: the weights at the read-stream ceiling, the state (read,
+    # updated and written back) at the read-modify-write ceiling, both measured here
     ceil = read_ceiling()
-    roofline["measured_ceiling"] = ceil["read_ceiling_gbs"]
-    roofline["frac_of_measured_ceiling"] = round(achieved / ceil["read_ceiling_gbs"], 4)
-    log(f"[bench] read-stream ceiling {ceil['read_ceiling_gbs']:.0f} GB/s: "
-        f"{100 * roofline['frac_of_measured_ceiling']:.1f}% of it")
+    rmw = rmw_ceiling()
+    w_bytes = cfg.n_layers * cfg.weight_bytes_per_layer()
+    s_bytes = cfg.n_layers * 2 * cfg.state_bytes_per_layer()
+    ceil_s = w_bytes / (ceil["read_ceiling_gbs"] * 1e9) + s_bytes / (rmw["rmw_ceiling_gbs"] * 1e9)
+    ceil_gbs = bytes_step / ceil_s / 1e9
+    roofline["measured_ceiling"] = round(ceil_gbs, 1)
+    roofline["frac_of_measured_ceiling"] = round(achieved / ceil_gbs, 4)
+    roofline["read_ceiling_gbs"] = ceil["read_ceiling_gbs"]
+    roofline["rmw_ceiling_gbs"] = rmw["rmw_ceiling_gbs"]
+    log(f"[bench] read-stream ceiling {ceil['read_ceiling_gbs']:.0f} GB/s, read-modify-write ceiling "
+        f"{rmw['rmw_ceiling_gbs']:.0f} GB/s; this step's bytes at those: {ceil_gbs:.0f} GB/s, "
+        f"{ceil_s * 1e6:.1f} us: {100 * roofline['frac_of_measured_ceiling']:.1f}% of it")
 
     rec = {
         "metric": "DeltaNet decode tokens/s (30-layer stack) + achieved HBM GB/s % of peak",
@@ -283,6 +294,41 @@ def read_ceiling(gib: int = 2, reps: int = 4):
                     best, shape = rate, (blocks, inflight)
     del buf
     return {"read_ceiling_gbs": round(best, 1), "bytes": nbytes, "blocks": shape[0], "loads_in_flight": shape[1],
+            "frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
+
+
+def rmw_ceiling(gib: int = 2, reps: int = 4):
+    """The read-modify-write ceiling of the device: an in-place stream over `gib` GiB (beyond the
+    last-level cache), every piece read and written back with nontemporal accesses, over a few grid
+    sizes and pieces in flight; bytes counted both ways (read + written), best rate after a warm-up
+    run of each shape."""
+    import ctypes
+
+    import torch
+
+    import gated_deltanet_layer_dn_amd as dn
+    lib = ctypes.CDLL(dn.PROBE_LIB_PATH)
+    lib.dn_probe_rmw_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.dn_probe_rmw_stream.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream()
+    best, shape = 0.0, None
+    for blocks in (cus * 4, cus * 8, cus * 16, cus * 32):
+        for inflight in (4, 8, 16):
+            for r in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                rc = lib.dn_probe_rmw_stream(buf.data_ptr(), nbytes, blocks, inflight, st.cuda_stream)
+                e1.record(st)
+                torch.cuda.synchronize()
+                assert rc == 0, rc
+                rate = 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                if r and rate > best:
+                    best, shape = rate, (blocks, inflight)
+    del buf
+    return {"rmw_ceiling_gbs": round(best, 1), "bytes": 2 * nbytes, "blocks": shape[0], "pieces_in_flight": shape[1],
             "frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
 
 

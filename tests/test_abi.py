@@ -53,6 +53,13 @@ def test_prefill_library_exports_exactly_its_declared_calls(built):
     assert _exports(built[1]) == _declared(PHDR)
 
 
+def test_probe_library_exports_exactly_its_declared_calls(built):
+    probe = os.path.join(PKG, "libdn_probe.so")
+    declared = _declared(os.path.join(ROOT, "include", "dn_probe.h"))
+    assert declared == {"dn_probe_read_stream", "dn_probe_rmw_stream"}
+    assert _exports(probe) == declared
+
+
 def test_libraries_load_and_resolve(built):
     L = ctypes.CDLL(built[0])
     for n in FIVE:
