@@ -684,10 +684,35 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         sm.gate[l][1] = a.beta[(size_t)l * Hv + g.bh];
       }
     }
+    // sixteen loads in flight per lane before their stores (one at a time, the loop would wait a
+    // memory latency per 64 values: about 30 us for the per-key decays of 30 layers)
     if constexpr (PK)
-      for (int e = lane; e < a.L * DK; e += 64)
-        apk[e / DK][e % DK] = a.alpha[((size_t)(e / DK) * Hv + g.bh) * DK + e % DK];
-    for (int e = lane; e < a.L * CB; e += 64) sm.nw[e / CB][e % CB] = a.layers[e / CB].norm_w[g.bcb * CB + e % CB];
+      for (int e0 = lane; e0 < a.L * DK; e0 += 64 * 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = min(e0 + 64 * u, a.L * DK - 1);
+          v[u] = a.alpha[((size_t)(e / DK) * Hv + g.bh) * DK + e % DK];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int e = e0 + 64 * u;
+          if (e < a.L * DK) apk[e / DK][e % DK] = v[u];
+        }
+      }
+    for (int e0 = lane; e0 < a.L * CB; e0 += 64 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(e0 + 64 * u, a.L * CB - 1);
+        v[u] = a.layers[e / CB].norm_w[g.bcb * CB + e % CB];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 64 * u;
+        if (e < a.L * CB) sm.nw[e / CB][e % CB] = v[u];
+      }
+    }
   }
 
   // GT: the gate row this wave computes (workgroups wg < 2 Hv, second communication wave), its

@@ -82,7 +82,12 @@ def run(config: str = "stack", n_tokens: int = 12) -> dict:
         raise RuntimeError("another build of libdn is already loaded in this process")
     dn.LIB_PATH = LIB_TIMERS
 
-    cfg = gi.CONFIGS[config]
+    if config == "stack_perkey":  # the stack with one decay per key channel (as bench.py builds it)
+        cfg = gi.CONFIGS["stack"].replace(name="stack_perkey", flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
+    elif config == "stack_gates":  # the stack with the gates computed on the card
+        cfg = gi.CONFIGS["stack"].replace(name="stack_gates", flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE)
+    else:
+        cfg = gi.CONFIGS[config]
     layers, stream = gi.generate(cfg, n_tokens=n_tokens)
     st = dn.DeltaNetStack.from_config(cfg, layers)
     try:
