@@ -33,9 +33,10 @@
 // GEMV arithmetic: activations split into three int8 terms, exact int32 dot products with
 // v_dot4_i32_i8 per lane, folded into one fp32 partial per lane and summed over the wave in fp32.
 //
-// Gates on the card (GT): in workgroups wg < 2 Hv the second communication wave computes in_proj
-// row R + wg (gate a of head wg, or gate b of head wg - Hv) during phase A and publishes it with
-// the other in_proj rows; phase B gathers its head's two gate values with q, k, v, z.
+// Gates on the card (GT): in every phase-B workgroup the second communication wave computes the
+// in_proj rows of its head's two gates (R + bh and R + Hv + bh) on the staged x during phase A and
+// hands the two values to phase B through LDS: no hand-off between workgroups for them (each head's
+// gate rows are read by its eight workgroups).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -210,7 +211,8 @@ struct Smem {
   int8_t xs[3 * 4096];     // three-term split of x for phase A
   float inv[64];           // per value head 1/rms of the readout
   float qk[2 * DK];        // raw q and k of phase B's key head
-  v4i gwl[2][64];          // GT: the next layer's gate row (lane's 16-byte chunks), copied straight to LDS
+  v4i gwl[2][2][64];       // GT: the next layer's two gate rows of this head (lane's 16-byte chunks), via LDS DMA
+  float gval[2];           // GT: the layer's gate pre-activations a, b of this head
   v4f sbuf[8 * 64];        // phase B's updated state slice until its write-back
   float stat[16];          // partial statistics from the communication waves, split scale
   float gate[MAXL][2];     // alpha, beta of this workgroup's value head, per layer
@@ -218,6 +220,7 @@ struct Smem {
   int a_done, b_done, c_done;  // progress counters of this workgroup's waves
   int u_done;                  // phase-B inputs received (the next layer's in_proj prefetch may start)
   int s_ready;                 // compute waves whose chunk of the layer's state slice is in LDS
+  int g_ready;                 // GT: layers whose gate values are in gval
   int abort_flag;
 };
 
@@ -715,20 +718,24 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
     }
   }
 
-  // GT: the gate row this wave computes (workgroups wg < 2 Hv, second communication wave), its
-  // weights held one layer ahead like the compute waves' rows
+  // GT: this head's two gate rows (in_proj rows R + bh and R + Hv + bh), computed by the second
+  // communication wave of every phase-B workgroup on the staged x while the first waits for the
+  // in_proj hand-off, and handed to phase B through LDS; their weights are held one layer ahead
+  // in LDS (this wave's registers are its other work's)
   constexpr int rowbytes_in = BITS == 8 ? D : D / 2;
-  const bool runs_gate = GT && cw == 1 && wg < 2 * Hv;
-  // the row's weights wait in LDS rather than in registers, which this wave's other work needs
+  const bool runs_gate = GT && cw == 1 && g.has_b;
   static_assert(NCHA <= 2, "");
-  float gsc = 0.f;
+  float gsc = 0.f;  // lane j < 2: the scale of gate row j
   auto load_g = [&](int l) {
-    const int8_t* wr = reinterpret_cast<const int8_t*>(a.layers[l].w_in) + (size_t)(a.R + wg) * rowbytes_in;
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the previous row's LDS reads are done
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the previous rows' LDS reads are done
 #pragma unroll
-    for (int k = 0; k < NCHA; ++k)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const v4i*>(wr) + lane + 64 * k, &sm.gwl[k][0], 16, 0, 0);
-    gsc = a.layers[l].s_in[a.R + wg];
+    for (int j = 0; j < 2; ++j) {
+      const int8_t* wr = reinterpret_cast<const int8_t*>(a.layers[l].w_in) + (size_t)(a.R + j * Hv + g.bh) * rowbytes_in;
+#pragma unroll
+      for (int k = 0; k < NCHA; ++k)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const v4i*>(wr) + lane + 64 * k, &sm.gwl[j][k][0], 16, 0, 0);
+    }
+    gsc = lane < 2 ? a.layers[l].s_in[a.R + lane * Hv + g.bh] : 0.f;
   };
   if (runs_gate) load_g(0);
 
@@ -785,14 +792,20 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
     lds_barrier();  // (2)
 
     if (runs_gate) {
-      // gate row R + wg on the staged x, published as in_proj output; then the next layer's row
-      int acc[1][3];
-      v4i gw[1][NCHA];
+      // the head's gate rows on the staged x, into LDS for phase B; then the next layer's rows
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the rows' direct-to-LDS copies have landed
+      int acc[2][3];
+      v4i gw[2][NCHA];
 #pragma unroll
-      for (int k = 0; k < NCHA; ++k) gw[0][k] = sm.gwl[k][lane];
-      dot_rows<BITS, 1, NCHA>(gw, sm.xs, D, lane, acc);
-      const float dot = reduce_rows<BITS, 1>(acc, sm.stat[8], lane);
-      if (lane == 0) ll_store(Ub + a.R + wg, gsc * dot, tag);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int k = 0; k < NCHA; ++k) gw[j][k] = sm.gwl[j][k][lane];
+      dot_rows<BITS, 2, NCHA>(gw, sm.xs, D, lane, acc);
+      const float dot = reduce_rows<BITS, 2>(acc, sm.stat[8], lane);
+      if (lane < 2) sm.gval[lane] = gsc * dot;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the values are in LDS before the count
+      asm volatile("" ::: "memory");
+      if (lane == 0) bump_counter(&sm.g_ready);
       if (l + 1 < a.L) load_g(l + 1);
     }
 
@@ -801,16 +814,11 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       // phase B: recurrence on the 128 x 16 state slice
       const int vcol = g.bh * DV + g.bcb * CB;
       // raw q and k rows lane and lane+64 of key head bg; v and z of this lane's column
-      // with GT also this head's gate values a and b (in_proj rows R + bh and R + Hv + bh)
-      constexpr int NU = GT ? 8 : 6;
+      constexpr int NU = 6;
       const int qo = g.bg * DK + lane;
       int off[NU];
       off[0] = qo; off[1] = qo + 64; off[2] = QK + qo; off[3] = QK + qo + 64;
       off[4] = 2 * QK + vcol + jc; off[5] = C + vcol + jc;
-      if constexpr (GT) {
-        off[6] = a.R + g.bh;
-        off[7] = a.R + Hv + g.bh;
-      }
       float val[NU];
 #pragma unroll
       for (int i = 0; i < NU; ++i) val[i] = 0.f;
@@ -829,8 +837,10 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         DN_MARK(a, l, 11);
         float alpha = sm.gate[l][0], beta = sm.gate[l][1];
         if constexpr (GT) {
-          alpha = dn_gate_alpha(val[6], sm.gate[l][0], sm.gate[l][1]);
-          beta = dn_gate_beta(val[7]);
+          wait_counter(&sm.g_ready, l + 1, &sm.abort_flag);  // this head's gate values are in LDS
+          asm volatile("" ::: "memory");
+          alpha = dn_gate_alpha(sm.gval[0], sm.gate[l][0], sm.gate[l][1]);
+          beta = dn_gate_beta(sm.gval[1]);
         }
         const v4f* Q4 = reinterpret_cast<const v4f*>(sm.qk + 32 * pr);
         const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DK + 32 * pr);
@@ -982,7 +992,7 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
 
   if (tid == 0) {
     sm.abort_flag = 0;
-    sm.a_done = sm.b_done = sm.c_done = sm.u_done = sm.s_ready = 0;
+    sm.a_done = sm.b_done = sm.c_done = sm.u_done = sm.s_ready = sm.g_ready = 0;
   }
 #ifdef DN_PHASE_TIMERS
   for (int e = tid; e < TS_MAXL * 32; e += NTHR) g_ts[e / 32][e % 32] = 0;
