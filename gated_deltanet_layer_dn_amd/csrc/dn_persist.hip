@@ -34,9 +34,9 @@
 // v_dot4_i32_i8 per lane, folded into one fp32 partial per lane and summed over the wave in fp32.
 //
 // Gates on the card (GT): in every phase-B workgroup the second communication wave computes the
-// in_proj rows of its head's two gates (R + bh and R + Hv + bh) on the staged x during phase A and
-// hands the two values to phase B through LDS: no hand-off between workgroups for them (each head's
-// gate rows are read by its eight workgroups).
+// in_proj rows of its head's two gates (R + bh and R + Hv + bh) on the staged x during phase A,
+// applies the gate functions, and hands alpha and beta to phase B through LDS: no hand-off between
+// workgroups for them (each head's gate rows are read by its eight workgroups).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -212,7 +212,7 @@ struct Smem {
   float inv[64];           // per value head 1/rms of the readout
   float qk[2 * DK];        // raw q and k of phase B's key head
   v4i gwl[2][2][64];       // GT: the next layer's two gate rows of this head (lane's 16-byte chunks), via LDS DMA
-  float gval[2];           // GT: the layer's gate pre-activations a, b of this head
+  float gval[2];           // GT: the layer's gates alpha, beta of this head
   v4f sbuf[8 * 64];        // phase B's updated state slice until its write-back
   float stat[16];          // partial statistics from the communication waves, split scale
   float gate[MAXL][2];     // alpha, beta of this workgroup's value head, per layer
@@ -720,8 +720,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
 
   // GT: this head's two gate rows (in_proj rows R + bh and R + Hv + bh), computed by the second
   // communication wave of every phase-B workgroup on the staged x while the first waits for the
-  // in_proj hand-off, and handed to phase B through LDS; their weights are held one layer ahead
-  // in LDS (this wave's registers are its other work's)
+  // in_proj hand-off, turned into alpha and beta and handed to phase B through LDS; their weights
+  // are held one layer ahead in LDS (this wave's registers are its other work's)
   constexpr int rowbytes_in = BITS == 8 ? D : D / 2;
   const bool runs_gate = GT && cw == 1 && g.has_b;
   static_assert(NCHA <= 2, "");
@@ -802,7 +802,9 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         for (int k = 0; k < NCHA; ++k) gw[j][k] = sm.gwl[j][k][lane];
       dot_rows<BITS, 2, NCHA>(gw, sm.xs, D, lane, acc);
       const float dot = reduce_rows<BITS, 2>(acc, sm.stat[8], lane);
-      if (lane < 2) sm.gval[lane] = gsc * dot;
+      // the gate functions too run here, off the recurrence's path
+      if (lane == 0) sm.gval[0] = dn_gate_alpha(gsc * dot, sm.gate[l][0], sm.gate[l][1]);
+      if (lane == 1) sm.gval[1] = dn_gate_beta(gsc * dot);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the values are in LDS before the count
       asm volatile("" ::: "memory");
       if (lane == 0) bump_counter(&sm.g_ready);
@@ -839,8 +841,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         if constexpr (GT) {
           wait_counter(&sm.g_ready, l + 1, &sm.abort_flag);  // this head's gate values are in LDS
           asm volatile("" ::: "memory");
-          alpha = dn_gate_alpha(sm.gval[0], sm.gate[l][0], sm.gate[l][1]);
-          beta = dn_gate_beta(sm.gval[1]);
+          alpha = sm.gval[0];
+          beta = sm.gval[1];
         }
         const v4f* Q4 = reinterpret_cast<const v4f*>(sm.qk + 32 * pr);
         const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DK + 32 * pr);
