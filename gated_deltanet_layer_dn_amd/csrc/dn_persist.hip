@@ -147,17 +147,20 @@ __device__ __forceinline__ int xpos(int c) {
   return (c & ~7) | ((c & 1) << 2) | ((c >> 1) & 3);
 }
 
-// Three-term int8 split of v with scale s1 (|v| <= 127 s1): v ~= s1 (h + (m + l/254)/254).
-__device__ __forceinline__ void split3(float v, float s1, float inv1, float s2, float inv2, float inv3,
-                                       int8_t& h8, int8_t& m8, int8_t& l8) {
-  const float h = fminf(fmaxf(rintf(v * inv1), -127.f), 127.f);
-  const float r1 = fmaf(-s1, h, v);
-  const float m = fminf(fmaxf(rintf(r1 * inv2), -127.f), 127.f);
-  const float r2 = fmaf(-s2, m, r1);
-  const float l = fminf(fmaxf(rintf(r2 * inv3), -127.f), 127.f);
-  h8 = (int8_t)h;
-  m8 = (int8_t)m;
-  l8 = (int8_t)l;
+// One term of the int8 split: q = rint(r inv) clamped to [-127, 127] (v_med3), found by adding
+// 1.5 * 2^23, which rounds to an integer (ties to even) and leaves it, two's complement, in the low
+// mantissa bits: the returned word's low byte is the int8 term, and q is that word minus the bias.
+constexpr float SPLIT_BIAS = 12582912.0f;
+__device__ __forceinline__ unsigned split_term(float r, float inv, float& q) {
+  const float t = __builtin_amdgcn_fmed3f(r * inv, -127.0f, 127.0f) + SPLIT_BIAS;
+  q = t - SPLIT_BIAS;
+  return __float_as_uint(t);
+}
+// The low bytes of four words, word i into byte i.
+__device__ __forceinline__ unsigned low_bytes(unsigned w0, unsigned w1, unsigned w2, unsigned w3) {
+  const unsigned lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u);  // w0.b0, w1.b0, 0, 0
+  const unsigned hi = __builtin_amdgcn_perm(w3, w2, 0x0c0c0400u);
+  return lo | (hi << 16);
 }
 
 
@@ -403,21 +406,40 @@ struct Geo {
 
 template <int BITS, int D>
 __device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid) {
+  // Three-term int8 split of the raw x with s1 = max|x| / 127: x ~= s1 (h + (m + l/254)/254); the
+  // RMS factor joins s1 in the fold of the dot products (sm.stat[8]). Each thread splits 8
+  // consecutive columns and writes each term as two dwords (4-bit weights: even columns in the
+  // first, odd in the second, the staged order of xpos).
+  constexpr int NT = D / 8;
   const float ss = (sm.stat[0] + sm.stat[1]) + (sm.stat[2] + sm.stat[3]);
   const float mx = fmaxf(fmaxf(sm.stat[4], sm.stat[5]), fmaxf(sm.stat[6], sm.stat[7]));
   const float scale = (a.flags & DN_X_RMSNORM) ? rsqrtf(ss / (float)D + a.eps_rms) : 1.0f;
-  float s1 = mx * scale * (1.0f / 127.0f);
+  float s1 = mx * (1.0f / 127.0f);
   if (!(s1 > 0.f)) s1 = 1.0f;
-  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2, inv3 = 254.0f / s2;
-  for (int c = tid; c < D; c += NTHR) {
-    int8_t h, m, lo;
-    split3(sm.raw[c] * scale, s1, inv1, s2, inv2, inv3, h, m, lo);
-    const int p = xpos<BITS>(c);
-    sm.xs[p] = h;
-    sm.xs[D + p] = m;
-    sm.xs[2 * D + p] = lo;
+  if (tid == 0) sm.stat[8] = s1 * scale;
+  if (tid >= NT) return;
+  const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = inv1 * 254.0f, inv3 = inv2 * 254.0f;
+  for (int t = tid; t < NT; t += NTHR) {
+    const v4f r0 = *reinterpret_cast<const v4f*>(sm.raw + 8 * t), r1 = *reinterpret_cast<const v4f*>(sm.raw + 8 * t + 4);
+    const float v[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    unsigned wh[8], wm[8], wl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float h, m, l;
+      wh[e] = split_term(v[e], inv1, h);
+      const float rr1 = fmaf(-s1, h, v[e]);
+      wm[e] = split_term(rr1, inv2, m);
+      const float rr2 = fmaf(-s2, m, rr1);
+      wl[e] = split_term(rr2, inv3, l);
+    }
+    // staged column order: identity for 8-bit weights; for 4-bit the even columns, then the odd
+    constexpr int o0 = 0, o1 = BITS == 8 ? 1 : 2, o2 = BITS == 8 ? 2 : 4, o3 = BITS == 8 ? 3 : 6;
+    constexpr int o4 = BITS == 8 ? 4 : 1, o5 = BITS == 8 ? 5 : 3, o6 = BITS == 8 ? 6 : 5, o7 = 7;
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<v2u*>(sm.xs + 8 * t) = v2u{low_bytes(wh[o0], wh[o1], wh[o2], wh[o3]), low_bytes(wh[o4], wh[o5], wh[o6], wh[o7])};
+    *reinterpret_cast<v2u*>(sm.xs + D + 8 * t) = v2u{low_bytes(wm[o0], wm[o1], wm[o2], wm[o3]), low_bytes(wm[o4], wm[o5], wm[o6], wm[o7])};
+    *reinterpret_cast<v2u*>(sm.xs + 2 * D + 8 * t) = v2u{low_bytes(wl[o0], wl[o1], wl[o2], wl[o3]), low_bytes(wl[o4], wl[o5], wl[o6], wl[o7])};
   }
-  if (tid == 0) sm.stat[8] = s1;
 }
 
 // Compute waves: phase A and phase C, weights prefetched one layer ahead in registers. (PK and GT
