@@ -611,92 +611,70 @@ __global__ __launch_bounds__(256) void k_bsplit_row(const BSplitArgs a) {
   }
 }
 
-// Whole-K projection with the epilogue fused (no partial sums), 8-bit weights: a workgroup of eight
-// waves owns 16*RT weight rows and 64 sequences; wave w takes the K quarter w % 4 (chunks of 128
-// columns (w % 4)*CPW .. +CPW-1) for the 32 sequences of half w / 4. The activations are split with
-// one scale per row (k_bsplit_row), so each wave keeps exact int32 sums of the three terms over its
-// whole K quarter (at most 127 * 127 * 1024 < 2^24 in magnitude: exact in fp32 too) and folds them
-// once.
-//  * Weights and split activations stream into registers, two chunks in flight; the two sequence
-//    halves read the same weight rows (the second from cache), and every workgroup reads the same
-//    few hundred KB of activations (L2-resident).
-//  * Epilogue inputs (row scales, conv taps, conv history, sums of squares) go to LDS by direct
-//    loads issued first, so their latency hides behind the stream.
-// The four K quarters' sums meet in LDS and are added in quarter order; then each (row, sequence)
-// gets k_bepi's epilogue. (Staging the weights in LDS instead, shared by the two halves, measured
-// slower: 19.7 against 17.2 us for the 12288 x 2048 in_proj at 64 sequences on MI355X.)
+// vmcnt(n) for n < 64 (the counter's low four bits and its high two), expcnt and lgkmcnt not waited
+constexpr int vm_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+// chunk xor permutation of the staged weight rows (row r of a 16-row tile): the operand reads of a
+// group of 16 lanes (rows 0..15, one 16-byte chunk each) meet every LDS bank once
+__device__ __forceinline__ int bp_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+typedef __attribute__((address_space(3))) void bp_lds_t;
+
+// Copy wave: publish in LDS that n chunks of its K quarter have landed. The store is written out by
+// hand: the compiler would otherwise wait for every direct-to-LDS load in flight before it.
+__device__ __forceinline__ void bp_publish(int* ready, int n) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the host pass has no LDS address space)
+  const unsigned at = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)ready;
+  asm volatile("ds_write_b32 %0, %1" ::"v"(at), "v"(n) : "memory");
+#endif
+}
+
+// Whole-K projection with the epilogue fused (no partial sums), 8-bit weights: a workgroup owns 16*RT
+// weight rows and 64 sequences, in twelve waves.
+//  * Copy waves 8..11: wave 8 + q requests the whole K quarter q of the workgroup's weight rows
+//    (CPW chunks of 128 columns) straight into LDS at once, each load instruction 8 whole rows of
+//    128 bytes, then the conv history of the epilogue, and publishes in LDS how many of its chunks
+//    have landed. The weights are the only HBM stream of the kernel, so all of it is in flight from
+//    the start.
+//  * MFMA waves 0..7: wave w takes K quarter w % 4 for the 32 sequences of half w / 4. The split
+//    activations (k_bsplit_row, one scale per row; the same few hundred KB for every workgroup,
+//    L2-resident) stream into registers two k-steps ahead; each k-step's weight fragments are read
+//    from LDS once its chunk is published. The two halves read the same staged weights.
+// Each wave keeps exact int32 sums of the three terms over its whole K quarter (at most
+// 127 * 127 * 1024 < 2^24 in magnitude: exact in fp32 too) and folds them once; the four K quarters'
+// sums meet in LDS (over the staged weights) and are added in quarter order; then each
+// (row, sequence) gets k_bepi's epilogue.
 template <int RT, int CPW>
-__global__ __launch_bounds__(512) void k_bproj(const BGemmArgs g, const BEpiArgs e) {
-  constexpr int ROWS = 16 * RT, NF = 2;  // sequence tiles of 16 per wave
-  // dynamic LDS (bproj_lds_bytes): [quarter sums 4*NT*ROWS | history 3*NT*ROWS | taps 4*ROWS |
-  // scales 64 | sums of squares NT] floats. The direct-to-LDS copies write it behind the compiler's
-  // back, which it must not assume to be unwritten.
+__global__ __launch_bounds__(768) void k_bproj(const BGemmArgs g, const BEpiArgs e) {
+  constexpr int ROWS = 16 * RT, NF = 2;  // sequence tiles of 16 per MFMA wave
+  constexpr int WT = 2 * RT;             // load instructions (8 rows x 128 bytes) per weight chunk
+  constexpr int WQ = CPW * WT * 1024;    // LDS bytes of one K quarter's weights
+  // the history: 3 NT segments (slot, sequence) of ROWS channels, 16 bytes (4 channels) per lane, SEGI
+  // whole segments per load instruction; NRW instructions per copy wave, always issued
+  constexpr int LPS = ROWS / 4, SEGI = 64 / LPS, NSEG = 3 * NT;
+  constexpr int NRI = (NSEG + SEGI - 1) / SEGI, NRW = (NRI + 3) / 4;
+  static_assert(NRW + CPW * WT + 3 <= 63 && NT * ROWS * 4 <= WQ, "");  // loads in flight per copy wave; sums fit
+  // dynamic LDS (bproj_lds_bytes): [weights 4 WQ bytes, later the quarter sums 4*NT*ROWS floats |
+  // history 3*NT*ROWS | taps 4*ROWS | scales 64 | sums of squares NT | 256 for the history loads past
+  // its end] floats. The direct-to-LDS
+  // copies write it behind the compiler's back, which it must not assume to be unwritten.
   extern __shared__ float bproj_lds[];
-  float(*red)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds);                     // [4]
-  float(*ring_l)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds + 4 * NT * ROWS);  // [3]
-  float* cw_l = bproj_lds + 7 * NT * ROWS;
+  __shared__ int wready[4];
+  char* const wl = reinterpret_cast<char*>(bproj_lds);
+  float(*red)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds);  // [4]
+  float(*ring_l)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds + WQ);  // [3]
+  float* cw_l = bproj_lds + WQ + 3 * NT * ROWS;
   float* s_l = cw_l + 4 * ROWS;
   float* ssq_l = s_l + 64;
+  float* spare_l = ssq_l + NT;
   // wave index uniform (scalar): the direct-to-LDS destinations derive from it
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kq = wave & 3, f0 = NF * (wave >> 2);
   const int rb = blockIdx.x, nb = blockIdx.y;
   const int M = g.M, K = g.K, B = g.B, NC = K / KC;
   const int row0 = rb * ROWS;
   const bool conv = e.conv_w != nullptr;
+  const bool hist = conv && row0 < e.C;
   const int Kc = e.Kc, C = e.C;
-
-  // epilogue inputs into LDS, slot 64 i + lane of instruction i (addresses clamped into range)
-  {
-    const int nring = (conv && row0 < C) ? (Kc - 1) * NT * ROWS / 64 : 0;
-    for (int i = wave; i < nring; i += 8) {
-      const int idx = 64 * i + lane, j = idx / (NT * ROWS), rem = idx % (NT * ROWS);
-      const int bl = rem / ROWS, rl = rem % ROWS;
-      const int b = min(nb * NT + bl, B - 1), r = min(row0 + rl, C - 1);
-      __builtin_amdgcn_global_load_lds(e.ring + ((size_t)b * (Kc - 1) + j) * C + r, &ring_l[0][0][0] + 64 * i, 4, 0, 0);
-    }
-    if (wave == 0) __builtin_amdgcn_global_load_lds(e.s + min(row0 + lane, M - 1), s_l, 4, 0, 0);
-    if (wave == 1) __builtin_amdgcn_global_load_lds(e.ssq + min(nb * NT + lane, B - 1), ssq_l, 4, 0, 0);
-    for (int i = wave; conv && row0 < C && i < ROWS * 4 / 64; i += 8) {
-      const int idx = 64 * i + lane, rl = idx / 4, q = idx % 4;
-      __builtin_amdgcn_global_load_lds(e.conv_w + (size_t)min(row0 + rl, C - 1) * Kc + min(q, Kc - 1), cw_l + 64 * i, 4, 0, 0);
-    }
-  }
-
-  // buffer loads: one VGPR offset per weight row tile and one for the activations, the chunk and
-  // k-step offsets in scalars, so that the chunks in flight hold no per-load addresses
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(g.W), (short)0, (int)((size_t)M * K), 0x00020000);
-  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(g.xs), (short)0, (int)((size_t)(nb + 1) * NC * 24576), 0x00020000);
-  // the lane's weight row in each row tile (rows past M read row M-1; their sums are discarded)
-  int wofs[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) wofs[rt] = min(row0 + 16 * rt + (lane & 15), M - 1) * K + 16 * (lane >> 4);
-  const int xofs = 16 * lane + f0 * 1024;
-  const int xblk = nb * NC * 24576;
-  float s1[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) s1[f] = g.sc[(size_t)nb * NT + 16 * (f0 + f) + (lane & 15)];
-
-  v4i A[2][KSC][RT];
-  v4i X[2][KSC][3][NF];
-  auto load_chunk = [&](int i, int buf) {
-    const int c = kq * CPW + i;
-#pragma unroll
-    for (int s = 0; s < KSC; ++s) {
-      const int kb = c * KC + 64 * s;  // byte offset of the k-step in a weight row
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        A[buf][s][rt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wofs[rt], kb, 0));
-#pragma unroll
-      for (int t = 0; t < 3; ++t)
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          X[buf][s][t][f] = __builtin_bit_cast(
-              v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, xofs + ((t * KSC + s) * 4 + f) * 1024, xblk + c * 24576, 0));
-    }
-  };
+  if (tid < 4) wready[tid] = 0;
+  __syncthreads();
 
   v4i acc[RT][3][NF];
 #pragma unroll
@@ -705,69 +683,170 @@ __global__ __launch_bounds__(512) void k_bproj(const BGemmArgs g, const BEpiArgs
     for (int t = 0; t < 3; ++t)
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[rt][t][f] = v4i{0, 0, 0, 0};
-  // Two chunks in flight, one per buffer. The scheduler would sink each load next to its first use;
-  // the barriers keep the lead, so the wait before a chunk's MFMAs leaves the other buffer's loads in
-  // flight.
-  load_chunk(0, 0);
-  if (CPW > 1) load_chunk(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
+  const int kq = wave & 3, f0 = NF * ((wave >> 2) & 1);
+  float s1[NF];
+
+  if (wave >= 8) {
+    // copy wave q = kq. First the epilogue's small inputs (their count varies; the waits below
+    // count only loads issued after the weights), addresses clamped into range.
+    if (kq == 0) {
+      __builtin_amdgcn_global_load_lds(e.s + min(row0 + lane, M - 1), s_l, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(e.ssq + min(nb * NT + lane, B - 1), ssq_l, 4, 0, 0);
+    }
+    for (int i = kq - 1; hist && i >= 0 && i < ROWS * 4 / 64; i += 3) {
+      const int idx = 64 * i + lane, rl = idx / 4, q = idx % 4;
+      __builtin_amdgcn_global_load_lds(e.conv_w + (size_t)min(row0 + rl, C - 1) * Kc + min(q, Kc - 1), cw_l + 64 * i, 4, 0, 0);
+    }
+    // the K quarter's weights: instruction (chunk c, group gi) fills rows 8 gi .. +7 of the chunk,
+    // lane l row 8 gi + l / 8, 16-byte chunk (l % 8) ^ bp_swz(row % 16); rows past M read row M-1
+    const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.W), (short)0, (int)((size_t)M * K), 0x00020000);
+    int woff[WT];
 #pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int buf = i & 1;
+    for (int gi = 0; gi < WT; ++gi)
+      woff[gi] = min(row0 + 8 * gi + (lane >> 3), M - 1) * K + 16 * ((lane & 7) ^ bp_swz(8 * (gi & 1) + (lane >> 3)));
+    auto copy = [&](int c, int gi) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the host pass rejects this form and then drops the kernel's stub)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (bp_lds_t*)(wl + ((kq * CPW + c) * WT + gi) * 1024), 16,
+                                               woff[gi], (kq * CPW + c) * KC, 0, 0);
+#endif
+    };
 #pragma unroll
-    for (int s = 0; s < KSC; ++s)
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int gi = 0; gi < WT; ++gi) copy(c, gi);
+    // the history: instruction n takes segments SEGI n .. +SEGI-1 (lane l: segment SEGI n + l / LPS,
+    // channels 4 (l % LPS) .. +3); lanes past the segments stay idle. Slots past the taps, channels
+    // past C and workgroups without history copy weight bytes instead (into slots nothing reads);
+    // instructions past the last segment, into the spare area.
+    for (int m = 0; m < NRW; ++m) {
+      const int n = kq + 4 * m, seg = SEGI * n + lane / LPS, ch = row0 + 4 * (lane % LPS);
+      const int j = seg / NT, bl = seg % NT;
+      const float* src = reinterpret_cast<const float*>(g.W);
+      if (hist && j < Kc - 1 && ch < C)
+        src = e.ring + ((size_t)min(nb * NT + bl, B - 1) * (Kc - 1) + j) * C + ch;
+      float* dst = n < NRI ? &ring_l[0][0][0] + SEGI * ROWS * n : spare_l;
+      if (lane < SEGI * LPS && (n >= NRI || seg < NSEG)) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    }
+    // chunk c has landed once at most the loads issued after it remain: the later chunks' and the
+    // history's
+    static_assert(CPW <= 4, "");
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      switch (CPW - 1 - c) {
+        case 0: __builtin_amdgcn_s_waitcnt(vm_imm(NRW)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vm_imm(NRW + WT)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vm_imm(NRW + 2 * WT)); break;
+        default: __builtin_amdgcn_s_waitcnt(vm_imm(NRW + 3 * WT)); break;
+      }
+      bp_publish(&wready[kq], c + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(vm_imm(0));  // the history has landed too
+  } else {
+    // buffer loads of the split activations: one VGPR offset, the chunk and k-step offsets in scalars
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(g.xs), (short)0, (int)((size_t)(nb + 1) * NC * 24576), 0x00020000);
+    const int xofs = 16 * lane + f0 * 1024;
+    const int xblk = nb * NC * 24576;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) s1[f] = g.sc[(size_t)nb * NT + 16 * (f0 + f) + (lane & 15)];
+    v4i X[2][3][NF];
+    auto load_x = [&](int ks, int buf) {
+      const int c = kq * CPW + ks / KSC, s = ks % KSC;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          X[buf][t][f] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(xrs, xofs + ((t * KSC + s) * 4 + f) * 1024, xblk + c * 24576, 0));
+    };
+    // operand reads within a chunk's 2 KB row tile: lane l, row l % 16, 16-byte chunk 4 s + l / 16
+    const int rr = lane & 15, rd0 = 16 * (64 * (rr >> 3) + 8 * (rr & 7) + ((lane >> 4) ^ bp_swz(rr)));
+    const int rd1 = rd0 ^ 64;
+    // Two k-steps of activations in flight. The scheduler would sink each load next to its first
+    // use; the barriers keep the lead.
+    load_x(0, 0);
+    load_x(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < CPW * KSC; ++ks) {
+      const int c = ks / KSC, s = ks % KSC, buf = ks & 1;
+      if (s == 0) {
+        while (__hip_atomic_load(&wready[kq], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <= c)
+          __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");  // the chunk's weights are read after its publication
+      }
+      const char* wb = wl + (kq * CPW + c) * WT * 1024 + (s ? rd1 : rd0);
+      v4i A[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) A[rt] = *reinterpret_cast<const v4i*>(wb + rt * 2048);
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int t = 0; t < 3; ++t)
-            acc[rt][t][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[buf][s][rt], X[buf][s][t][f], acc[rt][t][f], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 < CPW) load_chunk(i + 2, buf);
-    __builtin_amdgcn_sched_barrier(0);
+            acc[rt][t][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[rt], X[buf][t][f], acc[rt][t][f], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 2 < CPW * KSC) load_x(ks + 2, buf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  // fold the three exact term sums with the row scale; the MFMA output layout: lane holds sequence
-  // 16 f + lane % 16, rows 16 rt + 4 (lane / 16) + v
+  __syncthreads();  // every wave is done with the staged weights; every copy has landed
+  if (wave < 8) {
+    // fold the three exact term sums with the row scale; the MFMA output layout: lane holds sequence
+    // 16 f + lane % 16, rows 16 rt + 4 (lane / 16) + v
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float d = (float)acc[rt][0][f][v] +
-                        fmaf((float)acc[rt][2][f][v], 1.0f / 254.0f, (float)acc[rt][1][f][v]) * (1.0f / 254.0f);
-        red[kq][16 * (f0 + f) + (lane & 15)][16 * rt + 4 * (lane >> 4) + v] = s1[f] * d;
-      }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS copies have landed (they were issued first)
+        for (int v = 0; v < 4; ++v) {
+          const float d = (float)acc[rt][0][f][v] +
+                          fmaf((float)acc[rt][2][f][v], 1.0f / 254.0f, (float)acc[rt][1][f][v]) * (1.0f / 254.0f);
+          red[kq][16 * (f0 + f) + (lane & 15)][16 * rt + 4 * (lane >> 4) + v] = s1[f] * d;
+        }
+  }
   __syncthreads();
 
-  // epilogue, rows fastest (coalesced history and output)
-  constexpr int EPI = NT * ROWS / 512;
-  static_assert(NT * ROWS % 512 == 0, "");
-#pragma unroll
-  for (int j = 0; j < EPI; ++j) {
-    const int idx = j * 512 + tid, rl = idx % ROWS, bl = idx / ROWS;
+  // epilogue: a thread per sequence and 4 consecutive rows (16-byte LDS reads and stores; rows
+  // fastest across threads, so the history and output stores are coalesced)
+  for (int idx = tid; idx < NT * ROWS / 4; idx += 768) {
+    const int bl = idx / (ROWS / 4), rl = 4 * (idx % (ROWS / 4));
     const int r = row0 + rl, b = nb * NT + bl;
     if (r >= M || b >= B) continue;
-    const float sum = ((red[0][bl][rl] + red[1][bl][rl]) + red[2][bl][rl]) + red[3][bl][rl];
+    const v4f q0 = *reinterpret_cast<const v4f*>(&red[0][bl][rl]), q1 = *reinterpret_cast<const v4f*>(&red[1][bl][rl]);
+    const v4f q2 = *reinterpret_cast<const v4f*>(&red[2][bl][rl]), q3 = *reinterpret_cast<const v4f*>(&red[3][bl][rl]);
+    const v4f sv = *reinterpret_cast<const v4f*>(s_l + rl);
     const float pf = e.prenorm ? rsqrtf(ssq_l[bl] / (float)K + e.eps) : 1.0f;
-    const float u = s_l[rl] * pf * sum;
-    float o = u;
-    if (conv && r < C) {
-      float acc2 = 0.f;
+    v4f u, o;
 #pragma unroll
-      for (int q = 0; q < 3; ++q)
-        if (q < Kc - 1) acc2 = fmaf(cw_l[4 * rl + q], ring_l[q][bl][rl], acc2);
-      acc2 = fmaf(cw_l[4 * rl + min(3, Kc - 1)], u, acc2);
+    for (int v = 0; v < 4; ++v) {
+      const float sum = ((q0[v] + q1[v]) + q2[v]) + q3[v];
+      u[v] = sv[v] * pf * sum;
+    }
+    o = u;
+    if (conv && r < C) {
+      v4f h[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) h[q] = *reinterpret_cast<const v4f*>(&ring_l[q][bl][rl]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const v4f tap = *reinterpret_cast<const v4f*>(cw_l + 4 * (rl + v));
+        float acc2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          if (q < Kc - 1) acc2 = fmaf(tap[q], h[q][v], acc2);
+        acc2 = fmaf(tap[min(3, Kc - 1)], u[v], acc2);
+        o[v] = silu(acc2);
+      }
       float* rg = e.ring + (size_t)b * (Kc - 1) * C + r;
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        if (q + 1 < Kc - 1) rg[(size_t)q * C] = ring_l[q + 1][bl][rl];
-      if (Kc > 1) rg[(size_t)(Kc - 2) * C] = u;
-      o = silu(acc2);
+        if (q + 1 < Kc - 1) *reinterpret_cast<v4f*>(rg + (size_t)q * C) = h[q + 1];
+      if (Kc > 1) *reinterpret_cast<v4f*>(rg + (size_t)(Kc - 2) * C) = u;
     }
-    e.out[(size_t)b * e.out_stride + r] = o;
+    *reinterpret_cast<v4f*>(e.out + (size_t)b * e.out_stride + r) = o;
   }
 }
 
@@ -993,17 +1072,21 @@ hipError_t bgemm_bits(const BGemmArgs& a, int mf, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-constexpr size_t bproj_lds_bytes(int rt) { return sizeof(float) * (7 * NT * 16 * rt + 4 * 16 * rt + 64 + NT); }
+// staged weights (4 K quarters of cpw chunks x 2 rt load instructions of 1 KB), history, taps,
+// scales, sums of squares
+constexpr size_t bproj_lds_bytes(int rt, int cpw) {
+  return (size_t)4 * cpw * 2 * rt * 1024 + sizeof(float) * (3 * NT * 16 * rt + 4 * 16 * rt + 64 + NT + 256);
+}
 
 template <int RT, int CPW>
 hipError_t go_bproj(const BGemmArgs& g, const BEpiArgs& e, hipStream_t st) {
-  constexpr size_t lds = bproj_lds_bytes(RT);
+  constexpr size_t lds = bproj_lds_bytes(RT, CPW);
   static_assert(lds <= 160 * 1024, "");
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bproj<RT, CPW>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   const dim3 grid((g.M + 16 * RT - 1) / (16 * RT), (g.B + NT - 1) / NT);
-  hipLaunchKernelGGL((k_bproj<RT, CPW>), grid, dim3(512), lds, st, g, e);
+  hipLaunchKernelGGL((k_bproj<RT, CPW>), grid, dim3(768), lds, st, g, e);
   return hipGetLastError();
 }
 
@@ -1118,7 +1201,10 @@ bool bproj_shape_ok(int M, int K, int* rt) {
 
 hipError_t launch_bproj(const BGemmArgs& g, const BEpiArgs& e, int bits, int rt, hipStream_t st) {
   int want = 0;
-  if (bits != 8 || !bproj_shape_ok(g.M, g.K, &want) || (rt != 2 && rt != 3)) return hipErrorInvalidValue;
+  // (the history and the output move in 16-byte pieces: 4 rows)
+  if (bits != 8 || !bproj_shape_ok(g.M, g.K, &want) || (rt != 2 && rt != 3) || (e.conv_w && e.C % 4) || g.M % 4 ||
+      e.out_stride % 4)
+    return hipErrorInvalidValue;
   return rt == 2 ? bproj_rt<2>(g, e, st) : bproj_rt<3>(g, e, st);
 }
 
