@@ -629,11 +629,10 @@ __device__ __forceinline__ void bp_publish(int* ready, int n) {
 
 // Whole-K projection with the epilogue fused (no partial sums), 8-bit weights: a workgroup owns 16*RT
 // weight rows and 64 sequences, in twelve waves.
-//  * Copy waves 8..11: wave 8 + q requests the whole K quarter q of the workgroup's weight rows
-//    (CPW chunks of 128 columns) straight into LDS at once, each load instruction 8 whole rows of
-//    128 bytes, then the conv history of the epilogue, and publishes in LDS how many of its chunks
-//    have landed. The weights are the only HBM stream of the kernel, so all of it is in flight from
-//    the start.
+//  * Copy waves 8..11: wave 8 + q requests its share of the epilogue's conv history, then the whole
+//    K quarter q of the workgroup's weight rows (CPW chunks of 128 columns) straight into LDS at
+//    once, each load instruction 8 whole rows of 128 bytes, and publishes in LDS how many of its
+//    chunks have landed. So every HBM read of the kernel is in flight from the start.
 //  * MFMA waves 0..7: wave w takes K quarter w % 4 for the 32 sequences of half w / 4. The split
 //    activations (k_bsplit_row, one scale per row; the same few hundred KB for every workgroup,
 //    L2-resident) stream into registers two k-steps ahead; each k-step's weight fragments are read
@@ -648,20 +647,22 @@ __global__ __launch_bounds__(768) void k_bproj(const BGemmArgs g, const BEpiArgs
   constexpr int WT = 2 * RT;             // load instructions (8 rows x 128 bytes) per weight chunk
   constexpr int WQ = CPW * WT * 1024;    // LDS bytes of one K quarter's weights
   // the history: 3 NT segments (slot, sequence) of ROWS channels, 16 bytes (4 channels) per lane, SEGI
-  // whole segments per load instruction; NRW instructions per copy wave, always issued
+  // whole segments per load instruction; NRW instructions per copy wave
   constexpr int LPS = ROWS / 4, SEGI = 64 / LPS, NSEG = 3 * NT;
   constexpr int NRI = (NSEG + SEGI - 1) / SEGI, NRW = (NRI + 3) / 4;
-  static_assert(NRW + CPW * WT + 3 <= 63 && NT * ROWS * 4 <= WQ, "");  // loads in flight per copy wave; sums fit
-  // dynamic LDS (bproj_lds_bytes): [weights 4 WQ bytes, later the quarter sums 4*NT*ROWS floats |
-  // history 3*NT*ROWS | taps 4*ROWS | scales 64 | sums of squares NT | 256 for the history loads past
-  // its end] floats. The direct-to-LDS
+  // the quarter sums: rows padded to ROWS + 4 (16-byte writes of 8 lanes meet every bank once)
+  constexpr int RP = ROWS + 4, REG0 = WQ > 4 * NT * RP ? WQ : 4 * NT * RP;  // floats before the history
+  static_assert(NRW + CPW * WT + 3 <= 63, "");  // loads in flight per copy wave
+  // dynamic LDS (bproj_lds_bytes): [weights 4 WQ bytes, later the quarter sums 4*NT*RP floats (REG0
+  // floats for both) | history 3*NT*ROWS | taps 4*ROWS | scales 64 | sums of squares NT | 256 for the
+  // history loads past its end] floats. The direct-to-LDS
   // copies write it behind the compiler's back, which it must not assume to be unwritten.
   extern __shared__ float bproj_lds[];
   __shared__ int wready[4];
   char* const wl = reinterpret_cast<char*>(bproj_lds);
-  float(*red)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds);  // [4]
-  float(*ring_l)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds + WQ);  // [3]
-  float* cw_l = bproj_lds + WQ + 3 * NT * ROWS;
+  float(*red)[NT][RP] = reinterpret_cast<float(*)[NT][RP]>(bproj_lds);  // [4]
+  float(*ring_l)[NT][ROWS] = reinterpret_cast<float(*)[NT][ROWS]>(bproj_lds + REG0);  // [3]
+  float* cw_l = bproj_lds + REG0 + 3 * NT * ROWS;
   float* s_l = cw_l + 4 * ROWS;
   float* ssq_l = s_l + 64;
   float* spare_l = ssq_l + NT;
@@ -687,8 +688,8 @@ __global__ __launch_bounds__(768) void k_bproj(const BGemmArgs g, const BEpiArgs
   float s1[NF];
 
   if (wave >= 8) {
-    // copy wave q = kq. First the epilogue's small inputs (their count varies; the waits below
-    // count only loads issued after the weights), addresses clamped into range.
+    // copy wave q = kq. First the epilogue's inputs (their count varies; the waits below count only
+    // the weight loads issued later), addresses clamped into range.
     if (kq == 0) {
       __builtin_amdgcn_global_load_lds(e.s + min(row0 + lane, M - 1), s_l, 4, 0, 0);
       __builtin_amdgcn_global_load_lds(e.ssq + min(nb * NT + lane, B - 1), ssq_l, 4, 0, 0);
@@ -696,6 +697,19 @@ __global__ __launch_bounds__(768) void k_bproj(const BGemmArgs g, const BEpiArgs
     for (int i = kq - 1; hist && i >= 0 && i < ROWS * 4 / 64; i += 3) {
       const int idx = 64 * i + lane, rl = idx / 4, q = idx % 4;
       __builtin_amdgcn_global_load_lds(e.conv_w + (size_t)min(row0 + rl, C - 1) * Kc + min(q, Kc - 1), cw_l + 64 * i, 4, 0, 0);
+    }
+    // the history: instruction n takes segments SEGI n .. +SEGI-1 (lane l: segment SEGI n + l / LPS,
+    // channels 4 (l % LPS) .. +3); lanes past the segments stay idle. Slots past the taps, channels
+    // past C and workgroups without history copy weight bytes instead (into slots nothing reads);
+    // instructions past the last segment, into the spare area.
+    for (int m = 0; m < NRW; ++m) {
+      const int n = kq + 4 * m, seg = SEGI * n + lane / LPS, ch = row0 + 4 * (lane % LPS);
+      const int j = seg / NT, bl = seg % NT;
+      const float* src = reinterpret_cast<const float*>(g.W);
+      if (hist && j < Kc - 1 && ch < C)
+        src = e.ring + ((size_t)min(nb * NT + bl, B - 1) * (Kc - 1) + j) * C + ch;
+      float* dst = n < NRI ? &ring_l[0][0][0] + SEGI * ROWS * n : spare_l;
+      if (lane < SEGI * LPS && (n >= NRI || seg < NSEG)) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
     // the K quarter's weights: instruction (chunk c, group gi) fills rows 8 gi .. +7 of the chunk,
     // lane l row 8 gi + l / 8, 16-byte chunk (l % 8) ^ bp_swz(row % 16); rows past M read row M-1
@@ -715,33 +729,18 @@ __global__ __launch_bounds__(768) void k_bproj(const BGemmArgs g, const BEpiArgs
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
       for (int gi = 0; gi < WT; ++gi) copy(c, gi);
-    // the history: instruction n takes segments SEGI n .. +SEGI-1 (lane l: segment SEGI n + l / LPS,
-    // channels 4 (l % LPS) .. +3); lanes past the segments stay idle. Slots past the taps, channels
-    // past C and workgroups without history copy weight bytes instead (into slots nothing reads);
-    // instructions past the last segment, into the spare area.
-    for (int m = 0; m < NRW; ++m) {
-      const int n = kq + 4 * m, seg = SEGI * n + lane / LPS, ch = row0 + 4 * (lane % LPS);
-      const int j = seg / NT, bl = seg % NT;
-      const float* src = reinterpret_cast<const float*>(g.W);
-      if (hist && j < Kc - 1 && ch < C)
-        src = e.ring + ((size_t)min(nb * NT + bl, B - 1) * (Kc - 1) + j) * C + ch;
-      float* dst = n < NRI ? &ring_l[0][0][0] + SEGI * ROWS * n : spare_l;
-      if (lane < SEGI * LPS && (n >= NRI || seg < NSEG)) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-    }
-    // chunk c has landed once at most the loads issued after it remain: the later chunks' and the
-    // history's
+    // chunk c has landed once at most the later chunks' loads remain
     static_assert(CPW <= 4, "");
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       switch (CPW - 1 - c) {
-        case 0: __builtin_amdgcn_s_waitcnt(vm_imm(NRW)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(vm_imm(NRW + WT)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(vm_imm(NRW + 2 * WT)); break;
-        default: __builtin_amdgcn_s_waitcnt(vm_imm(NRW + 3 * WT)); break;
+        case 0: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vm_imm(WT)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vm_imm(2 * WT)); break;
+        default: __builtin_amdgcn_s_waitcnt(vm_imm(3 * WT)); break;
       }
       bp_publish(&wready[kq], c + 1);
     }
-    __builtin_amdgcn_s_waitcnt(vm_imm(0));  // the history has landed too
   } else {
     // buffer loads of the split activations: one VGPR offset, the chunk and k-step offsets in scalars
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -799,13 +798,16 @@ __global__ __launch_bounds__(768) void k_bproj(const BGemmArgs g, const BEpiArgs
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt) {
+        v4f dv;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float d = (float)acc[rt][0][f][v] +
                           fmaf((float)acc[rt][2][f][v], 1.0f / 254.0f, (float)acc[rt][1][f][v]) * (1.0f / 254.0f);
-          red[kq][16 * (f0 + f) + (lane & 15)][16 * rt + 4 * (lane >> 4) + v] = s1[f] * d;
+          dv[v] = s1[f] * d;
         }
+        *reinterpret_cast<v4f*>(&red[kq][16 * (f0 + f) + (lane & 15)][16 * rt + 4 * (lane >> 4)]) = dv;
+      }
   }
   __syncthreads();
 
@@ -1072,10 +1074,11 @@ hipError_t bgemm_bits(const BGemmArgs& a, int mf, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-// staged weights (4 K quarters of cpw chunks x 2 rt load instructions of 1 KB), history, taps,
-// scales, sums of squares
+// staged weights (4 K quarters of cpw chunks x 2 rt load instructions of 1 KB) or the padded quarter
+// sums, history, taps, scales, sums of squares, spare
 constexpr size_t bproj_lds_bytes(int rt, int cpw) {
-  return (size_t)4 * cpw * 2 * rt * 1024 + sizeof(float) * (3 * NT * 16 * rt + 4 * 16 * rt + 64 + NT + 256);
+  return sizeof(float) * ((cpw * 2 * rt * 1024 > 4 * NT * (16 * rt + 4) ? cpw * 2 * rt * 1024 : 4 * NT * (16 * rt + 4)) +
+                          3 * NT * 16 * rt + 4 * 16 * rt + 64 + NT + 256);
 }
 
 template <int RT, int CPW>
