@@ -113,9 +113,11 @@ def test_batched_agrees_with_layer_kernels(monkeypatch):
     assert state_err(Ra.cpu().numpy(), Rb.cpu().numpy()) <= 1e-5
 
 
-def test_batched_rerun_bitwise():
-    """Split-K partial sums are added in a fixed order: two runs are byte-identical."""
-    cfg = BATCHED["b_ragged"]
+@pytest.mark.parametrize("name", ["b_ragged", "b_wide"])
+def test_batched_rerun_bitwise(name):
+    """Split-K partial sums, and the whole-K kernel's K quarters, are added in a fixed order (whatever
+    order the staged weight chunks land in): two runs are byte-identical."""
+    cfg = BATCHED[name]
     layers, stream = gi.generate(cfg)
     outs, states = [], []
     for _ in range(2):
