@@ -29,6 +29,20 @@ def log(*a):
 KERNEL_SOURCES = ("gated_deltanet_layer_dn_amd/csrc/dn_persist.hip", "gated_deltanet_layer_dn_amd/csrc/dn_internal.h")
 
 
+def bench_config(gi, name):
+    """The decode workloads: the named configurations, and the stack's variants."""
+    stack = gi.CONFIGS["stack"]
+    if name == "stack_perkey":  # one decay per key channel
+        return stack.replace(name=name, flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
+    if name == "stack_gates":  # the gates computed on the card
+        return stack.replace(name=name, flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE)
+    if name == "stack_heads48":  # 48 value heads over the 16 key heads (more than the whole-stack kernel takes)
+        return stack.replace(name=name, n_v_heads=48)
+    if name == "stack_dim256":  # heads of 256: 8 key heads and 16 value heads of 256 columns
+        return stack.replace(name=name, n_k_heads=8, d_k=256, n_v_heads=16, d_v=256)
+    return gi.CONFIGS[name]
+
+
 def create_reporting_path(dn, cfg, layers):
     """Create the handle with DN_VERBOSE set and read which execution path the library chose
     from the line it prints on stderr (file descriptor 2)."""
@@ -88,7 +102,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="stack",
-                    choices=["stack", "stack_int4", "stack_perkey", "stack_gates", "layer", "batched", "prefill"])
+                    choices=["stack", "stack_int4", "stack_perkey", "stack_gates", "stack_heads48", "stack_dim256",
+                             "layer", "batched", "prefill"])
     ap.add_argument("--prompt", type=int, default=2048, help="prompt length of --config prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -136,12 +151,7 @@ def main():
 
     if args.config == "prefill":
         return bench_prefill(args, gi, dn, cpu)
-    if args.config == "stack_perkey":  # the stack workload with one decay per key channel
-        cfg = gi.CONFIGS["stack"].replace(name="stack_perkey", flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
-    elif args.config == "stack_gates":  # the stack workload with the gates computed on the card
-        cfg = gi.CONFIGS["stack"].replace(name="stack_gates", flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE)
-    else:
-        cfg = gi.CONFIGS[args.config]
+    cfg = bench_config(gi, args.config)
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     t0 = time.time()
@@ -350,12 +360,8 @@ def cpu_leg(args):
     import oracle as orc
     if args.config == "prefill":
         cfg = gi.CONFIGS["stack"].replace(name="prefill", n_tokens=args.prompt)
-    elif args.config == "stack_perkey":
-        cfg = gi.CONFIGS["stack"].replace(name="stack_perkey", flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
-    elif args.config == "stack_gates":
-        cfg = gi.CONFIGS["stack"].replace(name="stack_gates", flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE)
     else:
-        cfg = gi.CONFIGS[args.config]
+        cfg = bench_config(gi, args.config)
     layers, stream = gi.generate(cfg)
     orc.lib()
     # calibrate on one token, then run a bounded sample of the same workload
