@@ -54,6 +54,7 @@ void free_all(dn_layer* h) {
   dfree(h->ring);
   dfree(h->u);
   dfree(h->y);
+  dfree(h->yssq);
   dfree(h->gal);
   dfree(h->gbe);
   dfree(h->S_alt);
@@ -240,6 +241,8 @@ DN_API int dn_create(const dn_config* cfg, const dn_weights* w, dn_layer** out) 
   ok = ok && hipMalloc(&h->ring, sizeof(float) * (L * h->ring_elems + 1)) == hipSuccess;
   ok = ok && hipMalloc(&h->u, sizeof(float) * B * h->R) == hipSuccess;
   ok = ok && hipMalloc(&h->y, sizeof(float) * B * h->V) == hipSuccess;
+  if (cfg->d_k % 16 == 0 && cfg->d_v % 16 == 0 && cfg->d_k <= 256 && cfg->n_v_heads <= 64)
+    ok = ok && hipMalloc(&h->yssq, sizeof(float) * B * cfg->n_v_heads * (cfg->d_v / 16)) == hipSuccess;
   if (h->gates) {
     ok = ok && hipMalloc(&h->gal, sizeof(float) * B * cfg->n_v_heads) == hipSuccess;
     ok = ok && hipMalloc(&h->gbe, sizeof(float) * B * cfg->n_v_heads) == hipSuccess;
@@ -515,6 +518,7 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     ha.Hk = c.n_k_heads; ha.Hv = c.n_v_heads; ha.dk = c.d_k; ha.dv = c.d_v;
     ha.R = h->R; ha.C = h->C; ha.batch = (int)B;
     ha.eps_l2 = c.eps_l2; ha.eps_rms = c.eps_rms; ha.q_scale = c.q_scale;
+    ha.ssq = h->yssq;  // the column-split kernel when the shape allows it
     if (dn::launch_head(ha, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
 
@@ -524,6 +528,9 @@ DN_API int dn_step(dn_layer* h, const float* x, const float* alpha, const float*
     go.x_stride = h->V; go.out_stride = (int)D;
     go.prenorm = 0; go.eps = 0.f;
     go.conv_w = nullptr; go.ring = nullptr; go.C = 0; go.K = 0;
+    if (h->yssq) {  // the heads' 1/rms, from the column blocks' sums of squares
+      go.head_ssq = h->yssq; go.head_dim = c.d_v; go.head_nb = c.d_v / 16; go.head_eps = c.eps_rms;
+    }
     if (dn::launch_gemv(go, c.weight_bits, st) != hipSuccess) return fail(h, DN_E_DEVICE);
     if (h->sync_debug && hipStreamSynchronize(st) != hipSuccess) return fail(h, DN_E_DEVICE);
   }

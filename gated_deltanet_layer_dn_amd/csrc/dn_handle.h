@@ -30,6 +30,7 @@ struct dn_layer {
   float* ring = nullptr;  // [L][B][K-1][C], oldest first
   float* u = nullptr;     // [B][R] scratch: post-conv q|k|v, raw z
   float* y = nullptr;     // [B][V] scratch: gated RMSNorm output
+  float* yssq = nullptr;  // [B][Hv][dv/16] scratch: the readout's partial sums of squares
   // whole-stack kernel (single sequence, 128 x 128 state tiles)
   bool persist = false;
   int nwg = 0;

@@ -23,6 +23,11 @@ struct GemvArgs {
   const float* conv_w;  // [C][K]
   float* ring;          // [B][K-1][C], oldest first
   int C, K;
+  // when set, x is a gated readout still to be scaled per head of head_dim columns by
+  // 1/sqrt(sum of head_ssq [B][cols/head_dim][head_nb] / head_dim + head_eps)
+  const float* head_ssq;
+  int head_dim, head_nb;
+  float head_eps;
 };
 
 // One value head per workgroup: L2 norms, decay, delta rule, readout, gated RMSNorm.
@@ -36,6 +41,9 @@ struct HeadArgs {
   int Hk, Hv, dk, dv, R, C, batch;
   int alpha_per_key;    // 1: key row i of head h decays by alpha[b][h][i]
   float eps_l2, eps_rms, q_scale;
+  // when set (dk, dv multiples of 16): the column-split kernel, one workgroup per 16 value columns;
+  // y gets w o silu(z) without the head's 1/rms and ssq [B][Hv][dv/16] the blocks' sums of o^2
+  float* ssq;
 };
 
 hipError_t launch_gemv(const GemvArgs& a, int bits, hipStream_t st);

@@ -76,13 +76,28 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   __shared__ float redf[4];
   __shared__ int redi[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float hinv[64];
   const int b = blockIdx.y;
   const float* xb = a.x + (size_t)b * a.x_stride;
+
+  // 0. with head_ssq: x is a gated readout whose per-head RMS factors are still to be applied;
+  // head h's factor from its head_nb partial sums of squares
+  const bool hn = a.head_ssq != nullptr;
+  if (hn) {
+    for (int h = tid; h < a.cols / a.head_dim; h += 256) {
+      const float* p = a.head_ssq + ((size_t)b * (a.cols / a.head_dim) + h) * a.head_nb;
+      float sp = 0.f;
+      for (int k = 0; k < a.head_nb; ++k) sp += p[k];
+      hinv[h] = rsqrtf(sp / (float)a.head_dim + a.head_eps);
+    }
+    __syncthreads();
+  }
+  auto xv = [&](int c) { return hn ? xb[c] * hinv[c / a.head_dim] : xb[c]; };
 
   // 1. statistics of x: sum of squares (pre-norm) and max |x| (split scale)
   float ss = 0.f, mx = 0.f;
   for (int c = tid; c < a.cols; c += 256) {
-    const float v = xb[c];
+    const float v = xv(c);
     ss = fmaf(v, v, ss);
     mx = fmaxf(mx, fabsf(v));
   }
@@ -100,7 +115,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   int8_t* xl8 = xm8 + a.cols;
   int sum_h = 0, sum_m = 0, sum_l = 0;
   for (int c = tid; c < a.cols; c += 256) {
-    const float v = xb[c] * scale;
+    const float v = xv(c) * scale;
     const float h = fminf(fmaxf(rintf(v * inv1), -127.f), 127.f);
     const float r1 = fmaf(-s1, h, v);
     const float m = fminf(fmaxf(rintf(r1 * inv2), -127.f), 127.f);
@@ -311,6 +326,95 @@ __global__ __launch_bounds__(256) void k_head(const HeadArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Value head, split by columns: one workgroup per (head, block of 16 value columns, sequence), so
+// that a single sequence's states stream through many compute units (one workgroup per head
+// leaves most of them idle). The columns of a head's state are independent but for the gated
+// RMSNorm, which needs the head's sum of o^2: each block writes its columns' w o silu(z) and its
+// partial sum, and the out_proj GEMV applies the head's 1/rms when it stages its input.
+// Thread t: column 16 cb + t % 16, key rows t / 16 + 16 m.
+// ---------------------------------------------------------------------------------------------
+template <int DKMAX>
+__global__ __launch_bounds__(256) void k_head_cols(const HeadArgs a) {
+  constexpr int RPT = DKMAX / 16;  // key rows per thread
+  __shared__ float qs[DKMAX], ks[DKMAX], als[DKMAX];
+  __shared__ float red[16][17];
+  __shared__ double redd[4];
+  const int tid = threadIdx.x, jl = tid & 15, rg = tid >> 4;
+  const int nb = a.dv / 16, h = blockIdx.x / nb, cb = blockIdx.x % nb, b = blockIdx.y;
+  const int g = h / (a.Hv / a.Hk);
+  const int dk = a.dk, dv = a.dv, QK = a.Hk * dk, j = 16 * cb + jl;
+  const float* ub = a.u + (size_t)b * a.R;
+  const float* q = ub + (size_t)g * dk;
+  const float* k = ub + QK + (size_t)g * dk;
+  const float* ah = a.alpha + ((size_t)b * a.Hv + h) * (a.alpha_per_key ? dk : 1);
+
+  // the state block's loads first (their latency under the norms): rows rg + 16 m, column j
+  float* S = a.S + ((size_t)b * a.Hv + h) * dk * dv + j;
+  float s[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = rg + 16 * m;
+    s[m] = i < dk ? S[(size_t)i * dv] : 0.f;
+  }
+  // L2 norms in double, eps inside the sqrt
+  double sq = 0.0, sk = 0.0;
+  for (int i = tid; i < dk; i += 256) {
+    const float qv = q[i], kv = k[i];
+    qs[i] = qv;
+    ks[i] = kv;
+    als[i] = ah[a.alpha_per_key ? i : 0];
+    sq += (double)qv * qv;
+    sk += (double)kv * kv;
+  }
+  sq = block_sum(sq, redd);
+  sk = block_sum(sk, redd);
+  const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
+  const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
+
+  // decay; (decayed S)^T k^ of column j over this thread's rows, then over the row groups
+  float kvp = 0.f;
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = rg + 16 * m;
+    if (i < dk) {
+      s[m] *= als[i];
+      kvp = fmaf(s[m], ks[i] * kn, kvp);
+    }
+  }
+  red[rg][jl] = kvp;
+  __syncthreads();
+  float kv = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) kv += red[r][jl];
+  const float delta = a.beta[(size_t)b * a.Hv + h] * (ub[2 * QK + (size_t)h * dv + j] - kv);
+  // delta rule and the readout over the updated state
+  float op = 0.f;
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = rg + 16 * m;
+    if (i < dk) {
+      s[m] = fmaf(ks[i] * kn, delta, s[m]);
+      S[(size_t)i * dv] = s[m];
+      op = fmaf(s[m], qs[i] * qn, op);
+    }
+  }
+  __syncthreads();  // every read of red is done
+  red[rg][jl] = op;
+  __syncthreads();
+  if (tid < 16) {
+    float o = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o += red[r][tid];
+    const float z = ub[a.C + (size_t)h * dv + j];
+    a.y[(size_t)b * a.Hv * dv + (size_t)h * dv + j] = a.norm_w[j] * o * silu(z);
+    float o2 = o * o;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) o2 += __shfl_xor(o2, off, 16);
+    if (tid == 0) a.ssq[((size_t)b * a.Hv + h) * nb + cb] = o2;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
 template <int BITS, int NCH, int RB>
@@ -345,7 +449,20 @@ static hipError_t go_head(const HeadArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int DKMAX>
+static hipError_t go_head_cols(const HeadArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_head_cols<DKMAX>), dim3(a.Hv * (a.dv / 16), a.batch), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_head(const HeadArgs& a, hipStream_t st) {
+  if (a.ssq) {
+    if (a.dv % 16 || a.dk % 16) return hipErrorInvalidValue;
+    if (a.dk <= 64) return go_head_cols<64>(a, st);
+    if (a.dk <= 128) return go_head_cols<128>(a, st);
+    if (a.dk <= 256) return go_head_cols<256>(a, st);
+    return hipErrorInvalidValue;
+  }
   if (a.dk <= 16) return go_head<16>(a, st);
   if (a.dk <= 32) return go_head<32>(a, st);
   if (a.dk <= 64) return go_head<64>(a, st);
