@@ -73,7 +73,6 @@ __device__ __forceinline__ int x_pos(int c) {
 template <int BITS, int NCH, int RB>
 __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   extern __shared__ int smem[];  // staged x: three int8 terms, [cols] bytes each
-  __shared__ float redf[4];
   __shared__ int redi[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float hinv[64];
@@ -94,40 +93,62 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   }
   auto xv = [&](int c) { return hn ? xb[c] * hinv[c / a.head_dim] : xb[c]; };
 
-  // 1. statistics of x: sum of squares (pre-norm) and max |x| (split scale)
+  // 1. x into registers (XR values per thread, one read), its sum of squares (pre-norm) and
+  // max |x| (split scale), reduced together
+  constexpr int XR = (BITS == 8 ? 4 : 8) * NCH;  // cols <= 256 XR
+  __shared__ float red2[4][2];
+  float xr[XR];
   float ss = 0.f, mx = 0.f;
-  for (int c = tid; c < a.cols; c += 256) {
-    const float v = xv(c);
-    ss = fmaf(v, v, ss);
-    mx = fmaxf(mx, fabsf(v));
+#pragma unroll
+  for (int m = 0; m < XR; ++m) {
+    const int c = tid + 256 * m;
+    xr[m] = c < a.cols ? xv(c) : 0.f;
+    ss = fmaf(xr[m], xr[m], ss);
+    mx = fmaxf(mx, fabsf(xr[m]));
   }
-  ss = block_sum(ss, redf);
-  mx = block_max(mx, redf);
+  ss = wave_sum(ss);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    red2[wave][0] = ss;
+    red2[wave][1] = mx;
+  }
+  __syncthreads();
+  ss = (red2[0][0] + red2[1][0]) + (red2[2][0] + red2[3][0]);
+  mx = fmaxf(fmaxf(red2[0][1], red2[1][1]), fmaxf(red2[2][1], red2[3][1]));
   const float scale = a.prenorm ? rsqrtf(ss / (float)a.cols + a.eps) : 1.0f;
   float s1 = mx * scale * (1.0f / 127.0f);
   if (!(s1 > 0.f)) s1 = 1.0f;
   const float inv1 = 1.0f / s1, s2 = s1 * (1.0f / 254.0f), inv2 = 1.0f / s2;
   const float s3 = s2 * (1.0f / 254.0f), inv3 = 1.0f / s3;
 
-  // 2. split x into three int8 terms, staged in LDS
+  // 2. split x into three int8 terms, staged in LDS. Each term rounds by adding 1.5 * 2^23 to the
+  // clamped quotient (ties to even, as rintf): the integer lands in the low mantissa bits, whose
+  // low byte is the int8 term.
   int8_t* xh8 = reinterpret_cast<int8_t*>(smem);
   int8_t* xm8 = xh8 + a.cols;
   int8_t* xl8 = xm8 + a.cols;
+  constexpr float BIAS = 12582912.0f;
   int sum_h = 0, sum_m = 0, sum_l = 0;
-  for (int c = tid; c < a.cols; c += 256) {
-    const float v = xv(c) * scale;
-    const float h = fminf(fmaxf(rintf(v * inv1), -127.f), 127.f);
-    const float r1 = fmaf(-s1, h, v);
-    const float m = fminf(fmaxf(rintf(r1 * inv2), -127.f), 127.f);
-    const float r2 = fmaf(-s2, m, r1);
-    const float l = fminf(fmaxf(rintf(r2 * inv3), -127.f), 127.f);
-    const int p = x_pos<BITS>(c);
-    xh8[p] = (int8_t)h;
-    xm8[p] = (int8_t)m;
-    xl8[p] = (int8_t)l;
-    sum_h += (int)h;
-    sum_m += (int)m;
-    sum_l += (int)l;
+#pragma unroll
+  for (int m = 0; m < XR; ++m) {
+    const int c = tid + 256 * m;
+    if (c < a.cols) {
+      const float v = xr[m] * scale;
+      const float th = __builtin_amdgcn_fmed3f(v * inv1, -127.f, 127.f) + BIAS, h = th - BIAS;
+      const float r1 = fmaf(-s1, h, v);
+      const float tm = __builtin_amdgcn_fmed3f(r1 * inv2, -127.f, 127.f) + BIAS, mm = tm - BIAS;
+      const float r2 = fmaf(-s2, mm, r1);
+      const float tl = __builtin_amdgcn_fmed3f(r2 * inv3, -127.f, 127.f) + BIAS;
+      const int p = x_pos<BITS>(c);
+      xh8[p] = (int8_t)__float_as_uint(th);
+      xm8[p] = (int8_t)__float_as_uint(tm);
+      xl8[p] = (int8_t)__float_as_uint(tl);
+      if (BITS == 4) {
+        sum_h += (int)h;
+        sum_m += (int)mm;
+        sum_l += (int)(tl - BIAS);
+      }
+    }
   }
   if (BITS == 4) {
     sum_h = block_sum(sum_h, redi);
@@ -440,6 +461,8 @@ static hipError_t gemv_bits(const GemvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemv(const GemvArgs& a, int bits, hipStream_t st) {
+  // the input row is held in registers, at most 256 (4 NCH or, 4-bit, 8 NCH) columns per thread
+  if (a.cols > 16384) return hipErrorInvalidValue;
   return bits == 8 ? gemv_bits<8>(a, st) : gemv_bits<4>(a, st);
 }
 
