@@ -107,8 +107,9 @@ __device__ __forceinline__ void ll_store(uint64_t* p, float v, unsigned tag) {
   const uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
   __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t ll_load(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t ll_load(const __attribute__((address_space(1))) uint64_t* p) {
+  return __hip_atomic_load(const_cast<__attribute__((address_space(1))) uint64_t*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ unsigned coherent_load_u32(const unsigned* p) {
   return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -131,6 +132,15 @@ __device__ __forceinline__ void st_store(unsigned* p, float v, unsigned tag) {
 }
 __device__ __forceinline__ bool st_tagged(const v4u& q, unsigned t) {
   return ((q[0] & 3u) == t) & ((q[1] & 3u) == t) & ((q[2] & 3u) == t) & ((q[3] & 3u) == t);
+}
+// Global-address-space view of a device pointer. Pointers read from the per-layer table (or passed
+// through an empty asm statement) are generic to the compiler, which then emits flat loads; a flat
+// load counts on the LDS counter as well as the vector-memory one, so every LDS wait of the wave
+// (lgkmcnt(0), the workgroup barriers' included) would also wait for it. Through this view the
+// weight prefetches and the in_proj polls are global loads, which LDS waits do not wait for.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
 }
 // Buffer resource over `bytes` bytes at p (raw, untyped 32-bit accesses).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, unsigned bytes) {
@@ -352,7 +362,7 @@ __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&
   pend &= (1u << nvalid) - 1u;
   unsigned it = 0;
   while (__any(pend != 0)) {
-    const uint64_t* b = base;
+    const __attribute__((address_space(1))) uint64_t* b = gmem(base);
     asm volatile("" : "+v"(b));
     uint64_t w[N];
 #pragma unroll
@@ -475,7 +485,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
         const int n = (part == 0 ? i : i - EARLY) * NCHA + k, ntot = (part == 0 ? EARLY : RA - EARLY) * NCHA;
         if (n >= DN_PREFETCH_INFLIGHT && n < ntot - DN_PREFETCH_TAIL) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
         if (r < g.a_row_end)
-          wa[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_in) + lane + 64 * k);
+          wa[i][k] = __builtin_nontemporal_load(gmem(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_in) + lane + 64 * k));
         else
           wa[i][k] = v4i{0, 0, 0, 0};
       }
@@ -483,10 +493,10 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
     if (part != 0) return;
     const int r = g.a_row0 + lane;
     if (lane < RA && r < g.a_row_end) {
-      ra_s = W.s_in[r];
+      ra_s = *gmem(W.s_in + r);
       if (r < C) {
-        const float* cwp = W.conv_w + (size_t)r * K;
-        const float* rg = ring_in + (size_t)l * (K - 1) * C + r;
+        const auto cwp = gmem(W.conv_w + (size_t)r * K);
+        const auto rg = gmem(ring_in + (size_t)l * (K - 1) * C + r);
 #pragma unroll
         for (int j = 0; j < 4; ++j) ra_cw[j] = j < K ? cwp[j] : 0.f;
 #pragma unroll
@@ -504,13 +514,13 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       for (int k = 0; k < NCHC; ++k) {
         if ((i * NCHC + k) >= DN_PREFETCH_INFLIGHT) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
         if (r < g.c_row_end)
-          wc[i][k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_out) + lane + 64 * k);
+          wc[i][k] = __builtin_nontemporal_load(gmem(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_out) + lane + 64 * k));
         else
           wc[i][k] = v4i{0, 0, 0, 0};
       }
     }
     const int r = g.c_row0 + lane;
-    if (lane < RC && r < g.c_row_end) rc_s = W.s_out[r];
+    if (lane < RC && r < g.c_row_end) rc_s = *gmem(W.s_out + r);
   };
 
   // Phase B's state slice: compute wave w moves chunk w (lane's 4 floats at rows 32p + 4w, column
@@ -702,8 +712,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
     // the per-layer gates and norm weights this workgroup needs, fetched once per launch
     for (int l = lane; l < a.L; l += 64) {
       if constexpr (GT) {
-        sm.gate[l][0] = a.layers[l].a_log[g.bh];
-        sm.gate[l][1] = a.layers[l].a_bias[g.bh];
+        sm.gate[l][0] = *gmem(a.layers[l].a_log + g.bh);
+        sm.gate[l][1] = *gmem(a.layers[l].a_bias + g.bh);
       } else {
         sm.gate[l][0] = PK ? 0.f : a.alpha[(size_t)l * Hv + g.bh];
         sm.gate[l][1] = a.beta[(size_t)l * Hv + g.bh];
@@ -730,7 +740,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = min(e0 + 64 * u, a.L * CB - 1);
-        v[u] = a.layers[e / CB].norm_w[g.bcb * CB + e % CB];
+        v[u] = *gmem(a.layers[e / CB].norm_w + g.bcb * CB + e % CB);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -757,7 +767,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       for (int k = 0; k < NCHA; ++k)
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const v4i*>(wr) + lane + 64 * k, &sm.gwl[j][k][0], 16, 0, 0);
     }
-    gsc = lane < 2 ? a.layers[l].s_in[a.R + lane * Hv + g.bh] : 0.f;
+    gsc = lane < 2 ? *gmem(a.layers[l].s_in + a.R + lane * Hv + g.bh) : 0.f;
   };
   if (runs_gate) load_g(0);
 
