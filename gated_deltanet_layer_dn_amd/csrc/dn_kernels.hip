@@ -37,6 +37,15 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroup barrier that waits only for the wave's LDS accesses (__syncthreads() would also wait
+// for every outstanding global load, the weight rows requested ahead included).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Reductions over a 256-thread workgroup (4 waves). `buf` holds 4 elements; every thread
 // gets the result. Fixed order, so results are run-to-run identical.
 template <typename T>
@@ -73,36 +82,74 @@ __device__ __forceinline__ int x_pos(int c) {
 template <int BITS, int NCH, int RB>
 __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
   extern __shared__ int smem[];  // staged x: three int8 terms, [cols] bytes each
-  __shared__ int redi[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float hinv[64];
   const int b = blockIdx.y;
   const float* xb = a.x + (size_t)b * a.x_stride;
 
+  // The input row (and, for a gated readout, its heads' partial sums of squares) is requested
+  // first, then the wave's first RB weight rows: vector loads complete in order, so the staging
+  // below waits only for the input while the weight rows' HBM latency overlaps it (its barriers
+  // wait only for LDS).
+  const int nchunk = (BITS == 8 ? a.cols : a.cols / 2) >> 4;
+  const v4i* W = reinterpret_cast<const v4i*>(a.W);
+  v4i w[RB][NCH];
+  // (branch-free: an out-of-range piece reads piece 0 and is zeroed, so the compiler can count
+  // the loads in flight exactly instead of waiting for all of them at the next use of any load)
+  auto load_rows = [&](int r0) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const int c = lane + 64 * k, r = r0 + i;
+        const bool in = r < a.rows && c < nchunk;
+        const v4i v = __builtin_nontemporal_load(&W[in ? (size_t)r * nchunk + c : 0]);
+        w[i][k] = in ? v : v4i{0, 0, 0, 0};
+      }
+  };
   // 0. with head_ssq: x is a gated readout whose per-head RMS factors are still to be applied;
-  // head h's factor from its head_nb partial sums of squares
+  // head h's factor from its head_nb (at most HNB) partial sums of squares, thread h
+  constexpr int HNB = 16;
   const bool hn = a.head_ssq != nullptr;
-  if (hn) {
-    for (int h = tid; h < a.cols / a.head_dim; h += 256) {
-      const float* p = a.head_ssq + ((size_t)b * (a.cols / a.head_dim) + h) * a.head_nb;
-      float sp = 0.f;
-      for (int k = 0; k < a.head_nb; ++k) sp += p[k];
-      hinv[h] = rsqrtf(sp / (float)a.head_dim + a.head_eps);
-    }
-    __syncthreads();
+  const int nheads = hn ? a.cols / a.head_dim : 0;
+  float hp[HNB];
+  {
+    // (issued unconditionally, from x itself when there are no partials, and masked where they are
+    // summed, so that no wait for them is placed before the loads below)
+    const int nb = hn ? a.head_nb : 1;
+    const float* p = hn ? a.head_ssq + ((size_t)b * nheads + (tid < nheads ? tid : 0)) * a.head_nb : xb;
+#pragma unroll
+    for (int k = 0; k < HNB; ++k) hp[k] = p[k < nb ? k : 0];
   }
-  auto xv = [&](int c) { return hn ? xb[c] * hinv[c / a.head_dim] : xb[c]; };
-
   // 1. x into registers (XR values per thread, one read), its sum of squares (pre-norm) and
   // max |x| (split scale), reduced together
   constexpr int XR = (BITS == 8 ? 4 : 8) * NCH;  // cols <= 256 XR
   __shared__ float red2[4][2];
   float xr[XR];
-  float ss = 0.f, mx = 0.f;
 #pragma unroll
   for (int m = 0; m < XR; ++m) {
     const int c = tid + 256 * m;
-    xr[m] = c < a.cols ? xv(c) : 0.f;
+    const float v = xb[c < a.cols ? c : 0];
+    xr[m] = c < a.cols ? v : 0.f;
+  }
+  load_rows((blockIdx.x * 4 + wave) * RB);
+  if (hn) {
+    if (tid < nheads) {
+      float sp = 0.f;
+#pragma unroll
+      for (int k = 0; k < HNB; ++k) sp += k < a.head_nb ? hp[k] : 0.f;
+      hinv[tid] = rsqrtf(sp / (float)a.head_dim + a.head_eps);
+    }
+    lds_sync();
+#pragma unroll
+    for (int m = 0; m < XR; ++m) {
+      const int c = tid + 256 * m;
+      if (c < a.cols) xr[m] *= hinv[c / a.head_dim];
+    }
+  }
+  float ss = 0.f, mx = 0.f;
+#pragma unroll
+  for (int m = 0; m < XR; ++m) {
     ss = fmaf(xr[m], xr[m], ss);
     mx = fmaxf(mx, fabsf(xr[m]));
   }
@@ -112,7 +159,7 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
     red2[wave][0] = ss;
     red2[wave][1] = mx;
   }
-  __syncthreads();
+  lds_sync();
   ss = (red2[0][0] + red2[1][0]) + (red2[2][0] + red2[3][0]);
   mx = fmaxf(fmaxf(red2[0][1], red2[1][1]), fmaxf(red2[2][1], red2[3][1]));
   const float scale = a.prenorm ? rsqrtf(ss / (float)a.cols + a.eps) : 1.0f;
@@ -151,29 +198,31 @@ __global__ __launch_bounds__(256) void k_gemv(const GemvArgs a) {
     }
   }
   if (BITS == 4) {
-    sum_h = block_sum(sum_h, redi);
-    sum_m = block_sum(sum_m, redi);
-    sum_l = block_sum(sum_l, redi);
+    // three block sums in one pass over LDS
+    sum_h = wave_sum(sum_h);
+    sum_m = wave_sum(sum_m);
+    sum_l = wave_sum(sum_l);
+    __shared__ int redh[3][4];
+    if (lane == 0) {
+      redh[0][wave] = sum_h;
+      redh[1][wave] = sum_m;
+      redh[2][wave] = sum_l;
+    }
+    lds_sync();
+    sum_h = (redh[0][0] + redh[0][1]) + (redh[0][2] + redh[0][3]);
+    sum_m = (redh[1][0] + redh[1][1]) + (redh[1][2] + redh[1][3]);
+    sum_l = (redh[2][0] + redh[2][1]) + (redh[2][2] + redh[2][3]);
+  } else {
+    lds_sync();
   }
-  __syncthreads();
 
-  // 3. stream rows
-  const int nchunk = (BITS == 8 ? a.cols : a.cols / 2) >> 4;
-  const v4i* W = reinterpret_cast<const v4i*>(a.W);
+  // 3. stream rows (the first RB are in flight already)
   const v4i* XH = reinterpret_cast<const v4i*>(xh8);
   const v4i* XM = reinterpret_cast<const v4i*>(xm8);
   const v4i* XL = reinterpret_cast<const v4i*>(xl8);
   const int wave_stride = gridDim.x * 4 * RB;
   for (int r0 = (blockIdx.x * 4 + wave) * RB; r0 < a.rows; r0 += wave_stride) {
-    v4i w[RB][NCH];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-      for (int k = 0; k < NCH; ++k) {
-        const int c = lane + 64 * k, r = r0 + i;
-        if (r < a.rows && c < nchunk) w[i][k] = __builtin_nontemporal_load(&W[(size_t)r * nchunk + c]);
-        else w[i][k] = v4i{0, 0, 0, 0};
-      }
+    if (r0 != (blockIdx.x * 4 + wave) * RB) load_rows(r0);
     int ah[RB], am[RB], al[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) ah[i] = am[i] = al[i] = 0;
@@ -461,8 +510,10 @@ static hipError_t gemv_bits(const GemvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemv(const GemvArgs& a, int bits, hipStream_t st) {
-  // the input row is held in registers, at most 256 (4 NCH or, 4-bit, 8 NCH) columns per thread
+  // the input row is held in registers, at most 256 (4 NCH or, 4-bit, 8 NCH) columns per thread;
+  // a gated readout's head factors come from at most 16 partial sums for each of at most 64 heads
   if (a.cols > 16384) return hipErrorInvalidValue;
+  if (a.head_ssq && (a.head_nb > 16 || a.head_dim < 1 || a.cols / a.head_dim > 64)) return hipErrorInvalidValue;
   return bits == 8 ? gemv_bits<8>(a, st) : gemv_bits<4>(a, st);
 }
 
