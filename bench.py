@@ -111,6 +111,8 @@ def main():
                     help="only run a plain 256 MiB device copy 10 times (reference for the HBM byte counters)")
     ap.add_argument("--ceiling", action="store_true",
                     help="only measure the read-stream and read-modify-write ceilings of the device (libdn_probe) and print them")
+    ap.add_argument("--exchange", action="store_true",
+                    help="only measure the latency of hand-offs between workgroups (libdn_probe) and print it")
     ap.add_argument("--cpu-leg", type=int, default=0, metavar="THREADS",
                     help=argparse.SUPPRESS)  # internal: the oracle sample, run in a child process
     args = ap.parse_args()
@@ -126,7 +128,7 @@ def main():
 
     # the CPU baseline first, in child processes that never touch the GPU (OpenMP settings are
     # read when the oracle's library loads)
-    cpu = None if args.no_cpu_baseline or args.ceiling or args.copy_calibration else cpu_baseline(args)
+    cpu = None if args.no_cpu_baseline or args.ceiling or args.copy_calibration or args.exchange else cpu_baseline(args)
 
     import numpy as np
     import torch
@@ -134,6 +136,10 @@ def main():
     if args.ceiling:
         print(json.dumps(read_ceiling()), flush=True)
         print(json.dumps(rmw_ceiling()), flush=True)
+        return
+
+    if args.exchange:
+        print(json.dumps(exchange_latency()), flush=True)
         return
 
     if args.copy_calibration:
@@ -340,6 +346,58 @@ def rmw_ceiling(gib: int = 2, reps: int = 4):
     del buf
     return {"rmw_ceiling_gbs": round(best, 1), "bytes": 2 * nbytes, "blocks": shape[0], "pieces_in_flight": shape[1],
             "frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
+
+
+def exchange_latency(rounds: int = 2000):
+    """What a hand-off between workgroups costs on this device (libdn_probe's dn_probe_exchange, 256
+    workgroups of 768 threads, device-coherent polls as in the whole-stack kernel): a one-word ping
+    between workgroup 0 and workgroup 8 (the same XCD under the dispatcher's round-robin placement)
+    or 1 (another XCD), and a 256-way all-gather of 2048 and 4096 words; each with the device
+    otherwise quiet and with eight waves per compute unit streaming reads at 3 loads in flight per
+    lane, as the weight prefetch of the whole-stack kernel does. Microseconds: one way for the ping,
+    per round (median and slowest workgroup) for the all-gather."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_layer_dn_amd as dn
+    lib = ctypes.CDLL(dn.PROBE_LIB_PATH)
+    lib.dn_probe_exchange.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.dn_probe_exchange.restype = ctypes.c_int
+    nwg = torch.cuda.get_device_properties(0).multi_processor_count
+    words = torch.zeros(2 * 8 * 4096, dtype=torch.int32, device="cuda:0")
+    sbytes = 1 << 30
+    stream_buf = torch.ones(sbytes // 4, dtype=torch.float32, device="cuda:0")
+    ticks = torch.zeros(nwg, dtype=torch.int64, device="cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(nwg * 8, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+
+    def run(mode, arg, sif):
+        words.zero_()
+        ticks.zero_()
+        err.zero_()
+        torch.cuda.synchronize()
+        rc = lib.dn_probe_exchange(mode, arg, rounds, sif, words.data_ptr(), words.numel() * 4, stream_buf.data_ptr(),
+                                   sbytes, ticks.data_ptr(), err.data_ptr(), sink.data_ptr(), nwg, st.cuda_stream)
+        torch.cuda.synchronize()
+        assert rc == 0, rc
+        if int(err.item()) != 0:
+            return None  # a bounded wait ran out (the grid was not resident at once)
+        t = ticks.cpu().numpy().astype(np.float64) * 0.01  # 100 MHz ticks -> us
+        if mode == 0:
+            return round(float(t[0]) / (2 * rounds), 3)
+        return {"median": round(float(np.median(t)) / rounds, 3), "slowest": round(float(t.max()) / rounds, 3)}
+
+    out = {"workgroups": nwg, "rounds": rounds}
+    for sif, tag in ((0, "quiet"), (3, "streaming")):
+        out[tag] = {"ping_same_xcd_us": run(0, 8, sif), "ping_other_xcd_us": run(0, 1, sif),
+                    "allgather_2048_us": run(1, 2048, sif), "allgather_4096_us": run(1, 4096, sif)}
+    del stream_buf
+    return out
 
 
 def cpu_model() -> str:

@@ -56,7 +56,7 @@ def test_prefill_library_exports_exactly_its_declared_calls(built):
 def test_probe_library_exports_exactly_its_declared_calls(built):
     probe = os.path.join(PKG, "libdn_probe.so")
     declared = _declared(os.path.join(ROOT, "include", "dn_probe.h"))
-    assert declared == {"dn_probe_read_stream", "dn_probe_rmw_stream"}
+    assert declared == {"dn_probe_read_stream", "dn_probe_rmw_stream", "dn_probe_exchange"}
     assert _exports(probe) == declared
 
 
