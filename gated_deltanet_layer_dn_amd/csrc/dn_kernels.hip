@@ -497,14 +497,26 @@ static hipError_t go_gemv(const GemvArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// rows per wave (RB) by 16-byte chunks per lane and row (NCH): 8 KiB of weights in flight per wave
+// for rows of up to 2048 and 4096 bytes (measured against 16 KiB: 48-value-head stack 915 -> 871 us per
+// token, heads of 256 836 -> 756 us; a row is reduced by one wave either way, so results are the same)
+#ifndef DN_GEMV_RB2
+#define DN_GEMV_RB2 4
+#endif
+#ifndef DN_GEMV_RB4
+#define DN_GEMV_RB4 2
+#endif
+#ifndef DN_GEMV_RB8
+#define DN_GEMV_RB8 2
+#endif
 template <int BITS>
 static hipError_t gemv_bits(const GemvArgs& a, hipStream_t st) {
   const int nchunk = (BITS == 8 ? a.cols : a.cols / 2) >> 4;
   const int nch = (nchunk + 63) / 64;
   if (nch <= 1) return go_gemv<BITS, 1, 8>(a, st);
-  if (nch <= 2) return go_gemv<BITS, 2, 8>(a, st);
-  if (nch <= 4) return go_gemv<BITS, 4, 4>(a, st);
-  if (nch <= 8) return go_gemv<BITS, 8, 2>(a, st);
+  if (nch <= 2) return go_gemv<BITS, 2, DN_GEMV_RB2>(a, st);
+  if (nch <= 4) return go_gemv<BITS, 4, DN_GEMV_RB4>(a, st);
+  if (nch <= 8) return go_gemv<BITS, 8, DN_GEMV_RB8>(a, st);
   if (nch <= 16) return go_gemv<BITS, 16, 1>(a, st);
   return hipErrorInvalidValue;
 }
