@@ -154,7 +154,7 @@ int setup_persist(dn_layer* h) {
   ok = ok && hipMalloc(&h->X, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
   const size_t u_words = h->R + (h->gates ? 2 * c.n_v_heads : 0);
   ok = ok && hipMalloc(&h->U, sizeof(uint64_t) * u_words) == hipSuccess;
-  ok = ok && hipMalloc(&h->G, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMalloc(&h->G, sizeof(unsigned) * 8 * (h->V + 512)) == hipSuccess;
   ok = ok && hipMalloc(&h->ctl, sizeof(dn::Ctl)) == hipSuccess;
   ok = ok && hipMalloc(&h->stage, sizeof(float) * L * h->s_elems) == hipSuccess;
   ok = ok && hipHostMalloc(&h->err_host, sizeof(unsigned), hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
@@ -182,7 +182,7 @@ int setup_persist(dn_layer* h) {
   ok = hipMemcpy(h->d_layers, lw.data(), sizeof(dn::LayerW) * L, hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemset(h->X, 0, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
   ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * u_words) == hipSuccess;
-  ok = ok && hipMemset(h->G, 0, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMemset(h->G, 0, sizeof(unsigned) * 8 * (h->V + 512)) == hipSuccess;
   ok = ok && hipMemcpy(h->ctl, &ctl0, sizeof(ctl0), hipMemcpyHostToDevice) == hipSuccess;
   if (!ok) return DN_E_DEVICE;
   *h->err_host = 0;
@@ -200,7 +200,7 @@ int reset_handoff(dn_layer* h) {
   const dn::Ctl ctl0{1u, 0u, 0u, 0u};
   bool ok = hipMemset(h->X, 0, sizeof(unsigned) * 8 * (c.d_model)) == hipSuccess;
   ok = ok && hipMemset(h->U, 0, sizeof(uint64_t) * u_words) == hipSuccess;
-  ok = ok && hipMemset(h->G, 0, sizeof(unsigned) * 8 * (h->V + 256)) == hipSuccess;
+  ok = ok && hipMemset(h->G, 0, sizeof(unsigned) * 8 * (h->V + 512)) == hipSuccess;
   ok = ok && hipMemcpy(h->ctl, &ctl0, sizeof(ctl0), hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   if (!ok) return DN_E_DEVICE;

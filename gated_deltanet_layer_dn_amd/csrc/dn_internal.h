@@ -283,7 +283,7 @@ struct PersistArgs {
   float* out;            // [L][D]
   unsigned* X;           // [8][D]  layer output, self-tagged 32-bit words, one copy per XCD
   uint64_t* U;           // [R (+ 2 Hv)]  tagged in_proj output (post-conv q|k|v, raw z, raw gate rows)
-  unsigned* G;           // [8][V + 256] gated readout and partial sums of squares of the readout,
+  unsigned* G;           // [8][V + 512] gated readout and partial sums of squares of the readout,
                          // self-tagged 32-bit words, in four segments [V/4 columns | partials of
                          // those heads], one copy per XCD
   Ctl* ctl;

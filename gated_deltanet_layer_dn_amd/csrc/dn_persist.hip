@@ -218,24 +218,40 @@ __device__ __forceinline__ void dot_rows(const v4i (&w)[RB][NCH], const int8_t* 
   }
 }
 
-struct Smem {
+// LDS of a workgroup. HB: communication waves that run phase B (1: a 128 x 16 state slice per
+// workgroup; 2: a 128 x 32 slice in two halves, for up to 64 value heads, with the out_proj rows
+// prefetched into LDS rather than registers to make room for 8 in_proj rows per compute wave).
+// LDS only the two-wave form uses (empty, and so of no size, for HB == 1)
+template <int HB>
+struct SmemB2 {};
+template <>
+struct SmemB2<2> {
+  int v_ready;             // layers whose second-half v, z are in vz
+  float vz[2 * CB];        // v and z of the second half's columns
+  v4i wcl[8 * 8 * 64];     // the out_proj row of each compute wave, [wave][chunk][lane]
+};
+template <int HB>
+struct SmemT : SmemB2<HB> {
+  static constexpr int VMAX = HB == 1 ? 4096 : 8192;  // readout columns
+  static constexpr int LMAX = HB == 1 ? MAXL : 64;    // layers whose per-layer tables are held
   float raw[4096];         // staged layer input x, fp32
-  float yf[4096];          // gated, normalised readout y (input of out_proj), fp32
+  float yf[VMAX];          // gated, normalised readout y (input of out_proj), fp32
   int8_t xs[3 * 4096];     // three-term split of x for phase A
   float inv[64];           // per value head 1/rms of the readout
   float qk[2 * DK];        // raw q and k of phase B's key head
   v4i gwl[2][2][64];       // GT: the next layer's two gate rows of this head (lane's 16-byte chunks), via LDS DMA
   float gval[2];           // GT: the layer's gates alpha, beta of this head
-  v4f sbuf[8 * 64];        // phase B's updated state slice until its write-back
+  v4f sbuf[HB][8 * 64];    // phase B's updated state slice until its write-back (HB halves of 16 columns)
   float stat[16];          // partial statistics from the communication waves, split scale
-  float gate[MAXL][2];     // alpha, beta of this workgroup's value head, per layer
-  float nw[MAXL][CB];      // gated RMSNorm weights of this workgroup's value columns, per layer
+  float gate[LMAX][2];     // alpha, beta of this workgroup's value head, per layer
+  float nw[LMAX][HB * CB]; // gated RMSNorm weights of this workgroup's value columns, per layer
   int a_done, b_done, c_done;  // progress counters of this workgroup's waves
   int u_done;                  // phase-B inputs received (the next layer's in_proj prefetch may start)
   int s_ready;                 // compute waves whose chunk of the layer's state slice is in LDS
   int g_ready;                 // GT: layers whose gate values are in gval
   int abort_flag;
 };
+using Smem = SmemT<1>;
 
 // Position in Smem::yf of readout column c: phase C reads, for lane l and 16-byte weight chunk k,
 // the readout quads of the chunk's columns as one contiguous 16-byte word per lane, so that the
@@ -384,23 +400,31 @@ __device__ __forceinline__ bool poll_words_at(const uint64_t* base, const int (&
 // the buffer, with device-coherent loads until every word carries `want` mod 4; quads i >= nvalid
 // are not polled. When ONE is set, the single word at byte offset boff1 is polled as well. Returns
 // false after `cap` rounds, or if another workgroup reported an error.
-template <int NQ, int QSTRIDE, bool ONE>
+template <int NQ, int QSTRIDE, int NX>
 __device__ __forceinline__ bool poll_quads(__amdgpu_buffer_rsrc_t rs, int boff, int boff1, unsigned want, v4u (&q)[NQ],
-                                           unsigned& w1, const unsigned* err, unsigned cap) {
+                                           unsigned (&w1)[2], const unsigned* err, unsigned cap) {
+  static_assert(NX >= 0 && NX <= 2, "");
   const unsigned t = want & 3u;
   unsigned pend = (1u << NQ) - 1u;
-  bool pend1 = ONE;
+  bool pend1 = NX > 0;
   unsigned it = 0;
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
   while (__any((pend != 0) | pend1)) {
 #pragma unroll
     for (int i = 0; i < NQ; ++i)
       if ((pend >> i) & 1)
         q[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, boff + i * QSTRIDE, 0, CPOL_SC1);
-    if (ONE && pend1) w1 = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1, 0, CPOL_SC1);
+    if (NX == 1 && pend1) w1[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, boff1, 0, CPOL_SC1);
+    if (NX == 2 && pend1) {
+      const v2u p = __builtin_amdgcn_raw_buffer_load_b64(rs, boff1, 0, CPOL_SC1);
+      w1[0] = p[0];
+      w1[1] = p[1];
+    }
 #pragma unroll
     for (int i = 0; i < NQ; ++i)
       if (((pend >> i) & 1) && st_tagged(q[i], t)) pend &= ~(1u << i);
-    if (ONE && pend1 && (w1 & 3u) == t) pend1 = false;
+    if (NX == 1 && pend1 && (w1[0] & 3u) == t) pend1 = false;
+    if (NX == 2 && pend1 && (w1[0] & 3u) == t && (w1[1] & 3u) == t) pend1 = false;
     if (++it > cap || ((it & 255) == 0 && coherent_load_u32(err))) return false;
   }
   return true;
@@ -414,8 +438,8 @@ struct Geo {
   int bh, bcb, bg;
 };
 
-template <int BITS, int D>
-__device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid) {
+template <int BITS, int D, typename SM>
+__device__ __forceinline__ void split_x(SM& sm, const PersistArgs& a, int tid) {
   // Three-term int8 split of the raw x with s1 = max|x| / 127: x ~= s1 (h + (m + l/254)/254); the
   // RMS factor joins s1 in the fold of the dot products (sm.stat[8]). Each thread splits 8
   // consecutive columns and writes each term as two dwords (4-bit weights: even columns in the
@@ -455,8 +479,8 @@ __device__ __forceinline__ void split_x(Smem& sm, const PersistArgs& a, int tid)
 // Compute waves: phase A and phase C, weights prefetched one layer ahead in registers. (PK and GT
 // do not change this role; they keep one specialisation per kernel instantiation, which the host
 // compiler pass needs when several instantiations of the kernel are referenced.)
-template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT>
-__device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT, int HB>
+__device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
                                              const float* S_in, float* S_out, const float* ring_in, float* ring_out,
                                              int tid, int lane) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
@@ -464,15 +488,22 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
   constexpr int rowbytes_in = BITS == 8 ? D : D / 2;
   constexpr int rowbytes_out = BITS == 8 ? V : V / 2;
   const int C = a.C, K = a.K;
+  // HB == 2: the out_proj row (RC == 1) is prefetched into LDS (sm.wcl) with direct-to-LDS loads,
+  // not into registers; wc then only carries a chunk at a time through phase C
+  constexpr bool WCL = HB == 2;
+  static_assert(!WCL || RC == 1, "");
   v4i wa[RA][NCHA];
-  v4i wc[RC][NCHC];
+  v4i wc[RC][WCL ? 1 : NCHC];
+  const int cwv = tid >> 6;
   float ra_s = 0.f, ra_cw[4] = {0.f, 0.f, 0.f, 0.f}, ra_ring[3] = {0.f, 0.f, 0.f};
   float rc_s = 0.f;
 
   // in_proj rows of layer l into registers: part 0 the first DN_PREFETCH_EARLY_ROWS rows (and the
   // rows' scales, conv taps and history), part 1 the others; each part throttled to
   // DN_PREFETCH_INFLIGHT loads in flight but for its last DN_PREFETCH_TAIL
-  constexpr int EARLY = DN_PREFETCH_EARLY_ROWS < RA ? DN_PREFETCH_EARLY_ROWS : RA;
+  // (with more rows per wave than 6, the extra ones join part 0: part 1 keeps its two rows)
+  constexpr int EARLY0 = DN_PREFETCH_EARLY_ROWS + (RA > 6 ? RA - 6 : 0);
+  constexpr int EARLY = EARLY0 < RA ? EARLY0 : RA;
   auto load_a = [&](int l, int part) {
     const LayerW& W = a.layers[l];
     const int8_t* wbase = reinterpret_cast<const int8_t*>(W.w_in);
@@ -513,10 +544,20 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 #pragma unroll
       for (int k = 0; k < NCHC; ++k) {
         if ((i * NCHC + k) >= DN_PREFETCH_INFLIGHT) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
-        if (r < g.c_row_end)
-          wc[i][k] = __builtin_nontemporal_load(gmem(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_out) + lane + 64 * k));
-        else
-          wc[i][k] = v4i{0, 0, 0, 0};
+        if constexpr (WCL) {
+          // the previous layer's phase C read these slots: its LDS reads are done before they refill
+          if (k == 0) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+          if (r < g.c_row_end)
+            __builtin_amdgcn_global_load_lds(gmem(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_out) + lane + 64 * k),
+                                             &sm.wcl[(cwv * 8 + k) * 64], 16, 0, 0);
+          else
+            sm.wcl[(cwv * 8 + k) * 64 + lane] = v4i{0, 0, 0, 0};
+        } else {
+          if (r < g.c_row_end)
+            wc[i][WCL ? 0 : k] = __builtin_nontemporal_load(gmem(reinterpret_cast<const v4i*>(wbase + (size_t)r * rowbytes_out) + lane + 64 * k));
+          else
+            wc[i][WCL ? 0 : k] = v4i{0, 0, 0, 0};
+        }
       }
     }
     const int r = g.c_row0 + lane;
@@ -526,10 +567,14 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
   // Phase B's state slice: compute wave w moves chunk w (lane's 4 floats at rows 32p + 4w, column
   // j, for lane 4j + p) between HBM and LDS: prefetched into LDS one layer ahead by a direct-to-LDS
   // load from the current state buffer, written back from LDS after phase C into the other one.
-  const int cwv = tid >> 6;
+  // (HB == 2: chunk w of each half; the halves are 16 columns, CB * DK floats, apart)
   const size_t s_off = ((size_t)g.bh * DK + g.bcb * CB + (lane >> 2)) * DK + 32 * (lane & 3) + 4 * cwv;
   const size_t s_layer = (size_t)a.Hv * DK * DK;
-  if (g.has_b) __builtin_amdgcn_global_load_lds(S_in + s_off, &sm.sbuf[64 * cwv], 16, 0, 0);
+  if (g.has_b) {
+#pragma unroll
+    for (int h = 0; h < HB; ++h)
+      __builtin_amdgcn_global_load_lds(S_in + s_off + (size_t)h * CB * DK, &sm.sbuf[h][64 * cwv], 16, 0, 0);
+  }
   load_a(0, 0);
   load_a(0, 1);
   load_c(0);
@@ -597,8 +642,14 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 #pragma unroll
       for (int i = 0; i < RC; ++i) acc[i] = 0.f;
       const v4f* Y4 = reinterpret_cast<const v4f*>(sm.yf);
+      if constexpr (WCL) {
+        // the row's direct-to-LDS loads were issued before every load still in flight
+        DN_WAIT_VMCNT(0);
+        asm volatile("" ::: "memory");
+      }
 #pragma unroll
       for (int k = 0; k < NCHC; ++k) {
+        if constexpr (WCL) wc[0][0] = sm.wcl[(cwv * 8 + k) * 64 + lane];
         if (BITS == 8) {
           const v4f yq[4] = {Y4[(k * 4 + 0) * 64 + lane], Y4[(k * 4 + 1) * 64 + lane], Y4[(k * 4 + 2) * 64 + lane],
                              Y4[(k * 4 + 3) * 64 + lane]};
@@ -606,7 +657,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
           for (int i = 0; i < RC; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const unsigned u = (unsigned)wc[i][k][e] ^ 0x80808080u;
+              const unsigned u = (unsigned)wc[i][WCL ? 0 : k][e] ^ 0x80808080u;
               acc[i] = fmaf((float)(u & 0xFFu), yq[e][0], acc[i]);
               acc[i] = fmaf((float)((u >> 8) & 0xFFu), yq[e][1], acc[i]);
               acc[i] = fmaf((float)((u >> 16) & 0xFFu), yq[e][2], acc[i]);
@@ -619,7 +670,7 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
             const v4f ya = Y4[(k * 8 + 2 * e) * 64 + lane], yb = Y4[(k * 8 + 2 * e + 1) * 64 + lane];
 #pragma unroll
             for (int i = 0; i < RC; ++i) {
-              const unsigned p = (unsigned)wc[i][k][e] ^ 0x88888888u;
+              const unsigned p = (unsigned)wc[i][WCL ? 0 : k][e] ^ 0x88888888u;
               const unsigned lo = p & 0x0F0F0F0Fu, hi = (p >> 4) & 0x0F0F0F0Fu;
               acc[i] = fmaf((float)(lo & 0xFFu), ya[0], acc[i]);
               acc[i] = fmaf((float)(hi & 0xFFu), ya[1], acc[i]);
@@ -657,11 +708,17 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
       if (g.has_b) {
         // write back this wave's chunk of the updated slice (parked in LDS by phase B before
         // barrier 3), then prefetch the next layer's chunk into the same LDS slots
-        const v4f v = sm.sbuf[64 * cwv + lane];
-        *reinterpret_cast<v4f*>(S_out + (size_t)l * s_layer + s_off) = v;
+#pragma unroll
+        for (int h = 0; h < HB; ++h) {
+          const v4f v = sm.sbuf[h][64 * cwv + lane];
+          *reinterpret_cast<v4f*>(S_out + (size_t)l * s_layer + s_off + (size_t)h * CB * DK) = v;
+        }
         if (l + 1 < a.L) {
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS read is done before the slots refill
-          __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + s_off, &sm.sbuf[64 * cwv], 16, 0, 0);
+#pragma unroll
+          for (int h = 0; h < HB; ++h)
+            __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + s_off + (size_t)h * CB * DK,
+                                             &sm.sbuf[h][64 * cwv], 16, 0, 0);
         }
       }
       if (l + 1 < a.L) {
@@ -678,17 +735,20 @@ __device__ __forceinline__ void compute_role(Smem& sm, const PersistArgs& a, con
 // them at once measured slower); the in_proj poll of the recurrence starts at once.
 // PK: one decay per key channel; apk [L][128] holds this head's decays (LDS).
 // GT: gates from the in_proj's gate rows; sm.gate holds this head's a_log, a_bias per layer.
-template <int BITS, int NCHA, int NCHC, bool PK, bool GT>
-__device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const PersistArgs& a, const Geo& g,
+template <int BITS, int NCHA, int NCHC, bool PK, bool GT, int HB>
+__device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const PersistArgs& a, const Geo& g,
                                           unsigned base_tag, int tid, int lane, int cw, int wg) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
   constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC, DV = 128;
   constexpr int XW = D / (64 * NCM);  // x words per lane
   constexpr int GW = V / (64 * NCM);  // gated readout words per lane
   constexpr int nblk = DV / CB;
-  constexpr int GSEG = V / NCM + 64;  // words per communication wave segment of the G buffer
+  // words per communication wave segment of the G buffer: V/NCM readout columns, then the norm
+  // partials of those heads (up to 64 HB of them: HB per lane in the staging)
+  constexpr int GSEG = V / NCM + 64 * HB;
   constexpr int XQ = XW / 4, GQ = GW / 4;  // 16-byte quads per lane
-  static_assert(XW % 4 == 0 && GW % 4 == 0 && XQ <= 4 && GQ <= 4, "");
+  static_assert(XW % 4 == 0 && GW % 4 == 0 && XQ <= 4 && GQ <= 8, "");
+  static_assert(HB == 1 || (HB == 2 && !GT && !PK), "");
   const int C = a.C, QK = a.QK, Hv = a.Hv;
   const int npart = Hv * nblk;
   const unsigned* err = &a.ctl->error;
@@ -707,8 +767,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
   // this XCD's copies of the broadcast buffers
   const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(a.X + (size_t)rep * D, 4u * D);
   const __amdgpu_buffer_rsrc_t grs = buf_rsrc(a.G + (size_t)rep * (NCM * GSEG), 4u * NCM * GSEG);
-  const bool runs_b = cw == 0 && g.has_b;
-  if (runs_b) {
+  const bool runs_b = cw < HB && g.has_b;  // HB == 2: wave 0 the first half of the slice, wave 1 the second
+  if (runs_b && cw == 0) {
     // the per-layer gates and norm weights this workgroup needs, fetched once per launch
     for (int l = lane; l < a.L; l += 64) {
       if constexpr (GT) {
@@ -735,17 +795,18 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
           if (e < a.L * DK) apk[e / DK][e % DK] = v[u];
         }
       }
-    for (int e0 = lane; e0 < a.L * CB; e0 += 64 * 8) {
+    constexpr int NWC = HB * CB;  // norm weights of this workgroup's columns, per layer
+    for (int e0 = lane; e0 < a.L * NWC; e0 += 64 * 8) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int e = min(e0 + 64 * u, a.L * CB - 1);
-        v[u] = *gmem(a.layers[e / CB].norm_w + g.bcb * CB + e % CB);
+        const int e = min(e0 + 64 * u, a.L * NWC - 1);
+        v[u] = *gmem(a.layers[e / NWC].norm_w + g.bcb * CB + e % NWC);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = e0 + 64 * u;
-        if (e < a.L * CB) sm.nw[e / CB][e % CB] = v[u];
+        if (e < a.L * NWC) sm.nw[e / NWC][e % NWC] = v[u];
       }
     }
   }
@@ -792,8 +853,8 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       } else {
         wait_counter(&sm.c_done, NCW * l, &sm.abort_flag);
         v4u q[XQ];
-        unsigned w1 = 0;
-        ok = poll_quads<XQ, 1024, false>(xrs, 4 * col0, 0, tag - 1, q, w1, err, a.spin_cap);
+        unsigned w1[2] = {0u, 0u};
+        ok = poll_quads<XQ, 1024, 0>(xrs, 4 * col0, 0, tag - 1, q, w1, err, a.spin_cap);
 #pragma unroll
         for (int h = 0; h < XQ; ++h)
 #pragma unroll
@@ -845,29 +906,57 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
 
     bool ok = true;
     if (runs_b) {
-      // phase B: recurrence on the 128 x 16 state slice
-      const int vcol = g.bh * DV + g.bcb * CB;
-      // raw q and k rows lane and lane+64 of key head bg; v and z of this lane's column
-      constexpr int NU = 6;
-      const int qo = g.bg * DK + lane;
-      int off[NU];
-      off[0] = qo; off[1] = qo + 64; off[2] = QK + qo; off[3] = QK + qo + 64;
-      off[4] = 2 * QK + vcol + jc; off[5] = C + vcol + jc;
+      // phase B: recurrence on the 128 x 16 state slice (HB == 2: this wave's half of the 128 x 32 one)
+      const int hb = HB == 1 ? 0 : cw;
+      const int vcol = g.bh * DV + (g.bcb + hb) * CB;
+      // raw q and k rows lane and lane+64 of key head bg; v and z of this lane's column (HB == 2:
+      // also the second half's v and z, which wave 0 hands to wave 1 through LDS)
+      constexpr int NU = 4 + 2 * HB;
       float val[NU];
 #pragma unroll
       for (int i = 0; i < NU; ++i) val[i] = 0.f;
-      // the poll starts at once: waiting for this workgroup's own phase A first measured slower
-      DN_MARK(a, l, 10);
-      unsigned rounds = 0;
-      ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, a.spin_cap, &rounds);
-      if (lane == 0) bump_counter(&sm.u_done);
-      DN_MARK(a, l, 4);
+      if (hb == 0) {
+        const int qo = g.bg * DK + lane;
+        int off[NU];
+        off[0] = qo; off[1] = qo + 64; off[2] = QK + qo; off[3] = QK + qo + 64;
+        off[4] = 2 * QK + vcol + jc; off[5] = C + vcol + jc;
+        if constexpr (HB == 2) {
+          off[6] = 2 * QK + vcol + CB + jc;
+          off[7] = C + vcol + CB + jc;
+        }
+        // the poll starts at once: waiting for this workgroup's own phase A first measured slower
+        DN_MARK(a, l, 10);
+        unsigned rounds = 0;
+        ok = poll_words_at<NU>(Ub, off, tag, val, (unsigned)NU, err, a.spin_cap, &rounds);
+        if (lane == 0) bump_counter(&sm.u_done);
+        DN_MARK(a, l, 4);
+      }
       if (__all(ok)) {
         // this wave's own LDS writes are visible to its later LDS reads (in-order LDS queue)
-        sm.qk[lane] = val[0];
-        sm.qk[lane + 64] = val[1];
-        sm.qk[DK + lane] = val[2];
-        sm.qk[DK + lane + 64] = val[3];
+        if (hb == 0) {
+          sm.qk[lane] = val[0];
+          sm.qk[lane + 64] = val[1];
+          sm.qk[DK + lane] = val[2];
+          sm.qk[DK + lane + 64] = val[3];
+          if constexpr (HB == 2) {
+            if (pr == 0) {
+              sm.vz[jc] = val[6];
+              sm.vz[CB + jc] = val[7];
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): q, k, v, z are in LDS before the count
+            asm volatile("" ::: "memory");
+            if (lane == 0) bump_counter(&sm.v_ready);
+          }
+        } else if constexpr (HB == 2) {
+          wait_counter(&sm.v_ready, l + 1, &sm.abort_flag);  // wave 0 has the inputs in LDS
+          asm volatile("" ::: "memory");
+          val[0] = sm.qk[lane];
+          val[1] = sm.qk[lane + 64];
+          val[2] = sm.qk[DK + lane];
+          val[3] = sm.qk[DK + lane + 64];
+          val[4] = sm.vz[jc];
+          val[5] = sm.vz[CB + jc];
+        }
         DN_MARK(a, l, 11);
         float alpha = sm.gate[l][0], beta = sm.gate[l][1];
         if constexpr (GT) {
@@ -888,7 +977,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         // same pass, so it is published before the update of the slice.
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const v4f kk = K4[q], qq = Q4[q], st = sm.sbuf[64 * q + lane];
+          const v4f kk = K4[q], qq = Q4[q], st = sm.sbuf[hb][64 * q + lane];
           v4f av = {alpha, alpha, alpha, alpha};  // decay of rows 32 pr + 4 q ..
           if constexpr (PK) av = A4[q];
 #pragma unroll
@@ -908,7 +997,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
         const float dk = beta * (val[4] - kv) * kn;  // delta times 1/|k|
         DN_MARK(a, l, 13);
         const float o = qn * fmaf(dk, quad_sum(kqp), quad_sum(qvp));
-        const float gt = sm.nw[l][jc] * o * silu(val[5]);
+        const float gt = sm.nw[l][hb * CB + jc] * o * silu(val[5]);
         const float osq = wave_total_f(pr == 0 ? o * o : 0.f);
         DN_MARK(a, l, 15);
         // G buffer: NCM segments of [V/NCM gated columns | partials of the same heads]
@@ -921,8 +1010,9 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
           const int r0 = 2 * pr;
           st_store(a.G + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
           st_store(a.G + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
+          const int unit = HB * wg + hb;  // = nblk * bh + this half's column block
           if (lane < NREP)
-            st_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (wg - pw * (npart / NCM)), osq, tag);
+            st_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (unit - pw * (npart / NCM)), osq, tag);
         }
         // the delta rule write, after the readout is out; the slice is parked in LDS and written
         // back while phase C runs
@@ -931,7 +1021,7 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
           const v4f kk = K4[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) sv[4 * q + e] = fmaf(kk[e], dk, sv[4 * q + e]);
-          sm.sbuf[q * 64 + lane] = v4f{sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]};
+          sm.sbuf[hb][q * 64 + lane] = v4f{sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]};
         }
         DN_MARK(a, l, 14);
         DN_MARK(a, l, 5);
@@ -941,37 +1031,45 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
       wait_counter(&sm.a_done, NCW * (l + 1), &sm.abort_flag);
       if (lane == 0) {
         bump_counter(&sm.u_done);
-        bump_counter(&sm.b_done);
+#pragma unroll
+        for (int h = 0; h < HB; ++h) bump_counter(&sm.b_done);
       }
     }
     if (__all(ok)) {
       // stage the gated readout: value columns [cw*V/NCM, (cw+1)*V/NCM) and the partials of those
       // heads, which follow them in this wave's segment of the buffer
-      wait_counter(&sm.b_done, l + 1, &sm.abort_flag);
-      float gv[GW + 1];
+      wait_counter(&sm.b_done, HB * (l + 1), &sm.abort_flag);
+      float gv[GW + HB];
       const int pn = npart / NCM, pbase = cw * pn;
       if (cw == 0) DN_MARK(a, l, 12);
       {
         // quad h of lane: columns cw V/4 + 256 h + 4 lane .. +3; then the partial of lane (< pn)
+        // the partials of this quarter's heads: HB consecutive ones per lane (lanes < pn / HB)
         v4u q[GQ];
-        unsigned w1 = 0;
+        unsigned w1[2] = {0u, 0u};
         const int w0 = cw * GSEG + 4 * lane;
-        if (lane < pn)
-          ok = poll_quads<GQ, 1024, true>(grs, 4 * w0, 4 * (cw * GSEG + V / NCM + lane), tag, q, w1, err, a.spin_cap);
+        if (HB * lane < pn)
+          ok = poll_quads<GQ, 1024, HB>(grs, 4 * w0, 4 * (cw * GSEG + V / NCM + HB * lane), tag, q, w1, err, a.spin_cap);
         else
-          ok = poll_quads<GQ, 1024, false>(grs, 4 * w0, 0, tag, q, w1, err, a.spin_cap);
+          ok = poll_quads<GQ, 1024, 0>(grs, 4 * w0, 0, tag, q, w1, err, a.spin_cap);
 #pragma unroll
         for (int h = 0; h < GQ; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) gv[4 * h + e] = st_value(q[h][e]);
-        gv[GW] = lane < pn ? st_value(w1) : 0.f;
+#pragma unroll
+        for (int h = 0; h < HB; ++h) gv[GW + h] = HB * lane < pn ? st_value(w1[h]) : 0.f;
       }
       if (cw == 0) DN_MARK(a, l, 6);
-      // per-head sums of the partials: head h's nblk partials sit in nblk consecutive lanes
+      // per-head sums of the partials: head h's nblk partials sit in nblk / HB consecutive lanes
       {
         static_assert(nblk == 8, "");
-        const float sp = oct_sum(gv[GW]);
-        if ((lane % nblk) == 0 && lane < pn) sm.inv[(pbase + lane) / nblk] = rsqrtf(sp / (float)DV + a.eps_rms);
+        if constexpr (HB == 1) {
+          const float sp = oct_sum(gv[GW]);
+          if ((lane % nblk) == 0 && lane < pn) sm.inv[(pbase + lane) / nblk] = rsqrtf(sp / (float)DV + a.eps_rms);
+        } else {
+          const float sp = quad_sum(gv[GW] + gv[GW + 1]);
+          if ((lane % 4) == 0 && 2 * lane < pn) sm.inv[(pbase + 2 * lane) / nblk] = rsqrtf(sp / (float)DV + a.eps_rms);
+        }
       }
       // y = g / rms(head), staged for phase C, and the sum of this quarter of y
       float sy = 0.f;
@@ -994,12 +1092,12 @@ __device__ __forceinline__ void comm_role(Smem& sm, float (*apk)[DK], const Pers
   }
 }
 
-template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT>
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT, int HB>
 __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
   constexpr int D = COLS_PER_CHUNK * NCHA;
   constexpr int nblk = 128 / CB;
-  __shared__ Smem sm;
+  __shared__ SmemT<HB> sm;
   __shared__ float apk[PK ? PK_MAXL : 1][DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NWG = gridDim.x, wg = blockIdx.x;
@@ -1019,14 +1117,17 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   const int c_per_wave = (c_per_wg + NCW - 1) / NCW;
   g.c_row0 = wg * c_per_wg + wave * c_per_wave;
   g.c_row_end = min(min(wg * c_per_wg + c_per_wg, D), g.c_row0 + c_per_wave);
-  g.has_b = wg < a.Hv * nblk;
-  g.bh = g.has_b ? wg / nblk : 0;
-  g.bcb = g.has_b ? wg % nblk : 0;
+  // phase-B workgroups: nblk / HB per value head, each HB column blocks of it (bcb the first)
+  constexpr int WPH = nblk / HB;
+  g.has_b = wg < a.Hv * WPH;
+  g.bh = g.has_b ? wg / WPH : 0;
+  g.bcb = g.has_b ? HB * (wg % WPH) : 0;
   g.bg = g.bh / (a.Hv / a.Hk);
 
   if (tid == 0) {
     sm.abort_flag = 0;
     sm.a_done = sm.b_done = sm.c_done = sm.u_done = sm.s_ready = sm.g_ready = 0;
+    if constexpr (HB == 2) sm.v_ready = 0;
   }
 #ifdef DN_PHASE_TIMERS
   for (int e = tid; e < TS_MAXL * 32; e += NTHR) g_ts[e / 32][e % 32] = 0;
@@ -1037,10 +1138,10 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   // go to the other ones.
   if (!skip) {
     if (wave < NCW)
-      compute_role<BITS, NCHA, NCHC, RA, RC, PK, GT>(sm, a, g, base_tag, a.S[par], a.S[par ^ 1u], a.ring[par],
+      compute_role<BITS, NCHA, NCHC, RA, RC, PK, GT, HB>(sm, a, g, base_tag, a.S[par], a.S[par ^ 1u], a.ring[par],
                                                      a.ring[par ^ 1u], tid, lane);
     else
-      comm_role<BITS, NCHA, NCHC, PK, GT>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
+      comm_role<BITS, NCHA, NCHC, PK, GT, HB>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
   }
 
 #ifdef DN_PHASE_TIMERS
@@ -1076,18 +1177,24 @@ hipError_t launch_one(F kern, const PersistArgs& a, int nwg, bool coop, hipStrea
   return hipGetLastError();
 }
 
+// 48 value heads of 128 over d_model 2048 (8-bit): 64 in_proj rows per workgroup (8 per compute
+// wave), the state in 128 x 32 slices (two phase-B waves), caller-given scalar decays
+hipError_t go_hb2(const PersistArgs& a, int nwg, bool coop, hipStream_t st) {
+  return launch_one(k_persist<8, 2, 6, 8, 1, false, false, 2>, a, nwg, coop, st);
+}
+
 template <int BITS, int NCHA, int NCHC>
 hipError_t go(const PersistArgs& a, int nwg, bool coop, hipStream_t st) {
-  if (a.alpha_per_key) return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, true, false>, a, nwg, coop, st);
-  if (a.gates) return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, false, true>, a, nwg, coop, st);
-  return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, false, false>, a, nwg, coop, st);
+  if (a.alpha_per_key) return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, true, false, 1>, a, nwg, coop, st);
+  if (a.gates) return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, false, true, 1>, a, nwg, coop, st);
+  return launch_one(k_persist<BITS, NCHA, NCHC, 6, 1, false, false, 1>, a, nwg, coop, st);
 }
 
 template <int BITS, int NCHA, int NCHC>
 hipError_t occ(int* blocks, bool pk, bool gt) {
-  if (pk) return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, true, false>, NTHR, 0);
-  if (gt) return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false, true>, NTHR, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false, false>, NTHR, 0);
+  if (pk) return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, true, false, 1>, NTHR, 0);
+  if (gt) return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false, true, 1>, NTHR, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, k_persist<BITS, NCHA, NCHC, 6, 1, false, false, 1>, NTHR, 0);
 }
 
 }  // namespace
@@ -1099,7 +1206,19 @@ static int chunks(int cols, int bits) {
   return bytes / 1024;
 }
 
+// The two-wave instantiation's shape: 8-bit weights, d_model 2048, value width 6144 (48 heads of 128),
+// caller-given scalar decays, at most 64 layers, 8 in_proj rows per compute wave.
+static bool hb2_shape(const PersistShape& s, int nwg) {
+  if (s.batch != 1 || s.dk != DK || s.dv != 128 || s.K < 1 || s.K > 4 || s.bits != 8) return false;
+  if (s.alpha_per_key || s.gates || s.L > SmemT<2>::LMAX) return false;
+  if (chunks(s.D, s.bits) != 2 || chunks(s.V, s.bits) != 6 || (s.Hv % NCM) || s.Hv > 64) return false;
+  if (s.Hv * (s.dv / CB) / 2 > nwg) return false;
+  const int a_per_wg = (s.R + nwg - 1) / nwg, c_per_wg = (s.D + nwg - 1) / nwg;
+  return (a_per_wg + NCW - 1) / NCW <= 8 && (c_per_wg + NCW - 1) / NCW <= 1;
+}
+
 bool persist_supported(const PersistShape& s, int nwg) {
+  if (hb2_shape(s, nwg)) return true;
   if (s.batch != 1 || s.dk != DK || s.dv != 128 || s.K < 1 || s.K > 4) return false;
   if (s.alpha_per_key && s.L > PK_MAXL) return false;
   if (s.alpha_per_key && s.gates) return false;
@@ -1118,12 +1237,15 @@ bool persist_supported(const PersistShape& s, int nwg) {
 hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu) {
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
   const bool pk = s.alpha_per_key != 0, gt = s.gates != 0;
+  if (s.bits == 8 && na == 2 && nc == 6)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_persist<8, 2, 6, 8, 1, false, false, 2>, NTHR, 0);
   if (s.bits == 8) return na == 2 ? occ<8, 2, 4>(blocks_per_cu, pk, gt) : occ<8, 1, 1>(blocks_per_cu, pk, gt);
   return nc == 2 ? occ<4, 1, 2>(blocks_per_cu, pk, gt) : occ<4, 1, 1>(blocks_per_cu, pk, gt);
 }
 
 hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, bool coop, hipStream_t st) {
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
+  if (s.bits == 8 && na == 2 && nc == 6) return go_hb2(a, nwg, coop, st);
   if (s.bits == 8) return na == 2 ? go<8, 2, 4>(a, nwg, coop, st) : go<8, 1, 1>(a, nwg, coop, st);
   return nc == 2 ? go<4, 1, 2>(a, nwg, coop, st) : go<4, 1, 1>(a, nwg, coop, st);
 }

@@ -33,6 +33,12 @@ PERSIST = {
     "p_perkey_full_int4": gi.custom("p_pk4", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=32, d_v=128,
                                     n_layers=2, n_tokens=5, weight_bits=4,
                                     flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY, ring_std=1.0),
+    # 48 value heads over 16 key heads at d_model 2048: the two-wave form (128 x 32 state slices on
+    # 192 workgroups, 8 in_proj rows per compute wave, out_proj rows staged in LDS)
+    "p_heads48": gi.custom("p_h48", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=48, d_v=128, n_layers=3,
+                           n_tokens=6, flags=gi.DN_X_RMSNORM, ring_std=1.0),
+    "p_heads48_conv2": gi.custom("p_h48c2", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=48, d_v=128,
+                                 n_layers=2, conv_k=2, n_tokens=5, ring_std=1.0),
 }
 
 
@@ -64,8 +70,9 @@ def test_persist_parity(name, capfd, monkeypatch):
     assert e <= OUT_TOL and es <= STATE_TOL and eh <= STATE_TOL
 
 
-def test_persist_agrees_with_layer_kernels(monkeypatch):
-    cfg = PERSIST["p_small"]
+@pytest.mark.parametrize("name", ["p_small", "p_heads48"])
+def test_persist_agrees_with_layer_kernels(name, monkeypatch):
+    cfg = PERSIST[name]
     layers, stream = gi.generate(cfg)
     a = make_stack(cfg, layers)
     out_a = run_gpu(a, stream)
