@@ -146,7 +146,13 @@ __device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
-constexpr int CPOL_SC1 = 16;  // cache policy of a device-coherent load
+constexpr int CPOL_SC1 = 16;  // cache policy of a device-coherent load (and store)
+// A self-tagged word stored through a buffer resource at byte offset boff, with the same
+// device-coherent write-through policy as the agent-scope atomic store above: the address is a
+// 32-bit offset from a scalar base instead of a 64-bit register pair per lane.
+__device__ __forceinline__ void st_store_rs(__amdgpu_buffer_rsrc_t rs, int boff, float v, unsigned tag) {
+  __builtin_amdgcn_raw_buffer_store_b32(st_pack(v, tag), rs, boff, 0, CPOL_SC1);
+}
 
 
 // Staged activation position of column c (4-bit weights hold 8 columns per dword as nibbles;
@@ -522,7 +528,9 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
       }
     }
     if (part != 0) return;
-    const int r = g.a_row0 + lane;
+    int ln = lane;
+    if constexpr (HB == 2) asm volatile("" : "+v"(ln));  // (recomputed here rather than held: it spilled)
+    const int r = g.a_row0 + ln;
     if (lane < RA && r < g.a_row_end) {
       ra_s = *gmem(W.s_in + r);
       if (r < C) {
@@ -540,7 +548,9 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
     const int8_t* wbase = reinterpret_cast<const int8_t*>(W.w_out);
 #pragma unroll
     for (int i = 0; i < RC; ++i) {
-      const int r = g.c_row0 + i;
+      // (HB == 2: the row index as a scalar, the wave's rows being uniform, so that the row's base
+      // address is not held per lane)
+      const int r = HB == 2 ? __builtin_amdgcn_readfirstlane(g.c_row0 + i) : g.c_row0 + i;
 #pragma unroll
       for (int k = 0; k < NCHC; ++k) {
         if ((i * NCHC + k) >= DN_PREFETCH_INFLIGHT) DN_WAIT_VMCNT(DN_PREFETCH_INFLIGHT - 1);
@@ -569,6 +579,17 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
   // load from the current state buffer, written back from LDS after phase C into the other one.
   // (HB == 2: chunk w of each half; the halves are 16 columns, CB * DK floats, apart)
   const size_t s_off = ((size_t)g.bh * DK + g.bcb * CB + (lane >> 2)) * DK + 32 * (lane & 3) + 4 * cwv;
+  // HB == 2: the same offset recomputed at each use from a laundered lane index (held across the
+  // layers, it and the addresses built on it were spilled)
+  auto soff = [&]() -> size_t {
+    if constexpr (HB == 2) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      return ((size_t)g.bh * DK + g.bcb * CB + (ln >> 2)) * DK + 32 * (ln & 3) + 4 * cwv;
+    } else {
+      return s_off;
+    }
+  };
   const size_t s_layer = (size_t)a.Hv * DK * DK;
   if (g.has_b) {
 #pragma unroll
@@ -699,7 +720,16 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
         for (int i = 0; i < RC; ++i) {
           const float oi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(o), i));
           const int ri = g.c_row0 + i;
-          if (lane < NREP && ri < g.c_row_end) st_store(a.X + (size_t)lane * D + ri, oi, tag);
+          if (lane < NREP && ri < g.c_row_end) {
+            if constexpr (HB == 2) {
+              // through a buffer resource, the offset computed here from a laundered lane index
+              // rather than held in a register across the layers (which spilled it)
+              int ln = lane;
+              asm volatile("" : "+v"(ln));
+              st_store_rs(buf_rsrc(a.X, 4u * NREP * D), 4 * (ln * D + ri), oi, tag);
+            } else
+              st_store(a.X + (size_t)lane * D + ri, oi, tag);
+          }
         }
       }
       if (lane < RC && r < g.c_row_end) a.out[(size_t)l * D + r] = o;
@@ -708,16 +738,17 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
       if (g.has_b) {
         // write back this wave's chunk of the updated slice (parked in LDS by phase B before
         // barrier 3), then prefetch the next layer's chunk into the same LDS slots
+        const size_t so = soff();
 #pragma unroll
         for (int h = 0; h < HB; ++h) {
           const v4f v = sm.sbuf[h][64 * cwv + lane];
-          *reinterpret_cast<v4f*>(S_out + (size_t)l * s_layer + s_off + (size_t)h * CB * DK) = v;
+          *reinterpret_cast<v4f*>(S_out + (size_t)l * s_layer + so + (size_t)h * CB * DK) = v;
         }
         if (l + 1 < a.L) {
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS read is done before the slots refill
 #pragma unroll
           for (int h = 0; h < HB; ++h)
-            __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + s_off + (size_t)h * CB * DK,
+            __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + so + (size_t)h * CB * DK,
                                              &sm.sbuf[h][64 * cwv], 16, 0, 0);
         }
       }
@@ -1008,11 +1039,19 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
         {
           const size_t off = (size_t)gw * GSEG + (gc - gw * (V / NCM));
           const int r0 = 2 * pr;
-          st_store(a.G + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
-          st_store(a.G + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
           const int unit = HB * wg + hb;  // = nblk * bh + this half's column block
-          if (lane < NREP)
-            st_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (unit - pw * (npart / NCM)), osq, tag);
+          if constexpr (HB == 2) {
+            const int poff = pw * GSEG + V / NCM + (unit - pw * (npart / NCM));  // (through a buffer resource: no 64-bit address kept per lane)
+            const __amdgpu_buffer_rsrc_t gall = buf_rsrc(a.G, 4u * NREP * NCM * GSEG);
+            st_store_rs(gall, 4 * (r0 * (NCM * GSEG) + (int)off), gt, tag);
+            st_store_rs(gall, 4 * ((r0 + 1) * (NCM * GSEG) + (int)off), gt, tag);
+            if (lane < NREP) st_store_rs(gall, 4 * (lane * (NCM * GSEG) + poff), osq, tag);
+          } else {
+            st_store(a.G + (size_t)r0 * (NCM * GSEG) + off, gt, tag);
+            st_store(a.G + (size_t)(r0 + 1) * (NCM * GSEG) + off, gt, tag);
+            if (lane < NREP)
+              st_store(a.G + (size_t)lane * (NCM * GSEG) + pw * GSEG + V / NCM + (unit - pw * (npart / NCM)), osq, tag);
+          }
         }
         // the delta rule write, after the readout is out; the slice is parked in LDS and written
         // back while phase C runs
