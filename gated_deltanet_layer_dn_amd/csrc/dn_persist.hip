@@ -239,7 +239,11 @@ struct SmemB2<2> {
 template <int HB>
 struct SmemT : SmemB2<HB> {
   static constexpr int VMAX = HB == 1 ? 4096 : 8192;  // readout columns
+#ifdef DN_PHASE_TIMERS
+  static constexpr int LMAX = HB == 1 ? MAXL : 32;    // (the instrumented build's marks take 8 KB of LDS)
+#else
   static constexpr int LMAX = HB == 1 ? MAXL : 64;    // layers whose per-layer tables are held
+#endif
   float raw[4096];         // staged layer input x, fp32
   float yf[VMAX];          // gated, normalised readout y (input of out_proj), fp32
   int8_t xs[3 * 4096];     // three-term split of x for phase A
