@@ -1,6 +1,6 @@
 """The ABI's size limits on the card: a stack of 256 layers (the most a handle takes) on the
-whole-stack kernel, and a batch of 1024 sequences (the most a handle takes) on the batched and
-per-layer paths.
+whole-stack kernel, the layer limits of its per-key and two-wave (48-head) forms, and a batch of 1024
+sequences (the most a handle takes) on the batched and per-layer paths.
 
 The 256-layer stack cannot be compared free-running with the oracle: the chain amplifies rounding
 by about 1.44x per layer. Each layer is instead checked against the oracle's step of that layer fed
@@ -60,6 +60,15 @@ def test_per_key_decay_at_the_whole_stack_layer_limit(L, path, capfd, monkeypatc
     takes the per-layer kernels."""
     cfg = gi.custom(f"lim_pk{L}", d_model=1024, n_k_heads=4, d_k=128, n_v_heads=8, d_v=128, n_layers=L, n_tokens=2,
                     flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY, ring_std=1.0)
+    _check_layers_fed_from_the_card(cfg, capfd, monkeypatch, path)
+
+
+@pytest.mark.parametrize("L,path", [(64, "whole-stack kernel"), (65, "per-layer kernels")])
+def test_48_heads_at_the_two_wave_layer_limit(L, path, capfd, monkeypatch):
+    """The whole-stack kernel's two-wave form (48 value heads over d_model 2048) keeps the per-layer
+    gate and norm tables of up to 64 layers in LDS; one more layer takes the per-layer kernels."""
+    cfg = gi.custom(f"lim_h48_{L}", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=48, d_v=128, n_layers=L,
+                    n_tokens=2, flags=gi.DN_X_RMSNORM, ring_std=1.0)
     _check_layers_fed_from_the_card(cfg, capfd, monkeypatch, path)
 
 
