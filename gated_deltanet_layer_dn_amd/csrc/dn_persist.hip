@@ -236,7 +236,7 @@ struct SmemB2<2> {
   float vz[2 * CB];        // v and z of the second half's columns
   v4i wcl[8 * 8 * 64];     // the out_proj row of each compute wave, [wave][chunk][lane]
 };
-template <int HB>
+template <int HB, int DKT = DK>
 struct SmemT : SmemB2<HB> {
   static constexpr int VMAX = HB == 1 ? 4096 : 8192;  // readout columns
 #ifdef DN_PHASE_TIMERS
@@ -248,10 +248,10 @@ struct SmemT : SmemB2<HB> {
   float yf[VMAX];          // gated, normalised readout y (input of out_proj), fp32
   int8_t xs[3 * 4096];     // three-term split of x for phase A
   float inv[64];           // per value head 1/rms of the readout
-  float qk[2 * DK];        // raw q and k of phase B's key head
+  float qk[2 * DKT];       // raw q and k of phase B's key head
   v4i gwl[2][2][64];       // GT: the next layer's two gate rows of this head (lane's 16-byte chunks), via LDS DMA
   float gval[2];           // GT: the layer's gates alpha, beta of this head
-  v4f sbuf[HB][8 * 64];    // phase B's updated state slice until its write-back (HB halves of 16 columns)
+  v4f sbuf[HB][DKT / 16 * 64];  // phase B's updated state slice until its write-back (HB halves of 16 columns)
   float stat[16];          // partial statistics from the communication waves, split scale
   float gate[LMAX][2];     // alpha, beta of this workgroup's value head, per layer
   float nw[LMAX][HB * CB]; // gated RMSNorm weights of this workgroup's value columns, per layer
@@ -489,8 +489,8 @@ __device__ __forceinline__ void split_x(SM& sm, const PersistArgs& a, int tid) {
 // Compute waves: phase A and phase C, weights prefetched one layer ahead in registers. (PK and GT
 // do not change this role; they keep one specialisation per kernel instantiation, which the host
 // compiler pass needs when several instantiations of the kernel are referenced.)
-template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT, int HB>
-__device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT, int HB, int DKT>
+__device__ __forceinline__ void compute_role(SmemT<HB, DKT>& sm, const PersistArgs& a, const Geo& g, unsigned base_tag,
                                              const float* S_in, float* S_out, const float* ring_in, float* ring_out,
                                              int tid, int lane) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
@@ -582,23 +582,28 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
   // j, for lane 4j + p) between HBM and LDS: prefetched into LDS one layer ahead by a direct-to-LDS
   // load from the current state buffer, written back from LDS after phase C into the other one.
   // (HB == 2: chunk w of each half; the halves are 16 columns, CB * DK floats, apart)
-  const size_t s_off = ((size_t)g.bh * DK + g.bcb * CB + (lane >> 2)) * DK + 32 * (lane & 3) + 4 * cwv;
+  // (DKT = 256: each lane of a phase-B wave holds 64 key rows, and each compute wave moves two chunks,
+  // cwv and cwv + 8, 32 floats apart)
+  constexpr int RPL = DKT / 4, NCP = DKT / 128;
+  const size_t s_off = ((size_t)g.bh * DKT + g.bcb * CB + (lane >> 2)) * DKT + RPL * (lane & 3) + 4 * cwv;
   // HB == 2: the same offset recomputed at each use from a laundered lane index (held across the
   // layers, it and the addresses built on it were spilled)
   auto soff = [&]() -> size_t {
     if constexpr (HB == 2) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      return ((size_t)g.bh * DK + g.bcb * CB + (ln >> 2)) * DK + 32 * (ln & 3) + 4 * cwv;
+      return ((size_t)g.bh * DKT + g.bcb * CB + (ln >> 2)) * DKT + RPL * (ln & 3) + 4 * cwv;
     } else {
       return s_off;
     }
   };
-  const size_t s_layer = (size_t)a.Hv * DK * DK;
+  const size_t s_layer = (size_t)a.Hv * DKT * DKT;
   if (g.has_b) {
 #pragma unroll
     for (int h = 0; h < HB; ++h)
-      __builtin_amdgcn_global_load_lds(S_in + s_off + (size_t)h * CB * DK, &sm.sbuf[h][64 * cwv], 16, 0, 0);
+#pragma unroll
+      for (int c = 0; c < NCP; ++c)
+        __builtin_amdgcn_global_load_lds(S_in + s_off + (size_t)h * CB * DKT + 32 * c, &sm.sbuf[h][64 * (cwv + 8 * c)], 16, 0, 0);
   }
   load_a(0, 0);
   load_a(0, 1);
@@ -744,16 +749,20 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
         // barrier 3), then prefetch the next layer's chunk into the same LDS slots
         const size_t so = soff();
 #pragma unroll
-        for (int h = 0; h < HB; ++h) {
-          const v4f v = sm.sbuf[h][64 * cwv + lane];
-          *reinterpret_cast<v4f*>(S_out + (size_t)l * s_layer + so + (size_t)h * CB * DK) = v;
-        }
+        for (int h = 0; h < HB; ++h)
+#pragma unroll
+          for (int c = 0; c < NCP; ++c) {
+            const v4f v = sm.sbuf[h][64 * (cwv + 8 * c) + lane];
+            *reinterpret_cast<v4f*>(S_out + (size_t)l * s_layer + so + (size_t)h * CB * DKT + 32 * c) = v;
+          }
         if (l + 1 < a.L) {
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS read is done before the slots refill
 #pragma unroll
           for (int h = 0; h < HB; ++h)
-            __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + so + (size_t)h * CB * DK,
-                                             &sm.sbuf[h][64 * cwv], 16, 0, 0);
+#pragma unroll
+            for (int c = 0; c < NCP; ++c)
+              __builtin_amdgcn_global_load_lds(S_in + (size_t)(l + 1) * s_layer + so + (size_t)h * CB * DKT + 32 * c,
+                                               &sm.sbuf[h][64 * (cwv + 8 * c)], 16, 0, 0);
         }
       }
       if (l + 1 < a.L) {
@@ -770,11 +779,11 @@ __device__ __forceinline__ void compute_role(SmemT<HB>& sm, const PersistArgs& a
 // them at once measured slower); the in_proj poll of the recurrence starts at once.
 // PK: one decay per key channel; apk [L][128] holds this head's decays (LDS).
 // GT: gates from the in_proj's gate rows; sm.gate holds this head's a_log, a_bias per layer.
-template <int BITS, int NCHA, int NCHC, bool PK, bool GT, int HB>
-__device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const PersistArgs& a, const Geo& g,
+template <int BITS, int NCHA, int NCHC, bool PK, bool GT, int HB, int DKT>
+__device__ __forceinline__ void comm_role(SmemT<HB, DKT>& sm, float (*apk)[DK], const PersistArgs& a, const Geo& g,
                                           unsigned base_tag, int tid, int lane, int cw, int wg) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
-  constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC, DV = 128;
+  constexpr int D = COLS_PER_CHUNK * NCHA, V = COLS_PER_CHUNK * NCHC, DV = DKT;  // (dv = dk)
   constexpr int XW = D / (64 * NCM);  // x words per lane
   constexpr int GW = V / (64 * NCM);  // gated readout words per lane
   constexpr int nblk = DV / CB;
@@ -783,7 +792,10 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
   constexpr int GSEG = V / NCM + 64 * HB;
   constexpr int XQ = XW / 4, GQ = GW / 4;  // 16-byte quads per lane
   static_assert(XW % 4 == 0 && GW % 4 == 0 && XQ <= 4 && GQ <= 8, "");
-  static_assert(HB == 1 || (HB == 2 && !GT && !PK), "");
+  static_assert(HB == 1 || (HB == 2 && !GT && !PK && DKT == 128), "");
+  static_assert(DKT == 128 || (DKT == 256 && HB == 1 && !GT && !PK), "");
+  // phase B: q and k words per lane (rows lane + 64 j), and the positions of v and z in val
+  constexpr int NQK = DKT / 64, VI = 2 * NQK, ZI = VI + 1, RPL = DKT / 4;
   const int C = a.C, QK = a.QK, Hv = a.Hv;
   const int npart = Hv * nblk;
   const unsigned* err = &a.ctl->error;
@@ -946,18 +958,22 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
       const int vcol = g.bh * DV + (g.bcb + hb) * CB;
       // raw q and k rows lane and lane+64 of key head bg; v and z of this lane's column (HB == 2:
       // also the second half's v and z, which wave 0 hands to wave 1 through LDS)
-      constexpr int NU = 4 + 2 * HB;
+      constexpr int NU = 2 * NQK + 2 * HB;
       float val[NU];
 #pragma unroll
       for (int i = 0; i < NU; ++i) val[i] = 0.f;
       if (hb == 0) {
-        const int qo = g.bg * DK + lane;
+        const int qo = g.bg * DKT + lane;
         int off[NU];
-        off[0] = qo; off[1] = qo + 64; off[2] = QK + qo; off[3] = QK + qo + 64;
-        off[4] = 2 * QK + vcol + jc; off[5] = C + vcol + jc;
+#pragma unroll
+        for (int j = 0; j < NQK; ++j) {
+          off[j] = qo + 64 * j;
+          off[NQK + j] = QK + qo + 64 * j;
+        }
+        off[VI] = 2 * QK + vcol + jc; off[ZI] = C + vcol + jc;
         if constexpr (HB == 2) {
-          off[6] = 2 * QK + vcol + CB + jc;
-          off[7] = C + vcol + CB + jc;
+          off[VI + 2] = 2 * QK + vcol + CB + jc;
+          off[VI + 3] = C + vcol + CB + jc;
         }
         // the poll starts at once: waiting for this workgroup's own phase A first measured slower
         DN_MARK(a, l, 10);
@@ -969,14 +985,15 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
       if (__all(ok)) {
         // this wave's own LDS writes are visible to its later LDS reads (in-order LDS queue)
         if (hb == 0) {
-          sm.qk[lane] = val[0];
-          sm.qk[lane + 64] = val[1];
-          sm.qk[DK + lane] = val[2];
-          sm.qk[DK + lane + 64] = val[3];
+#pragma unroll
+          for (int j = 0; j < NQK; ++j) {
+            sm.qk[lane + 64 * j] = val[j];
+            sm.qk[DKT + lane + 64 * j] = val[NQK + j];
+          }
           if constexpr (HB == 2) {
             if (pr == 0) {
-              sm.vz[jc] = val[6];
-              sm.vz[CB + jc] = val[7];
+              sm.vz[jc] = val[VI + 2];
+              sm.vz[CB + jc] = val[VI + 3];
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): q, k, v, z are in LDS before the count
             asm volatile("" ::: "memory");
@@ -985,12 +1002,13 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
         } else if constexpr (HB == 2) {
           wait_counter(&sm.v_ready, l + 1, &sm.abort_flag);  // wave 0 has the inputs in LDS
           asm volatile("" ::: "memory");
-          val[0] = sm.qk[lane];
-          val[1] = sm.qk[lane + 64];
-          val[2] = sm.qk[DK + lane];
-          val[3] = sm.qk[DK + lane + 64];
-          val[4] = sm.vz[jc];
-          val[5] = sm.vz[CB + jc];
+#pragma unroll
+          for (int j = 0; j < NQK; ++j) {
+            val[j] = sm.qk[lane + 64 * j];
+            val[NQK + j] = sm.qk[DKT + lane + 64 * j];
+          }
+          val[VI] = sm.vz[jc];
+          val[ZI] = sm.vz[CB + jc];
         }
         DN_MARK(a, l, 11);
         float alpha = sm.gate[l][0], beta = sm.gate[l][1];
@@ -1000,10 +1018,10 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
           alpha = sm.gval[0];
           beta = sm.gval[1];
         }
-        const v4f* Q4 = reinterpret_cast<const v4f*>(sm.qk + 32 * pr);
-        const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DK + 32 * pr);
-        const v4f* A4 = reinterpret_cast<const v4f*>(&apk[PK ? l : 0][32 * pr]);
-        float sv[32];
+        const v4f* Q4 = reinterpret_cast<const v4f*>(sm.qk + RPL * pr);
+        const v4f* K4 = reinterpret_cast<const v4f*>(sm.qk + DKT + RPL * pr);
+        const v4f* A4 = reinterpret_cast<const v4f*>(&apk[PK ? l : 0][RPL * pr]);
+        float sv[RPL];
         float kvp = 0.f, qvp = 0.f, kqp = 0.f;
         wait_counter(&sm.s_ready, NCW * (l + 1), &sm.abort_flag);  // the slice has landed in LDS
         // the sums run over the raw q and k; the 1/norm factors multiply the finished sums (and the
@@ -1011,7 +1029,7 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
         // over the updated state, (S' )^T q = (decayed S)^T q + delta (k . q), takes its sums in the
         // same pass, so it is published before the update of the slice.
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < RPL / 4; ++q) {
           const v4f kk = K4[q], qq = Q4[q], st = sm.sbuf[hb][64 * q + lane];
           v4f av = {alpha, alpha, alpha, alpha};  // decay of rows 32 pr + 4 q ..
           if constexpr (PK) av = A4[q];
@@ -1024,15 +1042,21 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
           }
         }
         // L2 norms in double, eps inside the sqrt (independent of the loop above, so the two overlap)
-        const double sq = wave_total_d((double)val[0] * val[0] + (double)val[1] * val[1]);
-        const double sk = wave_total_d((double)val[2] * val[2] + (double)val[3] * val[3]);
+        double sq0 = 0.0, sk0 = 0.0;
+#pragma unroll
+        for (int j = 0; j < NQK; ++j) {
+          sq0 += (double)val[j] * val[j];
+          sk0 += (double)val[NQK + j] * val[NQK + j];
+        }
+        const double sq = wave_total_d(sq0);
+        const double sk = wave_total_d(sk0);
         const float qn = (float)((double)a.q_scale / sqrt(sq + (double)a.eps_l2));
         const float kn = (float)(1.0 / sqrt(sk + (double)a.eps_l2));
         const float kv = kn * quad_sum(kvp);  // (decayed S)^T k^ of column jc
-        const float dk = beta * (val[4] - kv) * kn;  // delta times 1/|k|
+        const float dk = beta * (val[VI] - kv) * kn;  // delta times 1/|k|
         DN_MARK(a, l, 13);
         const float o = qn * fmaf(dk, quad_sum(kqp), quad_sum(qvp));
-        const float gt = sm.nw[l][hb * CB + jc] * o * silu(val[5]);
+        const float gt = sm.nw[l][hb * CB + jc] * o * silu(val[ZI]);
         const float osq = wave_total_f(pr == 0 ? o * o : 0.f);
         DN_MARK(a, l, 15);
         // G buffer: NCM segments of [V/NCM gated columns | partials of the same heads]
@@ -1060,7 +1084,7 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
         // the delta rule write, after the readout is out; the slice is parked in LDS and written
         // back while phase C runs
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < RPL / 4; ++q) {
           const v4f kk = K4[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) sv[4 * q + e] = fmaf(kk[e], dk, sv[4 * q + e]);
@@ -1105,9 +1129,10 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
       if (cw == 0) DN_MARK(a, l, 6);
       // per-head sums of the partials: head h's nblk partials sit in nblk / HB consecutive lanes
       {
-        static_assert(nblk == 8, "");
+        static_assert(nblk == 8 || (nblk == 16 && HB == 1), "");
         if constexpr (HB == 1) {
-          const float sp = oct_sum(gv[GW]);
+          float sp = oct_sum(gv[GW]);
+          if constexpr (nblk == 16) sp += __int_as_float(dpp_i<0x140>(__float_as_int(sp)));  // mirrored row of 16
           if ((lane % nblk) == 0 && lane < pn) sm.inv[(pbase + lane) / nblk] = rsqrtf(sp / (float)DV + a.eps_rms);
         } else {
           const float sp = quad_sum(gv[GW] + gv[GW + 1]);
@@ -1135,12 +1160,12 @@ __device__ __forceinline__ void comm_role(SmemT<HB>& sm, float (*apk)[DK], const
   }
 }
 
-template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT, int HB>
+template <int BITS, int NCHA, int NCHC, int RA, int RC, bool PK, bool GT, int HB, int DKT = DK>
 __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   constexpr int COLS_PER_CHUNK = BITS == 8 ? 1024 : 2048;
   constexpr int D = COLS_PER_CHUNK * NCHA;
-  constexpr int nblk = 128 / CB;
-  __shared__ SmemT<HB> sm;
+  constexpr int nblk = DKT / CB;  // column blocks per value head (dv = dk)
+  __shared__ SmemT<HB, DKT> sm;
   __shared__ float apk[PK ? PK_MAXL : 1][DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NWG = gridDim.x, wg = blockIdx.x;
@@ -1181,10 +1206,10 @@ __global__ __launch_bounds__(NTHR) void k_persist(const PersistArgs a) {
   // go to the other ones.
   if (!skip) {
     if (wave < NCW)
-      compute_role<BITS, NCHA, NCHC, RA, RC, PK, GT, HB>(sm, a, g, base_tag, a.S[par], a.S[par ^ 1u], a.ring[par],
+      compute_role<BITS, NCHA, NCHC, RA, RC, PK, GT, HB, DKT>(sm, a, g, base_tag, a.S[par], a.S[par ^ 1u], a.ring[par],
                                                      a.ring[par ^ 1u], tid, lane);
     else
-      comm_role<BITS, NCHA, NCHC, PK, GT, HB>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
+      comm_role<BITS, NCHA, NCHC, PK, GT, HB, DKT>(sm, apk, a, g, base_tag, tid, lane, wave - NCW, wg);
   }
 
 #ifdef DN_PHASE_TIMERS
@@ -1225,6 +1250,11 @@ hipError_t launch_one(F kern, const PersistArgs& a, int nwg, bool coop, hipStrea
 hipError_t go_hb2(const PersistArgs& a, int nwg, bool coop, hipStream_t st) {
   return launch_one(k_persist<8, 2, 6, 8, 1, false, false, 2>, a, nwg, coop, st);
 }
+// heads of 256 (dk = dv = 256) over d_model 2048 (8-bit), value width 4096: 256 x 16 state slices,
+// 64 key rows per lane of the phase-B wave, caller-given scalar decays
+hipError_t go_dk256(const PersistArgs& a, int nwg, bool coop, hipStream_t st) {
+  return launch_one(k_persist<8, 2, 4, 6, 1, false, false, 1, 256>, a, nwg, coop, st);
+}
 
 template <int BITS, int NCHA, int NCHC>
 hipError_t go(const PersistArgs& a, int nwg, bool coop, hipStream_t st) {
@@ -1260,8 +1290,18 @@ static bool hb2_shape(const PersistShape& s, int nwg) {
   return (a_per_wg + NCW - 1) / NCW <= 8 && (c_per_wg + NCW - 1) / NCW <= 1;
 }
 
+// The heads-of-256 instantiation's shape: 8-bit weights, d_model 2048, value width 4096, dk = dv = 256,
+// caller-given scalar decays, one 256 x 16 slice per workgroup.
+static bool dk256_shape(const PersistShape& s, int nwg) {
+  if (s.batch != 1 || s.dk != 256 || s.dv != 256 || s.K < 1 || s.K > 4 || s.bits != 8) return false;
+  if (s.alpha_per_key || s.gates) return false;
+  if (chunks(s.D, s.bits) != 2 || chunks(s.V, s.bits) != 4 || (s.Hv % NCM) || s.Hv * (s.dv / CB) > nwg) return false;
+  const int a_per_wg = (s.R + nwg - 1) / nwg, c_per_wg = (s.D + nwg - 1) / nwg;
+  return (a_per_wg + NCW - 1) / NCW <= 6 && (c_per_wg + NCW - 1) / NCW <= 1;
+}
+
 bool persist_supported(const PersistShape& s, int nwg) {
-  if (hb2_shape(s, nwg)) return true;
+  if (hb2_shape(s, nwg) || dk256_shape(s, nwg)) return true;
   if (s.batch != 1 || s.dk != DK || s.dv != 128 || s.K < 1 || s.K > 4) return false;
   if (s.alpha_per_key && s.L > PK_MAXL) return false;
   if (s.alpha_per_key && s.gates) return false;
@@ -1282,6 +1322,8 @@ hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu) {
   const bool pk = s.alpha_per_key != 0, gt = s.gates != 0;
   if (s.bits == 8 && na == 2 && nc == 6)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_persist<8, 2, 6, 8, 1, false, false, 2>, NTHR, 0);
+  if (s.dk == 256)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k_persist<8, 2, 4, 6, 1, false, false, 1, 256>, NTHR, 0);
   if (s.bits == 8) return na == 2 ? occ<8, 2, 4>(blocks_per_cu, pk, gt) : occ<8, 1, 1>(blocks_per_cu, pk, gt);
   return nc == 2 ? occ<4, 1, 2>(blocks_per_cu, pk, gt) : occ<4, 1, 1>(blocks_per_cu, pk, gt);
 }
@@ -1289,6 +1331,7 @@ hipError_t persist_occupancy(const PersistShape& s, int* blocks_per_cu) {
 hipError_t launch_persist(const PersistArgs& a, const PersistShape& s, int nwg, bool coop, hipStream_t st) {
   const int na = chunks(s.D, s.bits), nc = chunks(s.V, s.bits);
   if (s.bits == 8 && na == 2 && nc == 6) return go_hb2(a, nwg, coop, st);
+  if (s.dk == 256) return go_dk256(a, nwg, coop, st);
   if (s.bits == 8) return na == 2 ? go<8, 2, 4>(a, nwg, coop, st) : go<8, 1, 1>(a, nwg, coop, st);
   return nc == 2 ? go<4, 1, 2>(a, nwg, coop, st) : go<4, 1, 1>(a, nwg, coop, st);
 }

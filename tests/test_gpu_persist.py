@@ -39,6 +39,11 @@ PERSIST = {
                            n_tokens=6, flags=gi.DN_X_RMSNORM, ring_std=1.0),
     "p_heads48_conv2": gi.custom("p_h48c2", d_model=2048, n_k_heads=16, d_k=128, n_v_heads=48, d_v=128,
                                  n_layers=2, conv_k=2, n_tokens=5, ring_std=1.0),
+    # heads of 256 (8 key and 16 value heads) at d_model 2048: 256 x 16 state slices, 64 key rows per lane
+    "p_dim256": gi.custom("p_d256", d_model=2048, n_k_heads=8, d_k=256, n_v_heads=16, d_v=256, n_layers=3,
+                          n_tokens=6, flags=gi.DN_X_RMSNORM, ring_std=1.0),
+    "p_dim256_conv3": gi.custom("p_d256c3", d_model=2048, n_k_heads=8, d_k=256, n_v_heads=16, d_v=256,
+                                n_layers=2, conv_k=3, n_tokens=5, ring_std=1.0, q_scale=0.0625),
 }
 
 
@@ -70,7 +75,7 @@ def test_persist_parity(name, capfd, monkeypatch):
     assert e <= OUT_TOL and es <= STATE_TOL and eh <= STATE_TOL
 
 
-@pytest.mark.parametrize("name", ["p_small", "p_heads48"])
+@pytest.mark.parametrize("name", ["p_small", "p_heads48", "p_dim256"])
 def test_persist_agrees_with_layer_kernels(name, monkeypatch):
     cfg = PERSIST[name]
     layers, stream = gi.generate(cfg)
