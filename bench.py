@@ -36,7 +36,7 @@ def bench_config(gi, name):
         return stack.replace(name=name, flags=gi.DN_X_RMSNORM | gi.DN_ALPHA_PER_KEY)
     if name == "stack_gates":  # the gates computed on the card
         return stack.replace(name=name, flags=gi.DN_X_RMSNORM | gi.DN_GATES_ON_DEVICE)
-    if name == "stack_heads48":  # 48 value heads over the 16 key heads (more than the whole-stack kernel takes)
+    if name == "stack_heads48":  # 48 value heads over the 16 key heads (the whole-stack kernel's two-wave form)
         return stack.replace(name=name, n_v_heads=48)
     if name == "stack_dim256":  # heads of 256: 8 key heads and 16 value heads of 256 columns
         return stack.replace(name=name, n_k_heads=8, d_k=256, n_v_heads=16, d_v=256)
